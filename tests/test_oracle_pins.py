@@ -1,0 +1,273 @@
+"""Pins of the fp64 oracle against values and closed forms the pages fix.
+
+Each test names the page and section its value comes from.  None of these
+retypes an oracle formula: they use printed worked examples, derived closed
+forms, invariants or independent numerical facts.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import json
+import os
+
+import oracle
+from decoder_only_transformer_train_amd import synthetic
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_examples.json")))
+
+
+# ---- "Chapter 28 Data, evaluation and resume", 28.3: the B=2, T=3 example ----
+
+def test_make_batch_worked_example():
+    g = GOLD["batch_example"]
+    x, y = oracle.make_batch(np.array(g["buffer"]), 0, B=g["B"], T=g["T"])
+    assert x.tolist() == g["x"]
+    assert y.tolist() == g["y"]
+
+
+def test_make_batch_rank_offsets():
+    # R = 2 ranks: rank 0 reads inputs 0..5, rank 1 reads 6..11; next windows at 12 and 18
+    g = GOLD["rank_offsets"]
+    stream = np.arange(100)
+    B, T, R = g["B"], g["T"], g["R"]
+    starts = [B * T * r for r in range(R)]
+    xs = [oracle.make_batch(stream, s, B, T)[0].reshape(-1).tolist() for s in starts]
+    assert xs == g["inputs"]
+    nxt = [oracle.next_start(s, len(stream), B, T, rank=r, world=R) for r, s in enumerate(starts)]
+    assert nxt == g["next"]
+
+
+def test_make_batch_24_tokens_as_4x6():
+    # lecture, data loader: 24 tokens viewed as 4 rows of 6, targets one position later
+    x, y = oracle.make_batch(np.arange(100, 125), 0, B=4, T=6)
+    assert x.shape == (4, 6)
+    assert x[0].tolist() == list(range(100, 106)) and x[3].tolist() == list(range(118, 124))
+    assert (y == x + 1).all()
+
+
+def test_make_batch_wrap_and_range():
+    n = 20
+    B, T = 2, 3
+    pos = 0
+    seen = []
+    for _ in range(5):
+        seen.append(pos)
+        oracle.make_batch(np.arange(n), pos, B, T)  # never raises along the cursor
+        pos = oracle.next_start(pos, n, B, T)
+    # windows of 7 tokens advance by 6; 0, 6, 12 fit (12 + 6 + 1 <= 20), 18 does not
+    assert seen == [0, 6, 12, 0, 6]
+    with pytest.raises(ValueError):
+        oracle.make_batch(np.arange(n), 14, B, T)
+
+
+# ---- CS336 pretraining page, section 1 (cross-entropy) ----
+
+def test_ce_probability_0_1_and_0_8():
+    # uniform over 10 classes: p = 0.1 -> about 2.30; logits [ln 8, 0, 0]: p = 0.8 -> about 0.22
+    l1, _ = oracle.cross_entropy_rows(np.zeros((1, 10)), np.array([3]))
+    l2, _ = oracle.cross_entropy_rows(np.array([[math.log(8.0), 0.0, 0.0]]), np.array([0]))
+    g = GOLD["cross_entropy"]
+    assert round(float(l1[0]), 2) == g["p_0_1"]
+    assert round(float(l2[0]), 2) == g["p_0_8"]
+    # perplexity exp(L) at L = 2: the page prints about 7.39
+    # two classes, logits [0, ln(e^2 - 1)], target class 0: the loss is exactly 2
+    l2x, _ = oracle.cross_entropy_rows(np.array([[0.0, math.log(math.e ** 2 - 1)]]), np.array([0]))
+    assert abs(float(l2x[0]) - 2.0) < 1e-14
+    assert round(math.exp(float(l2x[0])), 2) == g["ppl_at_2"]
+    assert abs(float(l1[0]) - math.log(10.0)) < 1e-15
+    assert abs(float(l2[0]) + math.log(0.8)) < 1e-15
+
+
+def test_ce_shift_invariance_and_large_logits():
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((5, 17)) * 3
+    y = rng.integers(0, 17, 5)
+    a, _ = oracle.cross_entropy_rows(z, y)
+    b, _ = oracle.cross_entropy_rows(z + 1234.5, y)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-11)
+    # max subtraction keeps exp finite for logits far beyond exp's range
+    c, _ = oracle.cross_entropy_rows(z * 1000.0, y)
+    assert np.isfinite(c).all()
+
+
+def test_uniform_logits_give_ln_v():
+    # lecture: near-uniform predictions start the loss at about ln(V)
+    for V in (256, 50257, 50304):
+        X = np.zeros((3, 8))
+        W = np.random.default_rng(0).standard_normal((V, 8))
+        loss, _, _, _ = oracle.lmhead_ce(X, W, np.array([0, 1, V - 1]))
+        assert abs(loss - math.log(V)) < 1e-12
+
+
+def test_lmhead_dX_dW_against_bruteforce_fd():
+    rng = np.random.default_rng(7)
+    N, V, C = 4, 9, 5
+    X = rng.standard_normal((N, C))
+    W = rng.standard_normal((V, C)) * 0.5
+    y = rng.integers(0, V, N)
+    loss, _, dX, dW = oracle.lmhead_ce(X, W, y)
+    h = 1e-6
+    for (i, j) in [(0, 0), (3, 4), (2, 1)]:
+        Xp, Xm = X.copy(), X.copy()
+        Xp[i, j] += h
+        Xm[i, j] -= h
+        fd = (oracle.lmhead_ce(Xp, W, y)[0] - oracle.lmhead_ce(Xm, W, y)[0]) / (2 * h)
+        assert abs(fd - dX[i, j]) < 1e-8
+    for (i, j) in [(0, 0), (8, 4), (int(y[0]), 2)]:
+        Wp, Wm = W.copy(), W.copy()
+        Wp[i, j] += h
+        Wm[i, j] -= h
+        fd = (oracle.lmhead_ce(X, Wp, y)[0] - oracle.lmhead_ce(X, Wm, y)[0]) / (2 * h)
+        assert abs(fd - dW[i, j]) < 1e-8
+
+
+def test_initial_loss_near_ln_v_tiny_model():
+    # lecture: the loss at initialisation should be close to ln V.  Logits at init are
+    # near-Gaussian with variance C * 0.02^2, which adds about sigma^2 / 2.
+    p = synthetic.init_params(2, 64, 256, 32, seed=0)
+    toks = synthetic.uniform_tokens(4 * 32 + 1, 256, seed=0)
+    x, y = oracle.make_batch(toks, 0, 4, 32)
+    loss, _, _ = oracle.forward(p, x, y, n_head=4, keep=False)
+    assert abs(loss - math.log(256)) < 0.1
+    assert abs(loss - (math.log(256) + 64 * 0.02 ** 2 / 2)) < 0.05
+
+
+# ---- CS336 page, section 4 (resource accounting) ----
+
+def test_forward_flops_xl_swiglu_example():
+    # V=50257, D=1600, L=48, H=25, S=1024, d_ff=4288: about 3.52 TFLOP per sequence
+    g = GOLD["forward_flops"]
+    D, dff = g["D"], g["d_ff"]
+    f = oracle.forward_matmul_flops(g["S"], D, g["L"], g["V"], 4 * D * D + 3 * D * dff)
+    assert round(f / 1e12, 2) == g["tflop"]
+    # training = 3 x forward
+    seconds = g["batch"] * g["steps"] * 3 * f / (g["mfu"] * g["peak_tflops"] * 1e12)
+    assert round(seconds / 3600, -1) == g["hours"]
+    assert round(seconds / 86400) == g["days"]
+
+
+def test_state_bytes_tinystories_example():
+    # 22.70M params -> about 363 MB for fp32 params + grads + m + v
+    g = GOLD["state_memory"]
+    n = g["params"]
+    assert round(oracle.state_bytes(n) / 1e6, 2) == g["mb"]
+    saved = 10_000 * 512  # tying removes one V x D matrix (V=10000, D=512)
+    assert round(saved / 1e6, 2) == g["tie_saved_params_m"]
+    assert round(oracle.state_bytes(saved) / 1e6, 2) == g["tie_saved_mb"]
+    assert round(100 * saved / n, 1) == g["tie_saved_pct"]
+
+
+def test_gpt2_124m_parameter_count_and_embedding():
+    # lecture: the smallest GPT-2 has about 124M parameters; the shared embedding about 40M
+    g = GOLD["gpt2_small"]
+    lay = synthetic.tensor_layout(g["L"], g["C"], g["V"], g["T"])
+    n = sum(int(np.prod(s)) for _, s, _ in lay)
+    assert round(n / 1e6) == g["params_m"]
+    assert round(g["V"] * g["C"] / 1e7) == g["embedding_elems_1e7"]
+
+
+def test_training_flops_convention_124m():
+    f = oracle.training_flops_per_token(12, 768, 1024, 50304)
+    assert abs(f / 7.98e8 - 1) < 1e-3
+
+
+# ---- CS336 page, section 2 (AdamW) ----
+
+B1, B2, EPS, LR, WD = 0.9, 0.95, 1e-8, 6e-4, 0.1
+
+
+def test_adamw_first_step_closed_form():
+    # at t=1: m=(1-b1)g, v=(1-b2)g^2, so the move is lr*g/(|g| + eps/sqrt(1-b2)) plus decay
+    g = np.array([0.3, -2.0, 1e-9, 5.0])
+    p = np.array([1.0, -0.5, 0.25, 0.0])
+    p1, _, _ = oracle.adamw_update(p, g, 0 * g, 0 * g, 1, LR, B1, B2, EPS, WD)
+    expect = p * (1 - LR * WD) - LR * g / (np.abs(g) + EPS / math.sqrt(1 - B2))
+    np.testing.assert_allclose(p1, expect, rtol=1e-13, atol=1e-18)
+
+
+def test_adamw_constant_gradient_every_step():
+    g = np.array([0.7, -1e-3])
+    p = np.zeros(2)
+    m = np.zeros(2)
+    v = np.zeros(2)
+    for t in range(1, 30):
+        p_prev = p
+        p, m, v = oracle.adamw_update(p, g, m, v, t, LR, B1, B2, EPS, 0.0)
+        step = p_prev - p
+        expect = LR * g / (np.abs(g) + EPS / math.sqrt(1 - B2 ** t))
+        np.testing.assert_allclose(step, expect, rtol=1e-9)
+
+
+def test_adamw_zero_grad_is_pure_decoupled_decay():
+    p = np.array([2.0, -3.0])
+    z = np.zeros(2)
+    p1, _, _ = oracle.adamw_update(p, z, z, z, 5, LR, B1, B2, EPS, WD, decay=True)
+    np.testing.assert_array_equal(p1, p * (1 - LR * WD))
+    p2, _, _ = oracle.adamw_update(p, z, z, z, 5, LR, B1, B2, EPS, WD, decay=False)
+    np.testing.assert_array_equal(p2, p)
+
+
+def test_decay_groups_matrices_only():
+    lay = synthetic.tensor_layout(2, 8, 16, 4)
+    got = {n: oracle.decays(n, s) for n, s, _ in lay}
+    assert got["wte"] and got["wpe"] and got["h0.attn.w"] and got["h1.mlp_proj.w"]
+    assert not got["h0.attn.b"] and not got["h0.ln1.g"] and not got["lnf.b"]
+
+
+def _quadratic_theta():
+    import torch
+    torch.manual_seed(42)
+    return (5 * torch.randn(10, 10)).double().numpy()
+
+
+def test_quadratic_table_sgd_decay():
+    # CS336 page, section 2 (SGD): mean of squares over 100 numbers, loss 24.17 at init;
+    # ten updates give 19.75 (lr 1) and 2.85 (lr 10); lr 100 reaches zero at the 4th update.
+    g = GOLD["quadratic"]
+    th0 = _quadratic_theta()
+    assert round(float((th0 ** 2).mean()), 2) == g["loss0"]
+    for lr, want in ((float(k), v) for k, v in g["after10"].items()):
+        th = th0.copy()
+        for t in range(10):
+            th = th - lr / math.sqrt(t + 1) * (2 * th / th.size)
+        assert round(float((th ** 2).mean()), 2) == want
+    # constant-lr first-update factors 0.8 / -1 / -19 and the x361 loss
+    for lr, fac in ((int(k), v) for k, v in g["factors"].items()):
+        th1 = th0 - lr * (2 * th0 / th0.size)
+        np.testing.assert_allclose(th1, fac * th0, rtol=1e-12)
+    th1 = th0 - 1000 * (2 * th0 / th0.size)
+    assert round(float((th1 ** 2).mean() / (th0 ** 2).mean())) == g["loss_ratio_1000"]
+    th = th0.copy()
+    for t in range(g["zero_at_update_lr100"]):
+        th = th - 100 / math.sqrt(t + 1) * (2 * th / th.size)
+    assert float((th ** 2).mean()) < 1e-20
+
+
+def test_adamw_on_quadratic_bounded_and_decreasing():
+    th = _quadratic_theta().reshape(-1)
+    m = np.zeros_like(th)
+    v = np.zeros_like(th)
+    losses = [float((th ** 2).mean())]
+    lr = 0.05
+    for t in range(1, 21):
+        g = 2 * th / th.size
+        new, m, v = oracle.adamw_update(th, g, m, v, t, lr, B1, B2, EPS, 0.0)
+        # AdamW moves each coordinate by at most about lr per step
+        assert np.abs(new - th).max() <= 1.2 * lr
+        th = new
+        losses.append(float((th ** 2).mean()))
+    assert all(b < a for a, b in zip(losses, losses[1:]))
+
+
+# ---- gradient clipping (lecture; CS336 section 2; Zero page training loop) ----
+
+def test_clip_scales_to_threshold_and_keeps_direction():
+    g = {"a": np.array([3.0, 4.0]), "b": np.array([[12.0]])}  # global norm 13
+    c, n = oracle.clip_grads(g, 1.0)
+    assert n == 13.0
+    assert abs(oracle.grad_norm(c) - 13.0 / (13.0 + 1e-6)) < 1e-15
+    np.testing.assert_allclose(c["a"] / c["b"][0, 0], g["a"] / 12.0)
+    c2, _ = oracle.clip_grads(g, 100.0)
+    np.testing.assert_array_equal(c2["a"], g["a"])
