@@ -1,0 +1,43 @@
+"""Named model / batch configurations of the GPT-2 training step."""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+from . import binding
+
+
+@dataclass(frozen=True)
+class GPTConfig:
+    n_layer: int
+    n_embd: int
+    n_head: int
+    vocab: int
+    padded_vocab: int
+    max_seq: int
+    batch: int
+    seq: int
+    dtype: int = binding.GPT_BF16
+    accum: int = 1  # micro-steps per optimiser step
+
+    def to_c(self) -> binding.GPTConfigC:
+        return binding.GPTConfigC(self.n_layer, self.n_embd, self.n_head, self.vocab, self.padded_vocab,
+                                  self.max_seq, self.batch, self.seq, self.dtype)
+
+    def with_(self, **kw) -> "GPTConfig":
+        return replace(self, **kw)
+
+    @property
+    def tokens_per_step(self) -> int:
+        return self.batch * self.seq * self.accum
+
+
+# the lecture's GPT-2 small: 12 layers, width 768, 12 heads, 50257 tokens padded to 50304, 1024 positions
+TINY_F32 = GPTConfig(2, 64, 4, 256, 256, 32, 4, 32, binding.GPT_F32)
+GPT2_124M = GPTConfig(12, 768, 12, 50257, 50304, 1024, 16, 1024, binding.GPT_BF16)
+GPT2_350M = GPTConfig(24, 1024, 16, 50257, 50304, 1024, 8, 1024, binding.GPT_BF16)
+GPT2_1P5B = GPTConfig(48, 1600, 25, 50257, 50304, 1024, 4, 1024, binding.GPT_BF16, accum=4)
+
+PRESETS = {"tiny": TINY_F32, "gpt2-124m": GPT2_124M, "gpt2-350m": GPT2_350M, "gpt2-1.5b": GPT2_1P5B}
+
+# AdamW settings of the step (lecture: GPT-3 small peak lr 6e-4; betas (0.9, 0.95), eps 1e-8, wd 0.1)
+ADAMW = dict(lr=6e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)

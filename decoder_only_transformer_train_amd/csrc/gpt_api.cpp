@@ -1,0 +1,788 @@
+// Host side of libgpt.so: configuration, arena layout, launch sequences of
+// the training step, tensor access and kernel timing.  See include/gpt.h.
+#include "gpt.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err = "no error";
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIPCHK(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(GPT_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_));        \
+  } while (0)
+
+constexpr int RING = 4096;
+constexpr int64_t ALIGN = 256;
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct TensorDesc {
+  std::string name;
+  int64_t rows, cols;  // cols == 0: vector of `rows`
+  int decays;
+  int kind;            // 0: N(0,0.02), 1: N(0,0.02/sqrt(2L)), 2: zero, 3: one
+  int64_t off;         // element offset in the flat parameter buffer
+  int64_t numel() const { return cols ? rows * cols : rows; }
+};
+
+// Bump allocator over the arena; with base == nullptr it only measures.
+struct Carver {
+  char* base;
+  int64_t used = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename P> P* take(int64_t bytes) {
+    used = align_up(used, ALIGN);
+    P* p = base ? reinterpret_cast<P*>(base + used) : nullptr;
+    used += bytes;
+    return p;
+  }
+};
+
+struct Layer {
+  void* ln1;  // T [N][C]
+  float *mu1, *rs1;
+  void* qkv;  // T [N][3C]
+  void* att;  // T [N][C]
+  float* lse; // [B][H][T] (log2 domain)
+  float* res_mid;  // f32 [N][C]
+  void* ln2;
+  float *mu2, *rs2;
+  void* fcpre;  // T [N][4C]
+  void* fcact;  // T [N][4C]
+};
+
+struct Prof {
+  std::string cls;
+  std::vector<hipEvent_t> ev;  // start/stop pairs
+  size_t used = 0;
+  double flops = 0, bytes = 0;
+  int64_t launches = 0;
+};
+
+}  // namespace
+
+struct gpt_ctx {
+  gpt_config cfg;
+  hipStream_t stream;
+  int dt, es;  // dtype, element size of T
+  int64_t N, C, L, H, D, V, Vp, T, B;
+  std::vector<TensorDesc> tensors;  // logical (ABI) order
+  int64_t P, P_decay;               // flat parameter floats
+  float *params, *grads, *m, *v;
+  void* shadow;  // bf16 copy of params (bf16 mode) or null
+  int32_t* win;  // [N + 1] tokens
+  std::vector<float*> res;  // L + 1 residual streams
+  std::vector<Layer> layers;
+  void* lnf;
+  float *muf, *rsf;
+  // head
+  int64_t ldv, Nc;
+  float* logits;  // f32 [Nc][ldv]
+  void* dz;       // T [Nc][ldv]
+  float *tok_loss, *tok_lse, *dF, *loss;
+  float* ring;
+  int ring_wr = 0, ring_rd = 0;
+  // backward
+  float *dres, *dln;
+  void *dresT, *dfc, *datt, *dqkv;
+  float *Dv, *ln_part, *col_part, *splitk_ws;
+  uint32_t* keys;
+  float *norm_part, *scal;
+  int* step_dev;
+  bool wte_fresh = true, others_fresh = true, have_fwd = false, fwd_grad = false;
+  float last_scale = 0.f;
+  Prof prof;
+  // parameter pointers by logical id
+  float* P_(int id) { return params + tensors[id].off; }
+  float* G_(int id) { return grads + tensors[id].off; }
+  const void* W_(int id) {  // GEMM operand view of a parameter
+    return shadow ? (const void*)((uint16_t*)shadow + tensors[id].off) : (const void*)(params + tensors[id].off);
+  }
+};
+
+namespace {
+
+enum { T_WTE = 0, T_WPE = 1 };
+inline int tid(int l, int k) { return 2 + 12 * l + k; }  // k: 0 ln1.g .. 11 mlp_proj.b
+enum { K_LN1G, K_LN1B, K_ATTW, K_ATTB, K_PROJW, K_PROJB, K_LN2G, K_LN2B, K_FCW, K_FCB, K_MPW, K_MPB };
+inline int tid_lnf(int L, int k) { return 2 + 12 * L + k; }
+
+int check_cfg(const gpt_config* c) {
+  if (!c) return fail(GPT_EINVAL, "null config");
+  if (c->dtype != GPT_F32 && c->dtype != GPT_BF16) return fail(GPT_EINVAL, "dtype must be GPT_F32 or GPT_BF16");
+  if (c->n_layer < 1 || c->n_embd < 64 || c->n_head < 1 || c->vocab < 1 || c->batch < 1 || c->seq < 1)
+    return fail(GPT_EINVAL, "sizes must be positive (n_embd >= 64)");
+  if (c->n_embd % 64 != 0 || c->n_embd > 2048) return fail(GPT_EINVAL, "n_embd must be a multiple of 64, <= 2048");
+  if (c->n_embd % c->n_head != 0) return fail(GPT_EINVAL, "n_embd % n_head != 0");
+  const int D = c->n_embd / c->n_head;
+  if (c->dtype == GPT_BF16 && D != 64) return fail(GPT_EINVAL, "bf16 head size must be 64");
+  if (c->dtype == GPT_F32 && D != 16 && D != 32 && D != 64) return fail(GPT_EINVAL, "fp32 head size must be 16, 32 or 64");
+  if (c->padded_vocab < c->vocab) return fail(GPT_EINVAL, "padded_vocab < vocab");
+  if (c->seq > c->max_seq) return fail(GPT_EINVAL, "seq > max_seq");
+  const int64_t N = (int64_t)c->batch * c->seq;
+  if (N > 16384) return fail(GPT_EINVAL, "batch * seq must be <= 16384");
+  int shift = 0;
+  while ((1 << shift) < N) ++shift;
+  if (((uint64_t)c->padded_vocab << shift) > 0xFFFFFFFFull) return fail(GPT_EINVAL, "padded_vocab too large for this batch");
+  return 0;
+}
+
+std::vector<TensorDesc> make_tensors(const gpt_config* c, int64_t* P, int64_t* P_decay) {
+  const int64_t C = c->n_embd, L = c->n_layer;
+  std::vector<TensorDesc> t;
+  auto add = [&](const std::string& n, int64_t r, int64_t cc, int dec, int kind) {
+    t.push_back(TensorDesc{n, r, cc, dec, kind, 0});
+  };
+  add("wte", c->padded_vocab, C, 1, 0);
+  add("wpe", c->max_seq, C, 1, 0);
+  for (int64_t l = 0; l < L; ++l) {
+    const std::string p = "h" + std::to_string(l) + ".";
+    add(p + "ln1.g", C, 0, 0, 3);
+    add(p + "ln1.b", C, 0, 0, 2);
+    add(p + "attn.w", 3 * C, C, 1, 0);
+    add(p + "attn.b", 3 * C, 0, 0, 2);
+    add(p + "proj.w", C, C, 1, 1);
+    add(p + "proj.b", C, 0, 0, 2);
+    add(p + "ln2.g", C, 0, 0, 3);
+    add(p + "ln2.b", C, 0, 0, 2);
+    add(p + "fc.w", 4 * C, C, 1, 0);
+    add(p + "fc.b", 4 * C, 0, 0, 2);
+    add(p + "mlp_proj.w", C, 4 * C, 1, 1);
+    add(p + "mlp_proj.b", C, 0, 0, 2);
+  }
+  add("lnf.g", C, 0, 0, 3);
+  add("lnf.b", C, 0, 0, 2);
+  // memory order: every decayed (2-D) tensor first, then the vectors
+  int64_t off = 0;
+  for (auto& d : t)
+    if (d.decays) { d.off = off; off += align_up(d.numel(), 64); }
+  *P_decay = off;
+  for (auto& d : t)
+    if (!d.decays) { d.off = off; off += align_up(d.numel(), 64); }
+  *P = off;
+  return t;
+}
+
+int64_t splitk_floats(int64_t N, int64_t C) {
+  int64_t best = 0;
+  const int64_t shapes[4][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}};
+  for (auto& s : shapes) {
+    const int sp = gk::gemm_pick_splits((int)s[0], (int)s[1], (int)N);
+    if (sp > 1) best = std::max(best, (int64_t)sp * s[0] * s[1]);
+  }
+  return best;
+}
+
+// Lays out (base == nullptr: measures) everything the context needs.
+int64_t carve(gpt_ctx* x, void* base) {
+  Carver cv(base);
+  const int64_t N = x->N, C = x->C, es = x->es;
+  x->params = cv.take<float>(x->P * 4);
+  x->grads = cv.take<float>(x->P * 4);
+  x->m = cv.take<float>(x->P * 4);
+  x->v = cv.take<float>(x->P * 4);
+  x->shadow = (x->dt == GPT_BF16) ? cv.take<void>(x->P * 2) : nullptr;
+  x->win = cv.take<int32_t>((N + 1) * 4);
+  x->res.assign(x->L + 1, nullptr);
+  for (auto& r : x->res) r = cv.take<float>(N * C * 4);
+  x->layers.assign(x->L, Layer{});
+  const int64_t nh = x->B * x->H * x->T;
+  for (auto& l : x->layers) {
+    l.ln1 = cv.take<void>(N * C * es);
+    l.mu1 = cv.take<float>(N * 4);
+    l.rs1 = cv.take<float>(N * 4);
+    l.qkv = cv.take<void>(N * 3 * C * es);
+    l.att = cv.take<void>(N * C * es);
+    l.lse = cv.take<float>(nh * 4);
+    l.res_mid = cv.take<float>(N * C * 4);
+    l.ln2 = cv.take<void>(N * C * es);
+    l.mu2 = cv.take<float>(N * 4);
+    l.rs2 = cv.take<float>(N * 4);
+    l.fcpre = cv.take<void>(N * 4 * C * es);
+    l.fcact = cv.take<void>(N * 4 * C * es);
+  }
+  x->lnf = cv.take<void>(N * C * es);
+  x->muf = cv.take<float>(N * 4);
+  x->rsf = cv.take<float>(N * 4);
+  x->logits = cv.take<float>(x->Nc * x->ldv * 4);
+  x->dz = cv.take<void>(x->Nc * x->ldv * es);
+  x->tok_loss = cv.take<float>(N * 4);
+  x->tok_lse = cv.take<float>(N * 4);
+  x->dF = cv.take<float>(N * C * 4);
+  x->loss = cv.take<float>(64);
+  x->ring = cv.take<float>(RING * 4);
+  x->dres = cv.take<float>(N * C * 4);
+  x->dln = cv.take<float>(N * C * 4);
+  x->dresT = cv.take<void>(N * C * es);
+  x->dfc = cv.take<void>(N * 4 * C * es);
+  x->datt = cv.take<void>(N * C * es);
+  x->dqkv = cv.take<void>(N * 3 * C * es);
+  x->Dv = cv.take<float>(nh * 4);
+  x->ln_part = cv.take<float>((int64_t)gk::layernorm_bwd_blocks((int)N) * 2 * C * 4);
+  x->col_part = cv.take<float>((int64_t)((N + 255) / 256) * 4 * C * 4);
+  x->splitk_ws = cv.take<float>(std::max<int64_t>(1, splitk_floats(N, C)) * 4);
+  x->keys = cv.take<uint32_t>(N * 4);
+  x->norm_part = cv.take<float>(gk::sumsq_blocks(x->P) * 4);
+  x->scal = cv.take<float>(64);
+  x->step_dev = cv.take<int>(64);
+  return align_up(cv.used, ALIGN);
+}
+
+void setup_dims(gpt_ctx* x, const gpt_config* c) {
+  x->cfg = *c;
+  x->dt = c->dtype;
+  x->es = (c->dtype == GPT_BF16) ? 2 : 4;
+  x->L = c->n_layer;
+  x->C = c->n_embd;
+  x->H = c->n_head;
+  x->D = x->C / x->H;
+  x->V = c->vocab;
+  x->Vp = c->padded_vocab;
+  x->T = c->seq;
+  x->B = c->batch;
+  x->N = x->B * x->T;
+  x->ldv = align_up(x->Vp, 64);
+  x->Nc = std::min<int64_t>(x->N, 4096);
+  x->tensors = make_tensors(c, &x->P, &x->P_decay);
+}
+
+// ---- profiling (HIP events around launches of one kernel class) ----
+struct ProfScope {
+  gpt_ctx* x;
+  bool on;
+  ProfScope(gpt_ctx* x_, const char* cls, double flops, double bytes) : x(x_) {
+    on = !x->prof.cls.empty() && (x->prof.cls == "any" || x->prof.cls == cls);
+    if (!on) return;
+    if (x->prof.used + 2 > x->prof.ev.size()) {
+      for (int i = 0; i < 64; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) { on = false; return; }
+        x->prof.ev.push_back(e);
+      }
+    }
+    (void)hipEventRecord(x->prof.ev[x->prof.used], x->stream);
+    x->prof.flops += flops;
+    x->prof.bytes += bytes;
+    x->prof.launches += 1;
+  }
+  ~ProfScope() {
+    if (!on) return;
+    (void)hipEventRecord(x->prof.ev[x->prof.used + 1], x->stream);
+    x->prof.used += 2;
+  }
+};
+
+int run_gemm(gpt_ctx* x, const char* cls, const gk::Gemm& g) {
+  ProfScope ps(x, cls, 2.0 * g.M * g.N * (double)g.K, 0.0);
+  HIPCHK(gk::gemm(g, x->stream));
+  return 0;
+}
+
+gk::Gemm mk(gpt_ctx* x, int at, int bt, int epi, const void* A, int64_t lda, const void* B, int64_t ldb,
+            int64_t M, int64_t N, int64_t K, void* C, int64_t ldc) {
+  gk::Gemm g;
+  g.dtype = x->dt;
+  g.a_trans = at;
+  g.b_trans = bt;
+  g.epi = epi;
+  g.A = A;
+  g.B = B;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.C = C;
+  g.ldc = ldc;
+  return g;
+}
+
+inline void* off_T(gpt_ctx* x, void* p, int64_t elems) { return (char*)p + elems * x->es; }
+
+// weight gradient dW[M][N] (+)= sum_n A(m, n) B(n-th col): both operands token-major
+int wgrad(gpt_ctx* x, const void* dY, int64_t ldy, const void* Xin, int64_t ldx, int64_t M, int64_t Nn,
+          float* dW, int acc) {
+  gk::Gemm g = mk(x, 1, 1, gk::EPI_F32, dY, ldy, Xin, ldx, M, Nn, x->N, dW, Nn);
+  g.accumulate = acc;
+  g.splits = gk::gemm_pick_splits((int)M, (int)Nn, (int)x->N);
+  g.ws = x->splitk_ws;
+  return run_gemm(x, "gemm_wgrad", g);
+}
+
+int bias_grad(gpt_ctx* x, int dtype, const void* dY, int64_t cols, float* db, int acc) {
+  HIPCHK(gk::colsum_partial(dtype, dY, (int)x->N, (int)cols, x->col_part, x->stream));
+  HIPCHK(gk::reduce_rows_f32(x->col_part, (int)((x->N + 255) / 256), (int)cols, cols, db, acc, x->stream));
+  return 0;
+}
+
+int ln_bwd(gpt_ctx* x, const float* dy, const float* xin, const float* mu, const float* rs, int g_id, int b_id,
+           const float* dres_in, int acc) {
+  int nblk = 0;
+  {
+    ProfScope ps(x, "layernorm_bwd", 0.0, (double)x->N * x->C * (4 + 4 + 4 + 4 + x->es) + 8.0 * x->N);
+    HIPCHK(gk::layernorm_bwd(x->dt, dy, xin, mu, rs, x->P_(g_id), dres_in, x->dres, x->dresT, x->ln_part,
+                             (int)x->N, (int)x->C, &nblk, x->stream));
+  }
+  HIPCHK(gk::reduce_rows_f32(x->ln_part, nblk, (int)x->C, 2 * x->C, x->G_(g_id), acc, x->stream));
+  HIPCHK(gk::reduce_rows_f32(x->ln_part + x->C, nblk, (int)x->C, 2 * x->C, x->G_(b_id), acc, x->stream));
+  return 0;
+}
+
+int ln_fwd(gpt_ctx* x, const float* in, int g_id, int b_id, void* out, float* mu, float* rs) {
+  ProfScope ps(x, "layernorm_fwd", 0.0, (double)x->N * x->C * (4 + x->es) + 8.0 * x->N);
+  HIPCHK(gk::layernorm_fwd(x->dt, in, x->P_(g_id), x->P_(b_id), out, mu, rs, (int)x->N, (int)x->C, x->stream));
+  return 0;
+}
+
+// The fused tied head + cross-entropy over row chunks: logits of a chunk live
+// only in the chunk buffer; loss, dF and dW come out of the same pass.
+int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C,
+         float scale, float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, float* logits, void* dz,
+         int64_t ldv, int64_t Nc, int dtype) {
+  for (int64_t c0 = 0; c0 < N; c0 += Nc) {
+    const int64_t rows = std::min(Nc, N - c0);
+    const void* Fc = (const char*)Fin + c0 * C * (dtype == GPT_BF16 ? 2 : 4);
+    gk::Gemm g = mk(x, 0, 0, gk::EPI_F32, Fc, C, W, C, rows, V, C, logits, ldv);
+    g.dtype = dtype;
+    if (run_gemm(x, "head_gemm", g)) return GPT_EHIP;
+    {
+      ProfScope ps(x, "head_ce", 0.0, (double)rows * V * (4 + (scale > 0 ? (dtype == GPT_BF16 ? 2 : 4) : 0)));
+      HIPCHK(gk::ce_rows(dtype, logits, ldv, (int)V, y + c0, (int)rows, scale, tok_loss + c0, tok_lse + c0,
+                         scale > 0 ? dz : nullptr, x->stream));
+    }
+    if (scale > 0) {
+      if (dF) {
+        gk::Gemm d = mk(x, 0, 1, gk::EPI_F32, dz, ldv, W, C, rows, C, V, dF + c0 * C, C);
+        d.dtype = dtype;
+        if (run_gemm(x, "head_gemm", d)) return GPT_EHIP;
+      }
+      if (dW) {
+        gk::Gemm w = mk(x, 1, 1, gk::EPI_F32, dz, ldv, Fc, C, V, C, rows, dW, C);
+        w.dtype = dtype;
+        w.accumulate = (c0 > 0) || dW_acc;
+        if (run_gemm(x, "head_gemm", w)) return GPT_EHIP;
+      }
+    }
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gpt_arena_bytes(const gpt_config* cfg) {
+  if (check_cfg(cfg)) return 0;
+  gpt_ctx tmp;
+  setup_dims(&tmp, cfg);
+  return (size_t)carve(&tmp, nullptr);
+}
+
+int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_stream, uint64_t seed, gpt_ctx** out) {
+  if (int e = check_cfg(cfg)) return e;
+  if (!arena || !out) return fail(GPT_EINVAL, "null arena or out pointer");
+  if (((uintptr_t)arena) % ALIGN) return fail(GPT_EINVAL, "arena must be 256-byte aligned");
+  gpt_ctx* x = new gpt_ctx();
+  setup_dims(x, cfg);
+  const int64_t need = carve(x, nullptr);
+  if ((int64_t)arena_bytes < need) {
+    delete x;
+    return fail(GPT_ENOMEM, "arena too small: need " + std::to_string(need) + " bytes");
+  }
+  carve(x, arena);
+  x->stream = (hipStream_t)hip_stream;
+  hipStream_t s = x->stream;
+  int rc = 0;
+  auto chk = [&](hipError_t e) {
+    if (e != hipSuccess && !rc) rc = fail(GPT_EHIP, std::string("init: ") + hipGetErrorString(e));
+  };
+  chk(gk::fill_f32(x->params, x->P, 0.f, s));
+  chk(gk::fill_f32(x->grads, x->P, 0.f, s));
+  chk(gk::fill_f32(x->m, x->P, 0.f, s));
+  chk(gk::fill_f32(x->v, x->P, 0.f, s));
+  chk(gk::fill_f32(x->scal, 16, 0.f, s));
+  chk(gk::fill_f32((float*)x->step_dev, 16, 0.f, s));
+  chk(gk::fill_f32(x->ring, RING, 0.f, s));
+  const float std_r = 0.02f / std::sqrt(2.0f * (float)x->L);
+  uint64_t logical = 0;
+  for (auto& d : x->tensors) {
+    float* p = x->params + d.off;
+    if (d.kind == 0) chk(gk::init_normal(p, d.numel(), 0.02f, seed, logical, s));
+    else if (d.kind == 1) chk(gk::init_normal(p, d.numel(), std_r, seed, logical, s));
+    else if (d.kind == 3) chk(gk::fill_f32(p, d.numel(), 1.f, s));
+    logical += (uint64_t)d.numel();
+  }
+  if (x->shadow) chk(gk::to_bf16(x->params, x->shadow, x->P, s));
+  if (rc) {
+    delete x;
+    return rc;
+  }
+  *out = x;
+  return 0;
+}
+
+int gpt_destroy(gpt_ctx* x) {
+  if (!x) return 0;
+  for (auto e : x->prof.ev) (void)hipEventDestroy(e);
+  delete x;
+  return 0;
+}
+
+int gpt_make_batch(gpt_ctx* x, const int32_t* host_tokens, int64_t n_tokens, int64_t start) {
+  if (!x || !host_tokens) return fail(GPT_EINVAL, "null argument");
+  const int64_t need = x->N + 1;
+  if (start < 0 || start + need > n_tokens) return fail(GPT_ERANGE, "window past the end of the token stream");
+  for (int64_t i = 0; i < need; ++i) {
+    const int32_t t = host_tokens[start + i];
+    if (t < 0 || t >= x->V)
+      return fail(GPT_ERANGE, "token " + std::to_string(t) + " at " + std::to_string(start + i) + " outside [0, vocab)");
+  }
+  HIPCHK(hipMemcpyAsync(x->win, host_tokens + start, need * 4, hipMemcpyHostToDevice, x->stream));
+  HIPCHK(hipStreamSynchronize(x->stream));
+  return 0;
+}
+
+int64_t gpt_next_start(int64_t pos, int64_t n_tokens, int32_t B, int32_t T, int32_t rank, int32_t world) {
+  if (B < 1 || T < 1 || world < 1 || rank < 0 || rank >= world || n_tokens < 1)
+    return fail(GPT_EINVAL, "bad cursor arguments");
+  const int64_t step = (int64_t)B * T * world;
+  int64_t p = pos + step;
+  if (p + step + 1 > n_tokens) p = (int64_t)B * T * rank;
+  return p;
+}
+
+int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
+  if (!x) return fail(GPT_EINVAL, "null context");
+  if (!(loss_scale >= 0.f) || !std::isfinite(loss_scale)) return fail(GPT_EINVAL, "loss_scale must be >= 0");
+  hipStream_t s = x->stream;
+  const int64_t N = x->N, C = x->C;
+  const int32_t* xt = x->win;
+  const int32_t* yt = x->win + 1;
+  {
+    ProfScope ps(x, "layernorm_fwd", 0.0, (double)N * C * (4 + 4 + 4 + x->es) + 8.0 * N);
+    HIPCHK(gk::embed_ln_fwd(x->dt, xt, x->P_(T_WTE), x->P_(T_WPE), (int)x->T, x->res[0], x->P_(tid(0, K_LN1G)),
+                            x->P_(tid(0, K_LN1B)), x->layers[0].ln1, x->layers[0].mu1, x->layers[0].rs1, (int)N,
+                            (int)C, s));
+  }
+  for (int l = 0; l < x->L; ++l) {
+    Layer& ly = x->layers[l];
+    gk::Gemm g = mk(x, 0, 0, gk::EPI_STORE, ly.ln1, C, x->W_(tid(l, K_ATTW)), C, N, 3 * C, C, ly.qkv, 3 * C);
+    g.bias = x->P_(tid(l, K_ATTB));
+    if (int e = run_gemm(x, "gemm_qkv_fwd", g)) return e;
+    {
+      const double pairs = (double)x->B * x->H * x->T * (x->T + 1) / 2.0;
+      ProfScope ps(x, "attn_fwd", 4.0 * x->D * pairs, 0.0);
+      HIPCHK(gk::attn_fwd(x->dt, ly.qkv, ly.att, ly.lse, (int)x->B, (int)x->T, (int)x->H, (int)x->D, s));
+    }
+    g = mk(x, 0, 0, gk::EPI_RESID, ly.att, C, x->W_(tid(l, K_PROJW)), C, N, C, C, ly.res_mid, C);
+    g.bias = x->P_(tid(l, K_PROJB));
+    g.R = x->res[l];
+    if (int e = run_gemm(x, "gemm_proj_fwd", g)) return e;
+    if (int e = ln_fwd(x, ly.res_mid, tid(l, K_LN2G), tid(l, K_LN2B), ly.ln2, ly.mu2, ly.rs2)) return e;
+    g = mk(x, 0, 0, gk::EPI_GELU, ly.ln2, C, x->W_(tid(l, K_FCW)), C, N, 4 * C, C, ly.fcpre, 4 * C);
+    g.bias = x->P_(tid(l, K_FCB));
+    g.C2 = ly.fcact;
+    if (int e = run_gemm(x, "gemm_fc_fwd", g)) return e;
+    g = mk(x, 0, 0, gk::EPI_RESID, ly.fcact, 4 * C, x->W_(tid(l, K_MPW)), 4 * C, N, C, 4 * C, x->res[l + 1], C);
+    g.bias = x->P_(tid(l, K_MPB));
+    g.R = ly.res_mid;
+    if (int e = run_gemm(x, "gemm_mlpproj_fwd", g)) return e;
+    if (l + 1 < x->L) {
+      Layer& nx = x->layers[l + 1];
+      if (int e = ln_fwd(x, x->res[l + 1], tid(l + 1, K_LN1G), tid(l + 1, K_LN1B), nx.ln1, nx.mu1, nx.rs1)) return e;
+    } else {
+      if (int e = ln_fwd(x, x->res[l + 1], tid_lnf(x->L, 0), tid_lnf(x->L, 1), x->lnf, x->muf, x->rsf)) return e;
+    }
+  }
+  const float scale = loss_scale / (float)N;
+  const bool grad = loss_scale > 0.f;
+  if (int e = head(x, x->lnf, x->W_(T_WTE), x->Vp, yt, N, C, grad ? scale : 0.f, x->tok_loss, x->tok_lse,
+                   grad ? x->dF : nullptr, grad ? x->G_(T_WTE) : nullptr, x->wte_fresh ? 0 : 1, x->logits, x->dz,
+                   x->ldv, x->Nc, x->dt))
+    return e;
+  if (grad) x->wte_fresh = false;
+  HIPCHK(gk::mean_f32(x->tok_loss, (int)N, x->loss, x->ring, x->ring_wr % RING, s));
+  x->ring_wr++;
+  x->have_fwd = true;
+  x->fwd_grad = grad;
+  x->last_scale = loss_scale;
+  if (loss_host) {
+    HIPCHK(hipMemcpyAsync(loss_host, x->loss, 4, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    if (!std::isfinite(*loss_host)) return fail(GPT_ENONFINITE, "non-finite loss");
+  }
+  return 0;
+}
+
+int gpt_backward(gpt_ctx* x) {
+  if (!x) return fail(GPT_EINVAL, "null context");
+  if (!x->have_fwd || !x->fwd_grad) return fail(GPT_EINVAL, "gpt_backward needs a gpt_forward_loss with loss_scale > 0");
+  hipStream_t s = x->stream;
+  const int64_t N = x->N, C = x->C;
+  const int acc = x->others_fresh ? 0 : 1;
+  const int L = (int)x->L;
+  if (int e = ln_bwd(x, x->dF, x->res[L], x->muf, x->rsf, tid_lnf(L, 0), tid_lnf(L, 1), nullptr, acc)) return e;
+  for (int l = L - 1; l >= 0; --l) {
+    Layer& ly = x->layers[l];
+    // MLP output projection
+    if (int e = wgrad(x, x->dresT, C, ly.fcact, 4 * C, C, 4 * C, x->G_(tid(l, K_MPW)), acc)) return e;
+    if (int e = bias_grad(x, GPT_F32, x->dres, C, x->G_(tid(l, K_MPB)), acc)) return e;
+    gk::Gemm g = mk(x, 0, 1, gk::EPI_GELU_BWD, x->dresT, C, x->W_(tid(l, K_MPW)), 4 * C, N, 4 * C, C, x->dfc, 4 * C);
+    g.aux = ly.fcpre;
+    if (int e = run_gemm(x, "gemm_dgrad", g)) return e;
+    // MLP input projection
+    if (int e = wgrad(x, x->dfc, 4 * C, ly.ln2, C, 4 * C, C, x->G_(tid(l, K_FCW)), acc)) return e;
+    if (int e = bias_grad(x, x->dt, x->dfc, 4 * C, x->G_(tid(l, K_FCB)), acc)) return e;
+    g = mk(x, 0, 1, gk::EPI_F32, x->dfc, 4 * C, x->W_(tid(l, K_FCW)), C, N, C, 4 * C, x->dln, C);
+    if (int e = run_gemm(x, "gemm_dgrad", g)) return e;
+    if (int e = ln_bwd(x, x->dln, ly.res_mid, ly.mu2, ly.rs2, tid(l, K_LN2G), tid(l, K_LN2B), x->dres, acc)) return e;
+    // attention output projection
+    if (int e = wgrad(x, x->dresT, C, ly.att, C, C, C, x->G_(tid(l, K_PROJW)), acc)) return e;
+    if (int e = bias_grad(x, GPT_F32, x->dres, C, x->G_(tid(l, K_PROJB)), acc)) return e;
+    g = mk(x, 0, 1, gk::EPI_STORE, x->dresT, C, x->W_(tid(l, K_PROJW)), C, N, C, C, x->datt, C);
+    if (int e = run_gemm(x, "gemm_dgrad", g)) return e;
+    {
+      const double pairs = (double)x->B * x->H * x->T * (x->T + 1) / 2.0;
+      ProfScope ps(x, "attn_bwd", 8.0 * x->D * pairs, 0.0);
+      HIPCHK(gk::attn_bwd(x->dt, ly.qkv, ly.att, x->datt, ly.lse, x->Dv, x->dqkv, (int)x->B, (int)x->T, (int)x->H,
+                          (int)x->D, s));
+    }
+    // QKV projection
+    if (int e = wgrad(x, x->dqkv, 3 * C, ly.ln1, C, 3 * C, C, x->G_(tid(l, K_ATTW)), acc)) return e;
+    if (int e = bias_grad(x, x->dt, x->dqkv, 3 * C, x->G_(tid(l, K_ATTB)), acc)) return e;
+    g = mk(x, 0, 1, gk::EPI_F32, x->dqkv, 3 * C, x->W_(tid(l, K_ATTW)), C, N, C, 3 * C, x->dln, C);
+    if (int e = run_gemm(x, "gemm_dgrad", g)) return e;
+    if (int e = ln_bwd(x, x->dln, x->res[l], ly.mu1, ly.rs1, tid(l, K_LN1G), tid(l, K_LN1B), x->dres, acc)) return e;
+  }
+  // embeddings: token rows (deterministic segmented sum) and positions
+  {
+    ProfScope ps(x, "embed_bwd", 0.0, (double)N * C * 12);
+    HIPCHK(gk::sort_tokens(x->win, (int)N, x->keys, s));
+    HIPCHK(gk::embed_bwd_ws(x->keys, (int)N, x->dres, (int)C, x->dln, x->G_(T_WTE), s));
+    HIPCHK(gk::wpe_bwd(x->dres, (int)x->B, (int)x->T, (int)C, x->G_(T_WPE), acc, s));
+  }
+  x->others_fresh = false;
+  x->fwd_grad = false;
+  return 0;
+}
+
+int gpt_adamw_step(gpt_ctx* x, float lr, float beta1, float beta2, float eps, float weight_decay, float grad_clip,
+                   float* grad_norm_host) {
+  if (!x) return fail(GPT_EINVAL, "null context");
+  if (!(lr >= 0.f) || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(eps >= 0.f) ||
+      !(weight_decay >= 0.f))
+    return fail(GPT_EINVAL, "bad AdamW hyper-parameters");
+  if (x->wte_fresh || x->others_fresh) {
+    // some gradients were never written since the last update: they are zero
+    if (x->wte_fresh) HIPCHK(gk::fill_f32(x->G_(T_WTE), x->tensors[T_WTE].numel(), 0.f, x->stream));
+    if (x->others_fresh) {
+      HIPCHK(gk::fill_f32(x->grads + x->tensors[T_WPE].off, x->P - x->tensors[T_WPE].off, 0.f, x->stream));
+      // wte precedes wpe in memory; anything between is padding
+    }
+  }
+  hipStream_t s = x->stream;
+  int nblk = 0;
+  {
+    ProfScope ps(x, "adamw", 0.0, (double)x->P * (4.0 + (x->shadow ? 30.0 : 28.0)));
+    HIPCHK(gk::sumsq_partial(x->grads, x->P, x->norm_part, &nblk, s));
+    HIPCHK(gk::norm_finish(x->norm_part, nblk, grad_clip, x->scal, s));
+    HIPCHK(gk::adamw(x->params, x->grads, x->m, x->v, x->shadow, x->P, x->P_decay, x->scal, lr, beta1, beta2, eps,
+                     weight_decay, x->step_dev, s));
+  }
+  x->wte_fresh = x->others_fresh = true;
+  x->have_fwd = false;
+  if (grad_norm_host) {
+    float sc[8];
+    HIPCHK(hipMemcpyAsync(sc, x->scal, sizeof(sc), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    *grad_norm_host = sc[0];
+    if (sc[4] != 0.f) {
+      HIPCHK(gk::fill_f32(x->scal + 4, 1, 0.f, s));
+      x->wte_fresh = x->others_fresh = false;  // the skipped step's gradients stay readable
+      return fail(GPT_ENONFINITE, "non-finite gradient norm: update skipped");
+    }
+  }
+  return 0;
+}
+
+size_t gpt_lmhead_ce_ws_bytes(int64_t N, int64_t V, int64_t C, int32_t dtype) {
+  if (N < 1 || V < 1 || C < 64 || C % 64 || (dtype != GPT_F32 && dtype != GPT_BF16)) return 0;
+  const int64_t es = dtype == GPT_BF16 ? 2 : 4;
+  const int64_t ldv = align_up(V, 64), Nc = std::min<int64_t>(N, 4096);
+  return (size_t)(align_up(Nc * ldv * 4, ALIGN) + align_up(Nc * ldv * es, ALIGN) + 2 * align_up(N * 4, ALIGN));
+}
+
+int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int64_t V, int64_t C, int32_t dtype,
+                  float* loss_dev, float* dX, float* dW, void* ws, size_t ws_bytes, void* hip_stream) {
+  const size_t need = gpt_lmhead_ce_ws_bytes(N, V, C, dtype);
+  if (!need || !X || !W || !y || !loss_dev) return fail(GPT_EINVAL, "bad lmhead_ce arguments");
+  if (!ws || ws_bytes < need) return fail(GPT_ENOMEM, "lmhead_ce workspace too small");
+  if (N > 0x7fffffff || V > 0x7fffffff) return fail(GPT_EINVAL, "N, V too large");
+  gpt_ctx tmp;  // launch helpers only use the stream, dtype and profiling fields
+  tmp.stream = (hipStream_t)hip_stream;
+  tmp.dt = dtype;
+  tmp.es = dtype == GPT_BF16 ? 2 : 4;
+  const int64_t ldv = align_up(V, 64), Nc = std::min<int64_t>(N, 4096);
+  Carver cv(ws);
+  float* logits = cv.take<float>(Nc * ldv * 4);
+  void* dz = cv.take<void>(Nc * ldv * tmp.es);
+  float* tl = cv.take<float>(N * 4);
+  float* tlse = cv.take<float>(N * 4);
+  const bool grad = dX || dW;
+  if (int e = head(&tmp, X, W, V, y, N, C, grad ? 1.0f / (float)N : 0.f, tl, tlse, dX, dW, 0, logits, dz, ldv, Nc,
+                   dtype))
+    return e;
+  HIPCHK(gk::mean_f32(tl, (int)N, loss_dev, nullptr, 0, tmp.stream));
+  return 0;
+}
+
+int gpt_num_tensors(const gpt_ctx* x) { return x ? (int)x->tensors.size() : fail(GPT_EINVAL, "null context"); }
+
+int gpt_tensor_info(const gpt_ctx* x, int id, const char** name, int64_t shape[2], int* decays) {
+  if (!x || id < 0 || id >= (int)x->tensors.size()) return fail(GPT_EINVAL, "bad tensor id");
+  const TensorDesc& d = x->tensors[id];
+  if (name) *name = d.name.c_str();
+  if (shape) {
+    shape[0] = d.rows;
+    shape[1] = d.cols;
+  }
+  if (decays) *decays = d.decays;
+  return 0;
+}
+
+static float* kind_ptr(gpt_ctx* x, int kind) {
+  switch (kind) {
+    case GPT_PARAM: return x->params;
+    case GPT_GRAD: return x->grads;
+    case GPT_ADAM_M: return x->m;
+    case GPT_ADAM_V: return x->v;
+    default: return nullptr;
+  }
+}
+
+int gpt_get_tensor(gpt_ctx* x, int kind, int id, float* host, int64_t n) {
+  if (!x || !host || id < 0 || id >= (int)x->tensors.size()) return fail(GPT_EINVAL, "bad tensor access");
+  float* base = kind_ptr(x, kind);
+  if (!base) return fail(GPT_EINVAL, "bad tensor kind");
+  const TensorDesc& d = x->tensors[id];
+  if (n != d.numel()) return fail(GPT_EINVAL, "element count mismatch for " + d.name);
+  if (kind == GPT_GRAD && (id == T_WTE ? x->wte_fresh : x->others_fresh)) {
+    std::memset(host, 0, n * 4);  // cleared since the last update
+    return 0;
+  }
+  HIPCHK(hipMemcpyAsync(host, base + d.off, n * 4, hipMemcpyDeviceToHost, x->stream));
+  HIPCHK(hipStreamSynchronize(x->stream));
+  return 0;
+}
+
+int gpt_set_tensor(gpt_ctx* x, int kind, int id, const float* host, int64_t n) {
+  if (!x || !host || id < 0 || id >= (int)x->tensors.size()) return fail(GPT_EINVAL, "bad tensor access");
+  float* base = kind_ptr(x, kind);
+  if (!base) return fail(GPT_EINVAL, "bad tensor kind");
+  const TensorDesc& d = x->tensors[id];
+  if (n != d.numel()) return fail(GPT_EINVAL, "element count mismatch for " + d.name);
+  if (kind == GPT_GRAD) {
+    // materialise the cleared state before writing part of it
+    if (id == T_WTE && x->wte_fresh) {
+      HIPCHK(gk::fill_f32(x->G_(T_WTE), d.numel(), 0.f, x->stream));
+      x->wte_fresh = false;
+    } else if (id != T_WTE && x->others_fresh) {
+      HIPCHK(gk::fill_f32(x->grads + x->tensors[T_WPE].off, x->P - x->tensors[T_WPE].off, 0.f, x->stream));
+      x->others_fresh = false;
+    }
+  }
+  HIPCHK(hipMemcpyAsync(base + d.off, host, n * 4, hipMemcpyHostToDevice, x->stream));
+  if (kind == GPT_PARAM && x->shadow)
+    HIPCHK(gk::to_bf16(base + d.off, (uint16_t*)x->shadow + d.off, n, x->stream));
+  HIPCHK(hipStreamSynchronize(x->stream));
+  return 0;
+}
+
+int gpt_get_batch(gpt_ctx* x, int32_t* xh, int32_t* yh, int64_t n) {
+  if (!x || !xh || !yh || n != x->N) return fail(GPT_EINVAL, "need B*T ints for x and y");
+  HIPCHK(hipMemcpyAsync(xh, x->win, n * 4, hipMemcpyDeviceToHost, x->stream));
+  HIPCHK(hipMemcpyAsync(yh, x->win + 1, n * 4, hipMemcpyDeviceToHost, x->stream));
+  HIPCHK(hipStreamSynchronize(x->stream));
+  return 0;
+}
+
+int gpt_get_token_losses(gpt_ctx* x, float* host, int64_t n) {
+  if (!x || !host || n != x->N) return fail(GPT_EINVAL, "need B*T floats");
+  HIPCHK(hipMemcpyAsync(host, x->tok_loss, n * 4, hipMemcpyDeviceToHost, x->stream));
+  HIPCHK(hipStreamSynchronize(x->stream));
+  return 0;
+}
+
+int gpt_read_losses(gpt_ctx* x, float* host, int max) {
+  if (!x || !host || max < 0) return fail(GPT_EINVAL, "bad arguments");
+  std::vector<float> all(RING);
+  HIPCHK(hipMemcpyAsync(all.data(), x->ring, RING * 4, hipMemcpyDeviceToHost, x->stream));
+  float sc[8];
+  HIPCHK(hipMemcpyAsync(sc, x->scal, sizeof(sc), hipMemcpyDeviceToHost, x->stream));
+  HIPCHK(hipStreamSynchronize(x->stream));
+  int k = 0;
+  if (x->ring_wr - x->ring_rd > RING) x->ring_rd = x->ring_wr - RING;
+  while (x->ring_rd < x->ring_wr && k < max) host[k++] = all[(x->ring_rd++) % RING];
+  if (sc[4] != 0.f) {
+    HIPCHK(gk::fill_f32(x->scal + 4, 1, 0.f, x->stream));
+    HIPCHK(hipStreamSynchronize(x->stream));
+    return fail(GPT_ENONFINITE, "a non-finite gradient norm skipped an update");
+  }
+  return k;
+}
+
+int64_t gpt_step_count(const gpt_ctx* xc) {
+  gpt_ctx* x = const_cast<gpt_ctx*>(xc);
+  if (!x) return fail(GPT_EINVAL, "null context");
+  int t = 0;
+  if (hipMemcpyAsync(&t, x->step_dev, 4, hipMemcpyDeviceToHost, x->stream) != hipSuccess) return fail(GPT_EHIP, "copy");
+  if (hipStreamSynchronize(x->stream) != hipSuccess) return fail(GPT_EHIP, "sync");
+  return t;
+}
+
+int gpt_profile_begin(gpt_ctx* x, const char* cls) {
+  if (!x || !cls) return fail(GPT_EINVAL, "null argument");
+  x->prof.cls = cls;
+  x->prof.used = 0;
+  x->prof.flops = x->prof.bytes = 0;
+  x->prof.launches = 0;
+  return 0;
+}
+
+int gpt_profile_end(gpt_ctx* x, double* total_ms, int64_t* launches, double* flops, double* bytes) {
+  if (!x) return fail(GPT_EINVAL, "null context");
+  HIPCHK(hipStreamSynchronize(x->stream));
+  double ms = 0;
+  for (size_t i = 0; i + 1 < x->prof.used; i += 2) {
+    float t = 0;
+    HIPCHK(hipEventElapsedTime(&t, x->prof.ev[i], x->prof.ev[i + 1]));
+    ms += t;
+  }
+  if (total_ms) *total_ms = ms;
+  if (launches) *launches = x->prof.launches;
+  if (flops) *flops = x->prof.flops;
+  if (bytes) *bytes = x->prof.bytes;
+  x->prof.cls.clear();
+  x->prof.used = 0;
+  return 0;
+}
+
+const char* gpt_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

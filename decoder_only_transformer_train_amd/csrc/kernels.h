@@ -1,0 +1,112 @@
+// Host-side launchers of the gfx950 kernels (internal to libgpt.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gk {
+
+enum Dtype { F32 = 0, BF16 = 1 };
+
+// ---- GEMM: C[m][n] = sum_k A(m,k) B(n,k) ----
+// a_trans == 0: A stored [M][lda] (k contiguous); 1: A stored [K][lda] (m contiguous).
+// b_trans == 0: B stored [N][ldb] (k contiguous); 1: B stored [K][ldb] (n contiguous).
+enum Epi {
+  EPI_STORE = 0,     // C(T) = acc + bias
+  EPI_RESID = 1,     // C(f32) = R(f32) + acc + bias
+  EPI_GELU = 2,      // C(T) = acc + bias; C2(T) = gelu(acc + bias)
+  EPI_GELU_BWD = 3,  // C(T) = acc * gelu'(aux(T))
+  EPI_F32 = 4,       // C(f32) = (accumulate ? C : 0) + acc
+};
+
+struct Gemm {
+  int dtype;  // element type of A, B, and of T-typed outputs
+  int a_trans, b_trans, epi;
+  const void* A;
+  const void* B;
+  int64_t lda, ldb;
+  int M, N, K;
+  void* C;
+  int64_t ldc;
+  const float* bias = nullptr;
+  const float* R = nullptr;
+  void* C2 = nullptr;
+  const void* aux = nullptr;
+  int accumulate = 0;
+  // split-K (EPI_F32 only): when > 1, partial sums go to ws [splits][M][N] and are reduced in order
+  int splits = 1;
+  float* ws = nullptr;
+};
+hipError_t gemm(const Gemm& g, hipStream_t s);
+// split count and workspace floats a wgrad GEMM of this shape would use
+int gemm_pick_splits(int M, int N, int K);
+
+// ---- LayerNorm ----
+// y = (x - mu) * rstd * g + b per row of C; x fp32 [rows][C]; y T; mu, rstd fp32 [rows]
+hipError_t layernorm_fwd(int dtype, const float* x, const float* g, const float* b, void* y,
+                         float* mu, float* rstd, int rows, int C, hipStream_t s);
+// embedding (wte[tok] + wpe[t]) -> res0 (f32), fused with the first LayerNorm
+hipError_t embed_ln_fwd(int dtype, const int32_t* tok, const float* wte, const float* wpe, int T,
+                        float* res0, const float* g, const float* b, void* y, float* mu,
+                        float* rstd, int rows, int C, hipStream_t s);
+// LayerNorm backward: dres_out = dres_in + dx (f32, may alias dres_in), dres_T = T(dres_out);
+// dgb_part [nblk][2C] partial column sums of dy*xhat and dy (reduced by colsum_f32)
+hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float* mu,
+                         const float* rstd, const float* g, const float* dres_in,
+                         float* dres_out, void* dres_T, float* part, int rows, int C,
+                         int* nblk_out, hipStream_t s);
+int layernorm_bwd_blocks(int rows);
+// out[c] = (acc ? out[c] : 0) + sum_r part[r][c] for c < cols (fixed order)
+hipError_t reduce_rows_f32(const float* part, int nrows, int cols, int64_t ld, float* out,
+                           int accumulate, hipStream_t s);
+// column sums of a T matrix [rows][cols] -> part [cdiv(rows,256)][cols] (f32)
+hipError_t colsum_partial(int dtype, const void* x, int rows, int cols, float* part,
+                          hipStream_t s);
+
+// ---- attention (causal, flash) ----
+// qkv T [B*T][3C] (q | k | v, head h at channels h*D..), o T [B*T][C], lse f32 [B][H][T]
+hipError_t attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int D,
+                    hipStream_t s);
+// dO T [B*T][C] -> dqkv T [B*T][3C]; Dv f32 [B][H][T] workspace
+hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse,
+                    float* Dv, void* dqkv, int B, int T, int H, int D, hipStream_t s);
+
+// ---- cross-entropy rows over a chunk of logits ----
+// z f32 [rows][ldz] (first V columns valid) -> loss[r] = lse - z[y]; lse_out[r];
+// if dz != null: dz T [rows][ldz] = (softmax - onehot) * scale, zero in [V, ldz)
+hipError_t ce_rows(int dtype, const float* z, int64_t ldz, int V, const int32_t* y, int rows,
+                   float scale, float* loss, float* lse_out, void* dz, hipStream_t s);
+// mean of n floats in fixed order -> out[0] (and ring[slot] if ring != null)
+hipError_t mean_f32(const float* x, int n, float* out, float* ring, int slot, hipStream_t s);
+
+// ---- embedding backward ----
+// sort (tok[n], n) keys in one workgroup; keys u32 [n]; n <= 16384
+hipError_t sort_tokens(const int32_t* tok, int n, uint32_t* keys, hipStream_t s);
+// dwte[tok] += sum of dres rows with that token, in sorted order (deterministic);
+// part: workspace f32 [n][C]
+hipError_t embed_bwd_ws(const uint32_t* keys, int n, const float* dres, int C, float* part,
+                        float* dwte, hipStream_t s);
+// dwpe[t] (+)= sum_b dres[b][t]
+hipError_t wpe_bwd(const float* dres, int B, int T, int C, float* dwpe, int accumulate,
+                   hipStream_t s);
+
+// ---- optimiser ----
+// partial sums of squares of g [n] -> part[nblk]; then norm (and clip scale) into scal
+hipError_t sumsq_partial(const float* g, int64_t n, float* part, int* nblk, hipStream_t s);
+int sumsq_blocks(int64_t n);
+// scal[0] = norm, scal[1] = clip scale (1 if clip <= 0), scal[2] = finite flag,
+// scal[3] = AdamW step size, scal[4] = sticky non-finite flag
+hipError_t norm_finish(const float* part, int nblk, float clip, float* scal, hipStream_t s);
+// AdamW over [0, n) (n % 4 == 0); decay applies to [0, n_decay); shadow (bf16) may be null;
+// step_dev: device int update counter, advanced only when the norm is finite
+hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow, int64_t n,
+                 int64_t n_decay, float* scal, float lr, float b1, float b2, float eps, float wd,
+                 int* step_dev, hipStream_t s);
+// fp32 -> bf16 copy
+hipError_t to_bf16(const float* x, void* y, int64_t n, hipStream_t s);
+// x[i] = value
+hipError_t fill_f32(float* x, int64_t n, float value, hipStream_t s);
+// Philox4x32-10 + Box-Muller normals: x[i] = std * N(0,1) with counter (offset + i), key seed
+hipError_t init_normal(float* x, int64_t n, float std, uint64_t seed, uint64_t offset,
+                       hipStream_t s);
+
+}  // namespace gk

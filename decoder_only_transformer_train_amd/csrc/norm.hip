@@ -1,0 +1,297 @@
+// HBM-bound row kernels for gfx950: LayerNorm forward / backward (fused with
+// the embedding gather and the residual-gradient add), column reductions and
+// the cross-entropy row pass of the LM head.
+//
+// LayerNorm (lecture, pre-LN blocks and final LayerNorm; Zero page,
+// Transformer Block): y = (x - mu) / sqrt(var + 1e-5) * g + b over the C
+// channels of a row, biased variance, statistics in fp32.  One wavefront owns
+// one row; each lane keeps its float4 slices of the row in registers, so the
+// row is read once.
+#include "common.h"
+#include "kernels.h"
+
+namespace gk {
+namespace {
+
+constexpr float LN_EPS = 1e-5f;
+constexpr int MAXV = 8;  // float4 slices per lane: C <= 2048
+
+template <typename T, bool EMBED>
+__global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x, const int32_t* __restrict__ tok,
+                                                     const float* __restrict__ wte, const float* __restrict__ wpe,
+                                                     int Tn, float* __restrict__ res0, const float* __restrict__ g,
+                                                     const float* __restrict__ bb, T* __restrict__ y,
+                                                     float* __restrict__ mu, float* __restrict__ rs, int rows, int C) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int nc = C >> 2;
+  float4 v[MAXV];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nc) {
+      if constexpr (EMBED) {
+        const float4 a = load4(wte + (int64_t)tok[row] * C + 4 * j);
+        const float4 p = load4(wpe + (int64_t)(row % Tn) * C + 4 * j);
+        v[i] = make_float4(a.x + p.x, a.y + p.y, a.z + p.z, a.w + p.w);
+        store4(res0 + (int64_t)row * C + 4 * j, v[i]);
+      } else {
+        v[i] = load4(x + (int64_t)row * C + 4 * j);
+      }
+      s += v[i].x + v[i].y + v[i].z + v[i].w;
+    }
+  }
+  const float mean = wave_sum(s) / C;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nc) {
+      const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+      ss += a * a + b * b + c * c + d * d;
+    }
+  }
+  const float r = rsqrtf(wave_sum(ss) / C + LN_EPS);
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nc) {
+      const float4 gg = load4(g + 4 * j), b4 = load4(bb + 4 * j);
+      store4(y + (int64_t)row * C + 4 * j,
+             make_float4((v[i].x - mean) * r * gg.x + b4.x, (v[i].y - mean) * r * gg.y + b4.y,
+                         (v[i].z - mean) * r * gg.z + b4.z, (v[i].w - mean) * r * gg.w + b4.w));
+    }
+  }
+  if (lane == 0) {
+    mu[row] = mean;
+    rs[row] = r;
+  }
+}
+
+// LayerNorm backward.  dx = rstd (dxh - mean(dxh) - xh mean(dxh xh)) with
+// dxh = dy g, xh = (x - mu) rstd; dres_out = dres_in + dx and its T copy.
+// A workgroup handles LNB_ROWS rows and writes one partial row of
+// [sum dy*xh | sum dy] (2C floats).
+constexpr int LNB_ROWS = 32;
+
+template <typename T>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+                                                     const float* __restrict__ mu, const float* __restrict__ rs,
+                                                     const float* __restrict__ g, const float* dres_in,
+                                                     float* dres_out, T* __restrict__ dres_T,
+                                                     float* __restrict__ part, int rows, int C) {
+  __shared__ float red[4][2][2048];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nc = C >> 2;
+  float4 pg[MAXV], pb[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) pg[i] = pb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int r0 = blockIdx.x * LNB_ROWS;
+  for (int rr = w; rr < LNB_ROWS; rr += 4) {
+    const int row = r0 + rr;
+    if (row >= rows) break;
+    const float m = mu[row], r = rs[row];
+    float4 xh[MAXV], dxh[MAXV];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int j = lane + 64 * i;
+      if (j < nc) {
+        const float4 xv = load4(x + (int64_t)row * C + 4 * j);
+        const float4 d = load4(dy + (int64_t)row * C + 4 * j);
+        const float4 gg = load4(g + 4 * j);
+        xh[i] = make_float4((xv.x - m) * r, (xv.y - m) * r, (xv.z - m) * r, (xv.w - m) * r);
+        dxh[i] = make_float4(d.x * gg.x, d.y * gg.y, d.z * gg.z, d.w * gg.w);
+        s1 += dxh[i].x + dxh[i].y + dxh[i].z + dxh[i].w;
+        s2 += dxh[i].x * xh[i].x + dxh[i].y * xh[i].y + dxh[i].z * xh[i].z + dxh[i].w * xh[i].w;
+        pg[i].x += d.x * xh[i].x; pg[i].y += d.y * xh[i].y; pg[i].z += d.z * xh[i].z; pg[i].w += d.w * xh[i].w;
+        pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
+      }
+    }
+    const float m1 = wave_sum(s1) / C, m2 = wave_sum(s2) / C;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int j = lane + 64 * i;
+      if (j < nc) {
+        const int64_t o = (int64_t)row * C + 4 * j;
+        const float4 prev = dres_in ? load4(dres_in + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 out = make_float4(prev.x + r * (dxh[i].x - m1 - xh[i].x * m2),
+                                       prev.y + r * (dxh[i].y - m1 - xh[i].y * m2),
+                                       prev.z + r * (dxh[i].z - m1 - xh[i].z * m2),
+                                       prev.w + r * (dxh[i].w - m1 - xh[i].w * m2));
+        store4(dres_out + o, out);
+        store4(dres_T + o, out);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nc) {
+      *reinterpret_cast<float4*>(&red[w][0][4 * j]) = pg[i];
+      *reinterpret_cast<float4*>(&red[w][1][4 * j]) = pb[i];
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < 2 * C; c += 256) {
+    const int k = c / C, cc = c % C;
+    part[(int64_t)blockIdx.x * 2 * C + c] = red[0][k][cc] + red[1][k][cc] + red[2][k][cc] + red[3][k][cc];
+  }
+}
+
+__global__ void reduce_rows_kernel(const float* __restrict__ part, int nrows, int cols, int64_t ld,
+                                   float* out, int accumulate) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= cols) return;
+  float s = 0.f;
+  for (int r = 0; r < nrows; ++r) s += part[(int64_t)r * ld + c];
+  out[c] = accumulate ? out[c] + s : s;
+}
+
+template <typename T>
+__global__ void colsum_partial_kernel(const T* __restrict__ x, int rows, int cols, float* __restrict__ part) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= cols) return;
+  const int r0 = blockIdx.y * 256;
+  const int r1 = min(rows, r0 + 256);
+  float s = 0.f;
+  for (int r = r0; r < r1; ++r) s += to_f(x[(int64_t)r * cols + c]);
+  part[(int64_t)blockIdx.y * cols + c] = s;
+}
+
+// Cross-entropy over one row of logits (CS336 page, section 1: subtract the
+// row maximum, log-sum-exp, minus the target logit).  One workgroup per row.
+// With dz: dz = (softmax - onehot(y)) * scale, zero in the padding [V, ldz).
+template <typename T>
+__global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ z, int64_t ldz, int V,
+                                                      const int32_t* __restrict__ y, float scale,
+                                                      float* __restrict__ loss, float* __restrict__ lse_out,
+                                                      T* __restrict__ dz) {
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const float* zr = z + (int64_t)row * ldz;
+  float mx = -__builtin_huge_valf();
+  for (int j = t; j < V; j += 256) mx = fmaxf(mx, zr[j]);
+  mx = wave_max(mx);
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float s = 0.f;
+  for (int j = t; j < V; j += 256) s += hw_exp2((zr[j] - mx) * LOG2E);
+  s = wave_sum(s);
+  if (lane == 0) red[w] = s;
+  __syncthreads();
+  s = red[0] + red[1] + red[2] + red[3];
+  const float lse = mx + hw_log2(s) * LN2;
+  const int yy = y[row];
+  if (t == 0) {
+    loss[row] = lse - zr[yy];
+    if (lse_out) lse_out[row] = lse;
+  }
+  if (dz != nullptr) {
+    T* dr = dz + (int64_t)row * ldz;
+    for (int j = t; j < ldz; j += 256) {
+      float d = 0.f;
+      if (j < V) d = (hw_exp2((zr[j] - lse) * LOG2E) - (j == yy ? 1.f : 0.f)) * scale;
+      dr[j] = from_f<T>(d);
+    }
+  }
+}
+
+// out[0] = mean of x[0..n) summed in a fixed order; also ring[slot]
+__global__ __launch_bounds__(256) void mean_kernel(const float* __restrict__ x, int n, float* out, float* ring,
+                                                   int slot) {
+  __shared__ float red[4];
+  const int t = threadIdx.x;
+  float s = 0.f;
+  for (int i = t; i < n; i += 256) s += x[i];
+  s = wave_sum(s);
+  if ((t & 63) == 0) red[t >> 6] = s;
+  __syncthreads();
+  if (t == 0) {
+    const float m = (red[0] + red[1] + red[2] + red[3]) / n;
+    out[0] = m;
+    if (ring) ring[slot] = m;
+  }
+}
+
+}  // namespace
+
+hipError_t layernorm_fwd(int dtype, const float* x, const float* g, const float* b, void* y, float* mu,
+                         float* rstd, int rows, int C, hipStream_t s) {
+  dim3 grid(cdiv(rows, 4));
+  if (dtype == BF16)
+    hipLaunchKernelGGL((ln_fwd_kernel<bf16, false>), grid, dim3(256), 0, s, x, nullptr, nullptr, nullptr, 1,
+                       nullptr, g, b, (bf16*)y, mu, rstd, rows, C);
+  else
+    hipLaunchKernelGGL((ln_fwd_kernel<float, false>), grid, dim3(256), 0, s, x, nullptr, nullptr, nullptr, 1,
+                       nullptr, g, b, (float*)y, mu, rstd, rows, C);
+  return hipGetLastError();
+}
+
+hipError_t embed_ln_fwd(int dtype, const int32_t* tok, const float* wte, const float* wpe, int Tn, float* res0,
+                        const float* g, const float* b, void* y, float* mu, float* rstd, int rows, int C,
+                        hipStream_t s) {
+  dim3 grid(cdiv(rows, 4));
+  if (dtype == BF16)
+    hipLaunchKernelGGL((ln_fwd_kernel<bf16, true>), grid, dim3(256), 0, s, nullptr, tok, wte, wpe, Tn, res0, g, b,
+                       (bf16*)y, mu, rstd, rows, C);
+  else
+    hipLaunchKernelGGL((ln_fwd_kernel<float, true>), grid, dim3(256), 0, s, nullptr, tok, wte, wpe, Tn, res0, g,
+                       b, (float*)y, mu, rstd, rows, C);
+  return hipGetLastError();
+}
+
+int layernorm_bwd_blocks(int rows) { return cdiv(rows, LNB_ROWS); }
+
+hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float* mu, const float* rstd,
+                         const float* g, const float* dres_in, float* dres_out, void* dres_T, float* part,
+                         int rows, int C, int* nblk_out, hipStream_t s) {
+  const int nblk = layernorm_bwd_blocks(rows);
+  if (nblk_out) *nblk_out = nblk;
+  if (dtype == BF16)
+    hipLaunchKernelGGL(ln_bwd_kernel<bf16>, dim3(nblk), dim3(256), 0, s, dy, x, mu, rstd, g, dres_in, dres_out,
+                       (bf16*)dres_T, part, rows, C);
+  else
+    hipLaunchKernelGGL(ln_bwd_kernel<float>, dim3(nblk), dim3(256), 0, s, dy, x, mu, rstd, g, dres_in, dres_out,
+                       (float*)dres_T, part, rows, C);
+  return hipGetLastError();
+}
+
+hipError_t reduce_rows_f32(const float* part, int nrows, int cols, int64_t ld, float* out, int accumulate,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3(cdiv(cols, 256)), dim3(256), 0, s, part, nrows, cols, ld, out,
+                     accumulate);
+  return hipGetLastError();
+}
+
+hipError_t colsum_partial(int dtype, const void* x, int rows, int cols, float* part, hipStream_t s) {
+  dim3 grid(cdiv(cols, 256), cdiv(rows, 256));
+  if (dtype == BF16)
+    hipLaunchKernelGGL(colsum_partial_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, rows, cols, part);
+  else
+    hipLaunchKernelGGL(colsum_partial_kernel<float>, grid, dim3(256), 0, s, (const float*)x, rows, cols, part);
+  return hipGetLastError();
+}
+
+hipError_t ce_rows(int dtype, const float* z, int64_t ldz, int V, const int32_t* y, int rows, float scale,
+                   float* loss, float* lse_out, void* dz, hipStream_t s) {
+  if (dtype == BF16)
+    hipLaunchKernelGGL(ce_rows_kernel<bf16>, dim3(rows), dim3(256), 0, s, z, ldz, V, y, scale, loss, lse_out,
+                       (bf16*)dz);
+  else
+    hipLaunchKernelGGL(ce_rows_kernel<float>, dim3(rows), dim3(256), 0, s, z, ldz, V, y, scale, loss, lse_out,
+                       (float*)dz);
+  return hipGetLastError();
+}
+
+hipError_t mean_f32(const float* x, int n, float* out, float* ring, int slot, hipStream_t s) {
+  hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, s, x, n, out, ring, slot);
+  return hipGetLastError();
+}
+
+}  // namespace gk

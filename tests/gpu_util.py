@@ -1,0 +1,37 @@
+"""Helpers shared by the GPU tests (device contexts, comparison metrics)."""
+import numpy as np
+
+from decoder_only_transformer_train_amd import binding, synthetic
+
+
+def rel_err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    if nb == 0:
+        return float(np.linalg.norm(a))
+    return float(np.linalg.norm(a - b) / nb)
+
+
+def cosine(a, b):
+    a = np.asarray(a, dtype=np.float64).reshape(-1)
+    b = np.asarray(b, dtype=np.float64).reshape(-1)
+    na, nb = np.linalg.norm(a), np.linalg.norm(b)
+    if nb == 0:
+        return 1.0 if na <= 1e-6 else 0.0
+    return float(a @ b / (na * nb + 1e-300))
+
+
+def context(cfg, params=None, seed=0):
+    g = binding.GPT(cfg, seed=seed)
+    if params is not None:
+        g.set_params(params)
+    return g
+
+
+def init_for(cfg, seed=0):
+    return synthetic.init_params(cfg.n_layer, cfg.n_embd, cfg.padded_vocab, cfg.max_seq, seed=seed)
+
+
+def announce(msg):
+    print(f"[gpu-test] {msg}", flush=True)

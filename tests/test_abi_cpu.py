@@ -1,0 +1,102 @@
+"""The C ABI without a GPU: the library loads, exports what include/gpt.h
+declares, validates configurations and implements the host cursor rule."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from decoder_only_transformer_train_amd import binding, configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gpt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported():
+    lib = binding.load()
+    names = declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_exports_in_dynamic_symbol_table():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    syms = set(re.findall(r"\bT (gpt_\w+)", out))
+    assert set(declared_functions()) <= syms
+
+
+@pytest.mark.parametrize("name", list(configs.PRESETS))
+def test_arena_bytes_presets(name):
+    n = binding.arena_bytes(configs.PRESETS[name])
+    assert n > 0 and n % 256 == 0
+
+
+def test_arena_scales_with_model():
+    a = binding.arena_bytes(configs.GPT2_124M)
+    b = binding.arena_bytes(configs.GPT2_350M)
+    # 124M: 16 B/param fp32 state + 2 B/param shadow is at least 2.2 GB
+    assert a > 124e6 * 18 and b > a
+
+
+@pytest.mark.parametrize("bad", [
+    dict(n_embd=100), dict(n_head=5), dict(padded_vocab=100), dict(seq=2048), dict(dtype=7),
+    dict(batch=0), dict(n_layer=0), dict(n_embd=4096, n_head=64),
+])
+def test_invalid_configs_rejected(bad):
+    cfg = configs.GPT2_124M.with_(**bad)
+    assert binding.arena_bytes(cfg) == 0
+    lib = binding.load()
+    out = ctypes.c_void_p()
+    rc = lib.gpt_init(ctypes.byref(cfg.to_c()), ctypes.c_void_p(4096), 1 << 40, None, 0, ctypes.byref(out))
+    assert rc == binding.GPT_EINVAL
+    assert lib.gpt_last_error()
+
+
+def test_init_rejects_small_arena_before_touching_it():
+    lib = binding.load()
+    cfg = configs.TINY_F32.to_c()
+    out = ctypes.c_void_p()
+    need = lib.gpt_arena_bytes(ctypes.byref(cfg))
+    rc = lib.gpt_init(ctypes.byref(cfg), ctypes.c_void_p(1 << 20), need - 256, None, 0, ctypes.byref(out))
+    assert rc == binding.GPT_ENOMEM
+    assert b"arena too small" in lib.gpt_last_error()
+    rc = lib.gpt_init(ctypes.byref(cfg), ctypes.c_void_p((1 << 20) + 4), need, None, 0, ctypes.byref(out))
+    assert rc == binding.GPT_EINVAL
+
+
+def test_next_start_matches_oracle_cursor():
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        B, T = int(rng.integers(1, 5)), int(rng.integers(1, 9))
+        R = int(rng.integers(1, 4))
+        r = int(rng.integers(0, R))
+        n = int(rng.integers(B * T * R + 1, 400))
+        pos = B * T * r
+        for _ in range(6):
+            want = oracle.next_start(pos, n, B, T, r, R)
+            got = binding.next_start(pos, n, B, T, r, R)
+            assert got == want
+            pos = got
+
+
+def test_next_start_pages_example():
+    # 28.3: B=2, T=3, R=2: next windows at 12 and 18
+    assert [binding.next_start(6 * r, 100, 2, 3, r, 2) for r in range(2)] == [12, 18]
+    with pytest.raises(binding.GPTError):
+        binding.next_start(0, 100, 2, 3, 2, 2)
+
+
+def test_lmhead_ws_bytes():
+    lib = binding.load()
+    assert lib.gpt_lmhead_ce_ws_bytes(65536, 50257, 768, 1) > 0
+    assert lib.gpt_lmhead_ce_ws_bytes(65536, 50257, 100, 1) == 0
