@@ -164,7 +164,7 @@ int gpt_adamw_step(gpt_ctx* ctx, float lr, float beta1, float beta2, float eps,
  *   dX  device fp32 [N, C] (nullable): gradient of the mean loss w.r.t. X.
  *   dW  device fp32 [V, C] (nullable): gradient w.r.t. W (overwritten).
  *   ws  device workspace of at least gpt_lmhead_ce_ws_bytes(N, V, C, dtype).
- * N must be a multiple of 128; C a multiple of 64.
+ * C must be a multiple of 64.
  * Errors: EINVAL, ENOMEM (ws too small), EHIP.  Target ids are not checked.
  */
 size_t gpt_lmhead_ce_ws_bytes(int64_t N, int64_t V, int64_t C, int32_t dtype);
