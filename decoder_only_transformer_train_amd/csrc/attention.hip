@@ -176,21 +176,31 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
   }
 }
 
-// Dv[b,h,t] = sum_d dO[t, h*D + d] * O[t, h*D + d]
-template <typename T>
-__global__ void attn_bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dO, float* __restrict__ Dv,
-                                    int N, int Tn, int H, int D) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)N * H) return;
-  const int n = (int)(idx / H), h = (int)(idx % H);
-  const int64_t off = (int64_t)n * H * D + h * D;
+// Dv[b,h,t] = sum_d dO[t, h*D + d] * O[t, h*D + d].  A thread reads one 16-byte
+// chunk of both rows; the D/E lanes of one head reduce with shuffles.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dO,
+                                                           float* __restrict__ Dv, int N, int Tn, int H) {
+  constexpr int E = Tr<T>::E, LPH = D / E;  // lanes per head
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // chunk index over N * H * D / E
+  const int64_t total = (int64_t)N * H * LPH;
   float s = 0.f;
-  for (int d = 0; d < D; d += 4) {
-    const float4 a = load4(o + off + d), c = load4(dO + off + d);
-    s += a.x * c.x + a.y * c.y + a.z * c.z + a.w * c.w;
+  if (i < total) {
+    const float4 a0 = load4(o + i * E), c0 = load4(dO + i * E);
+    s = a0.x * c0.x + a0.y * c0.y + a0.z * c0.z + a0.w * c0.w;
+    if constexpr (E == 8) {
+      const float4 a1 = load4(o + i * E + 4), c1 = load4(dO + i * E + 4);
+      s += a1.x * c1.x + a1.y * c1.y + a1.z * c1.z + a1.w * c1.w;
+    }
   }
-  const int b = n / Tn, tt = n % Tn;
-  Dv[((int64_t)b * H + h) * Tn + tt] = s;
+#pragma unroll
+  for (int off = LPH / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, WAVE);
+  if (i < total && (i % LPH) == 0) {
+    const int64_t nh = i / LPH;
+    const int n = (int)(nh / H), h = (int)(nh % H);
+    const int b = n / Tn, tt = n % Tn;
+    Dv[((int64_t)b * H + h) * Tn + tt] = s;
+  }
 }
 
 template <typename T, int D>
@@ -362,8 +372,8 @@ template <typename T, int D>
 hipError_t bwd_t(const void* qkv, const void* o, const void* dO, const float* lse, float* Dv, void* dqkv,
                  int B, int Tn, int H, hipStream_t s) {
   const int N = B * Tn;
-  hipLaunchKernelGGL((attn_bwd_pre_kernel<T>), dim3(cdiv((int64_t)N * H, 256)), dim3(256), 0, s, (const T*)o,
-                     (const T*)dO, Dv, N, Tn, H, D);
+  hipLaunchKernelGGL((attn_bwd_pre_kernel<T, D>), dim3(cdiv((int64_t)N * H * (D / Tr<T>::E), 256)), dim3(256), 0,
+                     s, (const T*)o, (const T*)dO, Dv, N, Tn, H);
   dim3 grid((Tn + 63) / 64, B * H);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), grid, dim3(256), 0, s, (const T*)qkv, (const T*)dO, lse, Dv,
                      (T*)dqkv, Tn, H);

@@ -6,9 +6,11 @@
 // per MFMA step regardless of the element type.  Operands whose k dimension
 // is not contiguous in memory (the weight-gradient and data-gradient
 // products) are transposed in registers on their way into LDS, so global
-// loads stay 16-byte and coalesced.  Workgroup: 4 waves in 2x2, each wave a
-// 64x64 sub-tile of 4x4 MFMA tiles; LDS double-buffered with the next tile's
-// global loads in flight during the current tile's MFMAs.  Workgroup ids are
+// loads stay 16-byte and coalesced.  Workgroup: 4 waves in 2x2; the tile is
+// BM x BN (256x256, 256x128 or 128x128, chosen per shape), each wave owns a
+// (BM/2) x (BN/2) sub-tile, so a 256x256 tile reads half the LDS bytes per
+// MFMA of a 128x128 one.  LDS is double-buffered with the next tile's global
+// loads in flight during the current tile's MFMAs.  Workgroup ids are
 // remapped so each XCD (ids are dealt round-robin to the 8 XCDs) works on a
 // contiguous, grouped run of tiles that share operand rows in its L2.
 #include "common.h"
@@ -17,9 +19,8 @@
 namespace gk {
 namespace {
 
-constexpr int TM = 128, TN = 128, TKB = 128;  // tile rows, tile cols, k bytes per tile
-constexpr int PITCH = TKB + 16;               // LDS row pitch (bytes)
-constexpr int TILE_BYTES = 128 * PITCH;
+constexpr int TKB = 128;          // k bytes per tile (bf16: 64, fp32: 32 elements)
+constexpr int PITCH = TKB + 16;   // LDS row pitch (bytes)
 constexpr int GROUP_M = 8;
 
 struct Params {
@@ -39,11 +40,12 @@ struct Params {
   float* ws;
 };
 
-template <typename T, int TRANS>
+template <typename T, int TRANS, int ROWS>
 struct Loader {
-  uint4 r[4];
+  static constexpr int NR = ROWS / 32;  // 16-byte registers per thread
+  uint4 r[NR];
   // TRANS == 0: operand stored [rows][ld], k contiguous.
-  // TRANS == 1: operand stored [K][ld], rows contiguous.
+  // TRANS == 1: operand stored [K][ld], rows contiguous; a unit is 4 k-rows x E elements.
   __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, int row0, int rows,
                                        int k0, int kend, int t) {
     constexpr int E = Tr<T>::E;
@@ -51,7 +53,7 @@ struct Loader {
       const int cc = t & 7;
       const int k = k0 + cc * E;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NR; ++i) {
         const int row = row0 + (t >> 3) + 32 * i;
         if (row < rows && k < kend)
           r[i] = *reinterpret_cast<const uint4*>(base + (int64_t)row * ld + k);
@@ -59,16 +61,20 @@ struct Loader {
           r[i] = make_uint4(0, 0, 0, 0);
       }
     } else {
-      constexpr int MCH = 128 / E;
-      const int mc = t % MCH, kg = t / MCH;
-      const int row = row0 + mc * E;
+      constexpr int MCH = ROWS / E;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = k0 + kg * 4 + i;
-        if (k < kend && row < rows)
-          r[i] = *reinterpret_cast<const uint4*>(base + (int64_t)k * ld + row);
-        else
-          r[i] = make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < NR / 4; ++u) {
+        const int unit = t + 256 * u;
+        const int mc = unit % MCH, kg = unit / MCH;
+        const int row = row0 + mc * E;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = k0 + kg * 4 + i;
+          if (k < kend && row < rows)
+            r[4 * u + i] = *reinterpret_cast<const uint4*>(base + (int64_t)k * ld + row);
+          else
+            r[4 * u + i] = make_uint4(0, 0, 0, 0);
+        }
       }
     }
   }
@@ -76,39 +82,42 @@ struct Loader {
     if constexpr (TRANS == 0) {
       const int cc = t & 7;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NR; ++i)
         *reinterpret_cast<uint4*>(s + ((t >> 3) + 32 * i) * PITCH + cc * 16) = r[i];
-    } else if constexpr (sizeof(T) == 2) {
-      // 4 k-rows x 8 elements -> 8 rows x 4 k-elements (8 bytes each)
-      const int mc = t % 16, kg = t / 16;
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wi = e >> 1;
-        uint32_t lo, hi;
-        if (e & 1) {
-          lo = (w0[wi] >> 16) | (w1[wi] & 0xFFFF0000u);
-          hi = (w2[wi] >> 16) | (w3[wi] & 0xFFFF0000u);
-        } else {
-          lo = (w0[wi] & 0xFFFFu) | (w1[wi] << 16);
-          hi = (w2[wi] & 0xFFFFu) | (w3[wi] << 16);
-        }
-        *reinterpret_cast<uint2*>(s + (mc * 8 + e) * PITCH + kg * 8) = make_uint2(lo, hi);
-      }
     } else {
-      // fp32: 4 k-rows x 4 elements -> 4 rows x 4 k-elements (16 bytes each)
-      const int mc = t % 32, kg = t / 32;
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
+      constexpr int E = Tr<T>::E;
+      constexpr int MCH = ROWS / E;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<uint4*>(s + (mc * 4 + e) * PITCH + kg * 16) =
-            make_uint4(w0[e], w1[e], w2[e], w3[e]);
+      for (int u = 0; u < NR / 4; ++u) {
+        const int unit = t + 256 * u;
+        const int mc = unit % MCH, kg = unit / MCH;
+        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[4 * u + 0]);
+        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[4 * u + 1]);
+        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[4 * u + 2]);
+        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[4 * u + 3]);
+        if constexpr (sizeof(T) == 2) {
+          // 4 k-rows x 8 elements -> 8 rows x 4 k-elements (8 bytes each)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int wi = e >> 1;
+            uint32_t lo, hi;
+            if (e & 1) {
+              lo = (w0[wi] >> 16) | (w1[wi] & 0xFFFF0000u);
+              hi = (w2[wi] >> 16) | (w3[wi] & 0xFFFF0000u);
+            } else {
+              lo = (w0[wi] & 0xFFFFu) | (w1[wi] << 16);
+              hi = (w2[wi] & 0xFFFFu) | (w3[wi] << 16);
+            }
+            *reinterpret_cast<uint2*>(s + (mc * 8 + e) * PITCH + kg * 8) = make_uint2(lo, hi);
+          }
+        } else {
+          // fp32: 4 k-rows x 4 elements -> 4 rows x 4 k-elements (16 bytes each)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<uint4*>(s + (mc * 4 + e) * PITCH + kg * 16) =
+                make_uint4(w0[e], w1[e], w2[e], w3[e]);
+        }
+      }
     }
   }
 };
@@ -126,15 +135,18 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
   tn = in / gsize;
 }
 
-template <typename T, int TA, int TB, int EPI, int SPLIT>
+template <typename T, int TA, int TB, int EPI, int SPLIT, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE_BYTES];
+  constexpr int WM = BM / 2, WN = BN / 2;    // wave sub-tile
+  constexpr int FM = WM / 16, FN = WN / 16;  // 16x16 MFMA tiles per wave
+  constexpr int STAGE = (BM + BN) * PITCH;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
   int tm, tn;
   tile_coords(p, tm, tn);
-  const int m0 = tm * TM, n0 = tn * TN;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int kb0 = blockIdx.z * p.k_per_split;
   const int kend = min(p.K, kb0 + p.k_per_split);
   constexpr int BK = TKB / sizeof(T);
@@ -142,19 +154,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(Params p) {
 
   const T* A = reinterpret_cast<const T*>(p.A);
   const T* B = reinterpret_cast<const T*>(p.B);
-  Loader<T, TA> la;
-  Loader<T, TB> lb;
-  f32x4 acc[4][4];
+  Loader<T, TA, BM> la;
+  Loader<T, TB, BN> lb;
+  f32x4 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (nk > 0) {
     la.load(A, p.lda, m0, p.M, kb0, kend, t);
     lb.load(B, p.ldb, n0, p.N, kb0, kend, t);
-    la.store(smem[0][0], t);
-    lb.store(smem[0][1], t);
+    la.store(smem, t);
+    lb.store(smem + BM * PITCH, t);
   }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
@@ -164,41 +176,42 @@ __global__ __launch_bounds__(256) void gemm_kernel(Params p) {
       la.load(A, p.lda, m0, p.M, kb0 + (kt + 1) * BK, kend, t);
       lb.load(B, p.ldb, n0, p.N, kb0 + (kt + 1) * BK, kend, t);
     }
-    const char* sa = smem[cur][0];
-    const char* sb = smem[cur][1];
+    const char* sa = smem + cur * STAGE;
+    const char* sb = sa + BM * PITCH;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      uint4 af[4], bfr[4];
+      uint4 af[FM], bfr[FN];
       const int koff = ks * 64 + (lane >> 4) * 16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(sa + (wm * 64 + i * 16 + (lane & 15)) * PITCH + koff);
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(sa + (wm * WM + i * 16 + (lane & 15)) * PITCH + koff);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const uint4*>(sb + (wn * 64 + j * 16 + (lane & 15)) * PITCH + koff);
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const uint4*>(sb + (wn * WN + j * 16 + (lane & 15)) * PITCH + koff);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_frag(acc[i][j], af[i], bfr[j], T());
+        for (int j = 0; j < FN; ++j) mfma_frag(acc[i][j], af[i], bfr[j], T());
     }
     if (more) {
-      la.store(smem[cur ^ 1][0], t);
-      lb.store(smem[cur ^ 1][1], t);
+      char* sn = smem + (cur ^ 1) * STAGE;
+      la.store(sn, t);
+      lb.store(sn + BM * PITCH, t);
     }
     __syncthreads();
   }
 
   // epilogue: lane holds rows (lane / 16) * 4 + r, column lane % 16 of each 16x16 tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 64 + j * 16 + (lane & 15);
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * WN + j * 16 + (lane & 15);
       if (n >= p.N) continue;
       const float bn = (p.bias != nullptr) ? p.bias[n] : 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+        const int m = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + r;
         if (m >= p.M) continue;
         const float a = acc[i][j][r];
         if constexpr (SPLIT) {
@@ -239,46 +252,84 @@ __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, i
   *c = accumulate ? *c + s : s;
 }
 
-template <typename T, int TA, int TB, int EPI, int SPLIT>
+template <typename T, int TA, int TB, int EPI, int SPLIT, int BM, int BN>
 hipError_t launch(const Params& p, int splits, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
-  hipLaunchKernelGGL((gemm_kernel<T, TA, TB, EPI, SPLIT>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<T, TA, TB, EPI, SPLIT, BM, BN>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
+template <typename T, int TA, int TB, int EPI, int SPLIT>
+hipError_t launch_tile(const Params& p, int tile, int splits, hipStream_t s) {
+  switch (tile) {
+    case 0: return launch<T, TA, TB, EPI, SPLIT, 256, 256>(p, splits, s);
+    case 1: return launch<T, TA, TB, EPI, SPLIT, 256, 128>(p, splits, s);
+    default: return launch<T, TA, TB, EPI, SPLIT, 128, 128>(p, splits, s);
+  }
+}
+
 template <typename T>
-hipError_t dispatch(const Gemm& g, const Params& p, int splits, hipStream_t s) {
+hipError_t dispatch(const Gemm& g, const Params& p, int tile, int splits, hipStream_t s) {
   const int key = g.a_trans * 100 + g.b_trans * 10 + g.epi;
   if (splits > 1) {
-    if (g.a_trans == 1 && g.b_trans == 1) return launch<T, 1, 1, EPI_F32, 1>(p, splits, s);
-    if (g.a_trans == 0 && g.b_trans == 1) return launch<T, 0, 1, EPI_F32, 1>(p, splits, s);
+    if (g.a_trans == 1 && g.b_trans == 1) return launch_tile<T, 1, 1, EPI_F32, 1>(p, tile, splits, s);
+    if (g.a_trans == 0 && g.b_trans == 1) return launch_tile<T, 0, 1, EPI_F32, 1>(p, tile, splits, s);
     return hipErrorInvalidValue;
   }
   switch (key) {
-    case 0 + EPI_STORE: return launch<T, 0, 0, EPI_STORE, 0>(p, 1, s);
-    case 0 + EPI_RESID: return launch<T, 0, 0, EPI_RESID, 0>(p, 1, s);
-    case 0 + EPI_GELU: return launch<T, 0, 0, EPI_GELU, 0>(p, 1, s);
-    case 0 + EPI_F32: return launch<T, 0, 0, EPI_F32, 0>(p, 1, s);
-    case 10 + EPI_F32: return launch<T, 0, 1, EPI_F32, 0>(p, 1, s);
-    case 10 + EPI_STORE: return launch<T, 0, 1, EPI_STORE, 0>(p, 1, s);
-    case 10 + EPI_GELU_BWD: return launch<T, 0, 1, EPI_GELU_BWD, 0>(p, 1, s);
-    case 110 + EPI_F32: return launch<T, 1, 1, EPI_F32, 0>(p, 1, s);
+    case 0 + EPI_STORE: return launch_tile<T, 0, 0, EPI_STORE, 0>(p, tile, 1, s);
+    case 0 + EPI_RESID: return launch_tile<T, 0, 0, EPI_RESID, 0>(p, tile, 1, s);
+    case 0 + EPI_GELU: return launch_tile<T, 0, 0, EPI_GELU, 0>(p, tile, 1, s);
+    case 0 + EPI_F32: return launch_tile<T, 0, 0, EPI_F32, 0>(p, tile, 1, s);
+    case 10 + EPI_F32: return launch_tile<T, 0, 1, EPI_F32, 0>(p, tile, 1, s);
+    case 10 + EPI_STORE: return launch_tile<T, 0, 1, EPI_STORE, 0>(p, tile, 1, s);
+    case 10 + EPI_GELU_BWD: return launch_tile<T, 0, 1, EPI_GELU_BWD, 0>(p, tile, 1, s);
+    case 110 + EPI_F32: return launch_tile<T, 1, 1, EPI_F32, 0>(p, tile, 1, s);
     default: return hipErrorInvalidValue;
+  }
+}
+
+constexpr int TILE_BM[3] = {256, 256, 128};
+constexpr int TILE_BN[3] = {256, 128, 128};
+constexpr int TILE_SLOTS[3] = {256, 256, 512};          // resident workgroups on 256 CUs
+constexpr double TILE_RATE[3] = {1.0, 0.8, 0.55};       // relative MFMA efficiency per tile
+
+// Pick the tile (and, for split-capable products, the K split) with the
+// smallest modelled time: waves of resident workgroups x per-tile work / rate.
+void choose(int M, int N, int K, bool can_split, int* tile_out, int* splits_out) {
+  double best = 1e300;
+  for (int t = 0; t < 3; ++t) {
+    const int64_t tiles = (int64_t)cdiv(M, TILE_BM[t]) * cdiv(N, TILE_BN[t]);
+    for (int sp = 1; sp <= (can_split ? 32 : 1); ++sp) {
+      const int kps = cdiv(cdiv(K, sp), 64) * 64;
+      if (sp > 1 && kps < 256) break;
+      const int64_t wgs = tiles * sp;
+      const double waves = (double)((wgs + TILE_SLOTS[t] - 1) / TILE_SLOTS[t]);
+      double cost = waves * (double)TILE_BM[t] * TILE_BN[t] * kps / TILE_RATE[t];
+      if (sp > 1) cost += 3.0 * (double)sp * M * N;  // partial sums written, read, reduced
+      if (cost < best * 0.999) {
+        best = cost;
+        *tile_out = t;
+        *splits_out = sp;
+      }
+    }
   }
 }
 
 }  // namespace
 
 int gemm_pick_splits(int M, int N, int K) {
-  const int tiles = cdiv(M, TM) * cdiv(N, TN);
-  int splits = 1;
-  // aim for about two workgroups per CU (256 CUs) with at least 512 k per split
-  while (tiles * splits < 512 && K / (splits * 2) >= 512) splits *= 2;
+  int tile = 2, splits = 1;
+  choose(M, N, K, true, &tile, &splits);
   return splits;
 }
 
 hipError_t gemm(const Gemm& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  const bool can_split = g.ws != nullptr && g.splits > 1 && g.epi == EPI_F32;
+  int tile = 2, splits = 1;
+  choose(g.M, g.N, g.K, can_split, &tile, &splits);
+  if (can_split) splits = std::min(splits, g.splits);
   Params p{};
   p.A = g.A;
   p.B = g.B;
@@ -294,20 +345,18 @@ hipError_t gemm(const Gemm& g, hipStream_t s) {
   p.C2 = g.C2;
   p.aux = g.aux;
   p.accumulate = g.accumulate;
-  p.tiles_m = cdiv(g.M, TM);
-  p.tiles_n = cdiv(g.N, TN);
+  p.tiles_m = cdiv(g.M, TILE_BM[tile]);
+  p.tiles_n = cdiv(g.N, TILE_BN[tile]);
   p.ws = g.ws;
-  int splits = g.splits;
-  if (splits > 1 && (g.epi != EPI_F32 || g.ws == nullptr)) return hipErrorInvalidValue;
   const int bk = TKB / (g.dtype == BF16 ? 2 : 4);
   if (splits > 1) {
-    int kps = cdiv(cdiv(g.K, splits), bk) * bk;
+    const int kps = cdiv(cdiv(g.K, splits), bk) * bk;
     p.k_per_split = kps;
     splits = cdiv(g.K, kps);
   } else {
     p.k_per_split = g.K;
   }
-  hipError_t e = (g.dtype == BF16) ? dispatch<bf16>(g, p, splits, s) : dispatch<float>(g, p, splits, s);
+  hipError_t e = (g.dtype == BF16) ? dispatch<bf16>(g, p, tile, splits, s) : dispatch<float>(g, p, tile, splits, s);
   if (e != hipSuccess || splits <= 1) return e;
   const int64_t total = (int64_t)g.M * g.N;
   hipLaunchKernelGGL(splitk_reduce, dim3(cdiv(total, 256)), dim3(256), 0, s, g.ws, splits, g.M,

@@ -141,24 +141,57 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
   }
 }
 
-__global__ void reduce_rows_kernel(const float* __restrict__ part, int nrows, int cols, int64_t ld,
-                                   float* out, int accumulate) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= cols) return;
+// out[c] (+)= sum_r part[r][c]: a block covers 16 columns with 16 row groups;
+// each thread sums its rows in order, then the 16 group sums are added in order.
+__global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ part, int nrows, int cols,
+                                                          int64_t ld, float* out, int accumulate) {
+  __shared__ float red[16][17];
+  const int cl = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int c = blockIdx.x * 16 + cl;
   float s = 0.f;
-  for (int r = 0; r < nrows; ++r) s += part[(int64_t)r * ld + c];
-  out[c] = accumulate ? out[c] + s : s;
+  if (c < cols)
+    for (int r = rg; r < nrows; r += 16) s += part[(int64_t)r * ld + c];
+  red[rg][cl] = s;
+  __syncthreads();
+  if (rg == 0 && c < cols) {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot += red[i][cl];
+    out[c] = accumulate ? out[c] + tot : tot;
+  }
 }
 
+// part[y][c] = sum of rows [256 y, 256 y + 256) of column c.  A thread owns 8
+// consecutive columns (16-byte loads for bf16, two for fp32) and a quarter of
+// the block's rows; the four quarters are added in order through LDS.
 template <typename T>
-__global__ void colsum_partial_kernel(const T* __restrict__ x, int rows, int cols, float* __restrict__ part) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= cols) return;
+__global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict__ x, int rows, int cols,
+                                                             float* __restrict__ part) {
+  __shared__ float red[4][64 * 8];
+  const int ch = threadIdx.x & 63, sub = threadIdx.x >> 6;
+  const int chunk = blockIdx.x * 64 + ch;
+  const int c0 = chunk * 8;
   const int r0 = blockIdx.y * 256;
   const int r1 = min(rows, r0 + 256);
-  float s = 0.f;
-  for (int r = r0; r < r1; ++r) s += to_f(x[(int64_t)r * cols + c]);
-  part[(int64_t)blockIdx.y * cols + c] = s;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  if (c0 < cols) {
+#pragma unroll 4
+    for (int r = r0 + sub; r < r1; r += 4) {
+      const T* p = x + (int64_t)r * cols + c0;
+      const float4 a = load4(p), b = load4(p + 4);
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) red[sub][ch * 8 + k] = acc[k];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int c = blockIdx.x * 512 + i;
+    if (c < cols) part[(int64_t)blockIdx.y * cols + c] = red[0][i] + red[1][i] + red[2][i] + red[3][i];
+  }
 }
 
 // Cross-entropy over one row of logits (CS336 page, section 1: subtract the
@@ -169,24 +202,49 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ y, float scale,
                                                       float* __restrict__ loss, float* __restrict__ lse_out,
                                                       T* __restrict__ dz) {
-  __shared__ float red[4];
+  __shared__ float sm[4], ss[4];
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const float* zr = z + (int64_t)row * ldz;
-  float mx = -__builtin_huge_valf();
-  for (int j = t; j < V; j += 256) mx = fmaxf(mx, zr[j]);
-  mx = wave_max(mx);
-  if (lane == 0) red[w] = mx;
+  // running max and sum of 2^((z - max) log2 e), rescaled when the max grows
+  float m = -__builtin_huge_valf(), s = 0.f;
+  const int V4 = V >> 2;
+  for (int j = t; j < V4; j += 256) {
+    const float4 v = load4(zr + 4 * j);
+    const float mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    if (mx > m) {
+      s *= hw_exp2((m - mx) * LOG2E);
+      m = mx;
+    }
+    s += hw_exp2((v.x - m) * LOG2E) + hw_exp2((v.y - m) * LOG2E) + hw_exp2((v.z - m) * LOG2E) +
+         hw_exp2((v.w - m) * LOG2E);
+  }
+  for (int j = 4 * V4 + t; j < V; j += 256) {
+    const float v = zr[j];
+    if (v > m) {
+      s *= hw_exp2((m - v) * LOG2E);
+      m = v;
+    }
+    s += hw_exp2((v - m) * LOG2E);
+  }
+  // combine (m, s) pairs across the wave, then across the 4 waves
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float mo = __shfl_xor(m, o, WAVE), so = __shfl_xor(s, o, WAVE);
+    const float mn = fmaxf(m, mo);
+    s = (mn == -__builtin_huge_valf()) ? 0.f : s * hw_exp2((m - mn) * LOG2E) + so * hw_exp2((mo - mn) * LOG2E);
+    m = mn;
+  }
+  if (lane == 0) {
+    sm[w] = m;
+    ss[w] = s;
+  }
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float s = 0.f;
-  for (int j = t; j < V; j += 256) s += hw_exp2((zr[j] - mx) * LOG2E);
-  s = wave_sum(s);
-  if (lane == 0) red[w] = s;
-  __syncthreads();
-  s = red[0] + red[1] + red[2] + red[3];
-  const float lse = mx + hw_log2(s) * LN2;
+  const float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  float S = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) S += ss[i] * hw_exp2((sm[i] - M) * LOG2E);
+  const float lse = M + hw_log2(S) * LN2;
   const int yy = y[row];
   if (t == 0) {
     loss[row] = lse - zr[yy];
@@ -194,10 +252,25 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
   }
   if (dz != nullptr) {
     T* dr = dz + (int64_t)row * ldz;
-    for (int j = t; j < ldz; j += 256) {
-      float d = 0.f;
-      if (j < V) d = (hw_exp2((zr[j] - lse) * LOG2E) - (j == yy ? 1.f : 0.f)) * scale;
-      dr[j] = from_f<T>(d);
+    const int L4 = (int)(ldz >> 2);
+    for (int j = t; j < L4; j += 256) {
+      const int c = 4 * j;
+      float d[4] = {0.f, 0.f, 0.f, 0.f};
+      if (c + 3 < V) {
+        const float4 v = load4(zr + c);
+        d[0] = hw_exp2((v.x - lse) * LOG2E);
+        d[1] = hw_exp2((v.y - lse) * LOG2E);
+        d[2] = hw_exp2((v.z - lse) * LOG2E);
+        d[3] = hw_exp2((v.w - lse) * LOG2E);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (c + k < V) d[k] = hw_exp2((zr[c + k] - lse) * LOG2E);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (c + k == yy) d[k] -= 1.f;
+      store4(dr + c, make_float4(d[0] * scale, d[1] * scale, d[2] * scale, d[3] * scale));
     }
   }
 }
@@ -264,13 +337,14 @@ hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float
 
 hipError_t reduce_rows_f32(const float* part, int nrows, int cols, int64_t ld, float* out, int accumulate,
                            hipStream_t s) {
-  hipLaunchKernelGGL(reduce_rows_kernel, dim3(cdiv(cols, 256)), dim3(256), 0, s, part, nrows, cols, ld, out,
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3(cdiv(cols, 16)), dim3(256), 0, s, part, nrows, cols, ld, out,
                      accumulate);
   return hipGetLastError();
 }
 
 hipError_t colsum_partial(int dtype, const void* x, int rows, int cols, float* part, hipStream_t s) {
-  dim3 grid(cdiv(cols, 256), cdiv(rows, 256));
+  if (cols % 8) return hipErrorInvalidValue;
+  dim3 grid(cdiv(cols / 8, 64), cdiv(rows, 256));
   if (dtype == BF16)
     hipLaunchKernelGGL(colsum_partial_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, rows, cols, part);
   else

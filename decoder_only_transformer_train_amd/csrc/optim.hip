@@ -70,15 +70,13 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const
   const float cs = scal[1], a = scal[3];
   const float dec = 1.f - lr * wd;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
-    float4 pp = reinterpret_cast<float4*>(p)[i];
-    const float4 gg = reinterpret_cast<const float4*>(g)[i];
-    float4 mm = reinterpret_cast<float4*>(m)[i];
-    float4 vv = reinterpret_cast<float4*>(v)[i];
+    const float4 p4 = reinterpret_cast<const float4*>(p)[i];
+    const float4 g4 = reinterpret_cast<const float4*>(g)[i];
+    const float4 m4 = reinterpret_cast<const float4*>(m)[i];
+    const float4 v4 = reinterpret_cast<const float4*>(v)[i];
     const float d = (i < n4_decay) ? dec : 1.f;
-    float* pa = &pp.x;
-    const float* ga = &gg.x;
-    float* ma = &mm.x;
-    float* va = &vv.x;
+    float pa[4] = {p4.x, p4.y, p4.z, p4.w}, ga[4] = {g4.x, g4.y, g4.z, g4.w};
+    float ma[4] = {m4.x, m4.y, m4.z, m4.w}, va[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float gk_ = ga[k] * cs;
@@ -86,9 +84,10 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const
       va[k] = b2 * va[k] + (1.f - b2) * gk_ * gk_;
       pa[k] = pa[k] * d - a * ma[k] / (sqrtf(va[k]) + eps);
     }
+    const float4 pp = make_float4(pa[0], pa[1], pa[2], pa[3]);
     reinterpret_cast<float4*>(p)[i] = pp;
-    reinterpret_cast<float4*>(m)[i] = mm;
-    reinterpret_cast<float4*>(v)[i] = vv;
+    reinterpret_cast<float4*>(m)[i] = make_float4(ma[0], ma[1], ma[2], ma[3]);
+    reinterpret_cast<float4*>(v)[i] = make_float4(va[0], va[1], va[2], va[3]);
     if (shadow) store4(shadow + 4 * i, pp);
   }
 }
