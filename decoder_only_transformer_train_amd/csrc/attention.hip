@@ -374,6 +374,7 @@ hipError_t bwd_t(const void* qkv, const void* o, const void* dO, const float* ls
   const int N = B * Tn;
   hipLaunchKernelGGL((attn_bwd_pre_kernel<T, D>), dim3(cdiv((int64_t)N * H * (D / Tr<T>::E), 256)), dim3(256), 0,
                      s, (const T*)o, (const T*)dO, Dv, N, Tn, H);
+  if constexpr (sizeof(T) == 2 && D == 64) return attn_bwd_bf16_d64(qkv, dO, lse, Dv, dqkv, B, Tn, H, s);
   dim3 grid((Tn + 63) / 64, B * H);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), grid, dim3(256), 0, s, (const T*)qkv, (const T*)dO, lse, Dv,
                      (T*)dqkv, Tn, H);
@@ -385,7 +386,7 @@ hipError_t bwd_t(const void* qkv, const void* o, const void* dO, const float* ls
 }  // namespace
 
 hipError_t attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int Tn, int H, int D, hipStream_t s) {
-  if (dtype == BF16 && D == 64) return fwd_t<bf16, 64>(qkv, o, lse, B, Tn, H, s);
+  if (dtype == BF16 && D == 64) return attn_fwd_bf16_d64(qkv, o, lse, B, Tn, H, s);
   if (dtype == F32 && D == 64) return fwd_t<float, 64>(qkv, o, lse, B, Tn, H, s);
   if (dtype == F32 && D == 32) return fwd_t<float, 32>(qkv, o, lse, B, Tn, H, s);
   if (dtype == F32 && D == 16) return fwd_t<float, 16>(qkv, o, lse, B, Tn, H, s);

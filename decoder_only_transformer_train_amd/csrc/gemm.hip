@@ -1,23 +1,50 @@
 // MFMA GEMM for gfx950: C[m][n] = sum_k A(m,k) B(n,k) with fused epilogues.
 //
-// One template serves fp32 (16x16x4 f32 MFMA) and bf16 (16x16x32 bf16 MFMA):
-// operand tiles are staged in LDS as [128 rows][128 bytes of k] with a
-// 16-byte row pad, so every lane reads one conflict-free 16-byte fragment
-// per MFMA step regardless of the element type.  Operands whose k dimension
+// One template serves fp32 (16x16x4 f32 MFMA) and bf16 (32x32x16 bf16 MFMA,
+// the shape that reaches the chip's dense peak from a single wave per SIMD):
+// operand tiles are staged in LDS as [rows][128 bytes of k] with a 16-byte
+// row pad, so every lane reads one conflict-free 16-byte fragment per MFMA
+// step regardless of the element type.  Operands are read through buffer
+// descriptors whose range ends at the operand, so loads past M, N or K
+// return zeros without a branch.  Operands whose k dimension
 // is not contiguous in memory (the weight-gradient and data-gradient
 // products) are transposed in registers on their way into LDS, so global
 // loads stay 16-byte and coalesced.  Workgroup: 4 waves in 2x2; the tile is
 // BM x BN (256x256, 256x128 or 128x128, chosen per shape), each wave owns a
-// (BM/2) x (BN/2) sub-tile, so a 256x256 tile reads half the LDS bytes per
-// MFMA of a 128x128 one.  LDS is double-buffered with the next tile's global
-// loads in flight during the current tile's MFMAs.  Workgroup ids are
+// (BM/2) x (BN/2) sub-tile.  LDS is double-buffered with the next tile's
+// global loads in flight during the current tile's MFMAs; the 256x256 bf16
+// kernel additionally interleaves its LDS reads, stores and global loads
+// with the MFMAs by explicit scheduling groups.  Workgroup ids are
 // remapped so each XCD (ids are dealt round-robin to the 8 XCDs) works on a
 // contiguous, grouped run of tiles that share operand rows in its L2.
 #include "common.h"
 #include "kernels.h"
 
+#include <cstdlib>
+
 namespace gk {
 namespace {
+
+// MFMA geometry: bf16 uses 32x32x16 (one 16-byte fragment per lane: row lane % 32,
+// k-group lane / 32 of 8 elements; 16 accumulators per lane), fp32 uses four
+// 16x16x4 ops per fragment (row lane % 16, k-group lane / 16 of 4 elements).
+template <typename T> struct Mf;
+template <> struct Mf<bf16> {
+  static constexpr int R = 32, KG = 2, NA = 16;
+  typedef f32x16 acc_t;
+  static __device__ __forceinline__ void mma(acc_t& c, const uint4& a, const uint4& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(a), bitcast<bf16x8>(b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int row(int i, int lane) { return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
+  static __device__ __forceinline__ int col(int lane) { return lane & 31; }
+};
+template <> struct Mf<float> {
+  static constexpr int R = 16, KG = 4, NA = 4;
+  typedef f32x4 acc_t;
+  static __device__ __forceinline__ void mma(acc_t& c, const uint4& a, const uint4& b) { mfma_frag(c, a, b, 0.f); }
+  static __device__ __forceinline__ int row(int i, int lane) { return (lane >> 4) * 4 + i; }
+  static __device__ __forceinline__ int col(int lane) { return lane & 15; }
+};
 
 constexpr int TKB = 128;          // k bytes per tile (bf16: 64, fp32: 32 elements)
 constexpr int PITCH = TKB + 16;   // LDS row pitch (bytes)
@@ -40,25 +67,32 @@ struct Params {
   float* ws;
 };
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Buffer resource over [p, p + bytes): loads past the end return zero, which
+// is how every tile edge (rows past M/N, k-rows past K) is handled.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 template <typename T, int TRANS, int ROWS>
 struct Loader {
   static constexpr int NR = ROWS / 32;  // 16-byte registers per thread
   uint4 r[NR];
   // TRANS == 0: operand stored [rows][ld], k contiguous.
   // TRANS == 1: operand stored [K][ld], rows contiguous; a unit is 4 k-rows x E elements.
-  __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, int row0, int rows,
-                                       int k0, int kend, int t) {
+  __device__ __forceinline__ void load(rsrc_t rs, int64_t ld, int row0, int k0, int t) {
     constexpr int E = Tr<T>::E;
     if constexpr (TRANS == 0) {
       const int cc = t & 7;
-      const int k = k0 + cc * E;
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
-        const int row = row0 + (t >> 3) + 32 * i;
-        if (row < rows && k < kend)
-          r[i] = *reinterpret_cast<const uint4*>(base + (int64_t)row * ld + k);
-        else
-          r[i] = make_uint4(0, 0, 0, 0);
+        const int64_t row = row0 + (t >> 3) + 32 * i;
+        r[i] = bload(rs, (uint32_t)((row * ld + k0 + cc * E) * (int64_t)sizeof(T)));
       }
     } else {
       constexpr int MCH = ROWS / E;
@@ -66,14 +100,10 @@ struct Loader {
       for (int u = 0; u < NR / 4; ++u) {
         const int unit = t + 256 * u;
         const int mc = unit % MCH, kg = unit / MCH;
-        const int row = row0 + mc * E;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int k = k0 + kg * 4 + i;
-          if (k < kend && row < rows)
-            r[4 * u + i] = *reinterpret_cast<const uint4*>(base + (int64_t)k * ld + row);
-          else
-            r[4 * u + i] = make_uint4(0, 0, 0, 0);
+          const int64_t k = k0 + kg * 4 + i;
+          r[4 * u + i] = bload(rs, (uint32_t)((k * ld + row0 + mc * E) * (int64_t)sizeof(T)));
         }
       }
     }
@@ -137,8 +167,10 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
 
 template <typename T, int TA, int TB, int EPI, int SPLIT, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_kernel(Params p) {
-  constexpr int WM = BM / 2, WN = BN / 2;    // wave sub-tile
-  constexpr int FM = WM / 16, FN = WN / 16;  // 16x16 MFMA tiles per wave
+  using M_ = Mf<T>;
+  constexpr int WM = BM / 2, WN = BN / 2;          // wave sub-tile
+  constexpr int FM = WM / M_::R, FN = WN / M_::R;  // MFMA tiles per wave
+  constexpr int KSTEPS = TKB / (M_::KG * 16);
   constexpr int STAGE = (BM + BN) * PITCH;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   const int t = threadIdx.x;
@@ -152,68 +184,75 @@ __global__ __launch_bounds__(256) void gemm_kernel(Params p) {
   constexpr int BK = TKB / sizeof(T);
   const int nk = (kend - kb0 + BK - 1) / BK;
 
-  const T* A = reinterpret_cast<const T*>(p.A);
-  const T* B = reinterpret_cast<const T*>(p.B);
-  Loader<T, TA, BM> la;
-  Loader<T, TB, BN> lb;
-  f32x4 acc[FM][FN];
+  const rsrc_t ra = make_rsrc(p.A, (TA ? (int64_t)p.K : (int64_t)p.M) * p.lda * (int64_t)sizeof(T));
+  const rsrc_t rb = make_rsrc(p.B, (TB ? (int64_t)p.K : (int64_t)p.N) * p.ldb * (int64_t)sizeof(T));
+  typename M_::acc_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < M_::NA; ++e) acc[i][j][e] = 0.f;
 
+  const int frow = lane % M_::R, fk = (lane / M_::R) * 16;
+  auto compute = [&](const char* sa) {
+    const char* sb = sa + BM * PITCH;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint4 af[FM], bfr[FN];
+      const int koff = ks * (M_::KG * 16) + fk;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(sa + (wm * WM + i * M_::R + frow) * PITCH + koff);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const uint4*>(sb + (wn * WN + j * M_::R + frow) * PITCH + koff);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) M_::mma(acc[i][j], af[i], bfr[j]);
+    }
+  };
+
+  char* buf0 = smem;
+  char* buf1 = smem + STAGE;
+  Loader<T, TA, BM> la;
+  Loader<T, TB, BN> lb;
   if (nk > 0) {
-    la.load(A, p.lda, m0, p.M, kb0, kend, t);
-    lb.load(B, p.ldb, n0, p.N, kb0, kend, t);
-    la.store(smem, t);
-    lb.store(smem + BM * PITCH, t);
+    la.load(ra, p.lda, m0, kb0, t);
+    lb.load(rb, p.ldb, n0, kb0, t);
+    la.store(buf0, t);
+    lb.store(buf0 + BM * PITCH, t);
   }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
     const bool more = kt + 1 < nk;
     if (more) {
-      la.load(A, p.lda, m0, p.M, kb0 + (kt + 1) * BK, kend, t);
-      lb.load(B, p.ldb, n0, p.N, kb0 + (kt + 1) * BK, kend, t);
+      la.load(ra, p.lda, m0, kb0 + (kt + 1) * BK, t);
+      lb.load(rb, p.ldb, n0, kb0 + (kt + 1) * BK, t);
     }
-    const char* sa = smem + cur * STAGE;
-    const char* sb = sa + BM * PITCH;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 af[FM], bfr[FN];
-      const int koff = ks * 64 + (lane >> 4) * 16;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(sa + (wm * WM + i * 16 + (lane & 15)) * PITCH + koff);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const uint4*>(sb + (wn * WN + j * 16 + (lane & 15)) * PITCH + koff);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) mfma_frag(acc[i][j], af[i], bfr[j], T());
-    }
+    compute((kt & 1) ? buf1 : buf0);
     if (more) {
-      char* sn = smem + (cur ^ 1) * STAGE;
+      char* sn = (kt & 1) ? buf0 : buf1;
       la.store(sn, t);
       lb.store(sn + BM * PITCH, t);
     }
     __syncthreads();
   }
 
-  // epilogue: lane holds rows (lane / 16) * 4 + r, column lane % 16 of each 16x16 tile
+  // epilogue
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * WN + j * 16 + (lane & 15);
+      const int n = n0 + wn * WN + j * M_::R + M_::col(lane);
       if (n >= p.N) continue;
       const float bn = (p.bias != nullptr) ? p.bias[n] : 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + r;
+      for (int e = 0; e < M_::NA; ++e) {
+        const int m = m0 + wm * WM + i * M_::R + M_::row(e, lane);
         if (m >= p.M) continue;
-        const float a = acc[i][j][r];
+        const float a = acc[i][j][e];
         if constexpr (SPLIT) {
           p.ws[((int64_t)blockIdx.z * p.M + m) * p.N + n] = a;
         } else {
@@ -230,6 +269,144 @@ __global__ __launch_bounds__(256) void gemm_kernel(Params p) {
             const float u = to_f(reinterpret_cast<const T*>(p.aux)[o]);
             reinterpret_cast<T*>(p.C)[o] = from_f<T>(a * gelu_grad_f(u));
           } else {  // EPI_F32
+            float* c = reinterpret_cast<float*>(p.C);
+            c[o] = p.accumulate ? c[o] + a : a;
+          }
+        }
+      }
+    }
+  }
+}
+
+
+// 256x256 bf16 tile, 4 waves of 128x128, 32x32x16 MFMAs, explicitly interleaved:
+// every k-step issues its 16 MFMAs interleaved with the LDS reads of the next
+// k-step; the next tile's LDS stores and the tile after that's global loads are
+// spread over the middle k-steps; one barrier per k-tile, placed so the last
+// k-step's MFMAs overlap it.  The loop is branch-free: loads past the operands
+// read zeros through the buffer descriptors and land in the unused LDS stage.
+#define SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+template <int TA, int TB, int EPI, int SPLIT>
+__global__ __launch_bounds__(256, 1) void gemm256_kernel(Params p) {
+  typedef bf16 T;
+  using M_ = Mf<T>;
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128;
+  constexpr int FM = 4, FN = 4;
+  constexpr int STAGE = (BM + BN) * PITCH;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kb0 = blockIdx.z * p.k_per_split;
+  const int kend = min(p.K, kb0 + p.k_per_split);
+  constexpr int BK = 64;
+  const int nk = (kend - kb0 + BK - 1) / BK;
+  const rsrc_t ra = make_rsrc(p.A, (TA ? (int64_t)p.K : (int64_t)p.M) * p.lda * 2);
+  const rsrc_t rb = make_rsrc(p.B, (TB ? (int64_t)p.K : (int64_t)p.N) * p.ldb * 2);
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int frow = lane & 31, fk = (lane >> 5) * 16;
+  const int arow = (wm * WM + frow) * PITCH + fk, brow = (wn * WN + frow) * PITCH + fk;
+  Loader<T, TA, BM> la;
+  Loader<T, TB, BN> lb;
+  uint4 fa[2][FM], fb[2][FN];
+  auto read_frags = [&](const char* st, int ks, int slot) {
+    const char* sa = st + arow + ks * 32;
+    const char* sb = st + BM * PITCH + brow + ks * 32;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[slot][i] = *reinterpret_cast<const uint4*>(sa + i * 32 * PITCH);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[slot][j] = *reinterpret_cast<const uint4*>(sb + j * 32 * PITCH);
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) M_::mma(acc[i][j], fa[slot][i], fb[slot][j]);
+  };
+  constexpr int NLOAD = Loader<T, TA, BM>::NR + Loader<T, TB, BN>::NR;          // buffer loads per tile
+  constexpr int NSTORE = (TA ? (BM / 32) / 4 * 16 : BM / 32) + (TB ? (BN / 32) / 4 * 16 : BN / 32);
+  // prologue: tile 0 into LDS stage 0, tile 1 in flight, k-step 0 fragments read
+  la.load(ra, p.lda, m0, kb0, t);
+  lb.load(rb, p.ldb, n0, kb0, t);
+  la.store(smem, t);
+  lb.store(smem + BM * PITCH, t);
+  la.load(ra, p.lda, m0, kb0 + BK, t);
+  lb.load(rb, p.ldb, n0, kb0 + BK, t);
+  __syncthreads();
+  read_frags(smem, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    char* cur = smem + (kt & 1) * STAGE;
+    char* nxt = smem + ((kt & 1) ^ 1) * STAGE;
+    // k-step 0: MFMAs on slot 0, read k-step 1 into slot 1
+    read_frags(cur, 1, 1);
+    mfmas(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x100, 1); }
+    SGB(0x008, 8);
+    // k-step 1: store the next tile into the other stage while computing
+    read_frags(cur, 2, 0);
+    la.store(nxt, t);
+    lb.store(nxt + BM * PITCH, t);
+    mfmas(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x100, 1); }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x200, NSTORE / 8); }
+    // k-step 2: global loads of the tile after next
+    read_frags(cur, 3, 1);
+    la.load(ra, p.lda, m0, kb0 + (kt + 2) * BK, t);
+    lb.load(rb, p.ldb, n0, kb0 + (kt + 2) * BK, t);
+    mfmas(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x100, 1); }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x020, NLOAD / 8); }
+    __syncthreads();
+    // k-step 3: MFMAs on slot 1, read k-step 0 of the next tile into slot 0
+    read_frags(nxt, 0, 0);
+    mfmas(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x100, 1); }
+    SGB(0x008, 8);
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * WN + j * 32 + M_::col(lane);
+      if (n >= p.N) continue;
+      const float bn = (p.bias != nullptr) ? p.bias[n] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * WM + i * 32 + M_::row(e, lane);
+        if (m >= p.M) continue;
+        const float a = acc[i][j][e];
+        if constexpr (SPLIT) {
+          p.ws[((int64_t)blockIdx.z * p.M + m) * p.N + n] = a;
+        } else {
+          const int64_t o = (int64_t)m * p.ldc + n;
+          if constexpr (EPI == EPI_STORE) {
+            reinterpret_cast<T*>(p.C)[o] = from_f<T>(a + bn);
+          } else if constexpr (EPI == EPI_RESID) {
+            reinterpret_cast<float*>(p.C)[o] = p.R[o] + (a + bn);
+          } else if constexpr (EPI == EPI_GELU) {
+            const float u = a + bn;
+            reinterpret_cast<T*>(p.C)[o] = from_f<T>(u);
+            reinterpret_cast<T*>(p.C2)[o] = from_f<T>(gelu_f(u));
+          } else if constexpr (EPI == EPI_GELU_BWD) {
+            const float u = to_f(reinterpret_cast<const T*>(p.aux)[o]);
+            reinterpret_cast<T*>(p.C)[o] = from_f<T>(a * gelu_grad_f(u));
+          } else {
             float* c = reinterpret_cast<float*>(p.C);
             c[o] = p.accumulate ? c[o] + a : a;
           }
@@ -261,6 +438,13 @@ hipError_t launch(const Params& p, int splits, hipStream_t s) {
 
 template <typename T, int TA, int TB, int EPI, int SPLIT>
 hipError_t launch_tile(const Params& p, int tile, int splits, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (tile == 0) {
+      dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
+      hipLaunchKernelGGL((gemm256_kernel<TA, TB, EPI, SPLIT>), grid, dim3(256), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   switch (tile) {
     case 0: return launch<T, TA, TB, EPI, SPLIT, 256, 256>(p, splits, s);
     case 1: return launch<T, TA, TB, EPI, SPLIT, 256, 128>(p, splits, s);
@@ -291,44 +475,49 @@ hipError_t dispatch(const Gemm& g, const Params& p, int tile, int splits, hipStr
 
 constexpr int TILE_BM[3] = {256, 256, 128};
 constexpr int TILE_BN[3] = {256, 128, 128};
-constexpr int TILE_SLOTS[3] = {256, 256, 512};          // resident workgroups on 256 CUs
-constexpr double TILE_RATE[3] = {1.0, 0.8, 0.55};       // relative MFMA efficiency per tile
 
-// Pick the tile (and, for split-capable products, the K split) with the
-// smallest modelled time: waves of resident workgroups x per-tile work / rate.
-void choose(int M, int N, int K, bool can_split, int* tile_out, int* splits_out) {
-  double best = 1e300;
-  for (int t = 0; t < 3; ++t) {
-    const int64_t tiles = (int64_t)cdiv(M, TILE_BM[t]) * cdiv(N, TILE_BN[t]);
-    for (int sp = 1; sp <= (can_split ? 32 : 1); ++sp) {
-      const int kps = cdiv(cdiv(K, sp), 64) * 64;
-      if (sp > 1 && kps < 256) break;
-      const int64_t wgs = tiles * sp;
-      const double waves = (double)((wgs + TILE_SLOTS[t] - 1) / TILE_SLOTS[t]);
-      double cost = waves * (double)TILE_BM[t] * TILE_BN[t] * kps / TILE_RATE[t];
-      if (sp > 1) cost += 3.0 * (double)sp * M * N;  // partial sums written, read, reduced
-      if (cost < best * 0.999) {
-        best = cost;
-        *tile_out = t;
-        *splits_out = sp;
-      }
-    }
+// Tile and K-split choice from measurements of the step's shapes on MI355X:
+// 128x128 (two workgroups per CU) wins for K up to ~3K with most epilogues;
+// the interleaved 256x256 kernel wins for long-K products with enough tiles.
+// Split-K (weight gradients only) is sized so that tiles x splits fills about
+// two workgroups per CU with at least 512 k per split.
+void choose(int M, int N, int K, bool can_split, int dtype, int a_trans, int b_trans, int* tile_out,
+            int* splits_out) {
+  int tile = 2;
+  const int64_t t256 = (int64_t)cdiv(M, 256) * cdiv(N, 256);
+  if (dtype == BF16 && !a_trans && ((b_trans && K >= 3072) || K >= 8192) && t256 >= 160) tile = 0;
+  int splits = 1;
+  if (can_split) {
+    const int64_t tiles = (int64_t)cdiv(M, TILE_BM[tile]) * cdiv(N, TILE_BN[tile]);
+    while (tiles * splits < 512 && K / (splits * 2) >= 512) splits *= 2;
   }
+  *tile_out = tile;
+  *splits_out = splits;
 }
 
 }  // namespace
 
 int gemm_pick_splits(int M, int N, int K) {
   int tile = 2, splits = 1;
-  choose(M, N, K, true, &tile, &splits);
+  choose(M, N, K, true, BF16, 1, 1, &tile, &splits);
   return splits;
+}
+
+// GPT_GEMM_TILE=0|1|2 pins the tile (256x256, 256x128, 128x128) for tuning runs.
+static int forced_tile() {
+  static const int v = [] {
+    const char* e = getenv("GPT_GEMM_TILE");
+    return (e && e[0] >= '0' && e[0] <= '2') ? e[0] - '0' : -1;
+  }();
+  return v;
 }
 
 hipError_t gemm(const Gemm& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const bool can_split = g.ws != nullptr && g.splits > 1 && g.epi == EPI_F32;
   int tile = 2, splits = 1;
-  choose(g.M, g.N, g.K, can_split, &tile, &splits);
+  choose(g.M, g.N, g.K, can_split, g.dtype, g.a_trans, g.b_trans, &tile, &splits);
+  if (forced_tile() >= 0) tile = forced_tile();
   if (can_split) splits = std::min(splits, g.splits);
   Params p{};
   p.A = g.A;
@@ -349,6 +538,10 @@ hipError_t gemm(const Gemm& g, hipStream_t s) {
   p.tiles_n = cdiv(g.N, TILE_BN[tile]);
   p.ws = g.ws;
   const int bk = TKB / (g.dtype == BF16 ? 2 : 4);
+  // a k-contiguous operand is read in whole k-tiles: its rows must be padded
+  // (with zeros) up to the next tile when K is not a multiple of it
+  const int64_t kpad = (int64_t)cdiv(g.K, bk) * bk;
+  if ((!g.a_trans && g.lda < kpad) || (!g.b_trans && g.ldb < kpad)) return hipErrorInvalidValue;
   if (splits > 1) {
     const int kps = cdiv(cdiv(g.K, splits), bk) * bk;
     p.k_per_split = kps;

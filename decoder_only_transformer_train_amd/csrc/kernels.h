@@ -66,6 +66,10 @@ hipError_t colsum_partial(int dtype, const void* x, int rows, int cols, float* p
 // qkv T [B*T][3C] (q | k | v, head h at channels h*D..), o T [B*T][C], lse f32 [B][H][T]
 hipError_t attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int D,
                     hipStream_t s);
+// bf16, head size 64 kernels on 32x32x16 MFMAs (attention_bf16.hip); Dv precomputed
+hipError_t attn_fwd_bf16_d64(const void* qkv, void* o, float* lse, int B, int T, int H, hipStream_t s);
+hipError_t attn_bwd_bf16_d64(const void* qkv, const void* dO, const float* lse, const float* Dv,
+                             void* dqkv, int B, int T, int H, hipStream_t s);
 // dO T [B*T][C] -> dqkv T [B*T][3C]; Dv f32 [B][H][T] workspace
 hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse,
                     float* Dv, void* dqkv, int B, int T, int H, int D, hipStream_t s);
