@@ -59,10 +59,11 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float hw_exp(float x) { return hw_exp2(x * LOG2E); }
 
-// tanh from its definition through e^(2x): tanh x = 1 - 2 / (e^(2x) + 1).
+// tanh from its definition through e^(2x): tanh x = 1 - 2 / (e^(2x) + 1), with
+// the hardware reciprocal (v_rcp_f32, 1 ulp); e = inf gives rcp = 0, tanh = 1.
 __device__ __forceinline__ float tanh_exp(float x) {
   float e = hw_exp2(x * (2.0f * LOG2E));
-  return 1.0f - 2.0f / (e + 1.0f);
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
 }
 
 // tanh-approximate GELU and its derivative (Hendrycks & Gimpel 2016).

@@ -126,7 +126,11 @@ struct Loader {
         const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[4 * u + 2]);
         const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[4 * u + 3]);
         if constexpr (sizeof(T) == 2) {
-          // 4 k-rows x 8 elements -> 8 rows x 4 k-elements (8 bytes each)
+          // 4 k-rows x 8 elements -> 8 rows x 4 k-elements (8 bytes each).  Lanes
+          // that store together hold different m-chunks whose rows are 8 apart; each
+          // lane starts its 8 stores at row (mc % 8) so one store instruction spreads
+          // over the banks instead of stacking on 8 of them.
+          uint2 out[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int wi = e >> 1;
@@ -138,7 +142,17 @@ struct Loader {
               lo = (w0[wi] & 0xFFFFu) | (w1[wi] << 16);
               hi = (w2[wi] & 0xFFFFu) | (w3[wi] << 16);
             }
-            *reinterpret_cast<uint2*>(s + (mc * 8 + e) * PITCH + kg * 8) = make_uint2(lo, hi);
+            out[e] = make_uint2(lo, hi);
+          }
+          const int rot = mc & 7;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int e = (j + rot) & 7;
+            uint2 v = out[0];
+#pragma unroll
+            for (int q = 1; q < 8; ++q)
+              if (e == q) v = out[q];
+            *reinterpret_cast<uint2*>(s + (mc * 8 + e) * PITCH + kg * 8) = v;
           }
         } else {
           // fp32: 4 k-rows x 4 elements -> 4 rows x 4 k-elements (16 bytes each)
@@ -163,6 +177,104 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
   const int in = id - group * per_group;
   tm = first_m + in % gsize;
   tn = in / gsize;
+}
+
+
+// Epilogue through LDS: the accumulator tile is written to LDS as fp32 rows
+// (PASS_ROWS rows per pass), then every thread handles groups of 4 adjacent
+// columns with 16-byte (fp32) / 8-byte (bf16) coalesced global accesses.
+template <typename T, int EPI, int SPLIT>
+__device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 a) {
+  float v[4] = {a.x, a.y, a.z, a.w};
+  const bool full = n + 3 < p.N;
+  if constexpr (SPLIT) {
+    float* o = p.ws + ((int64_t)blockIdx.z * p.M + m) * p.N + n;
+    if (full && (p.N & 3) == 0) {
+      *reinterpret_cast<float4*>(o) = a;
+    } else {
+      for (int k = 0; k < 4; ++k)
+        if (n + k < p.N) o[k] = v[k];
+    }
+    return;
+  }
+  const int64_t o = (int64_t)m * p.ldc + n;
+  if (!full || (p.ldc & 3)) {  // ragged edge: element by element
+    for (int k = 0; k < 4; ++k) {
+      if (n + k >= p.N) break;
+      const float bn = p.bias ? p.bias[n + k] : 0.f;
+      const float x = v[k];
+      if constexpr (EPI == EPI_STORE) reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
+      else if constexpr (EPI == EPI_RESID) reinterpret_cast<float*>(p.C)[o + k] = p.R[o + k] + (x + bn);
+      else if constexpr (EPI == EPI_GELU) {
+        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
+        reinterpret_cast<T*>(p.C2)[o + k] = from_f<T>(gelu_f(x + bn));
+      } else if constexpr (EPI == EPI_GELU_BWD) {
+        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x * gelu_grad_f(to_f(reinterpret_cast<const T*>(p.aux)[o + k])));
+      } else {
+        float* c = reinterpret_cast<float*>(p.C);
+        c[o + k] = p.accumulate ? c[o + k] + x : x;
+      }
+    }
+    return;
+  }
+  float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (p.bias) b4 = *reinterpret_cast<const float4*>(p.bias + n);
+  if constexpr (EPI == EPI_STORE) {
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w));
+  } else if constexpr (EPI == EPI_RESID) {
+    const float4 r = *reinterpret_cast<const float4*>(p.R + o);
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) =
+        make_float4(r.x + (a.x + b4.x), r.y + (a.y + b4.y), r.z + (a.z + b4.z), r.w + (a.w + b4.w));
+  } else if constexpr (EPI == EPI_GELU) {
+    const float4 u = make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w);
+    store4(reinterpret_cast<T*>(p.C) + o, u);
+    store4(reinterpret_cast<T*>(p.C2) + o, make_float4(gelu_f(u.x), gelu_f(u.y), gelu_f(u.z), gelu_f(u.w)));
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    const float4 u = load4(reinterpret_cast<const T*>(p.aux) + o);
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x * gelu_grad_f(u.x), a.y * gelu_grad_f(u.y),
+                                                      a.z * gelu_grad_f(u.z), a.w * gelu_grad_f(u.w)));
+  } else {
+    float* c = reinterpret_cast<float*>(p.C) + o;
+    if (p.accumulate) {
+      const float4 c0 = *reinterpret_cast<const float4*>(c);
+      a = make_float4(c0.x + a.x, c0.y + a.y, c0.z + a.z, c0.w + a.w);
+    }
+    *reinterpret_cast<float4*>(c) = a;
+  }
+}
+
+// Stage acc through LDS (smem, at least PASS_ROWS * (BN + 4) floats) and run
+// the epilogue.  Waves whose sub-tile rows fall in the current pass write.
+template <typename T, int EPI, int SPLIT, int BM, int BN, int PASS_ROWS, typename ACC, int FM, int FN>
+__device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN], char* smem, int m0, int n0,
+                                             int wm, int wn, int lane, int t) {
+  using M_ = Mf<T>;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int LDW = BN + 4;
+  float* st = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int pass = 0; pass < BM / PASS_ROWS; ++pass) {
+    __syncthreads();
+    if (wm * WM >= pass * PASS_ROWS && wm * WM < (pass + 1) * PASS_ROWS) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < M_::NA; ++e) {
+            const int r = wm * WM - pass * PASS_ROWS + i * M_::R + M_::row(e, lane);
+            const int c = wn * WN + j * M_::R + M_::col(lane);
+            st[r * LDW + c] = acc[i][j][e];
+          }
+    }
+    __syncthreads();
+    for (int g = t; g < PASS_ROWS * (BN / 4); g += 256) {
+      const int r = g / (BN / 4), c4 = g % (BN / 4);
+      const int m = m0 + pass * PASS_ROWS + r, n = n0 + c4 * 4;
+      if (m >= p.M || n >= p.N) continue;
+      epi_group<T, EPI, SPLIT>(p, m, n, *reinterpret_cast<const float4*>(st + r * LDW + c4 * 4));
+    }
+  }
 }
 
 template <typename T, int TA, int TB, int EPI, int SPLIT, int BM, int BN>
@@ -240,44 +352,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(Params p) {
     __syncthreads();
   }
 
-  // epilogue
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * WN + j * M_::R + M_::col(lane);
-      if (n >= p.N) continue;
-      const float bn = (p.bias != nullptr) ? p.bias[n] : 0.f;
-#pragma unroll
-      for (int e = 0; e < M_::NA; ++e) {
-        const int m = m0 + wm * WM + i * M_::R + M_::row(e, lane);
-        if (m >= p.M) continue;
-        const float a = acc[i][j][e];
-        if constexpr (SPLIT) {
-          p.ws[((int64_t)blockIdx.z * p.M + m) * p.N + n] = a;
-        } else {
-          const int64_t o = (int64_t)m * p.ldc + n;
-          if constexpr (EPI == EPI_STORE) {
-            reinterpret_cast<T*>(p.C)[o] = from_f<T>(a + bn);
-          } else if constexpr (EPI == EPI_RESID) {
-            reinterpret_cast<float*>(p.C)[o] = p.R[o] + (a + bn);
-          } else if constexpr (EPI == EPI_GELU) {
-            const float u = a + bn;
-            reinterpret_cast<T*>(p.C)[o] = from_f<T>(u);
-            reinterpret_cast<T*>(p.C2)[o] = from_f<T>(gelu_f(u));
-          } else if constexpr (EPI == EPI_GELU_BWD) {
-            const float u = to_f(reinterpret_cast<const T*>(p.aux)[o]);
-            reinterpret_cast<T*>(p.C)[o] = from_f<T>(a * gelu_grad_f(u));
-          } else {  // EPI_F32
-            float* c = reinterpret_cast<float*>(p.C);
-            c[o] = p.accumulate ? c[o] + a : a;
-          }
-        }
-      }
-    }
-  }
+  // epilogue through LDS (the main loop's stages are free now)
+  static_assert(2 * STAGE >= (BM <= 128 ? BM : 128) * (BN + 4) * 4, "LDS too small for the epilogue");
+  epilogue_lds<T, EPI, SPLIT, BM, BN, (BM <= 128 ? BM : 128)>(p, acc, smem, m0, n0, wm, wn, lane, t);
 }
-
 
 // 256x256 bf16 tile, 4 waves of 128x128, 32x32x16 MFMAs, explicitly interleaved:
 // every k-step issues its 16 MFMAs interleaved with the LDS reads of the next
@@ -379,41 +457,7 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(Params p) {
     SGB(0x008, 8);
   }
 
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * WN + j * 32 + M_::col(lane);
-      if (n >= p.N) continue;
-      const float bn = (p.bias != nullptr) ? p.bias[n] : 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * WM + i * 32 + M_::row(e, lane);
-        if (m >= p.M) continue;
-        const float a = acc[i][j][e];
-        if constexpr (SPLIT) {
-          p.ws[((int64_t)blockIdx.z * p.M + m) * p.N + n] = a;
-        } else {
-          const int64_t o = (int64_t)m * p.ldc + n;
-          if constexpr (EPI == EPI_STORE) {
-            reinterpret_cast<T*>(p.C)[o] = from_f<T>(a + bn);
-          } else if constexpr (EPI == EPI_RESID) {
-            reinterpret_cast<float*>(p.C)[o] = p.R[o] + (a + bn);
-          } else if constexpr (EPI == EPI_GELU) {
-            const float u = a + bn;
-            reinterpret_cast<T*>(p.C)[o] = from_f<T>(u);
-            reinterpret_cast<T*>(p.C2)[o] = from_f<T>(gelu_f(u));
-          } else if constexpr (EPI == EPI_GELU_BWD) {
-            const float u = to_f(reinterpret_cast<const T*>(p.aux)[o]);
-            reinterpret_cast<T*>(p.C)[o] = from_f<T>(a * gelu_grad_f(u));
-          } else {
-            float* c = reinterpret_cast<float*>(p.C);
-            c[o] = p.accumulate ? c[o] + a : a;
-          }
-        }
-      }
-    }
-  }
+  epilogue_lds<T, EPI, SPLIT, BM, BN, 128>(p, acc, smem, m0, n0, wm, wn, lane, t);
 }
 
 // out[m][n] = (acc ? out : 0) + sum_z ws[z][m][n], z in increasing order
@@ -512,7 +556,7 @@ static int forced_tile() {
   return v;
 }
 
-hipError_t gemm(const Gemm& g, hipStream_t s) {
+hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const bool can_split = g.ws != nullptr && g.splits > 1 && g.epi == EPI_F32;
   int tile = 2, splits = 1;
@@ -550,6 +594,7 @@ hipError_t gemm(const Gemm& g, hipStream_t s) {
     p.k_per_split = g.K;
   }
   hipError_t e = (g.dtype == BF16) ? dispatch<bf16>(g, p, tile, splits, s) : dispatch<float>(g, p, tile, splits, s);
+  if (e == hipSuccess && after_main) e = hipEventRecord(after_main, s);
   if (e != hipSuccess || splits <= 1) return e;
   const int64_t total = (int64_t)g.M * g.N;
   hipLaunchKernelGGL(splitk_reduce, dim3(cdiv(total, 256)), dim3(256), 0, s, g.ws, splits, g.M,

@@ -281,16 +281,22 @@ struct ProfScope {
     x->prof.bytes += bytes;
     x->prof.launches += 1;
   }
+  // the stop event, for a caller that records it itself (nullptr when not profiling)
+  hipEvent_t stop_event() { return on ? x->prof.ev[x->prof.used + 1] : nullptr; }
   ~ProfScope() {
     if (!on) return;
-    (void)hipEventRecord(x->prof.ev[x->prof.used + 1], x->stream);
+    if (!stopped) (void)hipEventRecord(x->prof.ev[x->prof.used + 1], x->stream);
     x->prof.used += 2;
   }
+  bool stopped = false;
 };
 
+// GEMM classes time only the main kernel (a split-K reduction is not included)
 int run_gemm(gpt_ctx* x, const char* cls, const gk::Gemm& g) {
   ProfScope ps(x, cls, 2.0 * g.M * g.N * (double)g.K, 0.0);
-  HIPCHK(gk::gemm(g, x->stream));
+  hipEvent_t stop = ps.stop_event();
+  HIPCHK(gk::gemm(g, x->stream, stop));
+  ps.stopped = stop != nullptr;
   return 0;
 }
 

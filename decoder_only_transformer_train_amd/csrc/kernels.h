@@ -36,7 +36,8 @@ struct Gemm {
   int splits = 1;
   float* ws = nullptr;
 };
-hipError_t gemm(const Gemm& g, hipStream_t s);
+// after_main (nullable) is recorded right after the main kernel, before any split-K reduction
+hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main = nullptr);
 // split count and workspace floats a wgrad GEMM of this shape would use
 int gemm_pick_splits(int M, int N, int K);
 
