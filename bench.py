@@ -1,16 +1,25 @@
 """Training throughput of the GPT-2 124M step on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--breakdown]
+                [--roofline-kernel CLASS] [--copy-calibration BYTES]
 
 One step = make_batch (B*T+1 tokens of a seeded synthetic Zipf(1.1) stream
 with end-of-text separators) -> forward + fused head/CE -> backward -> AdamW,
 all through libgpt.so.  Prints one JSON line with tokens/s, MFU, the
 roofline of one kernel (timed with HIP events on the library's stream inside
 the timed region) and the fp64 CPU oracle timed on a bounded sample.
+
+The roofline's "traffic" (HBM bytes per launch of that kernel) comes from
+profiles/traffic.json, written from two rocprofv3 --pmc runs (FETCH_SIZE,
+WRITE_SIZE) of this script with --copy-calibration, which appends one plain
+device copy of known size so the counters can be scaled to bytes.  It is
+reported only while the kernel sources hash to what they were when the
+counters were taken; otherwise it is null.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -22,7 +31,41 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+# kernel classes the library can time (each GEMM class times its main kernel only)
+PROFILE_CLASSES = ["gemm_qkv_fwd", "gemm_proj_fwd", "gemm_fc_fwd", "gemm_mlpproj_fwd", "gemm_dgrad_mlp",
+                   "gemm_dgrad_attn", "gemm_wgrad_mlp", "gemm_wgrad_attn", "attn_fwd", "attn_bwd",
+                   "layernorm_fwd", "layernorm_bwd", "head_logits", "head_ce", "head_dx", "head_dw",
+                   "embed_bwd", "adamw"]
 METRIC = "train tokens/sec + MFU, GPT-2 124M B=16 T=1024 bf16, 1×MI355X"
+
+
+# sources whose change invalidates stored counter readings of a kernel class
+KERNEL_SOURCES = {
+    "gemm": ["csrc/gemm.hip", "csrc/common.h", "csrc/kernels.h"],
+    "attn": ["csrc/attention_bf16.hip", "csrc/attention.hip", "csrc/common.h", "csrc/kernels.h"],
+}
+
+
+def sources_sha(kernel_class):
+    fam = "attn" if kernel_class.startswith("attn") else "gemm"
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[fam]:
+        with open(os.path.join(ROOT, "decoder_only_transformer_train_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel_class):
+    """HBM bytes per launch measured by counters, or None when absent or stale."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel") != kernel_class or rec.get("sources_sha256") != sources_sha(kernel_class):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def model_flops_per_token(L, C, T, Vp):
@@ -47,9 +90,10 @@ def cpu_baseline(cfg, seconds_cap=30.0):
     t0 = time.perf_counter()
     loss, _, G = oracle.loss_and_grads(p, x, y, cfg.n_head)
     t_row = time.perf_counter() - t0
-    m = {k: np.zeros(v.shape) for k, v in p.items()}
+    m = {k: np.zeros(a.shape) for k, a in p.items()}
+    v = {k: np.zeros(a.shape) for k, a in p.items()}
     t0 = time.perf_counter()
-    oracle.adamw_step(p, G, m, m, 1, 6e-4, 0.9, 0.95, 1e-8, 0.1)
+    oracle.adamw_step(p, G, m, v, 1, 6e-4, 0.9, 0.95, 1e-8, 0.1)
     t_adam = time.perf_counter() - t0
     step_s = cfg.batch * t_row + t_adam
     return {"value": round(cfg.batch * cfg.seq / step_s, 2), "unit": "tokens/s", "cores": threads,
@@ -67,7 +111,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true")
-    ap.add_argument("--roofline-kernel", default="gemm_fc_fwd")
+    ap.add_argument("--roofline-kernel", default="gemm_wgrad_mlp", choices=PROFILE_CLASSES)
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="after the timed steps, copy this many bytes device-to-device once")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -102,9 +148,7 @@ def main():
     breakdown = None
     if args.breakdown:
         breakdown = {}
-        for cls in ["gemm_qkv_fwd", "gemm_proj_fwd", "gemm_fc_fwd", "gemm_mlpproj_fwd", "gemm_dgrad",
-                    "gemm_wgrad", "attn_fwd", "attn_bwd", "layernorm_fwd", "layernorm_bwd", "head_gemm",
-                    "head_ce", "embed_bwd", "adamw"]:
+        for cls in PROFILE_CLASSES:
             g.profile_begin(cls)
             step(0)
             r = g.profile_end()
@@ -134,8 +178,16 @@ def main():
         achieved = prof["bytes"] / max(1, prof["launches"]) / (avg_ms / 1e3)
         roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4), "traffic": None}
+    roof["traffic"] = stored_traffic(args.roofline_kernel)
     roof.update({"kernel": args.roofline_kernel, "avg_launch_ms": round(avg_ms, 4),
                  "launches": prof["launches"]})
+    if args.copy_calibration > 0:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
     out = {
         "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(dt / K * 1e3, 3), "higher_is_better": True, "scaling": "weak",

@@ -179,6 +179,12 @@ std::vector<TensorDesc> make_tensors(const gpt_config* c, int64_t* P, int64_t* P
   return t;
 }
 
+// split-K partial sums of the head's data gradient for a row chunk of Nc rows
+int64_t head_splitk_floats(int64_t Nc, int64_t C, int64_t V) {
+  const int sp = gk::gemm_pick_splits((int)Nc, (int)C, (int)V);
+  return sp > 1 ? (int64_t)sp * Nc * C : 0;
+}
+
 int64_t splitk_floats(int64_t N, int64_t C) {
   int64_t best = 0;
   const int64_t shapes[4][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}};
@@ -236,7 +242,8 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->Dv = cv.take<float>(nh * 4);
   x->ln_part = cv.take<float>((int64_t)gk::layernorm_bwd_blocks((int)N) * 2 * C * 4);
   x->col_part = cv.take<float>((int64_t)((N + 255) / 256) * 4 * C * 4);
-  x->splitk_ws = cv.take<float>(std::max<int64_t>(1, splitk_floats(N, C)) * 4);
+  x->splitk_ws = cv.take<float>(
+      std::max<int64_t>(1, std::max(splitk_floats(N, C), head_splitk_floats(x->Nc, C, x->Vp))) * 4);
   x->keys = cv.take<uint32_t>(N * 4);
   x->norm_part = cv.take<float>(gk::sumsq_blocks(x->P) * 4);
   x->scal = cv.take<float>(64);
@@ -322,13 +329,13 @@ gk::Gemm mk(gpt_ctx* x, int at, int bt, int epi, const void* A, int64_t lda, con
 inline void* off_T(gpt_ctx* x, void* p, int64_t elems) { return (char*)p + elems * x->es; }
 
 // weight gradient dW[M][N] (+)= sum_n A(m, n) B(n-th col): both operands token-major
-int wgrad(gpt_ctx* x, const void* dY, int64_t ldy, const void* Xin, int64_t ldx, int64_t M, int64_t Nn,
-          float* dW, int acc) {
+int wgrad(gpt_ctx* x, const char* cls, const void* dY, int64_t ldy, const void* Xin, int64_t ldx, int64_t M,
+          int64_t Nn, float* dW, int acc) {
   gk::Gemm g = mk(x, 1, 1, gk::EPI_F32, dY, ldy, Xin, ldx, M, Nn, x->N, dW, Nn);
   g.accumulate = acc;
   g.splits = gk::gemm_pick_splits((int)M, (int)Nn, (int)x->N);
   g.ws = x->splitk_ws;
-  return run_gemm(x, "gemm_wgrad", g);
+  return run_gemm(x, cls, g);
 }
 
 int bias_grad(gpt_ctx* x, int dtype, const void* dY, int64_t cols, float* db, int acc) {
@@ -360,13 +367,13 @@ int ln_fwd(gpt_ctx* x, const float* in, int g_id, int b_id, void* out, float* mu
 // only in the chunk buffer; loss, dF and dW come out of the same pass.
 int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C,
          float scale, float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, float* logits, void* dz,
-         int64_t ldv, int64_t Nc, int dtype) {
+         int64_t ldv, int64_t Nc, int dtype, float* ws) {
   for (int64_t c0 = 0; c0 < N; c0 += Nc) {
     const int64_t rows = std::min(Nc, N - c0);
     const void* Fc = (const char*)Fin + c0 * C * (dtype == GPT_BF16 ? 2 : 4);
     gk::Gemm g = mk(x, 0, 0, gk::EPI_F32, Fc, C, W, C, rows, V, C, logits, ldv);
     g.dtype = dtype;
-    if (run_gemm(x, "head_gemm", g)) return GPT_EHIP;
+    if (run_gemm(x, "head_logits", g)) return GPT_EHIP;
     {
       ProfScope ps(x, "head_ce", 0.0, (double)rows * V * (4 + (scale > 0 ? (dtype == GPT_BF16 ? 2 : 4) : 0)));
       HIPCHK(gk::ce_rows(dtype, logits, ldv, (int)V, y + c0, (int)rows, scale, tok_loss + c0, tok_lse + c0,
@@ -376,13 +383,15 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
       if (dF) {
         gk::Gemm d = mk(x, 0, 1, gk::EPI_F32, dz, ldv, W, C, rows, C, V, dF + c0 * C, C);
         d.dtype = dtype;
-        if (run_gemm(x, "head_gemm", d)) return GPT_EHIP;
+        d.splits = gk::gemm_pick_splits((int)rows, (int)C, (int)V);  // few output tiles, long K
+        d.ws = ws;
+        if (run_gemm(x, "head_dx", d)) return GPT_EHIP;
       }
       if (dW) {
         gk::Gemm w = mk(x, 1, 1, gk::EPI_F32, dz, ldv, Fc, C, V, C, rows, dW, C);
         w.dtype = dtype;
         w.accumulate = (c0 > 0) || dW_acc;
-        if (run_gemm(x, "head_gemm", w)) return GPT_EHIP;
+        if (run_gemm(x, "head_dw", w)) return GPT_EHIP;
       }
     }
   }
@@ -520,7 +529,7 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
   const bool grad = loss_scale > 0.f;
   if (int e = head(x, x->lnf, x->W_(T_WTE), x->Vp, yt, N, C, grad ? scale : 0.f, x->tok_loss, x->tok_lse,
                    grad ? x->dF : nullptr, grad ? x->G_(T_WTE) : nullptr, x->wte_fresh ? 0 : 1, x->logits, x->dz,
-                   x->ldv, x->Nc, x->dt))
+                   x->ldv, x->Nc, x->dt, x->splitk_ws))
     return e;
   if (grad) x->wte_fresh = false;
   HIPCHK(gk::mean_f32(x->tok_loss, (int)N, x->loss, x->ring, x->ring_wr % RING, s));
@@ -547,22 +556,22 @@ int gpt_backward(gpt_ctx* x) {
   for (int l = L - 1; l >= 0; --l) {
     Layer& ly = x->layers[l];
     // MLP output projection
-    if (int e = wgrad(x, x->dresT, C, ly.fcact, 4 * C, C, 4 * C, x->G_(tid(l, K_MPW)), acc)) return e;
+    if (int e = wgrad(x, "gemm_wgrad_mlp", x->dresT, C, ly.fcact, 4 * C, C, 4 * C, x->G_(tid(l, K_MPW)), acc)) return e;
     if (int e = bias_grad(x, GPT_F32, x->dres, C, x->G_(tid(l, K_MPB)), acc)) return e;
     gk::Gemm g = mk(x, 0, 1, gk::EPI_GELU_BWD, x->dresT, C, x->W_(tid(l, K_MPW)), 4 * C, N, 4 * C, C, x->dfc, 4 * C);
     g.aux = ly.fcpre;
-    if (int e = run_gemm(x, "gemm_dgrad", g)) return e;
+    if (int e = run_gemm(x, "gemm_dgrad_mlp", g)) return e;
     // MLP input projection
-    if (int e = wgrad(x, x->dfc, 4 * C, ly.ln2, C, 4 * C, C, x->G_(tid(l, K_FCW)), acc)) return e;
+    if (int e = wgrad(x, "gemm_wgrad_mlp", x->dfc, 4 * C, ly.ln2, C, 4 * C, C, x->G_(tid(l, K_FCW)), acc)) return e;
     if (int e = bias_grad(x, x->dt, x->dfc, 4 * C, x->G_(tid(l, K_FCB)), acc)) return e;
     g = mk(x, 0, 1, gk::EPI_F32, x->dfc, 4 * C, x->W_(tid(l, K_FCW)), C, N, C, 4 * C, x->dln, C);
-    if (int e = run_gemm(x, "gemm_dgrad", g)) return e;
+    if (int e = run_gemm(x, "gemm_dgrad_mlp", g)) return e;
     if (int e = ln_bwd(x, x->dln, ly.res_mid, ly.mu2, ly.rs2, tid(l, K_LN2G), tid(l, K_LN2B), x->dres, acc)) return e;
     // attention output projection
-    if (int e = wgrad(x, x->dresT, C, ly.att, C, C, C, x->G_(tid(l, K_PROJW)), acc)) return e;
+    if (int e = wgrad(x, "gemm_wgrad_attn", x->dresT, C, ly.att, C, C, C, x->G_(tid(l, K_PROJW)), acc)) return e;
     if (int e = bias_grad(x, GPT_F32, x->dres, C, x->G_(tid(l, K_PROJB)), acc)) return e;
     g = mk(x, 0, 1, gk::EPI_STORE, x->dresT, C, x->W_(tid(l, K_PROJW)), C, N, C, C, x->datt, C);
-    if (int e = run_gemm(x, "gemm_dgrad", g)) return e;
+    if (int e = run_gemm(x, "gemm_dgrad_attn", g)) return e;
     {
       const double pairs = (double)x->B * x->H * x->T * (x->T + 1) / 2.0;
       ProfScope ps(x, "attn_bwd", 8.0 * x->D * pairs, 0.0);
@@ -570,10 +579,10 @@ int gpt_backward(gpt_ctx* x) {
                           (int)x->D, s));
     }
     // QKV projection
-    if (int e = wgrad(x, x->dqkv, 3 * C, ly.ln1, C, 3 * C, C, x->G_(tid(l, K_ATTW)), acc)) return e;
+    if (int e = wgrad(x, "gemm_wgrad_attn", x->dqkv, 3 * C, ly.ln1, C, 3 * C, C, x->G_(tid(l, K_ATTW)), acc)) return e;
     if (int e = bias_grad(x, x->dt, x->dqkv, 3 * C, x->G_(tid(l, K_ATTB)), acc)) return e;
     g = mk(x, 0, 1, gk::EPI_F32, x->dqkv, 3 * C, x->W_(tid(l, K_ATTW)), C, N, C, 3 * C, x->dln, C);
-    if (int e = run_gemm(x, "gemm_dgrad", g)) return e;
+    if (int e = run_gemm(x, "gemm_dgrad_attn", g)) return e;
     if (int e = ln_bwd(x, x->dln, x->res[l], ly.mu1, ly.rs1, tid(l, K_LN1G), tid(l, K_LN1B), x->dres, acc)) return e;
   }
   // embeddings: token rows (deterministic segmented sum) and positions
@@ -631,7 +640,8 @@ size_t gpt_lmhead_ce_ws_bytes(int64_t N, int64_t V, int64_t C, int32_t dtype) {
   if (N < 1 || V < 1 || C < 64 || C % 64 || (dtype != GPT_F32 && dtype != GPT_BF16)) return 0;
   const int64_t es = dtype == GPT_BF16 ? 2 : 4;
   const int64_t ldv = align_up(V, 64), Nc = std::min<int64_t>(N, 4096);
-  return (size_t)(align_up(Nc * ldv * 4, ALIGN) + align_up(Nc * ldv * es, ALIGN) + 2 * align_up(N * 4, ALIGN));
+  return (size_t)(align_up(Nc * ldv * 4, ALIGN) + align_up(Nc * ldv * es, ALIGN) + 2 * align_up(N * 4, ALIGN) +
+                  align_up(std::max<int64_t>(1, head_splitk_floats(Nc, C, V)) * 4, ALIGN));
 }
 
 int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int64_t V, int64_t C, int32_t dtype,
@@ -650,9 +660,10 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
   void* dz = cv.take<void>(Nc * ldv * tmp.es);
   float* tl = cv.take<float>(N * 4);
   float* tlse = cv.take<float>(N * 4);
+  float* hws = cv.take<float>(std::max<int64_t>(1, head_splitk_floats(Nc, C, V)) * 4);
   const bool grad = dX || dW;
   if (int e = head(&tmp, X, W, V, y, N, C, grad ? 1.0f / (float)N : 0.f, tl, tlse, dX, dW, 0, logits, dz, ldv, Nc,
-                   dtype))
+                   dtype, hws))
     return e;
   HIPCHK(gk::mean_f32(tl, (int)N, loss_dev, nullptr, 0, tmp.stream));
   return 0;
