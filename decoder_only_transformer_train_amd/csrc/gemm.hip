@@ -1,25 +1,28 @@
 // MFMA GEMM for gfx950: C[m][n] = sum_k A(m,k) B(n,k) with fused epilogues.
 //
-// One template serves fp32 (16x16x4 f32 MFMA) and bf16 (32x32x16 bf16 MFMA,
-// the shape that reaches the chip's dense peak from a single wave per SIMD):
-// operand tiles are staged in LDS as [rows][128 bytes of k] with a 16-byte
-// row pad, so every lane reads one conflict-free 16-byte fragment per MFMA
-// step regardless of the element type.  Operands are read through buffer
-// descriptors whose range ends at the operand, so loads past M, N or K
-// return zeros without a branch.  Operands whose k dimension
-// is not contiguous in memory (the weight-gradient and data-gradient
-// products) are transposed in registers on their way into LDS, so global
-// loads stay 16-byte and coalesced.  Workgroup: 4 waves in 2x2; the tile is
-// BM x BN (256x256, 256x128 or 128x128, chosen per shape), each wave owns a
-// (BM/2) x (BN/2) sub-tile.  LDS is double-buffered with the next tile's
-// global loads in flight during the current tile's MFMAs; the 256x256 bf16
-// kernel additionally interleaves its LDS reads, stores and global loads
-// with the MFMAs by explicit scheduling groups.  Workgroup ids are
-// remapped so each XCD (ids are dealt round-robin to the 8 XCDs) works on a
-// contiguous, grouped run of tiles that share operand rows in its L2.
+// bf16 products run on 32x32x16 MFMAs (the shape that reaches the chip's
+// dense peak from one wave per SIMD) in a direct-load kernel: operand tiles go
+// from global memory straight into LDS with buffer_load_dwordx4 ... lds, one
+// wave instruction filling 1 KB, so no registers are spent staging them and
+// several k-tiles stay in flight.  k-contiguous operands sit in LDS as rows of
+// k with XOR-permuted 16-byte chunks and are read with ds_read_b128;
+// row-contiguous operands (the weight- and data-gradient products) sit as rows
+// of k-rows and are read with the LDS transpose read ds_read_b64_tr_b16, so no
+// operand is ever transposed in registers.  Two tiles: 256x128 with 3 stages
+// of 32 k and two workgroups per CU (one's epilogue overlaps the other's main
+// loop), and 256x256 with 2 stages of 64 k for very large outputs.  Workgroup:
+// 4 waves in 2x2, each owning a (BM/2) x (BN/2) sub-tile.  fp32 products (16x16x4
+// f32 MFMA) use a register-staged 128x128 kernel with padded LDS rows.
+// Operands are read through buffer descriptors whose range ends at the
+// operand, so loads past M, N or K return zeros without a branch.  Epilogues
+// stage the accumulators through LDS so bias, residual and GELU work uses
+// coalesced 16/8-byte accesses.  Workgroup ids are remapped so each XCD (ids
+// are dealt round-robin to the 8 XCDs) works on a contiguous, grouped run of
+// tiles that share operand rows in its L2.
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <cstdlib>
 
 namespace gk {
@@ -364,14 +367,162 @@ __global__ __launch_bounds__(256) void gemm_kernel(Params p) {
 // k-step's MFMAs overlap it.  The loop is branch-free: loads past the operands
 // read zeros through the buffer descriptors and land in the unused LDS stage.
 #define SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-template <int TA, int TB, int EPI, int SPLIT>
-__global__ __launch_bounds__(256, 1) void gemm256_kernel(Params p) {
+}  // namespace
+namespace dl {
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Tile configuration: BM = 256 rows x BN columns, BK k per stage, ST stages,
+// OCC workgroups per CU (the register and LDS budget follow from it).
+template <int BN_, int BK_, int ST_, int OCC_>
+struct DlCfg {
+  static constexpr int BM = 256, BN = BN_, BK = BK_, ST = ST_, OCC = OCC_;
+  static constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32, KSTEPS = BK / 16;
+};
+
+// k-contiguous operand rows hold BK * 2 bytes = CPR 16-byte chunks; the chunk
+// order is XOR-permuted by row so that the 16 rows one ds_read_b128 pass
+// touches land on distinct banks
+template <int CPR>
+__device__ __forceinline__ int swz_nt(int row) {
+  if constexpr (CPR == 4) return (row >> 2) & 3;
+  else return (row >> 1) & 7;
+}
+// row-contiguous operands: k-row kr's chunks are XOR-permuted so the 4 k-rows
+// a transpose read pass touches do not stack on the same banks
+__device__ __forceinline__ int swz_t(int kr) { return ((kr & 3) << 1) | ((kr & 1) << 3); }
+
+// one wave instruction: lane i's 16 bytes at voff land at lds + 16 i (kept out of
+// templates: host-side template instantiation drops kernels that call it directly)
+__device__ __forceinline__ void load_lds16(rsrc_t r, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+template <int TRANS, int ROWS, int BK>
+struct DlOperand {
+  static constexpr int BYTES = ROWS * BK * 2;  // per stage
+  static constexpr int NI = BYTES / 1024 / 4;  // load instructions per wave per stage
+  static constexpr int CPR = TRANS ? ROWS / 8 : BK / 8;  // 16-byte chunks per LDS row
+  static constexpr int RPI = 64 / CPR;                   // LDS rows per instruction
+  uint32_t off[NI];
+  uint32_t kstep;  // bytes per BK of k
+  __device__ __forceinline__ void init(int64_t ld, int row0, int kb0, int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int inst = w * NI + i;
+      const int r = inst * RPI + lane / CPR;
+      int64_t e;
+      if constexpr (TRANS == 0) {
+        const int c = (lane % CPR) ^ swz_nt<CPR>(r);
+        e = (int64_t)(row0 + r) * ld + kb0 + c * 8;
+      } else {
+        const int c = (lane % CPR) ^ swz_t(r);
+        e = (int64_t)(kb0 + r) * ld + row0 + c * 8;
+      }
+      off[i] = (uint32_t)(e * 2);
+    }
+    kstep = TRANS ? (uint32_t)(BK * ld * 2) : (uint32_t)(BK * 2);
+  }
+  __device__ __forceinline__ void issue(rsrc_t r, char* lds, int kt, int w) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) load_lds16(r, lds + (w * NI + i) * 1024, off[i] + (uint32_t)kt * kstep);
+  }
+  // 32x32x16 fragment: rows rb..rb+31 of the tile, k-step ks (16 k)
+  __device__ __forceinline__ uint4 frag(const char* lds, int rb, int ks, int lane) const {
+    if constexpr (TRANS == 0) {
+      const int row = rb + (lane & 31);
+      const int c = (ks * 2 + (lane >> 5)) ^ swz_nt<CPR>(row);
+      return *reinterpret_cast<const uint4*>(lds + row * (BK * 2) + c * 16);
+    } else {
+      const int g = lane >> 4, s = lane & 15;
+      const int mm = rb + 16 * (g & 1) + 4 * (s & 3);
+      const int kr0 = ks * 16 + 8 * (g >> 1) + (s >> 2);
+      const int c = mm >> 3, sub = (mm & 7) * 2;
+      const char* p0 = lds + kr0 * (ROWS * 2) + ((c ^ swz_t(kr0)) * 16) + sub;
+      const char* p1 = lds + (kr0 + 4) * (ROWS * 2) + ((c ^ swz_t(kr0 + 4)) * 16) + sub;
+      v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
+      v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p1);
+      uint2 a = bitcast<uint2>(lo), b = bitcast<uint2>(hi);
+      return make_uint4(a.x, a.y, b.x, b.y);
+    }
+  }
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt simm16 on gfx9: vmcnt bits [3:0] and [15:14]; expcnt [6:4] and
+  // lgkmcnt [11:8] left at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// wait until at most n tiles' loads (NL instructions each per wave) are outstanding, n in 0..3
+template <int NL>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if constexpr (3 * NL < 64) {
+    if (n >= 3) { wait_vm<3 * NL>(); return; }
+  }
+  if constexpr (2 * NL < 64) {
+    if (n == 2) { wait_vm<2 * NL>(); return; }
+  }
+  if (n >= 1) wait_vm<NL>();
+  else wait_vm<0>();
+}
+
+// Iteration j: once tile j has landed (explicit vmcnt wait) and every wave is
+// past the barrier - so every read of tile j-1 is complete - tile j+ST-1 is
+// loaded into tile j-1's stage (wr); then tile j's k-steps are read from its
+// stage (rd), each interleaved with the MFMAs of the previous k-step (for
+// k-step 0, the last k-step of tile j-1).  rd and wr are distinct stages:
+// declaring them __restrict__ lets the compiler drop its blanket wait on
+// outstanding direct-to-LDS loads before each LDS read; the real dependencies
+// are the explicit wait and the barrier.
+template <int TA, int TB, typename C, int NL>
+__device__ __forceinline__ void dl_iter(const char* __restrict__ rd, char* __restrict__ wr, int kt, int nk,
+                                        const DlOperand<TA, 256, C::BK>& oa, const DlOperand<TB, C::BN, C::BK>& ob,
+                                        rsrc_t ra, rsrc_t rb, f32x16 (&acc)[C::FM][C::FN], uint4 (&fa)[2][C::FM],
+                                        uint4 (&fb)[2][C::FN], int wm, int wn, int w, int lane) {
+  constexpr int FM = C::FM, FN = C::FN, ST = C::ST;
+  constexpr int ABYTES = DlOperand<TA, 256, C::BK>::BYTES;
+  constexpr int NR = (TA ? 2 : 1) * FM + (TB ? 2 : 1) * FN;  // LDS read instructions per k-step
+  wait_tiles<NL>(min(ST - 2, nk - 1 - kt));
+  __syncthreads();
+  if (kt + ST - 1 < nk) {
+    oa.issue(ra, wr, kt + ST - 1, w);
+    ob.issue(rb, wr + ABYTES, kt + ST - 1, w);
+  }
+#pragma unroll
+  for (int h = 0; h < C::KSTEPS; ++h) {
+    const int sl = h & 1;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[sl][i] = oa.frag(rd, wm * C::WM + i * 32, h, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[sl][j] = ob.frag(rd + ABYTES, wn * C::WN + j * 32, h, lane);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) Mf<bf16>::mma(acc[i][j], fa[sl ^ 1][i], fb[sl ^ 1][j]);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      SGB(0x008, 1);
+      SGB(0x100, 1);
+    }
+    SGB(0x008, FM * FN - NR > 0 ? FM * FN - NR : 0);
+  }
+}
+
+template <int TA, int TB, int EPI, int SPLIT, typename C>
+__global__ __launch_bounds__(256, C::OCC) void gemm_dl_kernel(Params p) {
   typedef bf16 T;
-  using M_ = Mf<T>;
-  constexpr int BM = 256, BN = 256, WM = 128, WN = 128;
-  constexpr int FM = 4, FN = 4;
-  constexpr int STAGE = (BM + BN) * PITCH;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN, ST = C::ST;
+  using OA = DlOperand<TA, BM, BK>;
+  using OB = DlOperand<TB, BN, BK>;
+  constexpr int STAGE = OA::BYTES + OB::BYTES;
+  constexpr int NL = OA::NI + OB::NI;
+  constexpr int EPI_BYTES = 128 * (BN + 4) * 4;
+  constexpr int SMEM = (ST * STAGE > EPI_BYTES) ? ST * STAGE : EPI_BYTES;
+  static_assert(C::KSTEPS % 2 == 0, "k-steps alternate between two fragment slots");
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -380,10 +531,13 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(Params p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int kb0 = blockIdx.z * p.k_per_split;
   const int kend = min(p.K, kb0 + p.k_per_split);
-  constexpr int BK = 64;
   const int nk = (kend - kb0 + BK - 1) / BK;
   const rsrc_t ra = make_rsrc(p.A, (TA ? (int64_t)p.K : (int64_t)p.M) * p.lda * 2);
   const rsrc_t rb = make_rsrc(p.B, (TB ? (int64_t)p.K : (int64_t)p.N) * p.ldb * 2);
+  OA oa;
+  OB ob;
+  oa.init(p.lda, m0, kb0, w, lane);
+  ob.init(p.ldb, n0, kb0, w, lane);
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -391,75 +545,37 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(Params p) {
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  const int frow = lane & 31, fk = (lane >> 5) * 16;
-  const int arow = (wm * WM + frow) * PITCH + fk, brow = (wn * WN + frow) * PITCH + fk;
-  Loader<T, TA, BM> la;
-  Loader<T, TB, BN> lb;
+  // slot 1 holds "the last k-step of tile -1": zeros, so the first MFMAs on it add nothing
   uint4 fa[2][FM], fb[2][FN];
-  auto read_frags = [&](const char* st, int ks, int slot) {
-    const char* sa = st + arow + ks * 32;
-    const char* sb = st + BM * PITCH + brow + ks * 32;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[slot][i] = *reinterpret_cast<const uint4*>(sa + i * 32 * PITCH);
+  for (int i = 0; i < FM; ++i) fa[1][i] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[slot][j] = *reinterpret_cast<const uint4*>(sb + j * 32 * PITCH);
-  };
-  auto mfmas = [&](int slot) {
+  for (int j = 0; j < FN; ++j) fb[1][j] = make_uint4(0, 0, 0, 0);
+  // prologue: tiles 0..ST-2 in flight (stage ST-1 is filled by the first iteration)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) M_::mma(acc[i][j], fa[slot][i], fb[slot][j]);
-  };
-  constexpr int NLOAD = Loader<T, TA, BM>::NR + Loader<T, TB, BN>::NR;          // buffer loads per tile
-  constexpr int NSTORE = (TA ? (BM / 32) / 4 * 16 : BM / 32) + (TB ? (BN / 32) / 4 * 16 : BN / 32);
-  // prologue: tile 0 into LDS stage 0, tile 1 in flight, k-step 0 fragments read
-  la.load(ra, p.lda, m0, kb0, t);
-  lb.load(rb, p.ldb, n0, kb0, t);
-  la.store(smem, t);
-  lb.store(smem + BM * PITCH, t);
-  la.load(ra, p.lda, m0, kb0 + BK, t);
-  lb.load(rb, p.ldb, n0, kb0 + BK, t);
-  __syncthreads();
-  read_frags(smem, 0, 0);
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nk) {
+      oa.issue(ra, smem + s * STAGE, s, w);
+      ob.issue(rb, smem + s * STAGE + OA::BYTES, s, w);
+    }
+  int sc = 0;  // stage of tile kt
   for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * STAGE;
-    char* nxt = smem + ((kt & 1) ^ 1) * STAGE;
-    // k-step 0: MFMAs on slot 0, read k-step 1 into slot 1
-    read_frags(cur, 1, 1);
-    mfmas(0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x100, 1); }
-    SGB(0x008, 8);
-    // k-step 1: store the next tile into the other stage while computing
-    read_frags(cur, 2, 0);
-    la.store(nxt, t);
-    lb.store(nxt + BM * PITCH, t);
-    mfmas(1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x100, 1); }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x200, NSTORE / 8); }
-    // k-step 2: global loads of the tile after next
-    read_frags(cur, 3, 1);
-    la.load(ra, p.lda, m0, kb0 + (kt + 2) * BK, t);
-    lb.load(rb, p.ldb, n0, kb0 + (kt + 2) * BK, t);
-    mfmas(0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x100, 1); }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x020, NLOAD / 8); }
-    __syncthreads();
-    // k-step 3: MFMAs on slot 1, read k-step 0 of the next tile into slot 0
-    read_frags(nxt, 0, 0);
-    mfmas(1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { SGB(0x008, 1); SGB(0x100, 1); }
-    SGB(0x008, 8);
+    const int sw = sc == 0 ? ST - 1 : sc - 1;
+    dl_iter<TA, TB, C, NL>(smem + sc * STAGE, smem + sw * STAGE, kt, nk, oa, ob, ra, rb, acc, fa, fb, wm, wn, w,
+                           lane);
+    sc = sc + 1 == ST ? 0 : sc + 1;
   }
-
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) Mf<bf16>::mma(acc[i][j], fa[1][i], fb[1][j]);
+  __syncthreads();
   epilogue_lds<T, EPI, SPLIT, BM, BN, 128>(p, acc, smem, m0, n0, wm, wn, lane, t);
 }
 
+}  // namespace dl
+namespace {
+using dl::gemm_dl_kernel;
 // out[m][n] = (acc ? out : 0) + sum_z ws[z][m][n], z in increasing order
 __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, int N, float* out,
                               int64_t ldc, int accumulate) {
@@ -480,20 +596,20 @@ hipError_t launch(const Params& p, int splits, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int TA, int TB, int EPI, int SPLIT, typename C>
+hipError_t launch_dl(const Params& p, int splits, hipStream_t s) {
+  dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
+  hipLaunchKernelGGL((gemm_dl_kernel<TA, TB, EPI, SPLIT, C>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 template <typename T, int TA, int TB, int EPI, int SPLIT>
 hipError_t launch_tile(const Params& p, int tile, int splits, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (tile == 0) {
-      dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
-      hipLaunchKernelGGL((gemm256_kernel<TA, TB, EPI, SPLIT>), grid, dim3(256), 0, s, p);
-      return hipGetLastError();
-    }
+    if (tile == 0) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<128, 32, 3, 2>>(p, splits, s);
+    if (tile == 1) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1>>(p, splits, s);
   }
-  switch (tile) {
-    case 0: return launch<T, TA, TB, EPI, SPLIT, 256, 256>(p, splits, s);
-    case 1: return launch<T, TA, TB, EPI, SPLIT, 256, 128>(p, splits, s);
-    default: return launch<T, TA, TB, EPI, SPLIT, 128, 128>(p, splits, s);
-  }
+  return launch<T, TA, TB, EPI, SPLIT, 128, 128>(p, splits, s);
 }
 
 template <typename T>
@@ -517,23 +633,31 @@ hipError_t dispatch(const Gemm& g, const Params& p, int tile, int splits, hipStr
   }
 }
 
+// tiles: 0 = bf16 256x128 direct-load (2 per CU), 1 = bf16 256x256 direct-load
+// (BK 64, 1 per CU), 2 = 128x128 register-staged (fp32 and the fallback)
 constexpr int TILE_BM[3] = {256, 256, 128};
-constexpr int TILE_BN[3] = {256, 128, 128};
+constexpr int TILE_BN[3] = {128, 256, 128};
 
 // Tile and K-split choice from measurements of the step's shapes on MI355X:
-// 128x128 (two workgroups per CU) wins for K up to ~3K with most epilogues;
-// the interleaved 256x256 kernel wins for long-K products with enough tiles.
-// Split-K (weight gradients only) is sized so that tiles x splits fills about
-// two workgroups per CU with at least 512 k per split.
+// the 256x128 direct-load kernel (two workgroups per CU, so one's epilogue
+// overlaps the other's main loop) wins almost everywhere; the 256x256 BK-64
+// kernel wins for very large outputs and for long-K products whose A is
+// k-contiguous.  Split-K (fp32 outputs only) takes the largest split count that
+// keeps one round of workgroups (2 or 1 per CU) with at least 512 k per split.
 void choose(int M, int N, int K, bool can_split, int dtype, int a_trans, int b_trans, int* tile_out,
             int* splits_out) {
+  (void)b_trans;
   int tile = 2;
-  const int64_t t256 = (int64_t)cdiv(M, 256) * cdiv(N, 256);
-  if (dtype == BF16 && !a_trans && ((b_trans && K >= 3072) || K >= 8192) && t256 >= 160) tile = 0;
+  if (dtype == BF16) {
+    const int64_t t256 = (int64_t)cdiv(M, 256) * cdiv(N, 256);
+    tile = (t256 >= 1024 || (K >= 16384 && !a_trans)) ? 1 : 0;
+  }
   int splits = 1;
   if (can_split) {
     const int64_t tiles = (int64_t)cdiv(M, TILE_BM[tile]) * cdiv(N, TILE_BN[tile]);
-    while (tiles * splits < 512 && K / (splits * 2) >= 512) splits *= 2;
+    const int64_t round = tile == 0 ? 512 : 256;
+    const int64_t by_round = round / tiles, by_k = K / 512;
+    splits = (int)std::max<int64_t>(1, std::min(by_round, by_k));
   }
   *tile_out = tile;
   *splits_out = splits;
@@ -541,9 +665,9 @@ void choose(int M, int N, int K, bool can_split, int dtype, int a_trans, int b_t
 
 }  // namespace
 
-int gemm_pick_splits(int M, int N, int K) {
+int gemm_pick_splits(int M, int N, int K, int a_trans, int b_trans) {
   int tile = 2, splits = 1;
-  choose(M, N, K, true, BF16, 1, 1, &tile, &splits);
+  choose(M, N, K, true, BF16, a_trans, b_trans, &tile, &splits);
   return splits;
 }
 
@@ -561,7 +685,7 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
   const bool can_split = g.ws != nullptr && g.splits > 1 && g.epi == EPI_F32;
   int tile = 2, splits = 1;
   choose(g.M, g.N, g.K, can_split, g.dtype, g.a_trans, g.b_trans, &tile, &splits);
-  if (forced_tile() >= 0) tile = forced_tile();
+  if (forced_tile() >= 0 && g.dtype == BF16) tile = forced_tile();
   if (can_split) splits = std::min(splits, g.splits);
   Params p{};
   p.A = g.A;
@@ -586,6 +710,10 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
   // (with zeros) up to the next tile when K is not a multiple of it
   const int64_t kpad = (int64_t)cdiv(g.K, bk) * bk;
   if ((!g.a_trans && g.lda < kpad) || (!g.b_trans && g.ldb < kpad)) return hipErrorInvalidValue;
+  // direct-to-LDS loads move aligned 16-byte chunks: bf16 rows must be 8-element multiples
+  if (g.dtype == BF16 && tile != 2 &&
+      ((g.lda & 7) || (g.ldb & 7) || ((uintptr_t)g.A & 15) || ((uintptr_t)g.B & 15)))
+    return hipErrorInvalidValue;
   if (splits > 1) {
     const int kps = cdiv(cdiv(g.K, splits), bk) * bk;
     p.k_per_split = kps;

@@ -181,7 +181,7 @@ std::vector<TensorDesc> make_tensors(const gpt_config* c, int64_t* P, int64_t* P
 
 // split-K partial sums of the head's data gradient for a row chunk of Nc rows
 int64_t head_splitk_floats(int64_t Nc, int64_t C, int64_t V) {
-  const int sp = gk::gemm_pick_splits((int)Nc, (int)C, (int)V);
+  const int sp = gk::gemm_pick_splits((int)Nc, (int)C, (int)V, 0, 1);
   return sp > 1 ? (int64_t)sp * Nc * C : 0;
 }
 
@@ -189,7 +189,7 @@ int64_t splitk_floats(int64_t N, int64_t C) {
   int64_t best = 0;
   const int64_t shapes[4][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}};
   for (auto& s : shapes) {
-    const int sp = gk::gemm_pick_splits((int)s[0], (int)s[1], (int)N);
+    const int sp = gk::gemm_pick_splits((int)s[0], (int)s[1], (int)N, 1, 1);
     if (sp > 1) best = std::max(best, (int64_t)sp * s[0] * s[1]);
   }
   return best;
@@ -333,7 +333,7 @@ int wgrad(gpt_ctx* x, const char* cls, const void* dY, int64_t ldy, const void* 
           int64_t Nn, float* dW, int acc) {
   gk::Gemm g = mk(x, 1, 1, gk::EPI_F32, dY, ldy, Xin, ldx, M, Nn, x->N, dW, Nn);
   g.accumulate = acc;
-  g.splits = gk::gemm_pick_splits((int)M, (int)Nn, (int)x->N);
+  g.splits = gk::gemm_pick_splits((int)M, (int)Nn, (int)x->N, 1, 1);
   g.ws = x->splitk_ws;
   return run_gemm(x, cls, g);
 }
@@ -383,7 +383,7 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
       if (dF) {
         gk::Gemm d = mk(x, 0, 1, gk::EPI_F32, dz, ldv, W, C, rows, C, V, dF + c0 * C, C);
         d.dtype = dtype;
-        d.splits = gk::gemm_pick_splits((int)rows, (int)C, (int)V);  // few output tiles, long K
+        d.splits = gk::gemm_pick_splits((int)rows, (int)C, (int)V, 0, 1);  // few output tiles, long K
         d.ws = ws;
         if (run_gemm(x, "head_dx", d)) return GPT_EHIP;
       }

@@ -39,7 +39,7 @@ struct Gemm {
 // after_main (nullable) is recorded right after the main kernel, before any split-K reduction
 hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main = nullptr);
 // split count and workspace floats a wgrad GEMM of this shape would use
-int gemm_pick_splits(int M, int N, int K);
+int gemm_pick_splits(int M, int N, int K, int a_trans, int b_trans);
 
 // ---- LayerNorm ----
 // y = (x - mu) * rstd * g + b per row of C; x fp32 [rows][C]; y T; mu, rstd fp32 [rows]
