@@ -2,28 +2,72 @@
 //
 // Same method as the fp32 kernels in attention.hip (online softmax over
 // 64-key blocks, log-sum-exp saved for a recomputing backward, dK/dV and dQ
-// in separate atomic-free kernels), laid out for the 32x32 MFMA:
-//  * The forward and dQ kernels give a workgroup a 256-query block; wave w
-//    owns the 32-row tiles w and 7 - w of it, so every wave has one early and
-//    one late tile and the causal work is balanced.  The dK/dV kernel gives
-//    a workgroup 128 keys, one 32-key tile per wave.
+// in separate atomic-free kernels), laid out for the 32x32 MFMA and the LDS
+// direct-load path:
+//  * Every streamed operand block is 64 rows x 64 d of a row-major [T][ld]
+//    tensor, moved by buffer_load_dwordx4 ... lds straight into an 8 KB LDS
+//    tile (one wave instruction = 8 rows); the next blocks are in flight while
+//    the current one is consumed.  The 16-byte chunks of row r sit XOR-permuted
+//    by swz(r), which keeps both read forms below free of bank conflicts.
+//  * A block is read two ways: as row fragments (ds_read_b128: lane = row,
+//    8 consecutive d) when its rows index the MFMA's output rows, and as
+//    transposed fragments (two ds_read_b64_tr_b16: lane = d, 8 rows) when its
+//    rows are the contraction index, so no transposed copy is ever stored.
 //  * Scores are computed in the orientation whose C tile feeds the next
 //    product as its B operand: lane l of a 32x32 C tile holds column l % 32
 //    and rows (e / 4) * 8 + (l / 32) * 4 + e % 4, e = 0..15; the 8 values of
-//    one 16-row half are exactly a 32x32x16 B fragment when the A operand
-//    reads the matching rows of a transposed LDS tile (two 8-byte reads).
-//  * Transposed LDS tiles are written from registers after a 4x8 transpose,
-//    so every LDS store is 8 bytes wide.
+//    one 16-row half are a 32x32x16 B fragment whose k order the transposed
+//    reads reproduce.
+//  * The forward and dQ kernels give a workgroup a 256-query block; wave w
+//    owns the 32-row tiles w and 7 - w, so every wave has one early and one
+//    late tile and the causal work is balanced.  The dK/dV kernel gives a
+//    workgroup 128 keys, one 32-key tile per wave.
+//  * Stage refills: iteration j waits for its block, passes the barrier
+//    (every wave is done with block j - 1), refills block j - 1's stage with
+//    block j + ST - 1 and consumes block j.  The stage pointers are distinct
+//    and passed as __restrict__, which lets the compiler drop its blanket wait
+//    on outstanding direct-to-LDS loads before LDS reads; the real
+//    dependencies are the explicit vmcnt wait and the barrier.
 #include "common.h"
 #include "kernels.h"
 
 namespace gk {
-namespace {
+namespace fa {
 
-constexpr int HD = 64;                 // head size
-constexpr int PR = HD * 2 + 16;        // pitch (bytes) of a row tile [64][64]
-constexpr int PT = 64 * 2 + 16;        // pitch (bytes) of a transposed tile [64 d][64 rows]
+constexpr int HD = 64;             // head size
+constexpr int TILE = 64 * HD * 2;  // bytes of one 64-row block
+constexpr int ST = 3;              // LDS stages
 constexpr float NEG_INF = -__builtin_huge_valf();
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+// one wave instruction: lane i's 16 (4) bytes at voff land at lds + 16 i (4 i);
+// loads past the descriptor's range write zeros
+__device__ __forceinline__ void dma16(rsrc_t r, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(rsrc_t r, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt simm16 on gfx9: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt at their maxima
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// wait until at most n (0 or 1) blocks' loads, NL instructions each, are outstanding
+template <int NL>
+__device__ __forceinline__ void wait_blocks(int n) {
+  if (n >= 1) wait_vm<NL>();
+  else wait_vm<0>();
+}
 
 __device__ __forceinline__ void mma32(f32x16& c, const uint4& a, const uint4& b) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(a), bitcast<bf16x8>(b), c, 0, 0, 0);
@@ -35,60 +79,52 @@ __device__ __forceinline__ void zero16(f32x16& c) {
 // row offset (within a 32-row C tile) of accumulator e for lane group g
 __device__ __forceinline__ int crow(int e, int g) { return (e >> 2) * 8 + g * 4 + (e & 3); }
 
-// rows [row0, row0 + 64) x 64 of a [T][ld] operand into a row tile (pitch PR)
-__device__ __forceinline__ void load_rows(const bf16* __restrict__ gsrc, int64_t ld, int row0, int nvalid, char* s,
-                                          int t) {
-  for (int i = t; i < 512; i += 256) {
-    const int r = i >> 3, c = i & 7;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + r < nvalid) v = *reinterpret_cast<const uint4*>(gsrc + (int64_t)(row0 + r) * ld + c * 8);
-    *reinterpret_cast<uint4*>(s + r * PR + c * 16) = v;
-  }
-}
-// the same rows into a transposed tile [64 d][64 rows] (pitch PT): a unit is
-// 4 rows x 8 columns, transposed in registers into 8 rows of 4 (8 bytes)
-__device__ __forceinline__ void load_trans(const bf16* __restrict__ gsrc, int64_t ld, int row0, int nvalid, char* s,
-                                           int t) {
-  if (t >= 128) return;
-  const int rg = t >> 3, dc = t & 7;
-  uint4 r[4];
+// chunk permutation of row r (8 chunks of 16 bytes per 128-byte row): for the
+// 16 rows one ds_read_b128 pass touches, and for the 4 rows x 4 chunks one
+// transpose-read pass touches, every 16-byte slot of a 256-byte bank window
+// is hit once
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+// Per-lane source offsets of one wave's 2 instructions (rows 8 i .. 8 i + 7 of
+// a block, i = 2 w + ii): lane L loads chunk (L % 8) ^ swz(row) of row L / 8.
+struct BlockLoad {
+  uint32_t off[2];
+  __device__ __forceinline__ void init(int64_t ld, int col0, int w, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = row0 + rg * 4 + i;
-    r[i] = (row < nvalid) ? *reinterpret_cast<const uint4*>(gsrc + (int64_t)row * ld + dc * 8) : make_uint4(0, 0, 0, 0);
-  }
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int wi = e >> 1;
-    uint32_t lo, hi;
-    if (e & 1) {
-      lo = (w0[wi] >> 16) | (w1[wi] & 0xFFFF0000u);
-      hi = (w2[wi] >> 16) | (w3[wi] & 0xFFFF0000u);
-    } else {
-      lo = (w0[wi] & 0xFFFFu) | (w1[wi] << 16);
-      hi = (w2[wi] & 0xFFFFu) | (w3[wi] << 16);
+    for (int ii = 0; ii < 2; ++ii) {
+      const int r = (w * 2 + ii) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      off[ii] = (uint32_t)(((int64_t)r * ld + col0 + c * 8) * 2);
     }
-    *reinterpret_cast<uint2*>(s + (dc * 8 + e) * PT + rg * 8) = make_uint2(lo, hi);
   }
-}
-// 32x32x16 operand fragment of row `row` of a row tile, k step kk (d = kk*16 ..)
+  // the block starting row0_bytes into the operand; rows past it read as zero
+  __device__ __forceinline__ void issue(rsrc_t r, char* s, uint32_t row0_bytes, int w) const {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) dma16(r, s + (w * 2 + ii) * 1024, off[ii] + row0_bytes);
+  }
+};
+
+// A fragment of block row `row`, d = 16 kk .. 16 kk + 15 (lane half g takes 8 of them)
 __device__ __forceinline__ uint4 frag_row(const char* s, int row, int kk, int g) {
-  return *reinterpret_cast<const uint4*>(s + row * PR + kk * 32 + g * 16);
+  const int c = (kk * 2 + g) ^ swz(row);
+  return *reinterpret_cast<const uint4*>(s + row * 128 + c * 16);
 }
-// fragment of row `row` of a transposed tile over the 16-row run hh:
-// slots 0-3 = rows 16 hh + 4 g + j, slots 4-7 = rows 16 hh + 8 + 4 g + j
-__device__ __forceinline__ uint4 frag_tr(const char* s, int row, int hh, int g) {
-  const char* p = s + row * PT;
-  const uint2 lo = *reinterpret_cast<const uint2*>(p + (16 * hh + 4 * g) * 2);
-  const uint2 hi = *reinterpret_cast<const uint2*>(p + (16 * hh + 8 + 4 * g) * 2);
-  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+// A fragment of the transposed block: lane l holds d = d0 + l % 32 and block
+// rows r0 + 4 (l / 32) + j, then r0 + 8 + 4 (l / 32) + j (j = 0..3) - the k
+// order of pack_half over a C tile's 16-row half starting at r0.  In each
+// 16-lane group G, lane s reads 4 consecutive d of one row; the transpose read
+// hands lane i element i % 4 of the row read by lane i / 4 + 4 j.
+__device__ __forceinline__ uint4 frag_tr(const char* s, int d0, int r0, int lane) {
+  const int G = lane >> 4, sl = lane & 15;
+  const int dd = d0 + 16 * (G & 1) + 4 * (sl & 3);
+  const int c = dd >> 3, sub = (dd & 7) * 2;
+  const int ra = r0 + 4 * (G >> 1) + (sl >> 2), rb = ra + 8;
+  v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(s + ra * 128 + ((c ^ swz(ra)) * 16) + sub));
+  v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(s + rb * 128 + ((c ^ swz(rb)) * 16) + sub));
+  const uint2 a = bitcast<uint2>(lo), b = bitcast<uint2>(hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
 }
-// B fragment from half hh of a 32x32 C tile (accumulators 8 hh .. 8 hh + 7),
-// whose slot order matches frag_tr
+// B fragment from half hh of a 32x32 C tile (accumulators 8 hh .. 8 hh + 7)
 __device__ __forceinline__ uint4 pack_half(const f32x16& c, int hh) {
   bf16x8 v;
 #pragma unroll
@@ -96,303 +132,416 @@ __device__ __forceinline__ uint4 pack_half(const f32x16& c, int hh) {
   return bitcast<uint4>(v);
 }
 
-__global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ o,
-                                                        float* __restrict__ lse2, int Tn, int H) {
-  __shared__ __attribute__((aligned(16))) char sK[64 * PR];
-  __shared__ __attribute__((aligned(16))) char sVt[64 * PT];
+// ---------------------------------------------------------------------------
+// Forward.  Stage = K block + V block (16 KB).
+struct FwdState {
+  uint4 qf[2][4];
+  f32x16 oacc[2][2];
+  float m[2], l[2];
+  int q[2], qlo[2];
+};
+
+__device__ __forceinline__ void fwd_block(const char* __restrict__ rd, char* __restrict__ wr, int kb, int nkb,
+                                          rsrc_t r, const BlockLoad& lk, const BlockLoad& lv, uint32_t blk_bytes,
+                                          FwdState& S, int Tn, int w, int lane) {
+  const int g = lane >> 5, c32 = lane & 31;
+  wait_blocks<4>(min(ST - 2, nkb - 1 - kb));
+  __syncthreads();
+  if (kb + ST - 1 < nkb) {
+    lk.issue(r, wr, (uint32_t)(kb + ST - 1) * blk_bytes, w);
+    lv.issue(r, wr + TILE, (uint32_t)(kb + ST - 1) * blk_bytes, w);
+  }
+  const char* sK = rd;
+  const char* sV = rd + TILE;
+  const float cs = LOG2E / 8.0f;  // log2(e) / sqrt(64)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (kb * 64 > S.qlo[i] + 31) continue;  // every key of the block is after every query of the tile
+    const int qc = min(S.q[i], Tn - 1);
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      zero16(s[kt]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) mma32(s[kt], frag_row(sK, kt * 32 + c32, kk, g), S.qf[i][kk]);
+    }
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb * 64 + kt * 32 + crow(e, g);
+        const float v = (key <= qc) ? s[kt][e] * cs : NEG_INF;
+        s[kt][e] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+    const float mnew = fmaxf(S.m[i], mx);
+    const float alpha = hw_exp2(S.m[i] - mnew);
+    float ls = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = hw_exp2(s[kt][e] - mnew);
+        s[kt][e] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 32, WAVE);
+    S.l[i] = S.l[i] * alpha + ls;
+    S.m[i] = mnew;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) S.oacc[i][dt] *= alpha;
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const uint4 bp = pack_half(s[hh >> 1], hh & 1);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) mma32(S.oacc[i][dt], frag_tr(sV, dt * 32, hh * 16, lane), bp);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ o,
+                                                     float* __restrict__ lse2, int Tn, int H) {
+  __shared__ __attribute__((aligned(16))) char smem[ST * 2 * TILE];
   const int nqb = (Tn + 255) / 256;
-  const int qb = nqb - 1 - blockIdx.x;
+  const int qb = nqb - 1 - blockIdx.x;  // latest (longest) query blocks first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int Cc = H * HD;
   const int64_t ld = 3 * (int64_t)Cc;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
+  const rsrc_t r = make_rsrc(base, (int64_t)Tn * ld * 2);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, c32 = lane & 31;
   const int q0 = qb * 256;
+  FwdState S;
   const int qt[2] = {w, 7 - w};
-  int q[2];
-  uint4 qf[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    q[i] = q0 + qt[i] * 32 + c32;
+    S.qlo[i] = q0 + qt[i] * 32;
+    S.q[i] = S.qlo[i] + c32;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      qf[i][kk] = (q[i] < Tn) ? *reinterpret_cast<const uint4*>(base + (int64_t)q[i] * ld + h * HD + kk * 16 + g * 8)
-                              : make_uint4(0, 0, 0, 0);
+      S.qf[i][kk] = (S.q[i] < Tn)
+                        ? *reinterpret_cast<const uint4*>(base + (int64_t)S.q[i] * ld + h * HD + kk * 16 + g * 8)
+                        : make_uint4(0, 0, 0, 0);
+    zero16(S.oacc[i][0]);
+    zero16(S.oacc[i][1]);
+    S.m[i] = NEG_INF;
+    S.l[i] = 0.f;
   }
-  f32x16 oacc[2][2];
-  float m[2] = {NEG_INF, NEG_INF}, l[2] = {0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < 2; ++i) { zero16(oacc[i][0]); zero16(oacc[i][1]); }
-  const float cs = LOG2E / 8.0f;  // log2(e) / sqrt(64)
+  BlockLoad lk, lv;
+  lk.init(ld, Cc + h * HD, w, lane);
+  lv.init(ld, 2 * Cc + h * HD, w, lane);
+  const uint32_t blk_bytes = (uint32_t)(64 * ld * 2);
   const int nkb = (min(Tn, q0 + 256) + 63) / 64;
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
-    load_rows(base + Cc + h * HD, ld, kb * 64, Tn, sK, t);
-    load_trans(base + 2 * Cc + h * HD, ld, kb * 64, Tn, sVt, t);
-    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int qlo = q0 + qt[i] * 32;
-      if (kb * 64 > qlo + 31) continue;  // every key of the block is after every query of the tile
-      const int qc = min(q[i], Tn - 1);
-      f32x16 s[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        zero16(s[kt]);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) mma32(s[kt], frag_row(sK, kt * 32 + c32, kk, g), qf[i][kk]);
-      }
-      float mx = NEG_INF;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb * 64 + kt * 32 + crow(e, g);
-          const float v = (key <= qc) ? s[kt][e] * cs : NEG_INF;
-          s[kt][e] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      const float mnew = fmaxf(m[i], mx);
-      const float alpha = hw_exp2(m[i] - mnew);
-      float ls = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = hw_exp2(s[kt][e] - mnew);
-          s[kt][e] = p;
-          ls += p;
-        }
-      ls += __shfl_xor(ls, 32, WAVE);
-      l[i] = l[i] * alpha + ls;
-      m[i] = mnew;
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) oacc[i][dt] *= alpha;
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const uint4 bp = pack_half(s[hh >> 1], hh & 1);
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) mma32(oacc[i][dt], frag_tr(sVt, dt * 32 + c32, hh, g), bp);
-      }
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nkb) {
+      lk.issue(r, smem + s * 2 * TILE, (uint32_t)s * blk_bytes, w);
+      lv.issue(r, smem + s * 2 * TILE + TILE, (uint32_t)s * blk_bytes, w);
     }
+  int sc = 0;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int sw = sc == 0 ? ST - 1 : sc - 1;
+    fwd_block(smem + sc * 2 * TILE, smem + sw * 2 * TILE, kb, nkb, r, lk, lv, blk_bytes, S, Tn, w, lane);
+    sc = sc + 1 == ST ? 0 : sc + 1;
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    if (q[i] >= Tn) continue;
-    const float inv = 1.f / l[i];
-    bf16* orow = o + (int64_t)(b * Tn + q[i]) * Cc + h * HD;
+    if (S.q[i] >= Tn) continue;
+    const float inv = 1.f / S.l[i];
+    bf16* orow = o + (int64_t)(b * Tn + S.q[i]) * Cc + h * HD;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
         store4(orow + dt * 32 + r4 * 8 + g * 4,
-               make_float4(oacc[i][dt][4 * r4] * inv, oacc[i][dt][4 * r4 + 1] * inv, oacc[i][dt][4 * r4 + 2] * inv,
-                           oacc[i][dt][4 * r4 + 3] * inv));
-    if (g == 0) lse2[(int64_t)bh * Tn + q[i]] = m[i] + hw_log2(l[i]);
+               make_float4(S.oacc[i][dt][4 * r4] * inv, S.oacc[i][dt][4 * r4 + 1] * inv,
+                           S.oacc[i][dt][4 * r4 + 2] * inv, S.oacc[i][dt][4 * r4 + 3] * inv));
+    if (g == 0) lse2[(int64_t)bh * Tn + S.q[i]] = S.m[i] + hw_log2(S.l[i]);
   }
 }
 
-// dK, dV for a 128-key block (one 32-key tile per wave): loops over 64-query
-// blocks from the block's diagonal to the end.
-__global__ __launch_bounds__(256, 2) void fa_bwd_dkdv_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ dO,
-                                                             const float* __restrict__ lse2,
-                                                             const float* __restrict__ Dv, bf16* __restrict__ dqkv,
-                                                             int Tn, int H) {
-  __shared__ __attribute__((aligned(16))) char sQ[64 * PR];
-  __shared__ __attribute__((aligned(16))) char sQt[64 * PT];
-  __shared__ __attribute__((aligned(16))) char sdO[64 * PR];
-  __shared__ __attribute__((aligned(16))) char sdOt[64 * PT];
-  __shared__ float slse[64], sDv[64];
+// ---------------------------------------------------------------------------
+// dK, dV for a 128-key block (one 32-key tile per wave): streams the 64-query
+// blocks from the block's diagonal to the end.  Stage = Q block + dO block +
+// 64 log-sum-exps + 64 D values (16 KB + 512 B); the two dword loads go to
+// waves 0 and 1, so those waves count 5 load instructions per block, the
+// others 4.
+constexpr int KV_STAGE = 2 * TILE + 512;
+
+struct KvState {
+  uint4 kf[4], vf[4];
+  f32x16 dk[2], dv[2];
+  int key, klo;
+};
+
+struct KvLoads {
+  rsrc_t rq, rdo, rl, rdv;
+  BlockLoad lq, ldo;
+  uint32_t qblk_bytes, dblk_bytes;
+  __device__ __forceinline__ void issue(char* st, int qb, int w, int lane) const {
+    lq.issue(rq, st, (uint32_t)qb * qblk_bytes, w);
+    ldo.issue(rdo, st + TILE, (uint32_t)qb * dblk_bytes, w);
+    if (w < 2) dma4(w == 0 ? rl : rdv, st + 2 * TILE + w * 256, (uint32_t)(qb * 64 + lane) * 4);
+  }
+};
+
+__device__ __forceinline__ void kv_block(const char* __restrict__ rd, char* __restrict__ wr, int j, int nblk,
+                                         int qb0, const KvLoads& L, KvState& S, int Tn, int w, int lane) {
+  const int g = lane >> 5, c32 = lane & 31;
+  const int n_out = min(ST - 2, nblk - 1 - j);
+  if (w < 2) wait_blocks<5>(n_out);
+  else wait_blocks<4>(n_out);
+  __syncthreads();
+  if (j + ST - 1 < nblk) L.issue(wr, qb0 + j + ST - 1, w, lane);
+  const int qb = qb0 + j;
+  if (qb * 64 + 63 < S.klo) return;  // every query of the block is before every key of the tile
+  const char* sQ = rd;
+  const char* sdO = rd + TILE;
+  const float* slse = reinterpret_cast<const float*>(rd + 2 * TILE);
+  const float* sDv = slse + 64;
+  const float cs = LOG2E / 8.0f;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    f32x16 s, dp;
+    zero16(s);
+    zero16(dp);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      mma32(s, frag_row(sQ, qt * 32 + c32, kk, g), S.kf[kk]);
+      mma32(dp, frag_row(sdO, qt * 32 + c32, kk, g), S.vf[kk]);
+    }
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int qi0 = qt * 32 + r4 * 8 + g * 4;  // rows crow(4 r4 .. 4 r4 + 3, g)
+      const float4 l4 = *reinterpret_cast<const float4*>(slse + qi0);
+      const float4 d4 = *reinterpret_cast<const float4*>(sDv + qi0);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int e = 4 * r4 + jj;
+        const int qrow = qb * 64 + qi0 + jj;
+        const bool ok = (S.key <= qrow) && (qrow < Tn) && (S.key < Tn);
+        const float p = ok ? hw_exp2(s[e] * cs - lv[jj]) : 0.f;
+        s[e] = p;
+        dp[e] = p * (dp[e] - dv[jj]);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint4 bp = pack_half(s, hh);
+      const uint4 bds = pack_half(dp, hh);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        mma32(S.dv[dt], frag_tr(sdO, dt * 32, qt * 32 + hh * 16, lane), bp);
+        mma32(S.dk[dt], frag_tr(sQ, dt * 32, qt * 32 + hh * 16, lane), bds);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void dkdv_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ dO,
+                                                      const float* __restrict__ lse2, const float* __restrict__ Dv,
+                                                      bf16* __restrict__ dqkv, int Tn, int H) {
+  __shared__ __attribute__((aligned(16))) char smem[ST * KV_STAGE];
   const int nqb = (Tn + 63) / 64;
-  const int kb = blockIdx.x;
+  const int kb = blockIdx.x;  // key block 0 has the most query blocks: first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int Cc = H * HD;
   const int64_t ld = 3 * (int64_t)Cc;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
   const bf16* dob = dO + (int64_t)b * Tn * Cc;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, c32 = lane & 31;
+  KvLoads L;
+  L.rq = make_rsrc(base, (int64_t)Tn * ld * 2);
+  L.rdo = make_rsrc(dob, (int64_t)Tn * Cc * 2);
+  L.rl = make_rsrc(lse2 + (int64_t)bh * Tn, (int64_t)Tn * 4);
+  L.rdv = make_rsrc(Dv + (int64_t)bh * Tn, (int64_t)Tn * 4);
+  L.lq.init(ld, h * HD, w, lane);
+  L.ldo.init(Cc, h * HD, w, lane);
+  L.qblk_bytes = (uint32_t)(64 * ld * 2);
+  L.dblk_bytes = (uint32_t)(64 * Cc * 2);
   const int k0 = kb * 128;
-  const int klo = k0 + w * 32;
-  const int key = klo + c32;
-  uint4 kf[4], vf[4];
+  KvState S;
+  S.klo = k0 + w * 32;
+  S.key = S.klo + c32;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const bool ok = key < Tn;
-    const int64_t off = (int64_t)key * ld + h * HD + kk * 16 + g * 8;
-    kf[kk] = ok ? *reinterpret_cast<const uint4*>(base + Cc + off) : make_uint4(0, 0, 0, 0);
-    vf[kk] = ok ? *reinterpret_cast<const uint4*>(base + 2 * Cc + off) : make_uint4(0, 0, 0, 0);
+    const bool ok = S.key < Tn;
+    const int64_t off = (int64_t)S.key * ld + h * HD + kk * 16 + g * 8;
+    S.kf[kk] = ok ? *reinterpret_cast<const uint4*>(base + Cc + off) : make_uint4(0, 0, 0, 0);
+    S.vf[kk] = ok ? *reinterpret_cast<const uint4*>(base + 2 * Cc + off) : make_uint4(0, 0, 0, 0);
   }
-  f32x16 dk[2], dv[2];
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt) { zero16(dk[dt]); zero16(dv[dt]); }
-  const float cs = LOG2E / 8.0f;
-  for (int qb = k0 / 64; qb < nqb; ++qb) {
-    __syncthreads();
-    load_rows(base + h * HD, ld, qb * 64, Tn, sQ, t);
-    load_trans(base + h * HD, ld, qb * 64, Tn, sQt, t);
-    load_rows(dob + h * HD, Cc, qb * 64, Tn, sdO, t);
-    load_trans(dob + h * HD, Cc, qb * 64, Tn, sdOt, t);
-    if (t < 64) {
-      const int qq = qb * 64 + t;
-      slse[t] = qq < Tn ? lse2[(int64_t)bh * Tn + qq] : 0.f;
-      sDv[t] = qq < Tn ? Dv[(int64_t)bh * Tn + qq] : 0.f;
-    }
-    __syncthreads();
-    if (qb * 64 + 63 < klo) continue;  // every query of the block is before every key of the tile
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      f32x16 s, dp;
-      zero16(s);
-      zero16(dp);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        mma32(s, frag_row(sQ, qt * 32 + c32, kk, g), kf[kk]);
-        mma32(dp, frag_row(sdO, qt * 32 + c32, kk, g), vf[kk]);
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qi = qt * 32 + crow(e, g);
-        const int qrow = qb * 64 + qi;
-        const bool ok = (key <= qrow) && (qrow < Tn) && (key < Tn);
-        const float p = ok ? hw_exp2(s[e] * cs - slse[qi]) : 0.f;
-        s[e] = p;
-        dp[e] = p * (dp[e] - sDv[qi]);
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint4 bp = pack_half(s, hh);
-        const uint4 bds = pack_half(dp, hh);
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          mma32(dv[dt], frag_tr(sdOt, dt * 32 + c32, qt * 2 + hh, g), bp);
-          mma32(dk[dt], frag_tr(sQt, dt * 32 + c32, qt * 2 + hh, g), bds);
-        }
-      }
-    }
+  for (int dt = 0; dt < 2; ++dt) {
+    zero16(S.dk[dt]);
+    zero16(S.dv[dt]);
   }
-  if (key < Tn) {
-    bf16* krow = dqkv + (int64_t)(b * Tn + key) * ld + Cc + h * HD;
+  const int qb0 = k0 / 64;
+  const int nblk = nqb - qb0;  // this workgroup streams query blocks qb0 .. nqb - 1
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nblk) L.issue(smem + s * KV_STAGE, qb0 + s, w, lane);
+  int sc = 0;
+  for (int j = 0; j < nblk; ++j) {
+    const int sw = sc == 0 ? ST - 1 : sc - 1;
+    kv_block(smem + sc * KV_STAGE, smem + sw * KV_STAGE, j, nblk, qb0, L, S, Tn, w, lane);
+    sc = sc + 1 == ST ? 0 : sc + 1;
+  }
+  if (S.key < Tn) {
+    bf16* krow = dqkv + (int64_t)(b * Tn + S.key) * ld + Cc + h * HD;
     bf16* vrow = krow + Cc;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = dt * 32 + r4 * 8 + g * 4;
-        store4(krow + d, make_float4(dk[dt][4 * r4] * 0.125f, dk[dt][4 * r4 + 1] * 0.125f,
-                                     dk[dt][4 * r4 + 2] * 0.125f, dk[dt][4 * r4 + 3] * 0.125f));
-        store4(vrow + d, make_float4(dv[dt][4 * r4], dv[dt][4 * r4 + 1], dv[dt][4 * r4 + 2], dv[dt][4 * r4 + 3]));
+        store4(krow + d, make_float4(S.dk[dt][4 * r4] * 0.125f, S.dk[dt][4 * r4 + 1] * 0.125f,
+                                     S.dk[dt][4 * r4 + 2] * 0.125f, S.dk[dt][4 * r4 + 3] * 0.125f));
+        store4(vrow + d,
+               make_float4(S.dv[dt][4 * r4], S.dv[dt][4 * r4 + 1], S.dv[dt][4 * r4 + 2], S.dv[dt][4 * r4 + 3]));
       }
   }
 }
 
-// dQ for a 256-query block: loops over 64-key blocks up to the block's diagonal.
-__global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ dO,
-                                                           const float* __restrict__ lse2,
-                                                           const float* __restrict__ Dv, bf16* __restrict__ dqkv,
-                                                           int Tn, int H) {
-  __shared__ __attribute__((aligned(16))) char sK[64 * PR];
-  __shared__ __attribute__((aligned(16))) char sKt[64 * PT];
-  __shared__ __attribute__((aligned(16))) char sV[64 * PR];
+// ---------------------------------------------------------------------------
+// dQ for a 256-query block: streams 64-key blocks up to the block's diagonal.
+// Stage = K block + V block (16 KB).
+struct DqState {
+  uint4 qf[2][4], dof[2][4];
+  f32x16 dq[2][2];
+  float lq[2], dd[2];
+  int q[2], qlo[2];
+};
+
+__device__ __forceinline__ void dq_block(const char* __restrict__ rd, char* __restrict__ wr, int kb, int nkb, rsrc_t r,
+                                         const BlockLoad& lk, const BlockLoad& lv, uint32_t blk_bytes, DqState& S,
+                                         int w, int lane) {
+  const int g = lane >> 5, c32 = lane & 31;
+  wait_blocks<4>(min(ST - 2, nkb - 1 - kb));
+  __syncthreads();
+  if (kb + ST - 1 < nkb) {
+    lk.issue(r, wr, (uint32_t)(kb + ST - 1) * blk_bytes, w);
+    lv.issue(r, wr + TILE, (uint32_t)(kb + ST - 1) * blk_bytes, w);
+  }
+  const char* sK = rd;
+  const char* sV = rd + TILE;
+  const float cs = LOG2E / 8.0f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (kb * 64 > S.qlo[i] + 31) continue;
+    // one 32-key half at a time: scores, dP, dS, then its two 16-key dQ steps
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 s, dp;
+      zero16(s);
+      zero16(dp);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        mma32(s, frag_row(sK, kt * 32 + c32, kk, g), S.qf[i][kk]);
+        mma32(dp, frag_row(sV, kt * 32 + c32, kk, g), S.dof[i][kk]);
+      }
+      // a query past the sequence has lse = D = 0 and its dQ is never stored;
+      // keys past the sequence come after every valid query
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kkey = kb * 64 + kt * 32 + crow(e, g);
+        const float p = (kkey <= S.q[i]) ? hw_exp2(s[e] * cs - S.lq[i]) : 0.f;
+        s[e] = p * (dp[e] - S.dd[i]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint4 bds = pack_half(s, hh);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+          mma32(S.dq[i][dt], frag_tr(sK, dt * 32, kt * 32 + hh * 16, lane), bds);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void dq_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ dO,
+                                                    const float* __restrict__ lse2, const float* __restrict__ Dv,
+                                                    bf16* __restrict__ dqkv, int Tn, int H) {
+  __shared__ __attribute__((aligned(16))) char smem[ST * 2 * TILE];
   const int nqb = (Tn + 255) / 256;
   const int qb = nqb - 1 - blockIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int Cc = H * HD;
   const int64_t ld = 3 * (int64_t)Cc;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
+  const rsrc_t r = make_rsrc(base, (int64_t)Tn * ld * 2);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, c32 = lane & 31;
   const int q0 = qb * 256;
+  DqState S;
   const int qt[2] = {w, 7 - w};
-  int q[2];
-  uint4 qf[2][4], dof[2][4];
-  float lq[2], dq_[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    q[i] = q0 + qt[i] * 32 + c32;
-    const bool ok = q[i] < Tn;
+    S.qlo[i] = q0 + qt[i] * 32;
+    S.q[i] = S.qlo[i] + c32;
+    const bool ok = S.q[i] < Tn;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      qf[i][kk] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)q[i] * ld + h * HD + kk * 16 + g * 8)
-                     : make_uint4(0, 0, 0, 0);
-      dof[i][kk] = ok ? *reinterpret_cast<const uint4*>(dO + (int64_t)(b * Tn + q[i]) * Cc + h * HD + kk * 16 + g * 8)
-                      : make_uint4(0, 0, 0, 0);
+      S.qf[i][kk] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)S.q[i] * ld + h * HD + kk * 16 + g * 8)
+                       : make_uint4(0, 0, 0, 0);
+      S.dof[i][kk] =
+          ok ? *reinterpret_cast<const uint4*>(dO + (int64_t)(b * Tn + S.q[i]) * Cc + h * HD + kk * 16 + g * 8)
+             : make_uint4(0, 0, 0, 0);
     }
-    lq[i] = ok ? lse2[(int64_t)bh * Tn + q[i]] : 0.f;
-    dq_[i] = ok ? Dv[(int64_t)bh * Tn + q[i]] : 0.f;
+    S.lq[i] = ok ? lse2[(int64_t)bh * Tn + S.q[i]] : 0.f;
+    S.dd[i] = ok ? Dv[(int64_t)bh * Tn + S.q[i]] : 0.f;
+    zero16(S.dq[i][0]);
+    zero16(S.dq[i][1]);
   }
-  f32x16 dq[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) { zero16(dq[i][0]); zero16(dq[i][1]); }
-  const float cs = LOG2E / 8.0f;
+  BlockLoad lk, lv;
+  lk.init(ld, Cc + h * HD, w, lane);
+  lv.init(ld, 2 * Cc + h * HD, w, lane);
+  const uint32_t blk_bytes = (uint32_t)(64 * ld * 2);
   const int nkb = (min(Tn, q0 + 256) + 63) / 64;
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
-    load_rows(base + Cc + h * HD, ld, kb * 64, Tn, sK, t);
-    load_trans(base + Cc + h * HD, ld, kb * 64, Tn, sKt, t);
-    load_rows(base + 2 * Cc + h * HD, ld, kb * 64, Tn, sV, t);
-    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int qlo = q0 + qt[i] * 32;
-      if (kb * 64 > qlo + 31) continue;
-      const bool qok = q[i] < Tn;
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        zero16(s[kt]);
-        zero16(dp[kt]);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          mma32(s[kt], frag_row(sK, kt * 32 + c32, kk, g), qf[i][kk]);
-          mma32(dp[kt], frag_row(sV, kt * 32 + c32, kk, g), dof[i][kk]);
-        }
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kkey = kb * 64 + kt * 32 + crow(e, g);
-          const bool ok = qok && kkey <= q[i];
-          const float p = ok ? hw_exp2(s[kt][e] * cs - lq[i]) : 0.f;
-          s[kt][e] = p * (dp[kt][e] - dq_[i]);
-        }
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const uint4 bds = pack_half(s[hh >> 1], hh & 1);
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) mma32(dq[i][dt], frag_tr(sKt, dt * 32 + c32, hh, g), bds);
-      }
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nkb) {
+      lk.issue(r, smem + s * 2 * TILE, (uint32_t)s * blk_bytes, w);
+      lv.issue(r, smem + s * 2 * TILE + TILE, (uint32_t)s * blk_bytes, w);
     }
+  int sc = 0;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int sw = sc == 0 ? ST - 1 : sc - 1;
+    dq_block(smem + sc * 2 * TILE, smem + sw * 2 * TILE, kb, nkb, r, lk, lv, blk_bytes, S, w, lane);
+    sc = sc + 1 == ST ? 0 : sc + 1;
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    if (q[i] >= Tn) continue;
-    bf16* qrow = dqkv + (int64_t)(b * Tn + q[i]) * ld + h * HD;
+    if (S.q[i] >= Tn) continue;
+    bf16* qrow = dqkv + (int64_t)(b * Tn + S.q[i]) * ld + h * HD;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
         store4(qrow + dt * 32 + r4 * 8 + g * 4,
-               make_float4(dq[i][dt][4 * r4] * 0.125f, dq[i][dt][4 * r4 + 1] * 0.125f,
-                           dq[i][dt][4 * r4 + 2] * 0.125f, dq[i][dt][4 * r4 + 3] * 0.125f));
+               make_float4(S.dq[i][dt][4 * r4] * 0.125f, S.dq[i][dt][4 * r4 + 1] * 0.125f,
+                           S.dq[i][dt][4 * r4 + 2] * 0.125f, S.dq[i][dt][4 * r4 + 3] * 0.125f));
   }
 }
 
-}  // namespace
+}  // namespace fa
 
 hipError_t attn_fwd_bf16_d64(const void* qkv, void* o, float* lse, int B, int Tn, int H, hipStream_t s) {
-  dim3 grid((Tn + 255) / 256, B * H);
-  hipLaunchKernelGGL(fa_fwd_kernel, grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)o, lse, Tn, H);
+  // buffer offsets are 32-bit: one sequence of qkv must stay under 4 GB
+  if ((int64_t)Tn * 3 * H * fa::HD * 2 >= (1ll << 32)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fa::fwd_kernel, dim3((Tn + 255) / 256, B * H), dim3(256), 0, s, (const bf16*)qkv, (bf16*)o,
+                     lse, Tn, H);
   return hipGetLastError();
 }
 
 hipError_t attn_bwd_bf16_d64(const void* qkv, const void* dO, const float* lse, const float* Dv, void* dqkv, int B,
                              int Tn, int H, hipStream_t s) {
-  dim3 grid((Tn + 255) / 256, B * H);
-  hipLaunchKernelGGL(fa_bwd_dkdv_kernel, dim3((Tn + 127) / 128, B * H), dim3(256), 0, s, (const bf16*)qkv,
+  if ((int64_t)Tn * 3 * H * fa::HD * 2 >= (1ll << 32)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fa::dkdv_kernel, dim3((Tn + 127) / 128, B * H), dim3(256), 0, s, (const bf16*)qkv,
                      (const bf16*)dO, lse, Dv, (bf16*)dqkv, Tn, H);
-  hipLaunchKernelGGL(fa_bwd_dq_kernel, grid, dim3(256), 0, s, (const bf16*)qkv, (const bf16*)dO, lse, Dv,
-                     (bf16*)dqkv, Tn, H);
+  hipLaunchKernelGGL(fa::dq_kernel, dim3((Tn + 255) / 256, B * H), dim3(256), 0, s, (const bf16*)qkv,
+                     (const bf16*)dO, lse, Dv, (bf16*)dqkv, Tn, H);
   return hipGetLastError();
 }
 
