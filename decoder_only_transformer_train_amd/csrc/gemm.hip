@@ -186,8 +186,10 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
 // Epilogue through LDS: the accumulator tile is written to LDS as fp32 rows
 // (PASS_ROWS rows per pass), then every thread handles groups of 4 adjacent
 // columns with 16-byte (fp32) / 8-byte (bf16) coalesced global accesses.
+// One group of 4 adjacent columns of row m, loading its own inputs (tiles too
+// large to prefetch a whole pass of inputs in registers).
 template <typename T, int EPI, int SPLIT>
-__device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 a) {
+__device__ __forceinline__ void epi_group_inline(const Params& p, int m, int n, float4 a) {
   float v[4] = {a.x, a.y, a.z, a.w};
   const bool full = n + 3 < p.N;
   if constexpr (SPLIT) {
@@ -246,17 +248,107 @@ __device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 
   }
 }
 
+// Epilogue inputs other than the accumulators: the residual (EPI_RESID), the
+// pre-activation (EPI_GELU_BWD) or the previous output (EPI_F32 accumulating).
+template <int EPI, int SPLIT>
+__device__ __forceinline__ constexpr bool epi_reads() {
+  return !SPLIT && (EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_F32);
+}
+template <typename T, int EPI, int SPLIT>
+__device__ __forceinline__ float4 epi_load(const Params& p, int64_t o) {
+  if constexpr (EPI == EPI_RESID) return *reinterpret_cast<const float4*>(p.R + o);
+  else if constexpr (EPI == EPI_GELU_BWD) return load4(reinterpret_cast<const T*>(p.aux) + o);
+  else if constexpr (EPI == EPI_F32) {
+    if (p.accumulate) return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.C) + o);
+  }
+  return make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// One group of 4 adjacent columns of row m.  full: the group is inside N and
+// 16-byte aligned, in = epi_load of it and b4 = its bias, both loaded ahead.
+template <typename T, int EPI, int SPLIT>
+__device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 a, bool full, float4 in, float4 b4) {
+  float v[4] = {a.x, a.y, a.z, a.w};
+  if constexpr (SPLIT) {
+    float* o = p.ws + ((int64_t)blockIdx.z * p.M + m) * p.N + n;
+    if (full && (p.N & 3) == 0) {
+      *reinterpret_cast<float4*>(o) = a;
+    } else {
+      for (int k = 0; k < 4; ++k)
+        if (n + k < p.N) o[k] = v[k];
+    }
+    return;
+  }
+  const int64_t o = (int64_t)m * p.ldc + n;
+  if (!full) {  // ragged edge: element by element
+    for (int k = 0; k < 4; ++k) {
+      if (n + k >= p.N) break;
+      const float bn = p.bias ? p.bias[n + k] : 0.f;
+      const float x = v[k];
+      if constexpr (EPI == EPI_STORE) reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
+      else if constexpr (EPI == EPI_RESID) reinterpret_cast<float*>(p.C)[o + k] = p.R[o + k] + (x + bn);
+      else if constexpr (EPI == EPI_GELU) {
+        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
+        reinterpret_cast<T*>(p.C2)[o + k] = from_f<T>(gelu_f(x + bn));
+      } else if constexpr (EPI == EPI_GELU_BWD) {
+        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x * gelu_grad_f(to_f(reinterpret_cast<const T*>(p.aux)[o + k])));
+      } else {
+        float* c = reinterpret_cast<float*>(p.C);
+        c[o + k] = p.accumulate ? c[o + k] + x : x;
+      }
+    }
+    return;
+  }
+  if constexpr (EPI == EPI_STORE) {
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w));
+  } else if constexpr (EPI == EPI_RESID) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) =
+        make_float4(in.x + (a.x + b4.x), in.y + (a.y + b4.y), in.z + (a.z + b4.z), in.w + (a.w + b4.w));
+  } else if constexpr (EPI == EPI_GELU) {
+    const float4 u = make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w);
+    store4(reinterpret_cast<T*>(p.C) + o, u);
+    store4(reinterpret_cast<T*>(p.C2) + o, make_float4(gelu_f(u.x), gelu_f(u.y), gelu_f(u.z), gelu_f(u.w)));
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x * gelu_grad_f(in.x), a.y * gelu_grad_f(in.y),
+                                                      a.z * gelu_grad_f(in.z), a.w * gelu_grad_f(in.w)));
+  } else {
+    if (p.accumulate) a = make_float4(in.x + a.x, in.y + a.y, in.z + a.z, in.w + a.w);
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) = a;
+  }
+}
+
 // Stage acc through LDS (smem, at least PASS_ROWS * (BN + 4) floats) and run
 // the epilogue.  Waves whose sub-tile rows fall in the current pass write.
+// A thread always handles the same 4 columns (256 is a multiple of BN / 4), so
+// its bias is loaded once; the pass's other inputs are loaded before the
+// accumulators are staged, so their latency overlaps the staging.
 template <typename T, int EPI, int SPLIT, int BM, int BN, int PASS_ROWS, typename ACC, int FM, int FN>
 __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN], char* smem, int m0, int n0,
                                              int wm, int wn, int lane, int t) {
   using M_ = Mf<T>;
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int LDW = BN + 4;
+  constexpr int CG = BN / 4;           // column groups per row
+  constexpr int RSTEP = 256 / CG;      // rows between a thread's groups
+  constexpr int NG = PASS_ROWS / RSTEP;
+  constexpr bool IN = epi_reads<EPI, SPLIT>() && NG <= 16;  // (register budget)
+  static_assert(256 % CG == 0 && PASS_ROWS % RSTEP == 0, "epilogue thread mapping");
   float* st = reinterpret_cast<float*>(smem);
+  const int c4 = t % CG, r0 = t / CG;
+  const int n = n0 + c4 * 4;
+  const bool full = n + 3 < p.N && (SPLIT || (p.ldc & 3) == 0);
+  float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (!SPLIT && full && p.bias) b4 = *reinterpret_cast<const float4*>(p.bias + n);
 #pragma unroll
   for (int pass = 0; pass < BM / PASS_ROWS; ++pass) {
+    float4 in[IN ? NG : 1];
+    if constexpr (IN) {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int m = m0 + pass * PASS_ROWS + r0 + i * RSTEP;
+        in[i] = (full && m < p.M) ? epi_load<T, EPI, SPLIT>(p, (int64_t)m * p.ldc + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
     __syncthreads();
     if (wm * WM >= pass * PASS_ROWS && wm * WM < (pass + 1) * PASS_ROWS) {
 #pragma unroll
@@ -271,11 +363,21 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
           }
     }
     __syncthreads();
-    for (int g = t; g < PASS_ROWS * (BN / 4); g += 256) {
-      const int r = g / (BN / 4), c4 = g % (BN / 4);
-      const int m = m0 + pass * PASS_ROWS + r, n = n0 + c4 * 4;
-      if (m >= p.M || n >= p.N) continue;
-      epi_group<T, EPI, SPLIT>(p, m, n, *reinterpret_cast<const float4*>(st + r * LDW + c4 * 4));
+    if constexpr (IN) {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int r = r0 + i * RSTEP;
+        const int m = m0 + pass * PASS_ROWS + r;
+        if (m >= p.M || n >= p.N) continue;
+        epi_group<T, EPI, SPLIT>(p, m, n, *reinterpret_cast<const float4*>(st + r * LDW + c4 * 4), full, in[i], b4);
+      }
+    } else {
+      for (int g = t; g < PASS_ROWS * CG; g += 256) {
+        const int r = g / CG, c = g % CG;
+        const int m = m0 + pass * PASS_ROWS + r, nn = n0 + c * 4;
+        if (m >= p.M || nn >= p.N) continue;
+        epi_group_inline<T, EPI, SPLIT>(p, m, nn, *reinterpret_cast<const float4*>(st + r * LDW + c * 4));
+      }
     }
   }
 }
@@ -686,6 +788,8 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
   int tile = 2, splits = 1;
   choose(g.M, g.N, g.K, can_split, g.dtype, g.a_trans, g.b_trans, &tile, &splits);
   if (forced_tile() >= 0 && g.dtype == BF16) tile = forced_tile();
+  // direct-to-LDS loads move 16-byte chunks: rows of other strides take the register-staged kernel
+  if (tile != 2 && ((g.lda & 7) || (g.ldb & 7) || ((uintptr_t)g.A & 15) || ((uintptr_t)g.B & 15))) tile = 2;
   if (can_split) splits = std::min(splits, g.splits);
   Params p{};
   p.A = g.A;
@@ -710,10 +814,7 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
   // (with zeros) up to the next tile when K is not a multiple of it
   const int64_t kpad = (int64_t)cdiv(g.K, bk) * bk;
   if ((!g.a_trans && g.lda < kpad) || (!g.b_trans && g.ldb < kpad)) return hipErrorInvalidValue;
-  // direct-to-LDS loads move aligned 16-byte chunks: bf16 rows must be 8-element multiples
-  if (g.dtype == BF16 && tile != 2 &&
-      ((g.lda & 7) || (g.ldb & 7) || ((uintptr_t)g.A & 15) || ((uintptr_t)g.B & 15)))
-    return hipErrorInvalidValue;
+
   if (splits > 1) {
     const int kps = cdiv(cdiv(g.K, splits), bk) * bk;
     p.k_per_split = kps;
