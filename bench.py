@@ -35,7 +35,7 @@ PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
 PROFILE_CLASSES = ["gemm_qkv_fwd", "gemm_proj_fwd", "gemm_fc_fwd", "gemm_mlpproj_fwd", "gemm_dgrad_mlp",
                    "gemm_dgrad_attn", "gemm_wgrad_mlp", "gemm_wgrad_attn", "attn_fwd", "attn_bwd",
                    "layernorm_fwd", "layernorm_bwd", "head_logits", "head_ce", "head_dx", "head_dw",
-                   "embed_bwd", "adamw"]
+                   "bias_colsum", "param_reduce", "embed_bwd", "adamw"]
 METRIC = "train tokens/sec + MFU, GPT-2 124M B=16 T=1024 bf16, 1×MI355X"
 
 

@@ -65,6 +65,9 @@ struct Layer {
   float *mu2, *rs2;
   void* fcpre;  // T [N][4C]
   void* fcact;  // T [N][4C]
+  // backward column-sum partials, reduced in one batch at the end of backward
+  float *ln1_part, *ln2_part;   // [N / 32][3C]: ln gain, ln shift, residual-gradient column sums
+  float *fcb_part, *attb_part;  // [N / 256][4C], [N / 256][3C]: fc and qkv bias gradients
 };
 
 struct Prof {
@@ -101,7 +104,10 @@ struct gpt_ctx {
   // backward
   float *dres, *dln;
   void *dresT, *dfc, *datt, *dqkv;
-  float *Dv, *ln_part, *col_part, *splitk_ws;
+  float *Dv, *lnf_part, *splitk_ws;
+  gk::RedJob* jobs_dev;
+  std::vector<gk::RedJob> jobs;
+  int nred_blocks = 0;
   uint32_t* keys;
   float *norm_part, *scal;
   int* step_dev;
@@ -209,7 +215,12 @@ int64_t carve(gpt_ctx* x, void* base) {
   for (auto& r : x->res) r = cv.take<float>(N * C * 4);
   x->layers.assign(x->L, Layer{});
   const int64_t nh = x->B * x->H * x->T;
+  const int64_t nlnb = gk::layernorm_bwd_blocks((int)N), ncs = (N + 255) / 256;
   for (auto& l : x->layers) {
+    l.ln1_part = cv.take<float>(nlnb * 3 * C * 4);
+    l.ln2_part = cv.take<float>(nlnb * 3 * C * 4);
+    l.fcb_part = cv.take<float>(ncs * 4 * C * 4);
+    l.attb_part = cv.take<float>(ncs * 3 * C * 4);
     l.ln1 = cv.take<void>(N * C * es);
     l.mu1 = cv.take<float>(N * 4);
     l.rs1 = cv.take<float>(N * 4);
@@ -240,8 +251,8 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->datt = cv.take<void>(N * C * es);
   x->dqkv = cv.take<void>(N * 3 * C * es);
   x->Dv = cv.take<float>(nh * 4);
-  x->ln_part = cv.take<float>((int64_t)gk::layernorm_bwd_blocks((int)N) * 2 * C * 4);
-  x->col_part = cv.take<float>((int64_t)((N + 255) / 256) * 4 * C * 4);
+  x->lnf_part = cv.take<float>(nlnb * 3 * C * 4);
+  x->jobs_dev = cv.take<gk::RedJob>((8 * x->L + 3) * (int64_t)sizeof(gk::RedJob));
   x->splitk_ws = cv.take<float>(
       std::max<int64_t>(1, std::max(splitk_floats(N, C), head_splitk_floats(x->Nc, C, x->Vp))) * 4);
   x->keys = cv.take<uint32_t>(N * 4);
@@ -249,6 +260,35 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->scal = cv.take<float>(64);
   x->step_dev = cv.take<int>(64);
   return align_up(cv.used, ALIGN);
+}
+
+// The batched end-of-backward reduction: every LayerNorm gain/shift gradient
+// and every bias gradient, each the fixed-order sum of its partial rows.
+void build_jobs(gpt_ctx* x) {
+  const int C = (int)x->C, N = (int)x->N, L = (int)x->L;
+  const int nlnb = gk::layernorm_bwd_blocks(N), ncs = (N + 255) / 256;
+  x->jobs.clear();
+  int blocks = 0;
+  auto add = [&](const float* part, int nrows, int cols, int ld, float* out) {
+    x->jobs.push_back(gk::RedJob{part, out, nrows, cols, ld, blocks});
+    blocks += (cols + 15) / 16;
+  };
+  // final LayerNorm; its residual-gradient column sums are the last MLP output bias gradient
+  add(x->lnf_part, nlnb, C, 3 * C, x->G_(tid_lnf(L, 0)));
+  add(x->lnf_part + C, nlnb, C, 3 * C, x->G_(tid_lnf(L, 1)));
+  add(x->lnf_part + 2 * C, nlnb, C, 3 * C, x->G_(tid(L - 1, K_MPB)));
+  for (int l = 0; l < L; ++l) {
+    const Layer& ly = x->layers[l];
+    add(ly.ln2_part, nlnb, C, 3 * C, x->G_(tid(l, K_LN2G)));
+    add(ly.ln2_part + C, nlnb, C, 3 * C, x->G_(tid(l, K_LN2B)));
+    add(ly.ln2_part + 2 * C, nlnb, C, 3 * C, x->G_(tid(l, K_PROJB)));
+    add(ly.ln1_part, nlnb, C, 3 * C, x->G_(tid(l, K_LN1G)));
+    add(ly.ln1_part + C, nlnb, C, 3 * C, x->G_(tid(l, K_LN1B)));
+    if (l > 0) add(ly.ln1_part + 2 * C, nlnb, C, 3 * C, x->G_(tid(l - 1, K_MPB)));
+    add(ly.fcb_part, ncs, 4 * C, 4 * C, x->G_(tid(l, K_FCB)));
+    add(ly.attb_part, ncs, 3 * C, 3 * C, x->G_(tid(l, K_ATTB)));
+  }
+  x->nred_blocks = blocks;
 }
 
 void setup_dims(gpt_ctx* x, const gpt_config* c) {
@@ -338,22 +378,20 @@ int wgrad(gpt_ctx* x, const char* cls, const void* dY, int64_t ldy, const void* 
   return run_gemm(x, cls, g);
 }
 
-int bias_grad(gpt_ctx* x, int dtype, const void* dY, int64_t cols, float* db, int acc) {
-  HIPCHK(gk::colsum_partial(dtype, dY, (int)x->N, (int)cols, x->col_part, x->stream));
-  HIPCHK(gk::reduce_rows_f32(x->col_part, (int)((x->N + 255) / 256), (int)cols, cols, db, acc, x->stream));
+// column partial sums of a bias gradient (reduced with the others at the end of backward)
+int bias_colsum(gpt_ctx* x, int dtype, const void* dY, int64_t cols, float* part) {
+  ProfScope ps(x, "bias_colsum", 0.0, (double)x->N * cols * (dtype == GPT_BF16 ? 2 : 4));
+  HIPCHK(gk::colsum_partial(dtype, dY, (int)x->N, (int)cols, part, x->stream));
   return 0;
 }
 
-int ln_bwd(gpt_ctx* x, const float* dy, const float* xin, const float* mu, const float* rs, int g_id, int b_id,
-           const float* dres_in, int acc) {
-  int nblk = 0;
-  {
-    ProfScope ps(x, "layernorm_bwd", 0.0, (double)x->N * x->C * (4 + 4 + 4 + 4 + x->es) + 8.0 * x->N);
-    HIPCHK(gk::layernorm_bwd(x->dt, dy, xin, mu, rs, x->P_(g_id), dres_in, x->dres, x->dresT, x->ln_part,
-                             (int)x->N, (int)x->C, &nblk, x->stream));
-  }
-  HIPCHK(gk::reduce_rows_f32(x->ln_part, nblk, (int)x->C, 2 * x->C, x->G_(g_id), acc, x->stream));
-  HIPCHK(gk::reduce_rows_f32(x->ln_part + x->C, nblk, (int)x->C, 2 * x->C, x->G_(b_id), acc, x->stream));
+// LayerNorm backward into x->dres (+ its T copy); gain/shift/residual column
+// partials into part
+int ln_bwd(gpt_ctx* x, const float* dy, const float* xin, const float* mu, const float* rs, int g_id,
+           const float* dres_in, float* part) {
+  ProfScope ps(x, "layernorm_bwd", 0.0, (double)x->N * x->C * (4 + 4 + 4 + 4 + x->es) + 8.0 * x->N);
+  HIPCHK(gk::layernorm_bwd(x->dt, dy, xin, mu, rs, x->P_(g_id), dres_in, x->dres, x->dresT, part, (int)x->N,
+                           (int)x->C, nullptr, x->stream));
   return 0;
 }
 
@@ -444,6 +482,8 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
     logical += (uint64_t)d.numel();
   }
   if (x->shadow) chk(gk::to_bf16(x->params, x->shadow, x->P, s));
+  build_jobs(x);
+  chk(hipMemcpyAsync(x->jobs_dev, x->jobs.data(), x->jobs.size() * sizeof(gk::RedJob), hipMemcpyHostToDevice, s));
   if (rc) {
     delete x;
     return rc;
@@ -552,24 +592,22 @@ int gpt_backward(gpt_ctx* x) {
   const int64_t N = x->N, C = x->C;
   const int acc = x->others_fresh ? 0 : 1;
   const int L = (int)x->L;
-  if (int e = ln_bwd(x, x->dF, x->res[L], x->muf, x->rsf, tid_lnf(L, 0), tid_lnf(L, 1), nullptr, acc)) return e;
+  if (int e = ln_bwd(x, x->dF, x->res[L], x->muf, x->rsf, tid_lnf(L, 0), nullptr, x->lnf_part)) return e;
   for (int l = L - 1; l >= 0; --l) {
     Layer& ly = x->layers[l];
     // MLP output projection
     if (int e = wgrad(x, "gemm_wgrad_mlp", x->dresT, C, ly.fcact, 4 * C, C, 4 * C, x->G_(tid(l, K_MPW)), acc)) return e;
-    if (int e = bias_grad(x, GPT_F32, x->dres, C, x->G_(tid(l, K_MPB)), acc)) return e;
     gk::Gemm g = mk(x, 0, 1, gk::EPI_GELU_BWD, x->dresT, C, x->W_(tid(l, K_MPW)), 4 * C, N, 4 * C, C, x->dfc, 4 * C);
     g.aux = ly.fcpre;
     if (int e = run_gemm(x, "gemm_dgrad_mlp", g)) return e;
     // MLP input projection
     if (int e = wgrad(x, "gemm_wgrad_mlp", x->dfc, 4 * C, ly.ln2, C, 4 * C, C, x->G_(tid(l, K_FCW)), acc)) return e;
-    if (int e = bias_grad(x, x->dt, x->dfc, 4 * C, x->G_(tid(l, K_FCB)), acc)) return e;
+    if (int e = bias_colsum(x, x->dt, x->dfc, 4 * C, ly.fcb_part)) return e;
     g = mk(x, 0, 1, gk::EPI_F32, x->dfc, 4 * C, x->W_(tid(l, K_FCW)), C, N, C, 4 * C, x->dln, C);
     if (int e = run_gemm(x, "gemm_dgrad_mlp", g)) return e;
-    if (int e = ln_bwd(x, x->dln, ly.res_mid, ly.mu2, ly.rs2, tid(l, K_LN2G), tid(l, K_LN2B), x->dres, acc)) return e;
+    if (int e = ln_bwd(x, x->dln, ly.res_mid, ly.mu2, ly.rs2, tid(l, K_LN2G), x->dres, ly.ln2_part)) return e;
     // attention output projection
     if (int e = wgrad(x, "gemm_wgrad_attn", x->dresT, C, ly.att, C, C, C, x->G_(tid(l, K_PROJW)), acc)) return e;
-    if (int e = bias_grad(x, GPT_F32, x->dres, C, x->G_(tid(l, K_PROJB)), acc)) return e;
     g = mk(x, 0, 1, gk::EPI_STORE, x->dresT, C, x->W_(tid(l, K_PROJW)), C, N, C, C, x->datt, C);
     if (int e = run_gemm(x, "gemm_dgrad_attn", g)) return e;
     {
@@ -580,10 +618,10 @@ int gpt_backward(gpt_ctx* x) {
     }
     // QKV projection
     if (int e = wgrad(x, "gemm_wgrad_attn", x->dqkv, 3 * C, ly.ln1, C, 3 * C, C, x->G_(tid(l, K_ATTW)), acc)) return e;
-    if (int e = bias_grad(x, x->dt, x->dqkv, 3 * C, x->G_(tid(l, K_ATTB)), acc)) return e;
+    if (int e = bias_colsum(x, x->dt, x->dqkv, 3 * C, ly.attb_part)) return e;
     g = mk(x, 0, 1, gk::EPI_F32, x->dqkv, 3 * C, x->W_(tid(l, K_ATTW)), C, N, C, 3 * C, x->dln, C);
     if (int e = run_gemm(x, "gemm_dgrad_attn", g)) return e;
-    if (int e = ln_bwd(x, x->dln, x->res[l], ly.mu1, ly.rs1, tid(l, K_LN1G), tid(l, K_LN1B), x->dres, acc)) return e;
+    if (int e = ln_bwd(x, x->dln, x->res[l], ly.mu1, ly.rs1, tid(l, K_LN1G), x->dres, ly.ln1_part)) return e;
   }
   // embeddings: token rows (deterministic segmented sum) and positions
   {
@@ -591,6 +629,10 @@ int gpt_backward(gpt_ctx* x) {
     HIPCHK(gk::sort_tokens(x->win, (int)N, x->keys, s));
     HIPCHK(gk::embed_bwd_ws(x->keys, (int)N, x->dres, (int)C, x->dln, x->G_(T_WTE), s));
     HIPCHK(gk::wpe_bwd(x->dres, (int)x->B, (int)x->T, (int)C, x->G_(T_WPE), acc, s));
+  }
+  {
+    ProfScope ps(x, "param_reduce", 0.0, 0.0);
+    HIPCHK(gk::reduce_jobs(x->jobs_dev, (int)x->jobs.size(), x->nred_blocks, acc, s));
   }
   x->others_fresh = false;
   x->fwd_grad = false;

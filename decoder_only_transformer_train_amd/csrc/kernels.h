@@ -50,12 +50,21 @@ hipError_t embed_ln_fwd(int dtype, const int32_t* tok, const float* wte, const f
                         float* res0, const float* g, const float* b, void* y, float* mu,
                         float* rstd, int rows, int C, hipStream_t s);
 // LayerNorm backward: dres_out = dres_in + dx (f32, may alias dres_in), dres_T = T(dres_out);
-// dgb_part [nblk][2C] partial column sums of dy*xhat and dy (reduced by colsum_f32)
+// part [nblk][3C]: per-block column sums of dy*xhat, dy and dres_out
 hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float* mu,
                          const float* rstd, const float* g, const float* dres_in,
                          float* dres_out, void* dres_T, float* part, int rows, int C,
                          int* nblk_out, hipStream_t s);
 int layernorm_bwd_blocks(int rows);
+// One column reduction of a batch: out[c] (+)= sum_r part[r * ld + c], c < cols;
+// blocks [first_block, first_block + cdiv(cols, 16)) of the batch launch serve it.
+struct RedJob {
+  const float* part;
+  float* out;
+  int nrows, cols, ld, first_block;
+};
+// all jobs (device array, first_block increasing) in one launch of nblocks blocks
+hipError_t reduce_jobs(const RedJob* jobs, int njobs, int nblocks, int accumulate, hipStream_t s);
 // out[c] = (acc ? out[c] : 0) + sum_r part[r][c] for c < cols (fixed order)
 hipError_t reduce_rows_f32(const float* part, int nrows, int cols, int64_t ld, float* out,
                            int accumulate, hipStream_t s);

@@ -73,7 +73,9 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 // LayerNorm backward.  dx = rstd (dxh - mean(dxh) - xh mean(dxh xh)) with
 // dxh = dy g, xh = (x - mu) rstd; dres_out = dres_in + dx and its T copy.
 // A workgroup handles LNB_ROWS rows and writes one partial row of
-// [sum dy*xh | sum dy] (2C floats).
+// [sum dy*xh | sum dy | sum dres_out] (3C floats): the gain and shift
+// gradients, and the column sums of the residual gradient it produces (the
+// bias gradient of the linear layer that feeds this residual stream).
 constexpr int LNB_ROWS = 32;
 
 template <typename T>
@@ -82,12 +84,12 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
                                                      const float* __restrict__ g, const float* dres_in,
                                                      float* dres_out, T* __restrict__ dres_T,
                                                      float* __restrict__ part, int rows, int C) {
-  __shared__ float red[4][2][2048];
+  __shared__ float red[4][2048];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nc = C >> 2;
-  float4 pg[MAXV], pb[MAXV];
+  float4 pg[MAXV], pb[MAXV], pc[MAXV];
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) pg[i] = pb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < MAXV; ++i) pg[i] = pb[i] = pc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   const int r0 = blockIdx.x * LNB_ROWS;
   for (int rr = w; rr < LNB_ROWS; rr += 4) {
     const int row = r0 + rr;
@@ -123,21 +125,50 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
                                        prev.w + r * (dxh[i].w - m1 - xh[i].w * m2));
         store4(dres_out + o, out);
         store4(dres_T + o, out);
+        pc[i].x += out.x; pc[i].y += out.y; pc[i].z += out.z; pc[i].w += out.w;
       }
     }
   }
+  // the 4 waves' partials, added in wave order, one quantity at a time
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int j = lane + 64 * i;
-    if (j < nc) {
-      *reinterpret_cast<float4*>(&red[w][0][4 * j]) = pg[i];
-      *reinterpret_cast<float4*>(&red[w][1][4 * j]) = pb[i];
+  for (int k = 0; k < 3; ++k) {
+    if (k) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int j = lane + 64 * i;
+      if (j < nc) *reinterpret_cast<float4*>(&red[w][4 * j]) = k == 0 ? pg[i] : (k == 1 ? pb[i] : pc[i]);
     }
+    __syncthreads();
+    for (int c = threadIdx.x; c < C; c += 256)
+      part[(int64_t)blockIdx.x * 3 * C + k * C + c] = red[0][c] + red[1][c] + red[2][c] + red[3][c];
   }
+}
+
+// Batched fixed-order column reductions: job j adds sum_r part[r][c] (rows in
+// order, in 16 interleaved row groups added in order) into out[c], or stores it.
+// Block b belongs to the job with first_block <= b < next job's first_block and
+// covers 16 of its columns.
+__global__ __launch_bounds__(256) void reduce_jobs_kernel(const RedJob* __restrict__ jobs, int njobs, int accumulate) {
+  __shared__ float red[16][17];
+  int lo = 0, hi = njobs - 1;
+  while (lo < hi) {  // last job whose first_block <= blockIdx.x
+    const int mid = (lo + hi + 1) >> 1;
+    if (jobs[mid].first_block <= (int)blockIdx.x) lo = mid;
+    else hi = mid - 1;
+  }
+  const RedJob J = jobs[lo];
+  const int cl = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int c = ((int)blockIdx.x - J.first_block) * 16 + cl;
+  float s = 0.f;
+  if (c < J.cols)
+    for (int r = rg; r < J.nrows; r += 16) s += J.part[(int64_t)r * J.ld + c];
+  red[rg][cl] = s;
   __syncthreads();
-  for (int c = threadIdx.x; c < 2 * C; c += 256) {
-    const int k = c / C, cc = c % C;
-    part[(int64_t)blockIdx.x * 2 * C + c] = red[0][k][cc] + red[1][k][cc] + red[2][k][cc] + red[3][k][cc];
+  if (rg == 0 && c < J.cols) {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot += red[i][cl];
+    J.out[c] = accumulate ? J.out[c] + tot : tot;
   }
 }
 
@@ -332,6 +363,12 @@ hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float
   else
     hipLaunchKernelGGL(ln_bwd_kernel<float>, dim3(nblk), dim3(256), 0, s, dy, x, mu, rstd, g, dres_in, dres_out,
                        (float*)dres_T, part, rows, C);
+  return hipGetLastError();
+}
+
+hipError_t reduce_jobs(const RedJob* jobs, int njobs, int nblocks, int accumulate, hipStream_t s) {
+  if (njobs <= 0 || nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_jobs_kernel, dim3(nblocks), dim3(256), 0, s, jobs, njobs, accumulate);
   return hipGetLastError();
 }
 
