@@ -306,6 +306,72 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
   }
 }
 
+// The same cross-entropy row with the row held in registers: 1024 threads
+// load the row once (NV float4 each), reduce the maximum, then the sum of
+// exp(z - max), and write dz from the same registers - one read of the logits
+// instead of two.  Columns in [V, ldz) are padding: excluded, dz = 0 there.
+template <typename T, int NV>
+__global__ __launch_bounds__(1024) void ce_reg_kernel(const float* __restrict__ z, int64_t ldz, int V,
+                                                      const int32_t* __restrict__ y, float scale,
+                                                      float* __restrict__ loss, float* __restrict__ lse_out,
+                                                      T* __restrict__ dz) {
+  __shared__ float red[2][16];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const float* zr = z + (int64_t)row * ldz;
+  const int L4 = (int)(ldz >> 2);
+  constexpr float NINF = -__builtin_huge_valf();
+  float4 v[NV];
+  float mx = NINF;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = t + 1024 * i, c = 4 * j;
+    v[i] = make_float4(NINF, NINF, NINF, NINF);
+    if (j < L4) {
+      const float4 a = load4(zr + c);
+      v[i] = make_float4(c < V ? a.x : NINF, c + 1 < V ? a.y : NINF, c + 2 < V ? a.z : NINF, c + 3 < V ? a.w : NINF);
+      mx = fmaxf(mx, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w)));
+    }
+  }
+  mx = wave_max(mx);
+  if (lane == 0) red[0][w] = mx;
+  __syncthreads();
+  float M = red[0][0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) M = fmaxf(M, red[0][i]);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    sum += hw_exp2((v[i].x - M) * LOG2E) + hw_exp2((v[i].y - M) * LOG2E) + hw_exp2((v[i].z - M) * LOG2E) +
+           hw_exp2((v[i].w - M) * LOG2E);
+  sum = wave_sum(sum);
+  if (lane == 0) red[1][w] = sum;
+  __syncthreads();
+  float S = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) S += red[1][i];
+  const float lse = M + hw_log2(S) * LN2;
+  const int yy = y[row];
+  if (t == 0) {
+    loss[row] = lse - zr[yy];
+    if (lse_out) lse_out[row] = lse;
+  }
+  if (dz != nullptr) {
+    T* dr = dz + (int64_t)row * ldz;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = t + 1024 * i, c = 4 * j;
+      if (j >= L4) break;
+      float d[4] = {hw_exp2((v[i].x - lse) * LOG2E), hw_exp2((v[i].y - lse) * LOG2E),
+                    hw_exp2((v[i].z - lse) * LOG2E), hw_exp2((v[i].w - lse) * LOG2E)};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (c + k == yy) d[k] -= 1.f;
+      store4(dr + c, make_float4(d[0] * scale, d[1] * scale, d[2] * scale, d[3] * scale));
+    }
+  }
+}
+
 // out[0] = mean of x[0..n) summed in a fixed order; also ring[slot]
 __global__ __launch_bounds__(256) void mean_kernel(const float* __restrict__ x, int n, float* out, float* ring,
                                                    int slot) {
@@ -389,8 +455,29 @@ hipError_t colsum_partial(int dtype, const void* x, int rows, int cols, float* p
   return hipGetLastError();
 }
 
+template <int NV>
+hipError_t ce_reg(int dtype, const float* z, int64_t ldz, int V, const int32_t* y, int rows, float scale, float* loss,
+                  float* lse_out, void* dz, hipStream_t s) {
+  if (dtype == BF16)
+    hipLaunchKernelGGL((ce_reg_kernel<bf16, NV>), dim3(rows), dim3(1024), 0, s, z, ldz, V, y, scale, loss, lse_out,
+                       (bf16*)dz);
+  else
+    hipLaunchKernelGGL((ce_reg_kernel<float, NV>), dim3(rows), dim3(1024), 0, s, z, ldz, V, y, scale, loss, lse_out,
+                       (float*)dz);
+  return hipGetLastError();
+}
+
 hipError_t ce_rows(int dtype, const float* z, int64_t ldz, int V, const int32_t* y, int rows, float scale,
                    float* loss, float* lse_out, void* dz, hipStream_t s) {
+  // rows of up to 64K columns are held in registers (one read of the logits)
+  if (ldz % 4 == 0) {
+    const int64_t nv = (ldz / 4 + 1023) / 1024;
+    if (nv <= 2) return ce_reg<2>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, s);
+    if (nv <= 4) return ce_reg<4>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, s);
+    if (nv <= 8) return ce_reg<8>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, s);
+    if (nv <= 13) return ce_reg<13>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, s);
+    if (nv <= 16) return ce_reg<16>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, s);
+  }
   if (dtype == BF16)
     hipLaunchKernelGGL(ce_rows_kernel<bf16>, dim3(rows), dim3(256), 0, s, z, ldz, V, y, scale, loss, lse_out,
                        (bf16*)dz);
