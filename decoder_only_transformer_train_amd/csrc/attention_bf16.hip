@@ -157,6 +157,8 @@ __device__ __forceinline__ void fwd_block(const char* __restrict__ rd, char* __r
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     if (kb * 64 > S.qlo[i] + 31) continue;  // every key of the block is after every query of the tile
+    // below the diagonal (every key of the block before every query of the tile) no key is masked
+    const bool diag = kb * 64 + 63 > S.qlo[i];
     const int qc = min(S.q[i], Tn - 1);
     f32x16 s[2];
 #pragma unroll
@@ -165,33 +167,44 @@ __device__ __forceinline__ void fwd_block(const char* __restrict__ rd, char* __r
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) mma32(s[kt], frag_row(sK, kt * 32 + c32, kk, g), S.qf[i][kk]);
     }
+    // row maximum of the raw scores (the scale cs > 0 keeps the order); masked scores -> -inf
     float mx = NEG_INF;
+    if (diag) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb * 64 + kt * 32 + crow(e, g);
-        const float v = (key <= qc) ? s[kt][e] * cs : NEG_INF;
-        s[kt][e] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb * 64 + kt * 32 + crow(e, g);
+          s[kt][e] = (key <= qc) ? s[kt][e] : NEG_INF;
+          mx = fmaxf(mx, s[kt][e]);
+        }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-    const float mnew = fmaxf(S.m[i], mx);
+    // running max in scaled log2 units; p = 2^(s cs - m) as one fma and one exp2
+    const float mnew = fmaxf(S.m[i], mx * cs);
     const float alpha = hw_exp2(S.m[i] - mnew);
     float ls = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = hw_exp2(s[kt][e] - mnew);
+        const float p = hw_exp2(fmaf(s[kt][e], cs, -mnew));
         s[kt][e] = p;
         ls += p;
       }
     ls += __shfl_xor(ls, 32, WAVE);
     S.l[i] = S.l[i] * alpha + ls;
     S.m[i] = mnew;
+    // the output only needs rescaling when some query's maximum grew
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) S.oacc[i][dt] *= alpha;
+      for (int dt = 0; dt < 2; ++dt) S.oacc[i][dt] *= alpha;
+    }
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
       const uint4 bp = pack_half(s[hh >> 1], hh & 1);
@@ -312,21 +325,30 @@ __device__ __forceinline__ void kv_block(const char* __restrict__ rd, char* __re
       mma32(s, frag_row(sQ, qt * 32 + c32, kk, g), S.kf[kk]);
       mma32(dp, frag_row(sdO, qt * 32 + c32, kk, g), S.vf[kk]);
     }
+    // Rows past the sequence need no mask: their Q and dO rows load as zeros, so
+    // their dS = p (dO.V - D) = p (0 - 0) and their P^T dO terms vanish.  Only the
+    // causal mask is left, and only on tiles that reach past the diagonal.
+    const bool diag = S.klo + 31 > qb * 64 + qt * 32;
+    float lv[16], dv[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int qi0 = qt * 32 + r4 * 8 + g * 4;  // rows crow(4 r4 .. 4 r4 + 3, g)
       const float4 l4 = *reinterpret_cast<const float4*>(slse + qi0);
       const float4 d4 = *reinterpret_cast<const float4*>(sDv + qi0);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+      lv[4 * r4] = l4.x; lv[4 * r4 + 1] = l4.y; lv[4 * r4 + 2] = l4.z; lv[4 * r4 + 3] = l4.w;
+      dv[4 * r4] = d4.x; dv[4 * r4 + 1] = d4.y; dv[4 * r4 + 2] = d4.z; dv[4 * r4 + 3] = d4.w;
+    }
+    if (diag) {
+      // keep s <= 0 mask inputs: score -> -inf for keys after the query, so p = 0
+      const int rel = qb * 64 + qt * 32 - S.key;  // query row of crow(e) minus this lane's key
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int e = 4 * r4 + jj;
-        const int qrow = qb * 64 + qi0 + jj;
-        const bool ok = (S.key <= qrow) && (qrow < Tn) && (S.key < Tn);
-        const float p = ok ? hw_exp2(s[e] * cs - lv[jj]) : 0.f;
-        s[e] = p;
-        dp[e] = p * (dp[e] - dv[jj]);
-      }
+      for (int e = 0; e < 16; ++e) s[e] = (rel + crow(e, g) >= 0) ? s[e] : NEG_INF;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = hw_exp2(fmaf(s[e], cs, -lv[e]));
+      s[e] = p;
+      dp[e] = p * (dp[e] - dv[e]);
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -444,12 +466,15 @@ __device__ __forceinline__ void dq_block(const char* __restrict__ rd, char* __re
       }
       // a query past the sequence has lse = D = 0 and its dQ is never stored;
       // keys past the sequence come after every valid query
+      // Only the causal mask, only where this half reaches past the tile's
+      // first query (keys past the sequence load as zeros and contribute nothing).
+      if (kb * 64 + kt * 32 + 31 > S.qlo[i]) {
+        const int rel = S.q[i] - (kb * 64 + kt * 32);  // this lane's query minus the half's first key
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kkey = kb * 64 + kt * 32 + crow(e, g);
-        const float p = (kkey <= S.q[i]) ? hw_exp2(s[e] * cs - S.lq[i]) : 0.f;
-        s[e] = p * (dp[e] - S.dd[i]);
+        for (int e = 0; e < 16; ++e) s[e] = (crow(e, g) <= rel) ? s[e] : NEG_INF;
       }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = hw_exp2(fmaf(s[e], cs, -S.lq[i])) * (dp[e] - S.dd[i]);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const uint4 bds = pack_half(s, hh);
