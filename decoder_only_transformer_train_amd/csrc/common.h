@@ -78,6 +78,13 @@ __device__ __forceinline__ float gelu_grad_f(float u) {
   float dt = GELU_K * (1.0f + 3.0f * GELU_A * u * u);
   return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * dt;
 }
+// both from one tanh: g = gelu(u), dg = gelu'(u)
+__device__ __forceinline__ void gelu_both(float u, float& g, float& dg) {
+  const float t = tanh_exp(GELU_K * (u + GELU_A * u * u * u));
+  const float dt = GELU_K * (1.0f + 3.0f * GELU_A * u * u);
+  g = 0.5f * u * (1.0f + t);
+  dg = 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * dt;
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

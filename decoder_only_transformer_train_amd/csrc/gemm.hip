@@ -211,10 +211,12 @@ __device__ __forceinline__ void epi_group_inline(const Params& p, int m, int n, 
       if constexpr (EPI == EPI_STORE) reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
       else if constexpr (EPI == EPI_RESID) reinterpret_cast<float*>(p.C)[o + k] = p.R[o + k] + (x + bn);
       else if constexpr (EPI == EPI_GELU) {
-        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
-        reinterpret_cast<T*>(p.C2)[o + k] = from_f<T>(gelu_f(x + bn));
+        float gg, dg;
+        gelu_both(x + bn, gg, dg);
+        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(dg);
+        reinterpret_cast<T*>(p.C2)[o + k] = from_f<T>(gg);
       } else if constexpr (EPI == EPI_GELU_BWD) {
-        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x * gelu_grad_f(to_f(reinterpret_cast<const T*>(p.aux)[o + k])));
+        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x * to_f(reinterpret_cast<const T*>(p.aux)[o + k]));
       } else {
         float* c = reinterpret_cast<float*>(p.C);
         c[o + k] = p.accumulate ? c[o + k] + x : x;
@@ -231,13 +233,16 @@ __device__ __forceinline__ void epi_group_inline(const Params& p, int m, int n, 
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) =
         make_float4(r.x + (a.x + b4.x), r.y + (a.y + b4.y), r.z + (a.z + b4.z), r.w + (a.w + b4.w));
   } else if constexpr (EPI == EPI_GELU) {
-    const float4 u = make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w);
-    store4(reinterpret_cast<T*>(p.C) + o, u);
-    store4(reinterpret_cast<T*>(p.C2) + o, make_float4(gelu_f(u.x), gelu_f(u.y), gelu_f(u.z), gelu_f(u.w)));
+    float g0, g1, g2, g3, d0, d1, d2, d3;
+    gelu_both(a.x + b4.x, g0, d0);
+    gelu_both(a.y + b4.y, g1, d1);
+    gelu_both(a.z + b4.z, g2, d2);
+    gelu_both(a.w + b4.w, g3, d3);
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(d0, d1, d2, d3));
+    store4(reinterpret_cast<T*>(p.C2) + o, make_float4(g0, g1, g2, g3));
   } else if constexpr (EPI == EPI_GELU_BWD) {
     const float4 u = load4(reinterpret_cast<const T*>(p.aux) + o);
-    store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x * gelu_grad_f(u.x), a.y * gelu_grad_f(u.y),
-                                                      a.z * gelu_grad_f(u.z), a.w * gelu_grad_f(u.w)));
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x * u.x, a.y * u.y, a.z * u.z, a.w * u.w));
   } else {
     float* c = reinterpret_cast<float*>(p.C) + o;
     if (p.accumulate) {
@@ -288,10 +293,12 @@ __device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 
       if constexpr (EPI == EPI_STORE) reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
       else if constexpr (EPI == EPI_RESID) reinterpret_cast<float*>(p.C)[o + k] = p.R[o + k] + (x + bn);
       else if constexpr (EPI == EPI_GELU) {
-        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
-        reinterpret_cast<T*>(p.C2)[o + k] = from_f<T>(gelu_f(x + bn));
+        float gg, dg;
+        gelu_both(x + bn, gg, dg);
+        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(dg);
+        reinterpret_cast<T*>(p.C2)[o + k] = from_f<T>(gg);
       } else if constexpr (EPI == EPI_GELU_BWD) {
-        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x * gelu_grad_f(to_f(reinterpret_cast<const T*>(p.aux)[o + k])));
+        reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x * to_f(reinterpret_cast<const T*>(p.aux)[o + k]));
       } else {
         float* c = reinterpret_cast<float*>(p.C);
         c[o + k] = p.accumulate ? c[o + k] + x : x;
@@ -305,12 +312,15 @@ __device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) =
         make_float4(in.x + (a.x + b4.x), in.y + (a.y + b4.y), in.z + (a.z + b4.z), in.w + (a.w + b4.w));
   } else if constexpr (EPI == EPI_GELU) {
-    const float4 u = make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w);
-    store4(reinterpret_cast<T*>(p.C) + o, u);
-    store4(reinterpret_cast<T*>(p.C2) + o, make_float4(gelu_f(u.x), gelu_f(u.y), gelu_f(u.z), gelu_f(u.w)));
+    float g0, g1, g2, g3, d0, d1, d2, d3;
+    gelu_both(a.x + b4.x, g0, d0);
+    gelu_both(a.y + b4.y, g1, d1);
+    gelu_both(a.z + b4.z, g2, d2);
+    gelu_both(a.w + b4.w, g3, d3);
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(d0, d1, d2, d3));
+    store4(reinterpret_cast<T*>(p.C2) + o, make_float4(g0, g1, g2, g3));
   } else if constexpr (EPI == EPI_GELU_BWD) {
-    store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x * gelu_grad_f(in.x), a.y * gelu_grad_f(in.y),
-                                                      a.z * gelu_grad_f(in.z), a.w * gelu_grad_f(in.w)));
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x * in.x, a.y * in.y, a.z * in.z, a.w * in.w));
   } else {
     if (p.accumulate) a = make_float4(in.x + a.x, in.y + a.y, in.z + a.z, in.w + a.w);
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) = a;

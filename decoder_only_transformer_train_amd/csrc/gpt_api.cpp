@@ -63,7 +63,7 @@ struct Layer {
   float* res_mid;  // f32 [N][C]
   void* ln2;
   float *mu2, *rs2;
-  void* fcpre;  // T [N][4C]
+  void* fcdg;   // T [N][4C]: GELU'(FC pre-activation), kept for the backward
   void* fcact;  // T [N][4C]
   // backward column-sum partials, reduced in one batch at the end of backward
   float *ln1_part, *ln2_part;   // [N / 32][3C]: ln gain, ln shift, residual-gradient column sums
@@ -103,6 +103,7 @@ struct gpt_ctx {
   int ring_wr = 0, ring_rd = 0;
   // backward
   float *dres, *dln;
+  void* dlnT;  // T [N][C]: gradient at a LayerNorm output
   void *dresT, *dfc, *datt, *dqkv;
   float *Dv, *lnf_part, *splitk_ws;
   gk::RedJob* jobs_dev;
@@ -231,7 +232,7 @@ int64_t carve(gpt_ctx* x, void* base) {
     l.ln2 = cv.take<void>(N * C * es);
     l.mu2 = cv.take<float>(N * 4);
     l.rs2 = cv.take<float>(N * 4);
-    l.fcpre = cv.take<void>(N * 4 * C * es);
+    l.fcdg = cv.take<void>(N * 4 * C * es);
     l.fcact = cv.take<void>(N * 4 * C * es);
   }
   x->lnf = cv.take<void>(N * C * es);
@@ -246,6 +247,7 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->ring = cv.take<float>(RING * 4);
   x->dres = cv.take<float>(N * C * 4);
   x->dln = cv.take<float>(N * C * 4);
+  x->dlnT = cv.take<void>(N * C * es);
   x->dresT = cv.take<void>(N * C * es);
   x->dfc = cv.take<void>(N * 4 * C * es);
   x->datt = cv.take<void>(N * C * es);
@@ -387,11 +389,11 @@ int bias_colsum(gpt_ctx* x, int dtype, const void* dY, int64_t cols, float* part
 
 // LayerNorm backward into x->dres (+ its T copy); gain/shift/residual column
 // partials into part
-int ln_bwd(gpt_ctx* x, const float* dy, const float* xin, const float* mu, const float* rs, int g_id,
+int ln_bwd(gpt_ctx* x, const void* dy, bool dy_is_t, const float* xin, const float* mu, const float* rs, int g_id,
            const float* dres_in, float* part) {
-  ProfScope ps(x, "layernorm_bwd", 0.0, (double)x->N * x->C * (4 + 4 + 4 + 4 + x->es) + 8.0 * x->N);
-  HIPCHK(gk::layernorm_bwd(x->dt, dy, xin, mu, rs, x->P_(g_id), dres_in, x->dres, x->dresT, part, (int)x->N,
-                           (int)x->C, nullptr, x->stream));
+  ProfScope ps(x, "layernorm_bwd", 0.0, (double)x->N * x->C * ((dy_is_t ? x->es : 4) + 4 + 4 + 4 + x->es) + 8.0 * x->N);
+  HIPCHK(gk::layernorm_bwd(x->dt, dy, dy_is_t ? 1 : 0, xin, mu, rs, x->P_(g_id), dres_in, x->dres, x->dresT, part,
+                           (int)x->N, (int)x->C, nullptr, x->stream));
   return 0;
 }
 
@@ -550,7 +552,7 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
     g.R = x->res[l];
     if (int e = run_gemm(x, "gemm_proj_fwd", g)) return e;
     if (int e = ln_fwd(x, ly.res_mid, tid(l, K_LN2G), tid(l, K_LN2B), ly.ln2, ly.mu2, ly.rs2)) return e;
-    g = mk(x, 0, 0, gk::EPI_GELU, ly.ln2, C, x->W_(tid(l, K_FCW)), C, N, 4 * C, C, ly.fcpre, 4 * C);
+    g = mk(x, 0, 0, gk::EPI_GELU, ly.ln2, C, x->W_(tid(l, K_FCW)), C, N, 4 * C, C, ly.fcdg, 4 * C);
     g.bias = x->P_(tid(l, K_FCB));
     g.C2 = ly.fcact;
     if (int e = run_gemm(x, "gemm_fc_fwd", g)) return e;
@@ -592,20 +594,20 @@ int gpt_backward(gpt_ctx* x) {
   const int64_t N = x->N, C = x->C;
   const int acc = x->others_fresh ? 0 : 1;
   const int L = (int)x->L;
-  if (int e = ln_bwd(x, x->dF, x->res[L], x->muf, x->rsf, tid_lnf(L, 0), nullptr, x->lnf_part)) return e;
+  if (int e = ln_bwd(x, x->dF, false, x->res[L], x->muf, x->rsf, tid_lnf(L, 0), nullptr, x->lnf_part)) return e;
   for (int l = L - 1; l >= 0; --l) {
     Layer& ly = x->layers[l];
     // MLP output projection
     if (int e = wgrad(x, "gemm_wgrad_mlp", x->dresT, C, ly.fcact, 4 * C, C, 4 * C, x->G_(tid(l, K_MPW)), acc)) return e;
     gk::Gemm g = mk(x, 0, 1, gk::EPI_GELU_BWD, x->dresT, C, x->W_(tid(l, K_MPW)), 4 * C, N, 4 * C, C, x->dfc, 4 * C);
-    g.aux = ly.fcpre;
+    g.aux = ly.fcdg;
     if (int e = run_gemm(x, "gemm_dgrad_mlp", g)) return e;
     // MLP input projection
     if (int e = wgrad(x, "gemm_wgrad_mlp", x->dfc, 4 * C, ly.ln2, C, 4 * C, C, x->G_(tid(l, K_FCW)), acc)) return e;
     if (int e = bias_colsum(x, x->dt, x->dfc, 4 * C, ly.fcb_part)) return e;
-    g = mk(x, 0, 1, gk::EPI_F32, x->dfc, 4 * C, x->W_(tid(l, K_FCW)), C, N, C, 4 * C, x->dln, C);
+    g = mk(x, 0, 1, gk::EPI_STORE, x->dfc, 4 * C, x->W_(tid(l, K_FCW)), C, N, C, 4 * C, x->dlnT, C);
     if (int e = run_gemm(x, "gemm_dgrad_mlp", g)) return e;
-    if (int e = ln_bwd(x, x->dln, ly.res_mid, ly.mu2, ly.rs2, tid(l, K_LN2G), x->dres, ly.ln2_part)) return e;
+    if (int e = ln_bwd(x, x->dlnT, true, ly.res_mid, ly.mu2, ly.rs2, tid(l, K_LN2G), x->dres, ly.ln2_part)) return e;
     // attention output projection
     if (int e = wgrad(x, "gemm_wgrad_attn", x->dresT, C, ly.att, C, C, C, x->G_(tid(l, K_PROJW)), acc)) return e;
     g = mk(x, 0, 1, gk::EPI_STORE, x->dresT, C, x->W_(tid(l, K_PROJW)), C, N, C, C, x->datt, C);
@@ -619,9 +621,9 @@ int gpt_backward(gpt_ctx* x) {
     // QKV projection
     if (int e = wgrad(x, "gemm_wgrad_attn", x->dqkv, 3 * C, ly.ln1, C, 3 * C, C, x->G_(tid(l, K_ATTW)), acc)) return e;
     if (int e = bias_colsum(x, x->dt, x->dqkv, 3 * C, ly.attb_part)) return e;
-    g = mk(x, 0, 1, gk::EPI_F32, x->dqkv, 3 * C, x->W_(tid(l, K_ATTW)), C, N, C, 3 * C, x->dln, C);
+    g = mk(x, 0, 1, gk::EPI_STORE, x->dqkv, 3 * C, x->W_(tid(l, K_ATTW)), C, N, C, 3 * C, x->dlnT, C);
     if (int e = run_gemm(x, "gemm_dgrad_attn", g)) return e;
-    if (int e = ln_bwd(x, x->dln, x->res[l], ly.mu1, ly.rs1, tid(l, K_LN1G), x->dres, ly.ln1_part)) return e;
+    if (int e = ln_bwd(x, x->dlnT, true, x->res[l], ly.mu1, ly.rs1, tid(l, K_LN1G), x->dres, ly.ln1_part)) return e;
   }
   // embeddings: token rows (deterministic segmented sum) and positions
   {

@@ -13,8 +13,8 @@ enum Dtype { F32 = 0, BF16 = 1 };
 enum Epi {
   EPI_STORE = 0,     // C(T) = acc + bias
   EPI_RESID = 1,     // C(f32) = R(f32) + acc + bias
-  EPI_GELU = 2,      // C(T) = acc + bias; C2(T) = gelu(acc + bias)
-  EPI_GELU_BWD = 3,  // C(T) = acc * gelu'(aux(T))
+  EPI_GELU = 2,      // u = acc + bias: C(T) = gelu'(u) (kept for the backward), C2(T) = gelu(u)
+  EPI_GELU_BWD = 3,  // C(T) = acc * aux(T) (aux = gelu'(u) from the forward)
   EPI_F32 = 4,       // C(f32) = (accumulate ? C : 0) + acc
 };
 
@@ -51,10 +51,10 @@ hipError_t embed_ln_fwd(int dtype, const int32_t* tok, const float* wte, const f
                         float* rstd, int rows, int C, hipStream_t s);
 // LayerNorm backward: dres_out = dres_in + dx (f32, may alias dres_in), dres_T = T(dres_out);
 // part [nblk][3C]: per-block column sums of dy*xhat, dy and dres_out
-hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float* mu,
-                         const float* rstd, const float* g, const float* dres_in,
-                         float* dres_out, void* dres_T, float* part, int rows, int C,
-                         int* nblk_out, hipStream_t s);
+// dy is T when dy_is_t (bf16 or fp32 as dtype), else fp32
+hipError_t layernorm_bwd(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu,
+                         const float* rstd, const float* g, const float* dres_in, float* dres_out, void* dres_T,
+                         float* part, int rows, int C, int* nblk_out, hipStream_t s);
 int layernorm_bwd_blocks(int rows);
 // One column reduction of a batch: out[c] (+)= sum_r part[r * ld + c], c < cols;
 // blocks [first_block, first_block + cdiv(cols, 16)) of the batch launch serve it.

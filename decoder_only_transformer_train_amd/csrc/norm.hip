@@ -78,8 +78,8 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 // bias gradient of the linear layer that feeds this residual stream).
 constexpr int LNB_ROWS = 32;
 
-template <typename T>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+template <typename TY, typename T>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(const TY* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ mu, const float* __restrict__ rs,
                                                      const float* __restrict__ g, const float* dres_in,
                                                      float* dres_out, T* __restrict__ dres_T,
@@ -418,17 +418,20 @@ hipError_t embed_ln_fwd(int dtype, const int32_t* tok, const float* wte, const f
 
 int layernorm_bwd_blocks(int rows) { return cdiv(rows, LNB_ROWS); }
 
-hipError_t layernorm_bwd(int dtype, const float* dy, const float* x, const float* mu, const float* rstd,
-                         const float* g, const float* dres_in, float* dres_out, void* dres_T, float* part,
-                         int rows, int C, int* nblk_out, hipStream_t s) {
+hipError_t layernorm_bwd(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu,
+                         const float* rstd, const float* g, const float* dres_in, float* dres_out, void* dres_T,
+                         float* part, int rows, int C, int* nblk_out, hipStream_t s) {
   const int nblk = layernorm_bwd_blocks(rows);
   if (nblk_out) *nblk_out = nblk;
-  if (dtype == BF16)
-    hipLaunchKernelGGL(ln_bwd_kernel<bf16>, dim3(nblk), dim3(256), 0, s, dy, x, mu, rstd, g, dres_in, dres_out,
-                       (bf16*)dres_T, part, rows, C);
+  if (dtype == BF16 && dy_is_t)
+    hipLaunchKernelGGL((ln_bwd_kernel<bf16, bf16>), dim3(nblk), dim3(256), 0, s, (const bf16*)dy, x, mu, rstd, g,
+                       dres_in, dres_out, (bf16*)dres_T, part, rows, C);
+  else if (dtype == BF16)
+    hipLaunchKernelGGL((ln_bwd_kernel<float, bf16>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu, rstd, g,
+                       dres_in, dres_out, (bf16*)dres_T, part, rows, C);
   else
-    hipLaunchKernelGGL(ln_bwd_kernel<float>, dim3(nblk), dim3(256), 0, s, dy, x, mu, rstd, g, dres_in, dres_out,
-                       (float*)dres_T, part, rows, C);
+    hipLaunchKernelGGL((ln_bwd_kernel<float, float>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu, rstd,
+                       g, dres_in, dres_out, (float*)dres_T, part, rows, C);
   return hipGetLastError();
 }
 
