@@ -111,7 +111,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true")
-    ap.add_argument("--roofline-kernel", default="gemm_wgrad_mlp", choices=PROFILE_CLASSES)
+    # the largest kernel that runs alone (backward weight gradients share the GPU with the data-gradient chain)
+    ap.add_argument("--roofline-kernel", default="head_logits", choices=PROFILE_CLASSES)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="after the timed steps, copy this many bytes device-to-device once")
     args = ap.parse_args()

@@ -104,7 +104,10 @@ struct gpt_ctx {
   // backward
   float *dres, *dln;
   void* dlnT;  // T [N][C]: gradient at a LayerNorm output
-  void *dresT, *dfc, *datt, *dqkv;
+  void *dresT2[2], *dfc, *datt, *dqkv;  // dresT2: two T copies of the residual gradient (see gpt_backward)
+  // weight-gradient products run on a second stream, ordered by events
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> sev;
   float *Dv, *lnf_part, *splitk_ws;
   gk::RedJob* jobs_dev;
   std::vector<gk::RedJob> jobs;
@@ -248,7 +251,8 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->dres = cv.take<float>(N * C * 4);
   x->dln = cv.take<float>(N * C * 4);
   x->dlnT = cv.take<void>(N * C * es);
-  x->dresT = cv.take<void>(N * C * es);
+  x->dresT2[0] = cv.take<void>(N * C * es);
+  x->dresT2[1] = cv.take<void>(N * C * es);
   x->dfc = cv.take<void>(N * 4 * C * es);
   x->datt = cv.take<void>(N * C * es);
   x->dqkv = cv.take<void>(N * 3 * C * es);
@@ -315,7 +319,9 @@ void setup_dims(gpt_ctx* x, const gpt_config* c) {
 struct ProfScope {
   gpt_ctx* x;
   bool on;
-  ProfScope(gpt_ctx* x_, const char* cls, double flops, double bytes) : x(x_) {
+  hipStream_t st;
+  ProfScope(gpt_ctx* x_, const char* cls, double flops, double bytes, hipStream_t s_ = nullptr)
+      : x(x_), st(s_ ? s_ : x_->stream) {
     on = !x->prof.cls.empty() && (x->prof.cls == "any" || x->prof.cls == cls);
     if (!on) return;
     if (x->prof.used + 2 > x->prof.ev.size()) {
@@ -325,7 +331,7 @@ struct ProfScope {
         x->prof.ev.push_back(e);
       }
     }
-    (void)hipEventRecord(x->prof.ev[x->prof.used], x->stream);
+    (void)hipEventRecord(x->prof.ev[x->prof.used], st);
     x->prof.flops += flops;
     x->prof.bytes += bytes;
     x->prof.launches += 1;
@@ -334,17 +340,18 @@ struct ProfScope {
   hipEvent_t stop_event() { return on ? x->prof.ev[x->prof.used + 1] : nullptr; }
   ~ProfScope() {
     if (!on) return;
-    if (!stopped) (void)hipEventRecord(x->prof.ev[x->prof.used + 1], x->stream);
+    if (!stopped) (void)hipEventRecord(x->prof.ev[x->prof.used + 1], st);
     x->prof.used += 2;
   }
   bool stopped = false;
 };
 
 // GEMM classes time only the main kernel (a split-K reduction is not included)
-int run_gemm(gpt_ctx* x, const char* cls, const gk::Gemm& g) {
-  ProfScope ps(x, cls, 2.0 * g.M * g.N * (double)g.K, 0.0);
+int run_gemm(gpt_ctx* x, const char* cls, const gk::Gemm& g, hipStream_t st = nullptr) {
+  if (!st) st = x->stream;
+  ProfScope ps(x, cls, 2.0 * g.M * g.N * (double)g.K, 0.0, st);
   hipEvent_t stop = ps.stop_event();
-  HIPCHK(gk::gemm(g, x->stream, stop));
+  HIPCHK(gk::gemm(g, st, stop));
   ps.stopped = stop != nullptr;
   return 0;
 }
@@ -371,28 +378,29 @@ gk::Gemm mk(gpt_ctx* x, int at, int bt, int epi, const void* A, int64_t lda, con
 inline void* off_T(gpt_ctx* x, void* p, int64_t elems) { return (char*)p + elems * x->es; }
 
 // weight gradient dW[M][N] (+)= sum_n A(m, n) B(n-th col): both operands token-major
+// (runs on the side stream in the backward; the split-K workspace is only used there)
 int wgrad(gpt_ctx* x, const char* cls, const void* dY, int64_t ldy, const void* Xin, int64_t ldx, int64_t M,
           int64_t Nn, float* dW, int acc) {
   gk::Gemm g = mk(x, 1, 1, gk::EPI_F32, dY, ldy, Xin, ldx, M, Nn, x->N, dW, Nn);
   g.accumulate = acc;
   g.splits = gk::gemm_pick_splits((int)M, (int)Nn, (int)x->N, 1, 1);
   g.ws = x->splitk_ws;
-  return run_gemm(x, cls, g);
+  return run_gemm(x, cls, g, x->side);
 }
 
 // column partial sums of a bias gradient (reduced with the others at the end of backward)
 int bias_colsum(gpt_ctx* x, int dtype, const void* dY, int64_t cols, float* part) {
-  ProfScope ps(x, "bias_colsum", 0.0, (double)x->N * cols * (dtype == GPT_BF16 ? 2 : 4));
-  HIPCHK(gk::colsum_partial(dtype, dY, (int)x->N, (int)cols, part, x->stream));
+  ProfScope ps(x, "bias_colsum", 0.0, (double)x->N * cols * (dtype == GPT_BF16 ? 2 : 4), x->side);
+  HIPCHK(gk::colsum_partial(dtype, dY, (int)x->N, (int)cols, part, x->side));
   return 0;
 }
 
 // LayerNorm backward into x->dres (+ its T copy); gain/shift/residual column
 // partials into part
 int ln_bwd(gpt_ctx* x, const void* dy, bool dy_is_t, const float* xin, const float* mu, const float* rs, int g_id,
-           const float* dres_in, float* part) {
+           const float* dres_in, float* part, void* dresT) {
   ProfScope ps(x, "layernorm_bwd", 0.0, (double)x->N * x->C * ((dy_is_t ? x->es : 4) + 4 + 4 + 4 + x->es) + 8.0 * x->N);
-  HIPCHK(gk::layernorm_bwd(x->dt, dy, dy_is_t ? 1 : 0, xin, mu, rs, x->P_(g_id), dres_in, x->dres, x->dresT, part,
+  HIPCHK(gk::layernorm_bwd(x->dt, dy, dy_is_t ? 1 : 0, xin, mu, rs, x->P_(g_id), dres_in, x->dres, dresT, part,
                            (int)x->N, (int)x->C, nullptr, x->stream));
   return 0;
 }
@@ -486,8 +494,12 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
   if (x->shadow) chk(gk::to_bf16(x->params, x->shadow, x->P, s));
   build_jobs(x);
   chk(hipMemcpyAsync(x->jobs_dev, x->jobs.data(), x->jobs.size() * sizeof(gk::RedJob), hipMemcpyHostToDevice, s));
+  // side stream (default priority) and its ordering events
+  chk(hipStreamCreateWithFlags(&x->side, hipStreamNonBlocking));
+  x->sev.assign((size_t)x->L * 8, nullptr);
+  for (auto& e : x->sev) chk(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   if (rc) {
-    delete x;
+    gpt_destroy(x);
     return rc;
   }
   *out = x;
@@ -497,6 +509,9 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
 int gpt_destroy(gpt_ctx* x) {
   if (!x) return 0;
   for (auto e : x->prof.ev) (void)hipEventDestroy(e);
+  for (auto e : x->sev)
+    if (e) (void)hipEventDestroy(e);
+  if (x->side) (void)hipStreamDestroy(x->side);
   delete x;
   return 0;
 }
@@ -590,28 +605,65 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
 int gpt_backward(gpt_ctx* x) {
   if (!x) return fail(GPT_EINVAL, "null context");
   if (!x->have_fwd || !x->fwd_grad) return fail(GPT_EINVAL, "gpt_backward needs a gpt_forward_loss with loss_scale > 0");
-  hipStream_t s = x->stream;
+  hipStream_t s = x->stream, ss = x->side;
   const int64_t N = x->N, C = x->C;
   const int acc = x->others_fresh ? 0 : 1;
   const int L = (int)x->L;
-  if (int e = ln_bwd(x, x->dF, false, x->res[L], x->muf, x->rsf, tid_lnf(L, 0), nullptr, x->lnf_part)) return e;
+  // The four weight-gradient products of a layer (and the fc/qkv bias column
+  // sums) run on the side stream ss, off the data-gradient chain on s.  Each
+  // side product starts after an event that s records when its input is
+  // written; s waits for the side product's completion event before it
+  // overwrites that input: dfc (next layer's GELU backward), dqkv (next
+  // layer's attention backward) and the residual-gradient T copies, which
+  // alternate between two buffers - T0 enters a layer, LN2 writes T1, LN1 T0.
+  // Events per layer: 0-3 mark the inputs ready, 4-7 the side products done.
+  auto ev = [&](int l, int k) { return x->sev[(size_t)l * 8 + k]; };
+  auto fork = [&](int l, int k) -> int {
+    HIPCHK(hipEventRecord(ev(l, k), s));
+    HIPCHK(hipStreamWaitEvent(ss, ev(l, k), 0));
+    return 0;
+  };
+  auto done = [&](int l, int k) -> int {
+    HIPCHK(hipEventRecord(ev(l, 4 + k), ss));
+    return 0;
+  };
+  auto wait_side = [&](int l, int k) -> int {
+    HIPCHK(hipStreamWaitEvent(s, ev(l, 4 + k), 0));
+    return 0;
+  };
+  void* T0 = x->dresT2[0];
+  void* T1 = x->dresT2[1];
+  if (int e = ln_bwd(x, x->dF, false, x->res[L], x->muf, x->rsf, tid_lnf(L, 0), nullptr, x->lnf_part, T0)) return e;
   for (int l = L - 1; l >= 0; --l) {
     Layer& ly = x->layers[l];
-    // MLP output projection
-    if (int e = wgrad(x, "gemm_wgrad_mlp", x->dresT, C, ly.fcact, 4 * C, C, 4 * C, x->G_(tid(l, K_MPW)), acc)) return e;
-    gk::Gemm g = mk(x, 0, 1, gk::EPI_GELU_BWD, x->dresT, C, x->W_(tid(l, K_MPW)), 4 * C, N, 4 * C, C, x->dfc, 4 * C);
+    // MLP output projection: dW on the side stream, GELU backward on s
+    if (int e = fork(l, 0)) return e;
+    if (int e = wgrad(x, "gemm_wgrad_mlp", T0, C, ly.fcact, 4 * C, C, 4 * C, x->G_(tid(l, K_MPW)), acc)) return e;
+    if (int e = done(l, 0)) return e;
+    if (l + 1 < L)
+      if (int e = wait_side(l + 1, 1)) return e;  // previous layer's fc dW finished reading dfc
+    gk::Gemm g = mk(x, 0, 1, gk::EPI_GELU_BWD, T0, C, x->W_(tid(l, K_MPW)), 4 * C, N, 4 * C, C, x->dfc, 4 * C);
     g.aux = ly.fcdg;
     if (int e = run_gemm(x, "gemm_dgrad_mlp", g)) return e;
     // MLP input projection
+    if (int e = fork(l, 1)) return e;
     if (int e = wgrad(x, "gemm_wgrad_mlp", x->dfc, 4 * C, ly.ln2, C, 4 * C, C, x->G_(tid(l, K_FCW)), acc)) return e;
     if (int e = bias_colsum(x, x->dt, x->dfc, 4 * C, ly.fcb_part)) return e;
+    if (int e = done(l, 1)) return e;
     g = mk(x, 0, 1, gk::EPI_STORE, x->dfc, 4 * C, x->W_(tid(l, K_FCW)), C, N, C, 4 * C, x->dlnT, C);
     if (int e = run_gemm(x, "gemm_dgrad_mlp", g)) return e;
-    if (int e = ln_bwd(x, x->dlnT, true, ly.res_mid, ly.mu2, ly.rs2, tid(l, K_LN2G), x->dres, ly.ln2_part)) return e;
+    if (l + 1 < L)
+      if (int e = wait_side(l + 1, 2)) return e;  // previous layer's proj dW finished reading T1
+    if (int e = ln_bwd(x, x->dlnT, true, ly.res_mid, ly.mu2, ly.rs2, tid(l, K_LN2G), x->dres, ly.ln2_part, T1))
+      return e;
     // attention output projection
-    if (int e = wgrad(x, "gemm_wgrad_attn", x->dresT, C, ly.att, C, C, C, x->G_(tid(l, K_PROJW)), acc)) return e;
-    g = mk(x, 0, 1, gk::EPI_STORE, x->dresT, C, x->W_(tid(l, K_PROJW)), C, N, C, C, x->datt, C);
+    if (int e = fork(l, 2)) return e;
+    if (int e = wgrad(x, "gemm_wgrad_attn", T1, C, ly.att, C, C, C, x->G_(tid(l, K_PROJW)), acc)) return e;
+    if (int e = done(l, 2)) return e;
+    g = mk(x, 0, 1, gk::EPI_STORE, T1, C, x->W_(tid(l, K_PROJW)), C, N, C, C, x->datt, C);
     if (int e = run_gemm(x, "gemm_dgrad_attn", g)) return e;
+    if (l + 1 < L)
+      if (int e = wait_side(l + 1, 3)) return e;  // previous layer's qkv dW finished reading dqkv
     {
       const double pairs = (double)x->B * x->H * x->T * (x->T + 1) / 2.0;
       ProfScope ps(x, "attn_bwd", 8.0 * x->D * pairs, 0.0);
@@ -619,12 +671,19 @@ int gpt_backward(gpt_ctx* x) {
                           (int)x->D, s));
     }
     // QKV projection
+    if (int e = fork(l, 3)) return e;
     if (int e = wgrad(x, "gemm_wgrad_attn", x->dqkv, 3 * C, ly.ln1, C, 3 * C, C, x->G_(tid(l, K_ATTW)), acc)) return e;
     if (int e = bias_colsum(x, x->dt, x->dqkv, 3 * C, ly.attb_part)) return e;
+    if (int e = done(l, 3)) return e;
     g = mk(x, 0, 1, gk::EPI_STORE, x->dqkv, 3 * C, x->W_(tid(l, K_ATTW)), C, N, C, 3 * C, x->dlnT, C);
     if (int e = run_gemm(x, "gemm_dgrad_attn", g)) return e;
-    if (int e = ln_bwd(x, x->dlnT, true, x->res[l], ly.mu1, ly.rs1, tid(l, K_LN1G), x->dres, ly.ln1_part)) return e;
+    if (int e = wait_side(l, 0)) return e;  // this layer's MLP-output dW finished reading T0
+    if (int e = ln_bwd(x, x->dlnT, true, x->res[l], ly.mu1, ly.rs1, tid(l, K_LN1G), x->dres, ly.ln1_part, T0))
+      return e;
   }
+  // join: every side product is done before the parameter reduction and AdamW
+  for (int k = 0; k < 4; ++k)
+    if (int e = wait_side(0, k)) return e;
   // embeddings: token rows (deterministic segmented sum) and positions
   {
     ProfScope ps(x, "embed_bwd", 0.0, (double)N * C * 12);
@@ -829,6 +888,7 @@ int gpt_profile_begin(gpt_ctx* x, const char* cls) {
 int gpt_profile_end(gpt_ctx* x, double* total_ms, int64_t* launches, double* flops, double* bytes) {
   if (!x) return fail(GPT_EINVAL, "null context");
   HIPCHK(hipStreamSynchronize(x->stream));
+  if (x->side) HIPCHK(hipStreamSynchronize(x->side));
   double ms = 0;
   for (size_t i = 0; i + 1 < x->prof.used; i += 2) {
     float t = 0;
