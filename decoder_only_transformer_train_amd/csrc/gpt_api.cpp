@@ -96,8 +96,8 @@ struct gpt_ctx {
   float *muf, *rsf;
   // head
   int64_t ldv, Nc;
-  float* logits;  // f32 [Nc][ldv]
-  void* dz;       // T [Nc][ldv]
+  void* logits;   // T [Nc][ldv]
+  void* dz2[2];   // T [Nc][ldv], alternating per chunk (the head's dW runs on the side stream)
   float *tok_loss, *tok_lse, *dF, *loss;
   float* ring;
   int ring_wr = 0, ring_rd = 0;
@@ -108,6 +108,8 @@ struct gpt_ctx {
   // weight-gradient products run on a second stream, ordered by events
   hipStream_t side = nullptr;
   std::vector<hipEvent_t> sev;
+  hipEvent_t head_ready[2] = {nullptr, nullptr}, head_done[2] = {nullptr, nullptr}, side_tail = nullptr;
+  bool dz_busy[2] = {false, false};
   float *Dv, *lnf_part, *splitk_ws;
   gk::RedJob* jobs_dev;
   std::vector<gk::RedJob> jobs;
@@ -241,8 +243,9 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->lnf = cv.take<void>(N * C * es);
   x->muf = cv.take<float>(N * 4);
   x->rsf = cv.take<float>(N * 4);
-  x->logits = cv.take<float>(x->Nc * x->ldv * 4);
-  x->dz = cv.take<void>(x->Nc * x->ldv * es);
+  x->logits = cv.take<void>(x->Nc * x->ldv * es);
+  x->dz2[0] = cv.take<void>(x->Nc * x->ldv * es);
+  x->dz2[1] = cv.take<void>(x->Nc * x->ldv * es);
   x->tok_loss = cv.take<float>(N * 4);
   x->tok_lse = cv.take<float>(N * 4);
   x->dF = cv.take<float>(N * C * 4);
@@ -411,23 +414,63 @@ int ln_fwd(gpt_ctx* x, const float* in, int g_id, int b_id, void* out, float* mu
   return 0;
 }
 
-// The fused tied head + cross-entropy over row chunks: logits of a chunk live
-// only in the chunk buffer; loss, dF and dW come out of the same pass.
+// main stream waits for all work queued on the side stream so far
+int join_side(gpt_ctx* x) {
+  if (!x->side) return 0;
+  HIPCHK(hipEventRecord(x->side_tail, x->side));
+  HIPCHK(hipStreamWaitEvent(x->stream, x->side_tail, 0));
+  x->dz_busy[0] = x->dz_busy[1] = false;
+  return 0;
+}
+
+// The fused tied head + cross-entropy over row chunks: logits of a chunk (in
+// the compute type, as the bf16 matrix product of the pages' mixed precision
+// leaves them) live only in the chunk buffer; loss, dF and dW come out of the same pass.  With a
+// side stream, a chunk's dW product runs there, beside the chunk's dF product
+// and into the next chunk's logits (chunks alternate between two dz buffers).
 int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C,
-         float scale, float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, float* logits, void* dz,
-         int64_t ldv, int64_t Nc, int dtype, float* ws) {
-  for (int64_t c0 = 0; c0 < N; c0 += Nc) {
+         float scale, float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, void* logits,
+         void* const dzb[2], int64_t ldv, int64_t Nc, int dtype, float* ws) {
+  const bool side = x->side != nullptr;
+  int ci = 0;
+  for (int64_t c0 = 0; c0 < N; c0 += Nc, ++ci) {
+    const int b = ci & 1;
+    void* dz = dzb[b];
     const int64_t rows = std::min(Nc, N - c0);
     const void* Fc = (const char*)Fin + c0 * C * (dtype == GPT_BF16 ? 2 : 4);
-    gk::Gemm g = mk(x, 0, 0, gk::EPI_F32, Fc, C, W, C, rows, V, C, logits, ldv);
+    gk::Gemm g = mk(x, 0, 0, gk::EPI_STORE, Fc, C, W, C, rows, V, C, logits, ldv);  // T logits, no bias
     g.dtype = dtype;
     if (run_gemm(x, "head_logits", g)) return GPT_EHIP;
+    if (side && x->dz_busy[b]) {  // an earlier chunk's dW still reads this dz buffer
+      HIPCHK(hipStreamWaitEvent(x->stream, x->head_done[b], 0));
+      x->dz_busy[b] = false;
+    }
     {
-      ProfScope ps(x, "head_ce", 0.0, (double)rows * V * (4 + (scale > 0 ? (dtype == GPT_BF16 ? 2 : 4) : 0)));
+      const int es = dtype == GPT_BF16 ? 2 : 4;
+      ProfScope ps(x, "head_ce", 0.0, (double)rows * V * (es + (scale > 0 ? es : 0)));
       HIPCHK(gk::ce_rows(dtype, logits, ldv, (int)V, y + c0, (int)rows, scale, tok_loss + c0, tok_lse + c0,
                          scale > 0 ? dz : nullptr, x->stream));
     }
     if (scale > 0) {
+      // dW (on the side stream when there is one) and dF both read only dz
+      // and operands of the forward, so they run side by side: dF's split-K
+      // product has few output tiles and leaves most of the chip to dW.
+      bool dw_here = false;
+      gk::Gemm w;
+      if (dW) {
+        w = mk(x, 1, 1, gk::EPI_F32, dz, ldv, Fc, C, V, C, rows, dW, C);
+        w.dtype = dtype;
+        w.accumulate = (c0 > 0) || dW_acc;
+        if (side) {
+          HIPCHK(hipEventRecord(x->head_ready[b], x->stream));
+          HIPCHK(hipStreamWaitEvent(x->side, x->head_ready[b], 0));
+          if (run_gemm(x, "head_dw", w, x->side)) return GPT_EHIP;
+          HIPCHK(hipEventRecord(x->head_done[b], x->side));
+          x->dz_busy[b] = true;
+        } else {
+          dw_here = true;
+        }
+      }
       if (dF) {
         gk::Gemm d = mk(x, 0, 1, gk::EPI_F32, dz, ldv, W, C, rows, C, V, dF + c0 * C, C);
         d.dtype = dtype;
@@ -435,12 +478,7 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
         d.ws = ws;
         if (run_gemm(x, "head_dx", d)) return GPT_EHIP;
       }
-      if (dW) {
-        gk::Gemm w = mk(x, 1, 1, gk::EPI_F32, dz, ldv, Fc, C, V, C, rows, dW, C);
-        w.dtype = dtype;
-        w.accumulate = (c0 > 0) || dW_acc;
-        if (run_gemm(x, "head_dw", w)) return GPT_EHIP;
-      }
+      if (dw_here && run_gemm(x, "head_dw", w)) return GPT_EHIP;
     }
   }
   return 0;
@@ -498,6 +536,11 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
   chk(hipStreamCreateWithFlags(&x->side, hipStreamNonBlocking));
   x->sev.assign((size_t)x->L * 8, nullptr);
   for (auto& e : x->sev) chk(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  for (int b = 0; b < 2; ++b) {
+    chk(hipEventCreateWithFlags(&x->head_ready[b], hipEventDisableTiming));
+    chk(hipEventCreateWithFlags(&x->head_done[b], hipEventDisableTiming));
+  }
+  chk(hipEventCreateWithFlags(&x->side_tail, hipEventDisableTiming));
   if (rc) {
     gpt_destroy(x);
     return rc;
@@ -509,7 +552,10 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
 int gpt_destroy(gpt_ctx* x) {
   if (!x) return 0;
   for (auto e : x->prof.ev) (void)hipEventDestroy(e);
+  if (x->side) (void)hipStreamSynchronize(x->side);
   for (auto e : x->sev)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : {x->head_ready[0], x->head_ready[1], x->head_done[0], x->head_done[1], x->side_tail})
     if (e) (void)hipEventDestroy(e);
   if (x->side) (void)hipStreamDestroy(x->side);
   delete x;
@@ -546,6 +592,8 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
   const int64_t N = x->N, C = x->C;
   const int32_t* xt = x->win;
   const int32_t* yt = x->win + 1;
+  // a previous call's head dW may still read lnf / dz and write G(wte)
+  if (int e = join_side(x)) return e;
   {
     ProfScope ps(x, "layernorm_fwd", 0.0, (double)N * C * (4 + 4 + 4 + x->es) + 8.0 * N);
     HIPCHK(gk::embed_ln_fwd(x->dt, xt, x->P_(T_WTE), x->P_(T_WPE), (int)x->T, x->res[0], x->P_(tid(0, K_LN1G)),
@@ -585,7 +633,7 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
   const float scale = loss_scale / (float)N;
   const bool grad = loss_scale > 0.f;
   if (int e = head(x, x->lnf, x->W_(T_WTE), x->Vp, yt, N, C, grad ? scale : 0.f, x->tok_loss, x->tok_lse,
-                   grad ? x->dF : nullptr, grad ? x->G_(T_WTE) : nullptr, x->wte_fresh ? 0 : 1, x->logits, x->dz,
+                   grad ? x->dF : nullptr, grad ? x->G_(T_WTE) : nullptr, x->wte_fresh ? 0 : 1, x->logits, x->dz2,
                    x->ldv, x->Nc, x->dt, x->splitk_ws))
     return e;
   if (grad) x->wte_fresh = false;
@@ -681,9 +729,9 @@ int gpt_backward(gpt_ctx* x) {
     if (int e = ln_bwd(x, x->dlnT, true, x->res[l], ly.mu1, ly.rs1, tid(l, K_LN1G), x->dres, ly.ln1_part, T0))
       return e;
   }
-  // join: every side product is done before the parameter reduction and AdamW
-  for (int k = 0; k < 4; ++k)
-    if (int e = wait_side(0, k)) return e;
+  // join: every side product (the head's dW among them) is done before the
+  // embedding backward adds into G(wte), the parameter reduction and AdamW
+  if (int e = join_side(x)) return e;
   // embeddings: token rows (deterministic segmented sum) and positions
   {
     ProfScope ps(x, "embed_bwd", 0.0, (double)N * C * 12);
@@ -706,6 +754,7 @@ int gpt_adamw_step(gpt_ctx* x, float lr, float beta1, float beta2, float eps, fl
   if (!(lr >= 0.f) || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(eps >= 0.f) ||
       !(weight_decay >= 0.f))
     return fail(GPT_EINVAL, "bad AdamW hyper-parameters");
+  if (int e = join_side(x)) return e;  // gradients still being written on the side stream
   if (x->wte_fresh || x->others_fresh) {
     // some gradients were never written since the last update: they are zero
     if (x->wte_fresh) HIPCHK(gk::fill_f32(x->G_(T_WTE), x->tensors[T_WTE].numel(), 0.f, x->stream));
@@ -743,7 +792,7 @@ size_t gpt_lmhead_ce_ws_bytes(int64_t N, int64_t V, int64_t C, int32_t dtype) {
   if (N < 1 || V < 1 || C < 64 || C % 64 || (dtype != GPT_F32 && dtype != GPT_BF16)) return 0;
   const int64_t es = dtype == GPT_BF16 ? 2 : 4;
   const int64_t ldv = align_up(V, 64), Nc = std::min<int64_t>(N, 4096);
-  return (size_t)(align_up(Nc * ldv * 4, ALIGN) + align_up(Nc * ldv * es, ALIGN) + 2 * align_up(N * 4, ALIGN) +
+  return (size_t)(2 * align_up(Nc * ldv * es, ALIGN) + 2 * align_up(N * 4, ALIGN) +
                   align_up(std::max<int64_t>(1, head_splitk_floats(Nc, C, V)) * 4, ALIGN));
 }
 
@@ -759,13 +808,14 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
   tmp.es = dtype == GPT_BF16 ? 2 : 4;
   const int64_t ldv = align_up(V, 64), Nc = std::min<int64_t>(N, 4096);
   Carver cv(ws);
-  float* logits = cv.take<float>(Nc * ldv * 4);
+  void* logits = cv.take<void>(Nc * ldv * tmp.es);
   void* dz = cv.take<void>(Nc * ldv * tmp.es);
   float* tl = cv.take<float>(N * 4);
   float* tlse = cv.take<float>(N * 4);
   float* hws = cv.take<float>(std::max<int64_t>(1, head_splitk_floats(Nc, C, V)) * 4);
   const bool grad = dX || dW;
-  if (int e = head(&tmp, X, W, V, y, N, C, grad ? 1.0f / (float)N : 0.f, tl, tlse, dX, dW, 0, logits, dz, ldv, Nc,
+  void* const dzb[2] = {dz, dz};  // no side stream here: chunks run in order on one buffer
+  if (int e = head(&tmp, X, W, V, y, N, C, grad ? 1.0f / (float)N : 0.f, tl, tlse, dX, dW, 0, logits, dzb, ldv, Nc,
                    dtype, hws))
     return e;
   HIPCHK(gk::mean_f32(tl, (int)N, loss_dev, nullptr, 0, tmp.stream));
@@ -802,6 +852,7 @@ int gpt_get_tensor(gpt_ctx* x, int kind, int id, float* host, int64_t n) {
   if (!base) return fail(GPT_EINVAL, "bad tensor kind");
   const TensorDesc& d = x->tensors[id];
   if (n != d.numel()) return fail(GPT_EINVAL, "element count mismatch for " + d.name);
+  if (int e = join_side(x)) return e;  // gradients may still be written on the side stream
   if (kind == GPT_GRAD && (id == T_WTE ? x->wte_fresh : x->others_fresh)) {
     std::memset(host, 0, n * 4);  // cleared since the last update
     return 0;
@@ -817,6 +868,7 @@ int gpt_set_tensor(gpt_ctx* x, int kind, int id, const float* host, int64_t n) {
   if (!base) return fail(GPT_EINVAL, "bad tensor kind");
   const TensorDesc& d = x->tensors[id];
   if (n != d.numel()) return fail(GPT_EINVAL, "element count mismatch for " + d.name);
+  if (int e = join_side(x)) return e;  // side-stream products read activations and write gradients
   if (kind == GPT_GRAD) {
     // materialise the cleared state before writing part of it
     if (id == T_WTE && x->wte_fresh) {

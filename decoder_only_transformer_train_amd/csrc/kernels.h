@@ -85,9 +85,9 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, c
                     float* Dv, void* dqkv, int B, int T, int H, int D, hipStream_t s);
 
 // ---- cross-entropy rows over a chunk of logits ----
-// z f32 [rows][ldz] (first V columns valid) -> loss[r] = lse - z[y]; lse_out[r];
+// z T [rows][ldz] (first V columns valid) -> loss[r] = lse - z[y]; lse_out[r];
 // if dz != null: dz T [rows][ldz] = (softmax - onehot) * scale, zero in [V, ldz)
-hipError_t ce_rows(int dtype, const float* z, int64_t ldz, int V, const int32_t* y, int rows,
+hipError_t ce_rows(int dtype, const void* z, int64_t ldz, int V, const int32_t* y, int rows,
                    float scale, float* loss, float* lse_out, void* dz, hipStream_t s);
 // mean of n floats in fixed order -> out[0] (and ring[slot] if ring != null)
 hipError_t mean_f32(const float* x, int n, float* out, float* ring, int slot, hipStream_t s);

@@ -227,16 +227,18 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict
 
 // Cross-entropy over one row of logits (CS336 page, section 1: subtract the
 // row maximum, log-sum-exp, minus the target logit).  One workgroup per row.
+// Logits z and dz are both T (bf16 logits are widened to fp32, as the page's
+// loss does, before any arithmetic).
 // With dz: dz = (softmax - onehot(y)) * scale, zero in the padding [V, ldz).
 template <typename T>
-__global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ z, int64_t ldz, int V,
+__global__ __launch_bounds__(256) void ce_rows_kernel(const T* __restrict__ z, int64_t ldz, int V,
                                                       const int32_t* __restrict__ y, float scale,
                                                       float* __restrict__ loss, float* __restrict__ lse_out,
                                                       T* __restrict__ dz) {
   __shared__ float sm[4], ss[4];
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const float* zr = z + (int64_t)row * ldz;
+  const T* zr = z + (int64_t)row * ldz;
   // running max and sum of 2^((z - max) log2 e), rescaled when the max grows
   float m = -__builtin_huge_valf(), s = 0.f;
   const int V4 = V >> 2;
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
          hw_exp2((v.w - m) * LOG2E);
   }
   for (int j = 4 * V4 + t; j < V; j += 256) {
-    const float v = zr[j];
+    const float v = to_f(zr[j]);
     if (v > m) {
       s *= hw_exp2((m - v) * LOG2E);
       m = v;
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
   const float lse = M + hw_log2(S) * LN2;
   const int yy = y[row];
   if (t == 0) {
-    loss[row] = lse - zr[yy];
+    loss[row] = lse - to_f(zr[yy]);
     if (lse_out) lse_out[row] = lse;
   }
   if (dz != nullptr) {
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
       } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (c + k < V) d[k] = hw_exp2((zr[c + k] - lse) * LOG2E);
+          if (c + k < V) d[k] = hw_exp2((to_f(zr[c + k]) - lse) * LOG2E);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k)
@@ -307,18 +309,18 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
 }
 
 // The same cross-entropy row with the row held in registers: 1024 threads
-// load the row once (NV float4 each), reduce the maximum, then the sum of
+// load the row once (NV groups of 4 each), reduce the maximum, then the sum of
 // exp(z - max), and write dz from the same registers - one read of the logits
 // instead of two.  Columns in [V, ldz) are padding: excluded, dz = 0 there.
 template <typename T, int NV>
-__global__ __launch_bounds__(1024) void ce_reg_kernel(const float* __restrict__ z, int64_t ldz, int V,
+__global__ __launch_bounds__(1024) void ce_reg_kernel(const T* __restrict__ z, int64_t ldz, int V,
                                                       const int32_t* __restrict__ y, float scale,
                                                       float* __restrict__ loss, float* __restrict__ lse_out,
                                                       T* __restrict__ dz) {
   __shared__ float red[2][16];
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const float* zr = z + (int64_t)row * ldz;
+  const T* zr = z + (int64_t)row * ldz;
   const int L4 = (int)(ldz >> 2);
   constexpr float NINF = -__builtin_huge_valf();
   float4 v[NV];
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(1024) void ce_reg_kernel(const float* __restrict__ 
   const float lse = M + hw_log2(S) * LN2;
   const int yy = y[row];
   if (t == 0) {
-    loss[row] = lse - zr[yy];
+    loss[row] = lse - to_f(zr[yy]);
     if (lse_out) lse_out[row] = lse;
   }
   if (dz != nullptr) {
@@ -459,18 +461,18 @@ hipError_t colsum_partial(int dtype, const void* x, int rows, int cols, float* p
 }
 
 template <int NV>
-hipError_t ce_reg(int dtype, const float* z, int64_t ldz, int V, const int32_t* y, int rows, float scale, float* loss,
+hipError_t ce_reg(int dtype, const void* z, int64_t ldz, int V, const int32_t* y, int rows, float scale, float* loss,
                   float* lse_out, void* dz, hipStream_t s) {
   if (dtype == BF16)
-    hipLaunchKernelGGL((ce_reg_kernel<bf16, NV>), dim3(rows), dim3(1024), 0, s, z, ldz, V, y, scale, loss, lse_out,
-                       (bf16*)dz);
+    hipLaunchKernelGGL((ce_reg_kernel<bf16, NV>), dim3(rows), dim3(1024), 0, s, (const bf16*)z, ldz, V, y, scale,
+                       loss, lse_out, (bf16*)dz);
   else
-    hipLaunchKernelGGL((ce_reg_kernel<float, NV>), dim3(rows), dim3(1024), 0, s, z, ldz, V, y, scale, loss, lse_out,
-                       (float*)dz);
+    hipLaunchKernelGGL((ce_reg_kernel<float, NV>), dim3(rows), dim3(1024), 0, s, (const float*)z, ldz, V, y, scale,
+                       loss, lse_out, (float*)dz);
   return hipGetLastError();
 }
 
-hipError_t ce_rows(int dtype, const float* z, int64_t ldz, int V, const int32_t* y, int rows, float scale,
+hipError_t ce_rows(int dtype, const void* z, int64_t ldz, int V, const int32_t* y, int rows, float scale,
                    float* loss, float* lse_out, void* dz, hipStream_t s) {
   // rows of up to 64K columns are held in registers (one read of the logits)
   if (ldz % 4 == 0) {
@@ -482,11 +484,11 @@ hipError_t ce_rows(int dtype, const float* z, int64_t ldz, int V, const int32_t*
     if (nv <= 16) return ce_reg<16>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, s);
   }
   if (dtype == BF16)
-    hipLaunchKernelGGL(ce_rows_kernel<bf16>, dim3(rows), dim3(256), 0, s, z, ldz, V, y, scale, loss, lse_out,
-                       (bf16*)dz);
+    hipLaunchKernelGGL(ce_rows_kernel<bf16>, dim3(rows), dim3(256), 0, s, (const bf16*)z, ldz, V, y, scale, loss,
+                       lse_out, (bf16*)dz);
   else
-    hipLaunchKernelGGL(ce_rows_kernel<float>, dim3(rows), dim3(256), 0, s, z, ldz, V, y, scale, loss, lse_out,
-                       (float*)dz);
+    hipLaunchKernelGGL(ce_rows_kernel<float>, dim3(rows), dim3(256), 0, s, (const float*)z, ldz, V, y, scale, loss,
+                       lse_out, (float*)dz);
   return hipGetLastError();
 }
 
