@@ -78,32 +78,54 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 // bias gradient of the linear layer that feeds this residual stream).
 constexpr int LNB_ROWS = 32;
 
-template <typename TY, typename T>
+template <typename TY, typename T, int NV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const TY* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ mu, const float* __restrict__ rs,
                                                      const float* __restrict__ g, const float* dres_in,
                                                      float* dres_out, T* __restrict__ dres_T,
                                                      float* __restrict__ part, int rows, int C) {
-  __shared__ float red[4][2048];
+  __shared__ float red[4][NV * 256];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nc = C >> 2;
-  float4 pg[MAXV], pb[MAXV], pc[MAXV];
+  float4 pg[NV], pb[NV], pc[NV], gv[NV];
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) pg[i] = pb[i] = pc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < NV; ++i) {
+    pg[i] = pb[i] = pc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int j = lane + 64 * i;
+    gv[i] = j < nc ? load4(g + 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const int r0 = blockIdx.x * LNB_ROWS;
-  for (int rr = w; rr < LNB_ROWS; rr += 4) {
-    const int row = r0 + rr;
-    if (row >= rows) break;
-    const float m = mu[row], r = rs[row];
-    float4 xh[MAXV], dxh[MAXV];
-    float s1 = 0.f, s2 = 0.f;
+  // a wave's rows are r0 + w, r0 + w + 4, ...: the next row's x, dy and
+  // incoming residual gradient are loaded before this row's reductions
+  float4 xa[NV], da[NV], qa[NV];
+  auto load_row = [&](int row, float4 (&xv)[NV], float4 (&dv)[NV], float4 (&qv)[NV]) {
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int j = lane + 64 * i;
       if (j < nc) {
-        const float4 xv = load4(x + (int64_t)row * C + 4 * j);
-        const float4 d = load4(dy + (int64_t)row * C + 4 * j);
-        const float4 gg = load4(g + 4 * j);
+        const int64_t o = (int64_t)row * C + 4 * j;
+        xv[i] = load4(x + o);
+        dv[i] = load4(dy + o);
+        qv[i] = dres_in ? load4(dres_in + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  if (r0 + w < rows) load_row(r0 + w, xa, da, qa);
+#pragma unroll
+  for (int k = 0; k < LNB_ROWS / 4; ++k) {
+    const int row = r0 + w + 4 * k;
+    if (row >= rows) break;
+    float4 xb[NV], db[NV], qb[NV];
+    const bool more = k + 1 < LNB_ROWS / 4 && row + 4 < rows;
+    if (more) load_row(row + 4, xb, db, qb);
+    const float m = mu[row], r = rs[row];
+    float4 xh[NV], dxh[NV];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = lane + 64 * i;
+      if (j < nc) {
+        const float4 xv = xa[i], d = da[i], gg = gv[i];
         xh[i] = make_float4((xv.x - m) * r, (xv.y - m) * r, (xv.z - m) * r, (xv.w - m) * r);
         dxh[i] = make_float4(d.x * gg.x, d.y * gg.y, d.z * gg.z, d.w * gg.w);
         s1 += dxh[i].x + dxh[i].y + dxh[i].z + dxh[i].w;
@@ -114,11 +136,11 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const TY* __restrict__ dy, 
     }
     const float m1 = wave_sum(s1) / C, m2 = wave_sum(s2) / C;
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int j = lane + 64 * i;
       if (j < nc) {
         const int64_t o = (int64_t)row * C + 4 * j;
-        const float4 prev = dres_in ? load4(dres_in + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 prev = qa[i];
         const float4 out = make_float4(prev.x + r * (dxh[i].x - m1 - xh[i].x * m2),
                                        prev.y + r * (dxh[i].y - m1 - xh[i].y * m2),
                                        prev.z + r * (dxh[i].z - m1 - xh[i].z * m2),
@@ -128,13 +150,21 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const TY* __restrict__ dy, 
         pc[i].x += out.x; pc[i].y += out.y; pc[i].z += out.z; pc[i].w += out.w;
       }
     }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        xa[i] = xb[i];
+        da[i] = db[i];
+        qa[i] = qb[i];
+      }
+    }
   }
   // the 4 waves' partials, added in wave order, one quantity at a time
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     if (k) __syncthreads();
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int j = lane + 64 * i;
       if (j < nc) *reinterpret_cast<float4*>(&red[w][4 * j]) = k == 0 ? pg[i] : (k == 1 ? pb[i] : pc[i]);
     }
@@ -312,29 +342,54 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const T* __restrict__ z, i
 // load the row once (NV groups of 4 each), reduce the maximum, then the sum of
 // exp(z - max), and write dz from the same registers - one read of the logits
 // instead of two.  Columns in [V, ldz) are padding: excluded, dz = 0 there.
+// the row's values as loaded (bf16 stays packed: half the registers, so two
+// rows' workgroups fit on a CU and one's loads overlap the other's reductions)
+template <typename T> struct CeRow;
+template <> struct CeRow<float> {
+  typedef float4 raw;
+  static __device__ __forceinline__ raw ld(const float* p) { return load4(p); }
+  static __device__ __forceinline__ float4 f(const raw& r) { return r; }
+};
+template <> struct CeRow<bf16> {
+  typedef bf16x4 raw;
+  static __device__ __forceinline__ raw ld(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+  static __device__ __forceinline__ float4 f(const raw& r) {
+    return make_float4((float)r[0], (float)r[1], (float)r[2], (float)r[3]);
+  }
+};
+
+// (bf16: at most 64 registers, eight waves per SIMD = two rows per CU)
 template <typename T, int NV>
-__global__ __launch_bounds__(1024) void ce_reg_kernel(const T* __restrict__ z, int64_t ldz, int V,
-                                                      const int32_t* __restrict__ y, float scale,
-                                                      float* __restrict__ loss, float* __restrict__ lse_out,
-                                                      T* __restrict__ dz) {
+__global__ __launch_bounds__(1024, sizeof(T) == 2 ? 8 : 4) void ce_reg_kernel(const T* __restrict__ z, int64_t ldz, int V,
+                                                         const int32_t* __restrict__ y, float scale,
+                                                         float* __restrict__ loss, float* __restrict__ lse_out,
+                                                         T* __restrict__ dz) {
+  using R = CeRow<T>;
   __shared__ float red[2][16];
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const T* zr = z + (int64_t)row * ldz;
   const int L4 = (int)(ldz >> 2);
   constexpr float NINF = -__builtin_huge_valf();
-  float4 v[NV];
-  float mx = NINF;
+  typename R::raw v[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int j = t + 1024 * i, c = 4 * j;
-    v[i] = make_float4(NINF, NINF, NINF, NINF);
-    if (j < L4) {
-      const float4 a = load4(zr + c);
-      v[i] = make_float4(c < V ? a.x : NINF, c + 1 < V ? a.y : NINF, c + 2 < V ? a.z : NINF, c + 3 < V ? a.w : NINF);
-      mx = fmaxf(mx, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w)));
-    }
+    const int j = t + 1024 * i;
+    if (j < L4) v[i] = R::ld(zr + 4 * j);
   }
+  // columns in [V, ldz) are padding: excluded from the statistics, dz = 0 there
+  auto val = [&](int i) {
+    const int c = 4 * (t + 1024 * i);
+    const float4 a = R::f(v[i]);
+    return make_float4(c < V ? a.x : NINF, c + 1 < V ? a.y : NINF, c + 2 < V ? a.z : NINF, c + 3 < V ? a.w : NINF);
+  };
+  float mx = NINF;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (t + 1024 * i < L4) {
+      const float4 a = val(i);
+      mx = fmaxf(mx, fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)));
+    }
   mx = wave_max(mx);
   if (lane == 0) red[0][w] = mx;
   __syncthreads();
@@ -344,8 +399,11 @@ __global__ __launch_bounds__(1024) void ce_reg_kernel(const T* __restrict__ z, i
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
-    sum += hw_exp2((v[i].x - M) * LOG2E) + hw_exp2((v[i].y - M) * LOG2E) + hw_exp2((v[i].z - M) * LOG2E) +
-           hw_exp2((v[i].w - M) * LOG2E);
+    if (t + 1024 * i < L4) {
+      const float4 a = val(i);
+      sum += hw_exp2((a.x - M) * LOG2E) + hw_exp2((a.y - M) * LOG2E) + hw_exp2((a.z - M) * LOG2E) +
+             hw_exp2((a.w - M) * LOG2E);
+    }
   sum = wave_sum(sum);
   if (lane == 0) red[1][w] = sum;
   __syncthreads();
@@ -364,8 +422,9 @@ __global__ __launch_bounds__(1024) void ce_reg_kernel(const T* __restrict__ z, i
     for (int i = 0; i < NV; ++i) {
       const int j = t + 1024 * i, c = 4 * j;
       if (j >= L4) break;
-      float d[4] = {hw_exp2((v[i].x - lse) * LOG2E), hw_exp2((v[i].y - lse) * LOG2E),
-                    hw_exp2((v[i].z - lse) * LOG2E), hw_exp2((v[i].w - lse) * LOG2E)};
+      const float4 a = val(i);
+      float d[4] = {hw_exp2((a.x - lse) * LOG2E), hw_exp2((a.y - lse) * LOG2E), hw_exp2((a.z - lse) * LOG2E),
+                    hw_exp2((a.w - lse) * LOG2E)};
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (c + k == yy) d[k] -= 1.f;
@@ -420,21 +479,37 @@ hipError_t embed_ln_fwd(int dtype, const int32_t* tok, const float* wte, const f
 
 int layernorm_bwd_blocks(int rows) { return cdiv(rows, LNB_ROWS); }
 
+template <int NV>
+hipError_t ln_bwd_nv(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu, const float* rstd,
+                     const float* g, const float* dres_in, float* dres_out, void* dres_T, float* part, int rows,
+                     int C, int nblk, hipStream_t s) {
+  if (dtype == BF16 && dy_is_t)
+    hipLaunchKernelGGL((ln_bwd_kernel<bf16, bf16, NV>), dim3(nblk), dim3(256), 0, s, (const bf16*)dy, x, mu, rstd,
+                       g, dres_in, dres_out, (bf16*)dres_T, part, rows, C);
+  else if (dtype == BF16)
+    hipLaunchKernelGGL((ln_bwd_kernel<float, bf16, NV>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu,
+                       rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, C);
+  else
+    hipLaunchKernelGGL((ln_bwd_kernel<float, float, NV>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu,
+                       rstd, g, dres_in, dres_out, (float*)dres_T, part, rows, C);
+  return hipGetLastError();
+}
+
 hipError_t layernorm_bwd(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu,
                          const float* rstd, const float* g, const float* dres_in, float* dres_out, void* dres_T,
                          float* part, int rows, int C, int* nblk_out, hipStream_t s) {
   const int nblk = layernorm_bwd_blocks(rows);
   if (nblk_out) *nblk_out = nblk;
-  if (dtype == BF16 && dy_is_t)
-    hipLaunchKernelGGL((ln_bwd_kernel<bf16, bf16>), dim3(nblk), dim3(256), 0, s, (const bf16*)dy, x, mu, rstd, g,
-                       dres_in, dres_out, (bf16*)dres_T, part, rows, C);
-  else if (dtype == BF16)
-    hipLaunchKernelGGL((ln_bwd_kernel<float, bf16>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu, rstd, g,
-                       dres_in, dres_out, (bf16*)dres_T, part, rows, C);
-  else
-    hipLaunchKernelGGL((ln_bwd_kernel<float, float>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu, rstd,
-                       g, dres_in, dres_out, (float*)dres_T, part, rows, C);
-  return hipGetLastError();
+  if (C % 4 || C > 4 * 64 * MAXV) return hipErrorInvalidValue;
+  switch ((C / 4 + 63) / 64) {  // float4 slices per lane
+    case 1: return ln_bwd_nv<1>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
+    case 2: return ln_bwd_nv<2>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
+    case 3: return ln_bwd_nv<3>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
+    case 4: return ln_bwd_nv<4>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
+    case 5:
+    case 6: return ln_bwd_nv<6>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
+    default: return ln_bwd_nv<8>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
+  }
 }
 
 hipError_t reduce_jobs(const RedJob* jobs, int njobs, int nblocks, int accumulate, hipStream_t s) {

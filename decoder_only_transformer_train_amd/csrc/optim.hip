@@ -61,6 +61,20 @@ __global__ void adamw_prep_kernel(float* scal, int* step_dev, float lr, float b1
   scal[3] = (float)((double)lr * sqrt(c2) / c1);
 }
 
+// Streaming loads and stores (non-temporal: p, g, m, v are touched once per
+// step) of two float4 groups per thread, whose eight loads are issued before
+// any arithmetic; one thread per pair of groups, no grid-stride loop.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_stream(const float* p, int64_t i) {
+  const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p) + i);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(float* p, int64_t i, float4 a) {
+  const f32x4v v = {a.x, a.y, a.z, a.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4v*>(p) + i);
+}
+constexpr int ADAMW_U = 2;  // float4 groups per thread
+
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     bf16* __restrict__ shadow, int64_t n4, int64_t n4_decay,
@@ -69,14 +83,25 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const
   if (scal[2] == 0.f) return;  // non-finite gradient norm: no update
   const float cs = scal[1], a = scal[3];
   const float dec = 1.f - lr * wd;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
-    const float4 p4 = reinterpret_cast<const float4*>(p)[i];
-    const float4 g4 = reinterpret_cast<const float4*>(g)[i];
-    const float4 m4 = reinterpret_cast<const float4*>(m)[i];
-    const float4 v4 = reinterpret_cast<const float4*>(v)[i];
+  const int64_t i0 = (int64_t)blockIdx.x * 256 * ADAMW_U + threadIdx.x;
+  float4 p4[ADAMW_U], g4[ADAMW_U], m4[ADAMW_U], v4[ADAMW_U];
+#pragma unroll
+  for (int u = 0; u < ADAMW_U; ++u) {
+    const int64_t i = i0 + u * 256;
+    if (i < n4) {
+      p4[u] = ld_stream(p, i);
+      g4[u] = ld_stream(g, i);
+      m4[u] = ld_stream(m, i);
+      v4[u] = ld_stream(v, i);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < ADAMW_U; ++u) {
+    const int64_t i = i0 + u * 256;
+    if (i >= n4) continue;
     const float d = (i < n4_decay) ? dec : 1.f;
-    float pa[4] = {p4.x, p4.y, p4.z, p4.w}, ga[4] = {g4.x, g4.y, g4.z, g4.w};
-    float ma[4] = {m4.x, m4.y, m4.z, m4.w}, va[4] = {v4.x, v4.y, v4.z, v4.w};
+    float pa[4] = {p4[u].x, p4[u].y, p4[u].z, p4[u].w}, ga[4] = {g4[u].x, g4[u].y, g4[u].z, g4[u].w};
+    float ma[4] = {m4[u].x, m4[u].y, m4[u].z, m4[u].w}, va[4] = {v4[u].x, v4[u].y, v4[u].z, v4[u].w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float gk_ = ga[k] * cs;
@@ -85,9 +110,9 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const
       pa[k] = pa[k] * d - a * ma[k] / (sqrtf(va[k]) + eps);
     }
     const float4 pp = make_float4(pa[0], pa[1], pa[2], pa[3]);
-    reinterpret_cast<float4*>(p)[i] = pp;
-    reinterpret_cast<float4*>(m)[i] = make_float4(ma[0], ma[1], ma[2], ma[3]);
-    reinterpret_cast<float4*>(v)[i] = make_float4(va[0], va[1], va[2], va[3]);
+    st_stream(p, i, pp);
+    st_stream(m, i, make_float4(ma[0], ma[1], ma[2], ma[3]));
+    st_stream(v, i, make_float4(va[0], va[1], va[2], va[3]));
     if (shadow) store4(shadow + 4 * i, pp);
   }
 }
@@ -229,8 +254,10 @@ hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow, int
                  float* scal, float lr, float b1, float b2, float eps, float wd, int* step_dev, hipStream_t s) {
   hipLaunchKernelGGL(adamw_prep_kernel, dim3(1), dim3(1), 0, s, scal, step_dev, lr, b1, b2);
   const int64_t n4 = n / 4;
-  const int blocks = (int)std::min<int64_t>(cdiv(n4, 256), 256 * 16);
-  hipLaunchKernelGGL(adamw_kernel, dim3(blocks), dim3(256), 0, s, p, g, m, v, (bf16*)shadow, n4, n_decay / 4,
+  const int64_t blocks = cdiv(n4, 256 * ADAMW_U);
+  if (blocks == 0) return hipGetLastError();
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, g, m, v, (bf16*)shadow, n4, n_decay / 4,
                      scal, lr, b1, b2, eps, wd);
   return hipGetLastError();
 }
