@@ -111,8 +111,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true")
-    # the largest kernel that runs alone (backward weight gradients share the GPU with the data-gradient chain)
-    ap.add_argument("--roofline-kernel", default="head_logits", choices=PROFILE_CLASSES)
+    # the largest kernel class that runs alone: the backward's two streams and the head's dW share the GPU
+    ap.add_argument("--roofline-kernel", default="gemm_fc_fwd", choices=PROFILE_CLASSES)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="after the timed steps, copy this many bytes device-to-device once")
     args = ap.parse_args()
@@ -148,12 +148,20 @@ def main():
 
     breakdown = None
     if args.breakdown:
-        breakdown = {}
+        # per kernel class: time per step and the class's algorithmic rate against its peak
+        # (classes on the backward's second stream share the GPU with the first stream)
+        breakdown, rates = {}, {}
         for cls in PROFILE_CLASSES:
             g.profile_begin(cls)
             step(0)
             r = g.profile_end()
             breakdown[cls] = round(r["ms"], 3)
+            if r["ms"] > 0 and r["flops"] > 0:
+                a = r["flops"] / (r["ms"] / 1e3)
+                rates[cls] = {"TFLOP/s": round(a / 1e12, 1), "frac": round(a / PEAK_BF16, 3)}
+            elif r["ms"] > 0 and r["bytes"] > 0:
+                a = r["bytes"] / (r["ms"] / 1e3)
+                rates[cls] = {"GB/s": round(a / 1e9, 1), "frac": round(a / PEAK_HBM, 3)}
         g.read_losses()
 
     torch.cuda.synchronize()
@@ -204,6 +212,7 @@ def main():
     }
     if breakdown is not None:
         out["breakdown_ms"] = breakdown
+        out["breakdown_rate"] = rates
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)

@@ -169,10 +169,19 @@ struct Loader {
   }
 };
 
-__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
-  const int nwg = gridDim.x;
-  int id = blockIdx.x;
-  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+// Work item of this workgroup: output tile (tm, tn) and k-split kz.  The
+// hardware places workgroup i on XCD i % 8; each XCD is given a contiguous
+// range of the (split-major, then grouped-tile) work list, so the workgroups
+// sharing an XCD's L2 share k-slabs of the operands (a split-K product reads
+// each split's slabs once per XCD instead of once per tile column) and, within
+// a split, form GROUP_M-row blocks of tiles.
+__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn, int& kz) {
+  const int total = gridDim.x, lin = blockIdx.x;
+  const int x = lin & 7, base = total >> 3, rem = total & 7;
+  const int w = x * base + min(x, rem) + (lin >> 3);  // XCD x holds base + (x < rem) work items
+  const int tiles = p.tiles_m * p.tiles_n;
+  kz = w / tiles;
+  const int id = w - kz * tiles;
   const int per_group = GROUP_M * p.tiles_n;
   const int group = id / per_group;
   const int first_m = group * GROUP_M;
@@ -193,7 +202,7 @@ __device__ __forceinline__ void epi_group_inline(const Params& p, int m, int n, 
   float v[4] = {a.x, a.y, a.z, a.w};
   const bool full = n + 3 < p.N;
   if constexpr (SPLIT) {
-    float* o = p.ws + ((int64_t)blockIdx.z * p.M + m) * p.N + n;
+    float* o = p.ws + (int64_t)m * p.N + n;  // ws: this split's slice
     if (full && (p.N & 3) == 0) {
       *reinterpret_cast<float4*>(o) = a;
     } else {
@@ -275,7 +284,7 @@ template <typename T, int EPI, int SPLIT>
 __device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 a, bool full, float4 in, float4 b4) {
   float v[4] = {a.x, a.y, a.z, a.w};
   if constexpr (SPLIT) {
-    float* o = p.ws + ((int64_t)blockIdx.z * p.M + m) * p.N + n;
+    float* o = p.ws + (int64_t)m * p.N + n;  // ws: this split's slice
     if (full && (p.N & 3) == 0) {
       *reinterpret_cast<float4*>(o) = a;
     } else {
@@ -403,10 +412,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(Params p) {
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
-  int tm, tn;
-  tile_coords(p, tm, tn);
+  int tm, tn, kz;
+  tile_coords(p, tm, tn, kz);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int kb0 = blockIdx.z * p.k_per_split;
+  const int kb0 = kz * p.k_per_split;
+  Params pe = p;  // the epilogue's view: a split writes its own slice of the workspace
+  if (SPLIT) pe.ws = p.ws + (int64_t)kz * p.M * p.N;
   const int kend = min(p.K, kb0 + p.k_per_split);
   constexpr int BK = TKB / sizeof(T);
   const int nk = (kend - kb0 + BK - 1) / BK;
@@ -469,7 +480,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(Params p) {
 
   // epilogue through LDS (the main loop's stages are free now)
   static_assert(2 * STAGE >= (BM <= 128 ? BM : 128) * (BN + 4) * 4, "LDS too small for the epilogue");
-  epilogue_lds<T, EPI, SPLIT, BM, BN, (BM <= 128 ? BM : 128)>(p, acc, smem, m0, n0, wm, wn, lane, t);
+  epilogue_lds<T, EPI, SPLIT, BM, BN, (BM <= 128 ? BM : 128)>(pe, acc, smem, m0, n0, wm, wn, lane, t);
 }
 
 // 256x256 bf16 tile, 4 waves of 128x128, 32x32x16 MFMAs, explicitly interleaved:
@@ -638,10 +649,12 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_dl_kernel(Params p) {
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
-  int tm, tn;
-  tile_coords(p, tm, tn);
+  int tm, tn, kz;
+  tile_coords(p, tm, tn, kz);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int kb0 = blockIdx.z * p.k_per_split;
+  const int kb0 = kz * p.k_per_split;
+  Params pe = p;  // the epilogue's view: a split writes its own slice of the workspace
+  if (SPLIT) pe.ws = p.ws + (int64_t)kz * p.M * p.N;
   const int kend = min(p.K, kb0 + p.k_per_split);
   const int nk = (kend - kb0 + BK - 1) / BK;
   const rsrc_t ra = make_rsrc(p.A, (TA ? (int64_t)p.K : (int64_t)p.M) * p.lda * 2);
@@ -682,7 +695,7 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_dl_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) Mf<bf16>::mma(acc[i][j], fa[1][i], fb[1][j]);
   __syncthreads();
-  epilogue_lds<T, EPI, SPLIT, BM, BN, 128>(p, acc, smem, m0, n0, wm, wn, lane, t);
+  epilogue_lds<T, EPI, SPLIT, BM, BN, 128>(pe, acc, smem, m0, n0, wm, wn, lane, t);
 }
 
 }  // namespace dl
@@ -703,14 +716,14 @@ __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, i
 
 template <typename T, int TA, int TB, int EPI, int SPLIT, int BM, int BN>
 hipError_t launch(const Params& p, int splits, hipStream_t s) {
-  dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
+  dim3 grid(p.tiles_m * p.tiles_n * splits);
   hipLaunchKernelGGL((gemm_kernel<T, TA, TB, EPI, SPLIT, BM, BN>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <int TA, int TB, int EPI, int SPLIT, typename C>
 hipError_t launch_dl(const Params& p, int splits, hipStream_t s) {
-  dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
+  dim3 grid(p.tiles_m * p.tiles_n * splits);
   hipLaunchKernelGGL((gemm_dl_kernel<TA, TB, EPI, SPLIT, C>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
