@@ -177,9 +177,12 @@ struct Loader {
 // a split, form GROUP_M-row blocks of tiles.
 __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn, int& kz) {
   const int total = gridDim.x, lin = blockIdx.x;
-  const int x = lin & 7, base = total >> 3, rem = total & 7;
-  const int w = x * base + min(x, rem) + (lin >> 3);  // XCD x holds base + (x < rem) work items
   const int tiles = p.tiles_m * p.tiles_n;
+  const int x = lin & 7, base = total >> 3, rem = total & 7;
+  // XCD x holds base + (x < rem) work items.  A single-split grid whose tile
+  // count is not a multiple of 8 keeps the hardware order (measured: the LM
+  // head's 50304-row weight gradient fetched 28% more with the remap)
+  const int w = (total == tiles && rem) ? lin : x * base + min(x, rem) + (lin >> 3);
   kz = w / tiles;
   const int id = w - kz * tiles;
   const int per_group = GROUP_M * p.tiles_n;
