@@ -78,12 +78,18 @@ __device__ __forceinline__ float gelu_grad_f(float u) {
   float dt = GELU_K * (1.0f + 3.0f * GELU_A * u * u);
   return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * dt;
 }
-// both from one tanh: g = gelu(u), dg = gelu'(u)
+// both from one exponential: with x = K (u + A u^3), 0.5 (1 + tanh x) is the
+// logistic h = 1 / (1 + e^(-2x)), so g = u h and, since 1 - tanh^2 = 4 h (1 - h),
+// dg = h + u h (1 - h) 2 x'(u) = h (1 + u (1 - h) 2K (1 + 3 A u^2)).
+// e = inf (u very negative) gives h = 0, g = -0, dg = 0; e = 0 gives h = 1.
 __device__ __forceinline__ void gelu_both(float u, float& g, float& dg) {
-  const float t = tanh_exp(GELU_K * (u + GELU_A * u * u * u));
-  const float dt = GELU_K * (1.0f + 3.0f * GELU_A * u * u);
-  g = 0.5f * u * (1.0f + t);
-  dg = 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * dt;
+  constexpr float C1 = -2.0f * LOG2E * GELU_K, C2 = C1 * GELU_A;
+  const float u2 = u * u;
+  const float e = hw_exp2(u * __builtin_fmaf(C2, u2, C1));
+  const float h = __builtin_amdgcn_rcpf(1.0f + e);
+  g = u * h;
+  const float dx = __builtin_fmaf(6.0f * GELU_A * GELU_K, u2, 2.0f * GELU_K);
+  dg = __builtin_fmaf(h, u * (1.0f - h) * dx, h);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
