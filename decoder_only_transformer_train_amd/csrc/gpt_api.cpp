@@ -109,6 +109,7 @@ struct gpt_ctx {
   hipStream_t side = nullptr;
   std::vector<hipEvent_t> sev;
   hipEvent_t head_ready[2] = {nullptr, nullptr}, head_done[2] = {nullptr, nullptr}, side_tail = nullptr;
+  hipEvent_t fwd_start = nullptr;  // the forward's start, for side-stream work that needs only the batch
   bool dz_busy[2] = {false, false};
   float *Dv, *lnf_part, *splitk_ws;
   gk::RedJob* jobs_dev;
@@ -541,6 +542,7 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
     chk(hipEventCreateWithFlags(&x->head_done[b], hipEventDisableTiming));
   }
   chk(hipEventCreateWithFlags(&x->side_tail, hipEventDisableTiming));
+  chk(hipEventCreateWithFlags(&x->fwd_start, hipEventDisableTiming));
   if (rc) {
     gpt_destroy(x);
     return rc;
@@ -555,7 +557,7 @@ int gpt_destroy(gpt_ctx* x) {
   if (x->side) (void)hipStreamSynchronize(x->side);
   for (auto e : x->sev)
     if (e) (void)hipEventDestroy(e);
-  for (hipEvent_t e : {x->head_ready[0], x->head_ready[1], x->head_done[0], x->head_done[1], x->side_tail})
+  for (hipEvent_t e : {x->head_ready[0], x->head_ready[1], x->head_done[0], x->head_done[1], x->side_tail, x->fwd_start})
     if (e) (void)hipEventDestroy(e);
   if (x->side) (void)hipStreamDestroy(x->side);
   delete x;
@@ -571,6 +573,7 @@ int gpt_make_batch(gpt_ctx* x, const int32_t* host_tokens, int64_t n_tokens, int
     if (t < 0 || t >= x->V)
       return fail(GPT_ERANGE, "token " + std::to_string(t) + " at " + std::to_string(start + i) + " outside [0, vocab)");
   }
+  if (int e = join_side(x)) return e;  // the side stream's token sort may still read the previous batch
   HIPCHK(hipMemcpyAsync(x->win, host_tokens + start, need * 4, hipMemcpyHostToDevice, x->stream));
   HIPCHK(hipStreamSynchronize(x->stream));
   return 0;
@@ -594,6 +597,13 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
   const int32_t* yt = x->win + 1;
   // a previous call's head dW may still read lnf / dz and write G(wte)
   if (int e = join_side(x)) return e;
+  if (loss_scale > 0.f) {
+    // the embedding backward's token sort needs only the batch: it runs on the
+    // side stream beside the forward (its keys are read after backward's join)
+    HIPCHK(hipEventRecord(x->fwd_start, s));
+    HIPCHK(hipStreamWaitEvent(x->side, x->fwd_start, 0));
+    HIPCHK(gk::sort_tokens(x->win, (int)N, x->keys, x->side));
+  }
   {
     ProfScope ps(x, "layernorm_fwd", 0.0, (double)N * C * (4 + 4 + 4 + x->es) + 8.0 * N);
     HIPCHK(gk::embed_ln_fwd(x->dt, xt, x->P_(T_WTE), x->P_(T_WPE), (int)x->T, x->res[0], x->P_(tid(0, K_LN1G)),
@@ -735,7 +745,6 @@ int gpt_backward(gpt_ctx* x) {
   // embeddings: token rows (deterministic segmented sum) and positions
   {
     ProfScope ps(x, "embed_bwd", 0.0, (double)N * C * 12);
-    HIPCHK(gk::sort_tokens(x->win, (int)N, x->keys, s));
     HIPCHK(gk::embed_bwd_ws(x->keys, (int)N, x->dres, (int)C, x->dln, x->G_(T_WTE), s));
     HIPCHK(gk::wpe_bwd(x->dres, (int)x->B, (int)x->T, (int)C, x->G_(T_WPE), acc, s));
   }

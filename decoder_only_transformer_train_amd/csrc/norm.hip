@@ -433,18 +433,24 @@ __global__ __launch_bounds__(1024, sizeof(T) == 2 ? 8 : 4) void ce_reg_kernel(co
   }
 }
 
-// out[0] = mean of x[0..n) summed in a fixed order; also ring[slot]
-__global__ __launch_bounds__(256) void mean_kernel(const float* __restrict__ x, int n, float* out, float* ring,
-                                                   int slot) {
-  __shared__ float red[4];
+// out[0] = mean of x[0..n) summed in a fixed order; also ring[slot].  1024
+// threads; thread t adds x[t], x[t + 1024], ... in order, then the waves' sums
+// are added in wave order.
+__global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x, int n, float* out, float* ring,
+                                                    int slot) {
+  __shared__ float red[16];
   const int t = threadIdx.x;
   float s = 0.f;
-  for (int i = t; i < n; i += 256) s += x[i];
+#pragma unroll 8
+  for (int i = t; i < n; i += 1024) s += x[i];
   s = wave_sum(s);
   if ((t & 63) == 0) red[t >> 6] = s;
   __syncthreads();
   if (t == 0) {
-    const float m = (red[0] + red[1] + red[2] + red[3]) / n;
+    float m = red[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) m += red[k];
+    m /= n;
     out[0] = m;
     if (ring) ring[slot] = m;
   }
@@ -568,7 +574,7 @@ hipError_t ce_rows(int dtype, const void* z, int64_t ldz, int V, const int32_t* 
 }
 
 hipError_t mean_f32(const float* x, int n, float* out, float* ring, int slot, hipStream_t s) {
-  hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, s, x, n, out, ring, slot);
+  hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, s, x, n, out, ring, slot);
   return hipGetLastError();
 }
 
