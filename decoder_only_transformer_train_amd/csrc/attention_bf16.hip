@@ -22,6 +22,19 @@
 //    owns the 32-row tiles w and 7 - w, so every wave has one early and one
 //    late tile and the causal work is balanced.  The dK/dV kernel gives a
 //    workgroup 128 keys, one 32-key tile per wave.
+//  * Workgroup order: the grid is one-dimensional, longest blocks first, with
+//    (batch, head) varying fastest.  The hardware deals workgroup i to XCD
+//    i % 8, so every XCD gets the same mix of long and short causal blocks
+//    (a [blocks][heads] grid put all of one block index on the same XCDs, up
+//    to 1.8x the mean load on one of them), and the blocks of one head land
+//    on one XCD, whose L2 then serves their shared K/V (or Q/dO) rows.
+//  * Forward softmax: the two tiles of a wave share one read of the K and V
+//    fragments of a block.  The running maximum is updated lazily: the
+//    output is rescaled only when a block's maximum exceeds it by more than
+//    2^TAU, so p stays below 2^TAU (exact in bf16 range and fp32 sums) and
+//    the rescale branch is rare after a row's first block.  Each lane half
+//    keeps its own running sum of the bf16-rounded p (the values the PV
+//    product uses), added once at the end.
 //  * Stage refills: iteration j waits for its block, passes the barrier
 //    (every wave is done with block j - 1), refills block j - 1's stage with
 //    block j + ST - 1 and consumes block j.  The stage pointers are distinct
@@ -133,120 +146,194 @@ __device__ __forceinline__ uint4 pack_half(const f32x16& c, int hh) {
 }
 
 // ---------------------------------------------------------------------------
-// Forward.  Stage = K block + V block (16 KB).
-struct FwdState {
-  uint4 qf[2][4];
-  f32x16 oacc[2][2];
-  float m[2], l[2];
-  int q[2], qlo[2];
+// Forward.  Stage = K block + V block (16 KB).  A wave owns two 32-query tiles
+// (A early, B late); both read the same K and V fragments of a block.
+constexpr float TAU = 8.0f;  // lazy rescale: the running max may lag the true one by up to 2^8
+
+struct QTile {
+  uint4 qf[4];
+  f32x16 o[2];
+  float m, l;  // running max (scaled log2 units), this lane half's running sum
 };
 
-__device__ __forceinline__ void fwd_block(const char* __restrict__ rd, char* __restrict__ wr, int kb, int nkb,
-                                          rsrc_t r, const BlockLoad& lk, const BlockLoad& lv, uint32_t blk_bytes,
-                                          FwdState& S, int Tn, int w, int lane) {
+__device__ __forceinline__ void read_kf(uint4 (&kf)[2][4], const char* sK, int c32, int g) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kf[kt][kk] = frag_row(sK, kt * 32 + c32, kk, g);
+}
+__device__ __forceinline__ void read_vf(uint4 (&vf)[4][2], const char* sV, int lane) {
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) vf[hh][dt] = frag_tr(sV, dt * 32, hh * 16, lane);
+}
+__device__ __forceinline__ void scores(f32x16 (&s)[2], const uint4 (&kf)[2][4], const uint4 (&qf)[4]) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    zero16(s[kt]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) mma32(s[kt], kf[kt][kk], qf[kk]);
+  }
+}
+// keys after the query (or past the sequence: qc = min(q, T - 1)) -> -inf
+__device__ __forceinline__ void mask_keys(f32x16 (&s)[2], int key0, int qc, int g) {
+  int rel = qc - key0 - g * 4;  // query minus the lane half's first key
+  asm volatile("" : "+v"(rel));  // keep the compares in the block that uses them
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[kt][e] = (kt * 32 + (e >> 2) * 8 + (e & 3) <= rel) ? s[kt][e] : NEG_INF;
+}
+__device__ __forceinline__ float swap_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// the query's maximum raw score over the block (both lane halves)
+__device__ __forceinline__ float rowmax(const f32x16 (&s)[2]) {
+  float a = NEG_INF, b = NEG_INF;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    a = fmaxf(a, s[0][e]);
+    b = fmaxf(b, s[1][e]);
+  }
+  return swap_halves(fmaxf(a, b));
+}
+__device__ __forceinline__ void rescale(QTile& T, float mxs) {
+  const float mnew = fmaxf(T.m, mxs);
+  const float alpha = hw_exp2(T.m - mnew);
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt) T.o[dt] *= alpha;
+  T.l *= alpha;
+  T.m = mnew;
+}
+// p = 2^(s cs - m) packed to bf16 as the B fragments of the PV product; the
+// running sum adds the rounded p (the same values the product uses)
+__device__ __forceinline__ void probs(QTile& T, const f32x16 (&s)[2], uint4 (&p)[4], float cs) {
+  float l = T.l;
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (bf16)hw_exp2(fmaf(s[hh >> 1][8 * (hh & 1) + j], cs, -T.m));
+    p[hh] = bitcast<uint4>(v);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t one = {(bf16)1.0f, (bf16)1.0f};
+    l = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(p[hh].x), one, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(p[hh].y), one, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(p[hh].z), one, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(p[hh].w), one, l, false);
+  }
+  T.l = l;
+}
+__device__ __forceinline__ void pv(QTile& T, const uint4 (&vf)[4][2], const uint4 (&p)[4]) {
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) mma32(T.o[dt], vf[hh][dt], p[hh]);
+}
+
+// both tiles against one block; MASK: the block is the last of A (and of B if mB)
+template <bool MASK>
+__device__ __forceinline__ void fwd_both(const char* sK, const char* sV, QTile& A, QTile& B, int key0, int qcA,
+                                         int qcB, bool mB, int lane) {
   const int g = lane >> 5, c32 = lane & 31;
+  const float cs = LOG2E / 8.0f;
+  uint4 kf[2][4];
+  read_kf(kf, sK, c32, g);
+  f32x16 sA[2], sB[2];
+  scores(sA, kf, A.qf);
+  scores(sB, kf, B.qf);
+  if (MASK) {
+    mask_keys(sA, key0, qcA, g);
+    if (mB) mask_keys(sB, key0, qcB, g);
+  }
+  const float mxA = rowmax(sA) * cs, mxB = rowmax(sB) * cs;
+  uint4 vf[4][2];
+  read_vf(vf, sV, lane);
+  if (__any((mxA > A.m + TAU) | (mxB > B.m + TAU))) {
+    rescale(A, mxA);
+    rescale(B, mxB);
+  }
+  uint4 p[4];
+  probs(A, sA, p, cs);
+  pv(A, vf, p);
+  probs(B, sB, p, cs);
+  pv(B, vf, p);
+}
+template <bool MASK>
+__device__ __forceinline__ void fwd_one(const char* sK, const char* sV, QTile& B, int key0, int qcB, int lane) {
+  const int g = lane >> 5, c32 = lane & 31;
+  const float cs = LOG2E / 8.0f;
+  uint4 kf[2][4];
+  read_kf(kf, sK, c32, g);
+  f32x16 sB[2];
+  scores(sB, kf, B.qf);
+  if (MASK) mask_keys(sB, key0, qcB, g);
+  const float mxB = rowmax(sB) * cs;
+  uint4 vf[4][2];
+  read_vf(vf, sV, lane);
+  if (__any(mxB > B.m + TAU)) rescale(B, mxB);
+  uint4 p[4];
+  probs(B, sB, p, cs);
+  pv(B, vf, p);
+}
+
+// one key block: wait for it, refill the stage freed by the previous block, then
+// the tiles that still need this block (distinct __restrict__ stage pointers
+// keep the compiler from waiting on every outstanding direct-to-LDS load)
+__device__ __forceinline__ void fwd_iter(const char* __restrict__ rd, char* __restrict__ wr, int kb, int nkb, rsrc_t r,
+                                         const BlockLoad& lk, const BlockLoad& lv, uint32_t blk_bytes, QTile& A,
+                                         QTile& B, int lastA, int lastB, int qcA, int qcB, int w, int lane) {
   wait_blocks<4>(min(ST - 2, nkb - 1 - kb));
   __syncthreads();
   if (kb + ST - 1 < nkb) {
     lk.issue(r, wr, (uint32_t)(kb + ST - 1) * blk_bytes, w);
     lv.issue(r, wr + TILE, (uint32_t)(kb + ST - 1) * blk_bytes, w);
   }
-  const char* sK = rd;
-  const char* sV = rd + TILE;
-  const float cs = LOG2E / 8.0f;  // log2(e) / sqrt(64)
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (kb * 64 > S.qlo[i] + 31) continue;  // every key of the block is after every query of the tile
-    // below the diagonal (every key of the block before every query of the tile) no key is masked
-    const bool diag = kb * 64 + 63 > S.qlo[i];
-    const int qc = min(S.q[i], Tn - 1);
-    f32x16 s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      zero16(s[kt]);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) mma32(s[kt], frag_row(sK, kt * 32 + c32, kk, g), S.qf[i][kk]);
-    }
-    // row maximum of the raw scores (the scale cs > 0 keeps the order); masked scores -> -inf
-    float mx = NEG_INF;
-    if (diag) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb * 64 + kt * 32 + crow(e, g);
-          s[kt][e] = (key <= qc) ? s[kt][e] : NEG_INF;
-          mx = fmaxf(mx, s[kt][e]);
-        }
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-    // running max in scaled log2 units; p = 2^(s cs - m) as one fma and one exp2
-    const float mnew = fmaxf(S.m[i], mx * cs);
-    const float alpha = hw_exp2(S.m[i] - mnew);
-    float ls = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = hw_exp2(fmaf(s[kt][e], cs, -mnew));
-        s[kt][e] = p;
-        ls += p;
-      }
-    ls += __shfl_xor(ls, 32, WAVE);
-    S.l[i] = S.l[i] * alpha + ls;
-    S.m[i] = mnew;
-    // the output only needs rescaling when some query's maximum grew
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) S.oacc[i][dt] *= alpha;
-    }
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      const uint4 bp = pack_half(s[hh >> 1], hh & 1);
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) mma32(S.oacc[i][dt], frag_tr(sV, dt * 32, hh * 16, lane), bp);
-    }
-  }
+  if (kb < lastA) fwd_both<false>(rd, rd + TILE, A, B, kb * 64, qcA, qcB, false, lane);
+  else if (kb == lastA) fwd_both<true>(rd, rd + TILE, A, B, kb * 64, qcA, qcB, lastB == lastA, lane);
+  else if (kb < lastB) fwd_one<false>(rd, rd + TILE, B, kb * 64, qcB, lane);
+  else if (kb == lastB) fwd_one<true>(rd, rd + TILE, B, kb * 64, qcB, lane);
 }
 
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ o,
                                                      float* __restrict__ lse2, int Tn, int H) {
   __shared__ __attribute__((aligned(16))) char smem[ST * 2 * TILE];
   const int nqb = (Tn + 255) / 256;
-  const int qb = nqb - 1 - blockIdx.x;  // latest (longest) query blocks first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int BH = gridDim.x / nqb;
+  const int qb = nqb - 1 - (int)blockIdx.x / BH;  // latest (longest) query blocks first
+  const int bh = (int)blockIdx.x % BH, b = bh / H, h = bh % H;
   const int Cc = H * HD;
   const int64_t ld = 3 * (int64_t)Cc;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
   const rsrc_t r = make_rsrc(base, (int64_t)Tn * ld * 2);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, c32 = lane & 31;
   const int q0 = qb * 256;
-  FwdState S;
-  const int qt[2] = {w, 7 - w};
+  const int nkb = (min(Tn, q0 + 256) + 63) / 64;
+  QTile A, B;
+  QTile* tl[2] = {&A, &B};
+  const int qlo[2] = {q0 + w * 32, q0 + (7 - w) * 32};
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    S.qlo[i] = q0 + qt[i] * 32;
-    S.q[i] = S.qlo[i] + c32;
+    QTile& Q = *tl[i];
+    const int q = qlo[i] + c32;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      S.qf[i][kk] = (S.q[i] < Tn)
-                        ? *reinterpret_cast<const uint4*>(base + (int64_t)S.q[i] * ld + h * HD + kk * 16 + g * 8)
-                        : make_uint4(0, 0, 0, 0);
-    zero16(S.oacc[i][0]);
-    zero16(S.oacc[i][1]);
-    S.m[i] = NEG_INF;
-    S.l[i] = 0.f;
+      Q.qf[kk] = (q < Tn) ? *reinterpret_cast<const uint4*>(base + (int64_t)q * ld + h * HD + kk * 16 + g * 8)
+                          : make_uint4(0, 0, 0, 0);
+    zero16(Q.o[0]);
+    zero16(Q.o[1]);
+    Q.m = NEG_INF;
+    Q.l = 0.f;
   }
+  // each tile's last block (the only one that needs the causal mask)
+  const int lastA = min((qlo[0] + 31) / 64, nkb - 1), lastB = min((qlo[1] + 31) / 64, nkb - 1);
+  const int qcA = min(qlo[0] + c32, Tn - 1), qcB = min(qlo[1] + c32, Tn - 1);
   BlockLoad lk, lv;
   lk.init(ld, Cc + h * HD, w, lane);
   lv.init(ld, 2 * Cc + h * HD, w, lane);
   const uint32_t blk_bytes = (uint32_t)(64 * ld * 2);
-  const int nkb = (min(Tn, q0 + 256) + 63) / 64;
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
     if (s < nkb) {
@@ -256,22 +343,26 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const bf16* __restrict__ qk
   int sc = 0;
   for (int kb = 0; kb < nkb; ++kb) {
     const int sw = sc == 0 ? ST - 1 : sc - 1;
-    fwd_block(smem + sc * 2 * TILE, smem + sw * 2 * TILE, kb, nkb, r, lk, lv, blk_bytes, S, Tn, w, lane);
+    fwd_iter(smem + sc * 2 * TILE, smem + sw * 2 * TILE, kb, nkb, r, lk, lv, blk_bytes, A, B, lastA, lastB, qcA, qcB,
+             w, lane);
     sc = sc + 1 == ST ? 0 : sc + 1;
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    if (S.q[i] >= Tn) continue;
-    const float inv = 1.f / S.l[i];
-    bf16* orow = o + (int64_t)(b * Tn + S.q[i]) * Cc + h * HD;
+    QTile& Q = *tl[i];
+    const int q = qlo[i] + c32;
+    const float lsum = Q.l + __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(Q.l), __float_as_uint(Q.l), false, false)[g == 0 ? 1 : 0]);
+    if (q >= Tn) continue;
+    const float inv = 1.f / lsum;
+    bf16* orow = o + (int64_t)(b * Tn + q) * Cc + h * HD;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
         store4(orow + dt * 32 + r4 * 8 + g * 4,
-               make_float4(S.oacc[i][dt][4 * r4] * inv, S.oacc[i][dt][4 * r4 + 1] * inv,
-                           S.oacc[i][dt][4 * r4 + 2] * inv, S.oacc[i][dt][4 * r4 + 3] * inv));
-    if (g == 0) lse2[(int64_t)bh * Tn + S.q[i]] = S.m[i] + hw_log2(S.l[i]);
+               make_float4(Q.o[dt][4 * r4] * inv, Q.o[dt][4 * r4 + 1] * inv, Q.o[dt][4 * r4 + 2] * inv,
+                           Q.o[dt][4 * r4 + 3] * inv));
+    if (g == 0) lse2[(int64_t)bh * Tn + q] = Q.m + hw_log2(lsum);
   }
 }
 
@@ -368,8 +459,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(const bf16* __restrict__ q
                                                       bf16* __restrict__ dqkv, int Tn, int H) {
   __shared__ __attribute__((aligned(16))) char smem[ST * KV_STAGE];
   const int nqb = (Tn + 63) / 64;
-  const int kb = blockIdx.x;  // key block 0 has the most query blocks: first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int BH = gridDim.x / ((Tn + 127) / 128);
+  const int kb = (int)blockIdx.x / BH;  // key block 0 has the most query blocks: first
+  const int bh = (int)blockIdx.x % BH, b = bh / H, h = bh % H;
   const int Cc = H * HD;
   const int64_t ld = 3 * (int64_t)Cc;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
@@ -491,8 +583,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const bf16* __restrict__ qkv
                                                     bf16* __restrict__ dqkv, int Tn, int H) {
   __shared__ __attribute__((aligned(16))) char smem[ST * 2 * TILE];
   const int nqb = (Tn + 255) / 256;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int BH = gridDim.x / nqb;
+  const int qb = nqb - 1 - (int)blockIdx.x / BH;
+  const int bh = (int)blockIdx.x % BH, b = bh / H, h = bh % H;
   const int Cc = H * HD;
   const int64_t ld = 3 * (int64_t)Cc;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
@@ -555,7 +648,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const bf16* __restrict__ qkv
 hipError_t attn_fwd_bf16_d64(const void* qkv, void* o, float* lse, int B, int Tn, int H, hipStream_t s) {
   // buffer offsets are 32-bit: one sequence of qkv must stay under 4 GB
   if ((int64_t)Tn * 3 * H * fa::HD * 2 >= (1ll << 32)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fa::fwd_kernel, dim3((Tn + 255) / 256, B * H), dim3(256), 0, s, (const bf16*)qkv, (bf16*)o,
+  hipLaunchKernelGGL(fa::fwd_kernel, dim3((Tn + 255) / 256 * B * H), dim3(256), 0, s, (const bf16*)qkv, (bf16*)o,
                      lse, Tn, H);
   return hipGetLastError();
 }
@@ -563,9 +656,9 @@ hipError_t attn_fwd_bf16_d64(const void* qkv, void* o, float* lse, int B, int Tn
 hipError_t attn_bwd_bf16_d64(const void* qkv, const void* dO, const float* lse, const float* Dv, void* dqkv, int B,
                              int Tn, int H, hipStream_t s) {
   if ((int64_t)Tn * 3 * H * fa::HD * 2 >= (1ll << 32)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fa::dkdv_kernel, dim3((Tn + 127) / 128, B * H), dim3(256), 0, s, (const bf16*)qkv,
+  hipLaunchKernelGGL(fa::dkdv_kernel, dim3((Tn + 127) / 128 * B * H), dim3(256), 0, s, (const bf16*)qkv,
                      (const bf16*)dO, lse, Dv, (bf16*)dqkv, Tn, H);
-  hipLaunchKernelGGL(fa::dq_kernel, dim3((Tn + 255) / 256, B * H), dim3(256), 0, s, (const bf16*)qkv,
+  hipLaunchKernelGGL(fa::dq_kernel, dim3((Tn + 255) / 256 * B * H), dim3(256), 0, s, (const bf16*)qkv,
                      (const bf16*)dO, lse, Dv, (bf16*)dqkv, Tn, H);
   return hipGetLastError();
 }

@@ -86,6 +86,16 @@ def test_gpt2_1p5b_layer_shapes_with_accumulation():
     check_step(cfg, stream, accum=2)
 
 
+def test_gpt2_124m_ragged_sequence():
+    # T = 200: attention blocks run past the sequence end (64-key blocks, 256-query
+    # workgroups, 32-row tiles partly or wholly beyond T) and B*H = 24 is not a
+    # multiple of the 8 XCDs the workgroups are dealt to
+    cfg = configs.GPT2_124M.with_(n_layer=1, batch=2, seq=200, max_seq=256)
+    stream = synthetic.zipf_eot_stream(2 * 200 + 1, cfg.vocab, seed=5)
+    announce("124M-shaped 1-layer step, T=200")
+    check_step(cfg, stream, seed=5)
+
+
 def test_bf16_adamw_update_matches_oracle():
     cfg = configs.GPT2_124M.with_(n_layer=1, batch=1, seq=256, max_seq=256)
     stream = synthetic.zipf_eot_stream(257, cfg.vocab, seed=4)
