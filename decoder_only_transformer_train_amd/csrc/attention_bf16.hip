@@ -2,7 +2,7 @@
 //
 // Same method as the fp32 kernels in attention.hip (online softmax over
 // 64-key blocks, log-sum-exp saved for a recomputing backward, dK/dV and dQ
-// in separate atomic-free kernels), laid out for the 32x32 MFMA and the LDS
+// by separate atomic-free workgroups), laid out for the 32x32 MFMA and the LDS
 // direct-load path:
 //  * Every streamed operand block is 64 rows x 64 d of a row-major [T][ld]
 //    tensor, moved by buffer_load_dwordx4 ... lds straight into an 8 KB LDS
@@ -18,16 +18,18 @@
 //    and rows (e / 4) * 8 + (l / 32) * 4 + e % 4, e = 0..15; the 8 values of
 //    one 16-row half are a 32x32x16 B fragment whose k order the transposed
 //    reads reproduce.
-//  * The forward and dQ kernels give a workgroup a 256-query block; wave w
-//    owns the 32-row tiles w and 7 - w, so every wave has one early and one
-//    late tile and the causal work is balanced.  The dK/dV kernel gives a
-//    workgroup 128 keys, one 32-key tile per wave.
-//  * Workgroup order: the grid is one-dimensional, longest blocks first, with
-//    (batch, head) varying fastest.  The hardware deals workgroup i to XCD
-//    i % 8, so every XCD gets the same mix of long and short causal blocks
-//    (a [blocks][heads] grid put all of one block index on the same XCDs, up
-//    to 1.8x the mean load on one of them), and the blocks of one head land
-//    on one XCD, whose L2 then serves their shared K/V (or Q/dO) rows.
+//  * Forward and dQ workgroups take a 256-query block; wave w owns the
+//    32-row tiles w and 7 - w, so every wave has one early and one late tile
+//    and the causal work is balanced.  A dK/dV workgroup takes 128 keys, one
+//    32-key tile per wave.
+//  * Workgroup order: the grids are one-dimensional, longest blocks first,
+//    with (batch, head) varying fastest.  The hardware deals workgroup i to
+//    XCD i % 8, so every XCD gets the same mix of long and short causal
+//    blocks (a [blocks][heads] grid put all of one block index on the same
+//    XCDs, up to 1.8x the mean load on one of them), and the blocks of one
+//    head land on one XCD, whose L2 then serves their shared rows.  The
+//    backward's dK/dV and dQ blocks share one launch and one such order, so
+//    a single tail ends both.
 //  * Forward softmax: the two tiles of a wave share one read of the K and V
 //    fragments of a block.  The running maximum is updated lazily: the
 //    output is rescaled only when a block's maximum exceeds it by more than
@@ -41,6 +43,9 @@
 //    and passed as __restrict__, which lets the compiler drop its blanket wait
 //    on outstanding direct-to-LDS loads before LDS reads; the real
 //    dependencies are the explicit vmcnt wait and the barrier.
+#include <algorithm>
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -454,14 +459,11 @@ __device__ __forceinline__ void kv_block(const char* __restrict__ rd, char* __re
   }
 }
 
-__global__ __launch_bounds__(256, 2) void dkdv_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ dO,
-                                                      const float* __restrict__ lse2, const float* __restrict__ Dv,
-                                                      bf16* __restrict__ dqkv, int Tn, int H) {
-  __shared__ __attribute__((aligned(16))) char smem[ST * KV_STAGE];
+__device__ __forceinline__ void dkdv_item(char* smem, int kb, int bh, const bf16* __restrict__ qkv,
+                                          const bf16* __restrict__ dO, const float* __restrict__ lse2,
+                                          const float* __restrict__ Dv, bf16* __restrict__ dqkv, int Tn, int H) {
   const int nqb = (Tn + 63) / 64;
-  const int BH = gridDim.x / ((Tn + 127) / 128);
-  const int kb = (int)blockIdx.x / BH;  // key block 0 has the most query blocks: first
-  const int bh = (int)blockIdx.x % BH, b = bh / H, h = bh % H;
+  const int b = bh / H, h = bh % H;
   const int Cc = H * HD;
   const int64_t ld = 3 * (int64_t)Cc;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
@@ -578,14 +580,10 @@ __device__ __forceinline__ void dq_block(const char* __restrict__ rd, char* __re
   }
 }
 
-__global__ __launch_bounds__(256, 2) void dq_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ dO,
-                                                    const float* __restrict__ lse2, const float* __restrict__ Dv,
-                                                    bf16* __restrict__ dqkv, int Tn, int H) {
-  __shared__ __attribute__((aligned(16))) char smem[ST * 2 * TILE];
-  const int nqb = (Tn + 255) / 256;
-  const int BH = gridDim.x / nqb;
-  const int qb = nqb - 1 - (int)blockIdx.x / BH;
-  const int bh = (int)blockIdx.x % BH, b = bh / H, h = bh % H;
+__device__ __forceinline__ void dq_item(char* smem, int qb, int bh, const bf16* __restrict__ qkv,
+                                        const bf16* __restrict__ dO, const float* __restrict__ lse2,
+                                        const float* __restrict__ Dv, bf16* __restrict__ dqkv, int Tn, int H) {
+  const int b = bh / H, h = bh % H;
   const int Cc = H * HD;
   const int64_t ld = 3 * (int64_t)Cc;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
@@ -643,6 +641,24 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const bf16* __restrict__ qkv
   }
 }
 
+// The dK/dV and dQ work of one backward in one launch: class c of the grid
+// (blockIdx.x / BH) is a dK/dV key block or a dQ query block, the classes in
+// decreasing order of work, (batch, head) varying fastest within a class.
+constexpr int MAX_CLASSES = 256;
+struct BwdOrder {
+  unsigned short cls[MAX_CLASSES];  // bit 15: dQ query block, else dK/dV key block; low bits: block index
+};
+
+__global__ __launch_bounds__(256, 2) void bwd_kernel(const bf16* __restrict__ qkv, const bf16* __restrict__ dO,
+                                                     const float* __restrict__ lse2, const float* __restrict__ Dv,
+                                                     bf16* __restrict__ dqkv, int Tn, int H, int BH, BwdOrder ord) {
+  __shared__ __attribute__((aligned(16))) char smem[ST * KV_STAGE > ST * 2 * TILE ? ST * KV_STAGE : ST * 2 * TILE];
+  const int c = (int)blockIdx.x / BH, bh = (int)blockIdx.x % BH;
+  const int e = ord.cls[c];
+  if (e & 0x8000) dq_item(smem, e & 0x7fff, bh, qkv, dO, lse2, Dv, dqkv, Tn, H);
+  else dkdv_item(smem, e, bh, qkv, dO, lse2, Dv, dqkv, Tn, H);
+}
+
 }  // namespace fa
 
 hipError_t attn_fwd_bf16_d64(const void* qkv, void* o, float* lse, int B, int Tn, int H, hipStream_t s) {
@@ -656,10 +672,26 @@ hipError_t attn_fwd_bf16_d64(const void* qkv, void* o, float* lse, int B, int Tn
 hipError_t attn_bwd_bf16_d64(const void* qkv, const void* dO, const float* lse, const float* Dv, void* dqkv, int B,
                              int Tn, int H, hipStream_t s) {
   if ((int64_t)Tn * 3 * H * fa::HD * 2 >= (1ll << 32)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fa::dkdv_kernel, dim3((Tn + 127) / 128 * B * H), dim3(256), 0, s, (const bf16*)qkv,
-                     (const bf16*)dO, lse, Dv, (bf16*)dqkv, Tn, H);
-  hipLaunchKernelGGL(fa::dq_kernel, dim3((Tn + 255) / 256 * B * H), dim3(256), 0, s, (const bf16*)qkv,
-                     (const bf16*)dO, lse, Dv, (bf16*)dqkv, Tn, H);
+  // classes and their work in streamed blocks: a dK/dV key block (128 keys) streams
+  // the 64-query blocks from its diagonal on (32 MFMAs per wave each); a dQ query
+  // block (256 queries) streams the 64-key blocks up to its end (48 per wave each)
+  const int nkv = (Tn + 127) / 128, nq64 = (Tn + 63) / 64, nqd = (Tn + 255) / 256;
+  if (nkv + nqd > fa::MAX_CLASSES) return hipErrorInvalidValue;
+  int cost[fa::MAX_CLASSES];
+  fa::BwdOrder ord;
+  int n = 0;
+  for (int kb = 0; kb < nkv; ++kb) { ord.cls[n] = (unsigned short)kb; cost[n++] = 2 * (nq64 - 2 * kb); }
+  for (int qb = 0; qb < nqd; ++qb) {
+    ord.cls[n] = (unsigned short)(0x8000 | qb);
+    cost[n++] = 3 * ((std::min(Tn, qb * 256 + 256) + 63) / 64);
+  }
+  for (int i = 1; i < n; ++i)  // insertion sort, decreasing work (stable)
+    for (int j = i; j > 0 && cost[j] > cost[j - 1]; --j) {
+      std::swap(cost[j], cost[j - 1]);
+      std::swap(ord.cls[j], ord.cls[j - 1]);
+    }
+  hipLaunchKernelGGL(fa::bwd_kernel, dim3(n * B * H), dim3(256), 0, s, (const bf16*)qkv, (const bf16*)dO, lse, Dv,
+                     (bf16*)dqkv, Tn, H, B * H, ord);
   return hipGetLastError();
 }
 
