@@ -281,6 +281,36 @@ __device__ __forceinline__ float4 epi_load(const Params& p, int64_t o) {
   return make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// One group of 4 adjacent columns of row m inside the output (16-byte aligned),
+// with in = epi_load of it and b4 = its bias, both loaded ahead: no loads here.
+template <typename T, int EPI, int SPLIT>
+__device__ __forceinline__ void epi_group_full(const Params& p, int m, int n, float4 a, float4 in, float4 b4) {
+  if constexpr (SPLIT) {
+    *reinterpret_cast<float4*>(p.ws + (int64_t)m * p.N + n) = a;  // ws: this split's slice
+    return;
+  }
+  const int64_t o = (int64_t)m * p.ldc + n;
+  if constexpr (EPI == EPI_STORE) {
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w));
+  } else if constexpr (EPI == EPI_RESID) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) =
+        make_float4(in.x + (a.x + b4.x), in.y + (a.y + b4.y), in.z + (a.z + b4.z), in.w + (a.w + b4.w));
+  } else if constexpr (EPI == EPI_GELU) {
+    float g0, g1, g2, g3, d0, d1, d2, d3;
+    gelu_both(a.x + b4.x, g0, d0);
+    gelu_both(a.y + b4.y, g1, d1);
+    gelu_both(a.z + b4.z, g2, d2);
+    gelu_both(a.w + b4.w, g3, d3);
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(d0, d1, d2, d3));
+    store4(reinterpret_cast<T*>(p.C2) + o, make_float4(g0, g1, g2, g3));
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x * in.x, a.y * in.y, a.z * in.z, a.w * in.w));
+  } else {
+    if (p.accumulate) a = make_float4(in.x + a.x, in.y + a.y, in.z + a.z, in.w + a.w);
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) = a;
+  }
+}
+
 // One group of 4 adjacent columns of row m.  full: the group is inside N and
 // 16-byte aligned, in = epi_load of it and b4 = its bias, both loaded ahead.
 template <typename T, int EPI, int SPLIT>
@@ -353,12 +383,19 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
   constexpr int CG = BN / 4;           // column groups per row
   constexpr int RSTEP = 256 / CG;      // rows between a thread's groups
   constexpr int NG = PASS_ROWS / RSTEP;
-  constexpr bool IN = epi_reads<EPI, SPLIT>() && NG <= 16;  // (register budget)
+  // a thread's NG groups of a pass are unrolled (register budget: NG <= 16), and
+  // every group uses the bias loaded once above: a load inside the group loop
+  // would be waited for after the previous groups' stores, and vmcnt counts
+  // stores too, so each group would wait for the last one's stores to complete
+  constexpr bool UNR = NG <= 16;
+  constexpr bool IN = epi_reads<EPI, SPLIT>() && UNR;
   static_assert(256 % CG == 0 && PASS_ROWS % RSTEP == 0, "epilogue thread mapping");
   float* st = reinterpret_cast<float*>(smem);
   const int c4 = t % CG, r0 = t / CG;
   const int n = n0 + c4 * 4;
   const bool full = n + 3 < p.N && (SPLIT || (p.ldc & 3) == 0);
+  // the whole tile inside the output, every group 16-byte aligned
+  const bool tile_full = m0 + BM <= p.M && n0 + BN <= p.N && (SPLIT ? (p.N & 3) == 0 : (p.ldc & 3) == 0);
   float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
   if (!SPLIT && full && p.bias) b4 = *reinterpret_cast<const float4*>(p.bias + n);
 #pragma unroll
@@ -385,13 +422,26 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
           }
     }
     __syncthreads();
-    if constexpr (IN) {
+    if constexpr (UNR) {
+      if (tile_full) {  // no loads among the stores: nothing makes a group wait for earlier stores
 #pragma unroll
-      for (int i = 0; i < NG; ++i) {
-        const int r = r0 + i * RSTEP;
-        const int m = m0 + pass * PASS_ROWS + r;
-        if (m >= p.M || n >= p.N) continue;
-        epi_group<T, EPI, SPLIT>(p, m, n, *reinterpret_cast<const float4*>(st + r * LDW + c4 * 4), full, in[i], b4);
+        for (int i = 0; i < NG; ++i) {
+          const int r = r0 + i * RSTEP;
+          float4 x_in = make_float4(0.f, 0.f, 0.f, 0.f);
+          if constexpr (IN) x_in = in[i];
+          epi_group_full<T, EPI, SPLIT>(p, m0 + pass * PASS_ROWS + r, n,
+                                        *reinterpret_cast<const float4*>(st + r * LDW + c4 * 4), x_in, b4);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+          const int r = r0 + i * RSTEP;
+          const int m = m0 + pass * PASS_ROWS + r;
+          if (m >= p.M || n >= p.N) continue;
+          float4 x_in = make_float4(0.f, 0.f, 0.f, 0.f);
+          if constexpr (IN) x_in = in[i];
+          epi_group<T, EPI, SPLIT>(p, m, n, *reinterpret_cast<const float4*>(st + r * LDW + c4 * 4), full, x_in, b4);
+        }
       }
     } else {
       for (int g = t; g < PASS_ROWS * CG; g += 256) {
