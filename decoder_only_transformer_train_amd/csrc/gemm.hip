@@ -398,10 +398,35 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
   const bool tile_full = m0 + BM <= p.M && n0 + BN <= p.N && (SPLIT ? (p.N & 3) == 0 : (p.ldc & 3) == 0);
   float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
   if (!SPLIT && full && p.bias) b4 = *reinterpret_cast<const float4*>(p.bias + n);
+  // A 16-bit input (the GELU derivative) is loaded for every pass before the
+  // first store, kept as raw bf16 pairs (as many registers as one pass of
+  // floats): a later pass's loads would otherwise wait for the earlier passes'
+  // stores.  Wider inputs are loaded pass by pass (register budget).
+  constexpr int NP = BM / PASS_ROWS;
+  constexpr bool PRE = IN && EPI == EPI_GELU_BWD && sizeof(T) == 2;
+  uint2 raw[PRE ? NP : 1][PRE ? NG : 1];
+  if constexpr (PRE) {
 #pragma unroll
-  for (int pass = 0; pass < BM / PASS_ROWS; ++pass) {
+    for (int ps = 0; ps < NP; ++ps)
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int m = m0 + ps * PASS_ROWS + r0 + i * RSTEP;
+        raw[ps][i] = (full && m < p.M)
+                         ? *reinterpret_cast<const uint2*>(reinterpret_cast<const T*>(p.aux) + (int64_t)m * p.ldc + n)
+                         : make_uint2(0u, 0u);
+      }
+  }
+#pragma unroll
+  for (int pass = 0; pass < NP; ++pass) {
     float4 in[IN ? NG : 1];
-    if constexpr (IN) {
+    if constexpr (PRE) {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {  // bf16 element k sits in the high half of its 32-bit slot
+        const uint2 v = raw[pass][i];
+        in[i] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                            __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+      }
+    } else if constexpr (IN) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const int m = m0 + pass * PASS_ROWS + r0 + i * RSTEP;
