@@ -383,12 +383,13 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
   constexpr int CG = BN / 4;           // column groups per row
   constexpr int RSTEP = 256 / CG;      // rows between a thread's groups
   constexpr int NG = PASS_ROWS / RSTEP;
-  // a thread's NG groups of a pass are unrolled (register budget: NG <= 16), and
-  // every group uses the bias loaded once above: a load inside the group loop
-  // would be waited for after the previous groups' stores, and vmcnt counts
-  // stores too, so each group would wait for the last one's stores to complete
-  constexpr bool UNR = NG <= 16;
-  constexpr bool IN = epi_reads<EPI, SPLIT>() && UNR;
+  // a thread's NG groups of a pass are unrolled and every group uses the bias
+  // loaded once above: a load inside the group loop would be waited for after
+  // the previous groups' stores, and vmcnt counts stores too, so each group
+  // would wait for the last one's stores to complete.  Epilogues that read an
+  // input keep a pass of it in registers, which bounds them to NG <= 16.
+  constexpr bool IN = epi_reads<EPI, SPLIT>() && NG <= 16;
+  constexpr bool UNR = IN || !epi_reads<EPI, SPLIT>();
   static_assert(256 % CG == 0 && PASS_ROWS % RSTEP == 0, "epilogue thread mapping");
   float* st = reinterpret_cast<float*>(smem);
   const int c4 = t % CG, r0 = t / CG;

@@ -26,20 +26,32 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   const int nc = C >> 2;
-  float4 v[MAXV];
-  float s = 0.f;
+  // every load (row, gain, shift) is issued before the first store: a load
+  // issued after a store would wait for it (the vector memory counter counts both)
+  float4 v[MAXV], gv[MAXV], bv[MAXV];
+  int64_t wrow = 0;
+  if constexpr (EMBED) wrow = (int64_t)tok[row] * C;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int j = lane + 64 * i;
     if (j < nc) {
       if constexpr (EMBED) {
-        const float4 a = load4(wte + (int64_t)tok[row] * C + 4 * j);
+        const float4 a = load4(wte + wrow + 4 * j);
         const float4 p = load4(wpe + (int64_t)(row % Tn) * C + 4 * j);
         v[i] = make_float4(a.x + p.x, a.y + p.y, a.z + p.z, a.w + p.w);
-        store4(res0 + (int64_t)row * C + 4 * j, v[i]);
       } else {
         v[i] = load4(x + (int64_t)row * C + 4 * j);
       }
+      gv[i] = load4(g + 4 * j);
+      bv[i] = load4(bb + 4 * j);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nc) {
+      if constexpr (EMBED) store4(res0 + (int64_t)row * C + 4 * j, v[i]);
       s += v[i].x + v[i].y + v[i].z + v[i].w;
     }
   }
@@ -58,7 +70,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
   for (int i = 0; i < MAXV; ++i) {
     const int j = lane + 64 * i;
     if (j < nc) {
-      const float4 gg = load4(g + 4 * j), b4 = load4(bb + 4 * j);
+      const float4 gg = gv[i], b4 = bv[i];
       store4(y + (int64_t)row * C + 4 * j,
              make_float4((v[i].x - mean) * r * gg.x + b4.x, (v[i].y - mean) * r * gg.y + b4.y,
                          (v[i].z - mean) * r * gg.z + b4.z, (v[i].w - mean) * r * gg.w + b4.w));
