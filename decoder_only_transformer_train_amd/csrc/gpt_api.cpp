@@ -246,7 +246,7 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->rsf = cv.take<float>(N * 4);
   x->logits = cv.take<void>(x->Nc * x->ldv * es);
   x->dz2[0] = cv.take<void>(x->Nc * x->ldv * es);
-  x->dz2[1] = cv.take<void>(x->Nc * x->ldv * es);
+  x->dz2[1] = x->N > x->Nc ? cv.take<void>(x->Nc * x->ldv * es) : x->dz2[0];  // a second chunk alternates
   x->tok_loss = cv.take<float>(N * 4);
   x->tok_lse = cv.take<float>(N * 4);
   x->dF = cv.take<float>(N * C * 4);
@@ -315,7 +315,9 @@ void setup_dims(gpt_ctx* x, const gpt_config* c) {
   x->B = c->batch;
   x->N = x->B * x->T;
   x->ldv = align_up(x->Vp, 64);
-  x->Nc = std::min<int64_t>(x->N, 4096);
+  // the head runs as one chunk of all N <= 16384 rows: measured faster than 4096- or
+  // 8192-row chunks (fewer, fuller launches; the dW product overlaps the backward instead)
+  x->Nc = x->N;
   x->tensors = make_tensors(c, &x->P, &x->P_decay);
 }
 
