@@ -374,14 +374,15 @@ __device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 
 // A thread always handles the same 4 columns (256 is a multiple of BN / 4), so
 // its bias is loaded once; the pass's other inputs are loaded before the
 // accumulators are staged, so their latency overlaps the staging.
-template <typename T, int EPI, int SPLIT, int BM, int BN, int PASS_ROWS, typename ACC, int FM, int FN>
+template <typename T, int EPI, int SPLIT, int BM, int BN, int PASS_ROWS, typename ACC, int FM, int FN, int NT = 256,
+          int WCOLS = 2>
 __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN], char* smem, int m0, int n0,
                                              int wm, int wn, int lane, int t) {
   using M_ = Mf<T>;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / 2, WN = BN / WCOLS;  // waves: 2 rows x WCOLS columns of sub-tiles
   constexpr int LDW = BN + 4;
   constexpr int CG = BN / 4;           // column groups per row
-  constexpr int RSTEP = 256 / CG;      // rows between a thread's groups
+  constexpr int RSTEP = NT / CG;       // rows between a thread's groups
   constexpr int NG = PASS_ROWS / RSTEP;
   // a thread's NG groups of a pass are unrolled and every group uses the bias
   // loaded once above: a load inside the group loop would be waited for after
@@ -390,7 +391,7 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
   // input keep a pass of it in registers, which bounds them to NG <= 16.
   constexpr bool IN = epi_reads<EPI, SPLIT>() && NG <= 16;
   constexpr bool UNR = IN || !epi_reads<EPI, SPLIT>();
-  static_assert(256 % CG == 0 && PASS_ROWS % RSTEP == 0, "epilogue thread mapping");
+  static_assert(NT % CG == 0 && PASS_ROWS % RSTEP == 0, "epilogue thread mapping");
   float* st = reinterpret_cast<float*>(smem);
   const int c4 = t % CG, r0 = t / CG;
   const int n = n0 + c4 * 4;
@@ -470,7 +471,7 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
         }
       }
     } else {
-      for (int g = t; g < PASS_ROWS * CG; g += 256) {
+      for (int g = t; g < PASS_ROWS * CG; g += NT) {
         const int r = g / CG, c = g % CG;
         const int m = m0 + pass * PASS_ROWS + r, nn = n0 + c * 4;
         if (m >= p.M || nn >= p.N) continue;
@@ -577,10 +578,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Tile configuration: BM = 256 rows x BN columns, BK k per stage, ST stages,
 // OCC workgroups per CU (the register and LDS budget follow from it).
-template <int BN_, int BK_, int ST_, int OCC_>
+template <int BN_, int BK_, int ST_, int OCC_, int WAVES_ = 4>
 struct DlCfg {
-  static constexpr int BM = 256, BN = BN_, BK = BK_, ST = ST_, OCC = OCC_;
-  static constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32, KSTEPS = BK / 16;
+  static constexpr int BM = 256, BN = BN_, BK = BK_, ST = ST_, OCC = OCC_, WAVES = WAVES_;
+  static constexpr int THREADS = 64 * WAVES, WCOLS = WAVES / 2;
+  static constexpr int WM = BM / 2, WN = BN / WCOLS, FM = WM / 32, FN = WN / 32, KSTEPS = BK / 16;
+  static constexpr int WAVES_PER_SIMD = OCC * WAVES / 4;  // for the launch bounds
 };
 
 // k-contiguous operand rows hold BK * 2 bytes = CPR 16-byte chunks; the chunk
@@ -601,10 +604,11 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, char* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
-template <int TRANS, int ROWS, int BK>
+template <int TRANS, int ROWS, int BK, int WAVES = 4>
 struct DlOperand {
-  static constexpr int BYTES = ROWS * BK * 2;  // per stage
-  static constexpr int NI = BYTES / 1024 / 4;  // load instructions per wave per stage
+  static constexpr int BYTES = ROWS * BK * 2;      // per stage
+  static constexpr int NI = BYTES / 1024 / WAVES;  // load instructions per wave per stage
+  static_assert(NI * 1024 * WAVES == BYTES, "whole load instructions per wave");
   static constexpr int CPR = TRANS ? ROWS / 8 : BK / 8;  // 16-byte chunks per LDS row
   static constexpr int RPI = 64 / CPR;                   // LDS rows per instruction
   uint32_t off[NI];
@@ -681,11 +685,12 @@ __device__ __forceinline__ void wait_tiles(int n) {
 // are the explicit wait and the barrier.
 template <int TA, int TB, typename C, int NL>
 __device__ __forceinline__ void dl_iter(const char* __restrict__ rd, char* __restrict__ wr, int kt, int nk,
-                                        const DlOperand<TA, 256, C::BK>& oa, const DlOperand<TB, C::BN, C::BK>& ob,
+                                        const DlOperand<TA, 256, C::BK, C::WAVES>& oa,
+                                        const DlOperand<TB, C::BN, C::BK, C::WAVES>& ob,
                                         rsrc_t ra, rsrc_t rb, f32x16 (&acc)[C::FM][C::FN], uint4 (&fa)[2][C::FM],
                                         uint4 (&fb)[2][C::FN], int wm, int wn, int w, int lane) {
   constexpr int FM = C::FM, FN = C::FN, ST = C::ST;
-  constexpr int ABYTES = DlOperand<TA, 256, C::BK>::BYTES;
+  constexpr int ABYTES = DlOperand<TA, 256, C::BK, C::WAVES>::BYTES;
   constexpr int NR = (TA ? 2 : 1) * FM + (TB ? 2 : 1) * FN;  // LDS read instructions per k-step
   wait_tiles<NL>(min(ST - 2, nk - 1 - kt));
   __syncthreads();
@@ -714,11 +719,11 @@ __device__ __forceinline__ void dl_iter(const char* __restrict__ rd, char* __res
 }
 
 template <int TA, int TB, int EPI, int SPLIT, typename C>
-__global__ __launch_bounds__(256, C::OCC) void gemm_dl_kernel(Params p) {
+__global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void gemm_dl_kernel(Params p) {
   typedef bf16 T;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN, ST = C::ST;
-  using OA = DlOperand<TA, BM, BK>;
-  using OB = DlOperand<TB, BN, BK>;
+  using OA = DlOperand<TA, BM, BK, C::WAVES>;
+  using OB = DlOperand<TB, BN, BK, C::WAVES>;
   constexpr int STAGE = OA::BYTES + OB::BYTES;
   constexpr int NL = OA::NI + OB::NI;
   constexpr int EPI_BYTES = 128 * (BN + 4) * 4;
@@ -727,7 +732,7 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_dl_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / C::WCOLS, wn = w % C::WCOLS;
   int tm, tn, kz;
   tile_coords(p, tm, tn, kz);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -774,7 +779,8 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_dl_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) Mf<bf16>::mma(acc[i][j], fa[1][i], fb[1][j]);
   __syncthreads();
-  epilogue_lds<T, EPI, SPLIT, BM, BN, 128>(pe, acc, smem, m0, n0, wm, wn, lane, t);
+  epilogue_lds<T, EPI, SPLIT, BM, BN, 128, f32x16, FM, FN, C::THREADS, C::WCOLS>(pe, acc, smem, m0, n0, wm, wn,
+                                                                                lane, t);
 }
 
 }  // namespace dl
@@ -803,7 +809,7 @@ hipError_t launch(const Params& p, int splits, hipStream_t s) {
 template <int TA, int TB, int EPI, int SPLIT, typename C>
 hipError_t launch_dl(const Params& p, int splits, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n * splits);
-  hipLaunchKernelGGL((gemm_dl_kernel<TA, TB, EPI, SPLIT, C>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_dl_kernel<TA, TB, EPI, SPLIT, C>), grid, dim3(C::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
@@ -812,6 +818,7 @@ hipError_t launch_tile(const Params& p, int tile, int splits, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     if (tile == 0) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<128, 32, 3, 2>>(p, splits, s);
     if (tile == 1) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1>>(p, splits, s);
+    if (tile == 3) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1, 8>>(p, splits, s);
   }
   return launch<T, TA, TB, EPI, SPLIT, 128, 128>(p, splits, s);
 }
@@ -838,23 +845,28 @@ hipError_t dispatch(const Gemm& g, const Params& p, int tile, int splits, hipStr
 }
 
 // tiles: 0 = bf16 256x128 direct-load (2 per CU), 1 = bf16 256x256 direct-load
-// (BK 64, 1 per CU), 2 = 128x128 register-staged (fp32 and the fallback)
-constexpr int TILE_BM[3] = {256, 256, 128};
-constexpr int TILE_BN[3] = {128, 256, 128};
+// (BK 64, 1 per CU), 2 = 128x128 register-staged (fp32 and the fallback),
+// 3 = bf16 256x256 direct-load with 8 waves (two per SIMD, so one issues its
+// loads while the other keeps the MFMA pipe busy; BK 64, 1 per CU)
+constexpr int TILE_BM[4] = {256, 256, 128, 256};
+constexpr int TILE_BN[4] = {128, 256, 128, 256};
 
 // Tile and K-split choice from measurements of the step's shapes on MI355X:
-// the 256x128 direct-load kernel (two workgroups per CU, so one's epilogue
-// overlaps the other's main loop) wins almost everywhere; the 256x256 BK-64
-// kernel wins for very large outputs and for long-K products whose A is
-// k-contiguous.  Split-K (fp32 outputs only) takes the largest split count that
-// keeps one round of workgroups (2 or 1 per CU) with at least 512 k per split.
+// the 8-wave 256x256 kernel for the forward products with k-contiguous
+// operands (fc, QKV, MLP projection, LM-head logits: the forward runs alone, so
+// holding a CU's LDS costs no other stream anything); the 256x256 4-wave kernel
+// for long-K products whose A is k-contiguous (LM-head data gradient); the
+// 256x128 kernel (two workgroups per CU, so one's epilogue overlaps the other's
+// main loop) for the rest.  Split-K (fp32 outputs only) takes the largest split
+// count that keeps one round of workgroups (2 or 1 per CU) with at least 512 k
+// per split.
 void choose(int M, int N, int K, bool can_split, int dtype, int a_trans, int b_trans, int* tile_out,
             int* splits_out) {
-  (void)b_trans;
   int tile = 2;
   if (dtype == BF16) {
-    const int64_t t256 = (int64_t)cdiv(M, 256) * cdiv(N, 256);
-    tile = (t256 >= 1024 || (K >= 16384 && !a_trans)) ? 1 : 0;
+    if (!a_trans && !b_trans && K <= 3072 && (N >= 2048 || K >= 3072)) tile = 3;
+    else if (K >= 16384 && !a_trans) tile = 1;
+    else tile = 0;
   }
   int splits = 1;
   if (can_split) {
@@ -879,7 +891,7 @@ int gemm_pick_splits(int M, int N, int K, int a_trans, int b_trans) {
 static int forced_tile() {
   static const int v = [] {
     const char* e = getenv("GPT_GEMM_TILE");
-    return (e && e[0] >= '0' && e[0] <= '2') ? e[0] - '0' : -1;
+    return (e && e[0] >= '0' && e[0] <= '3') ? e[0] - '0' : -1;
   }();
   return v;
 }
