@@ -852,22 +852,18 @@ constexpr int TILE_BM[4] = {256, 256, 128, 256};
 constexpr int TILE_BN[4] = {128, 256, 128, 256};
 
 // Tile and K-split choice from measurements of the step's shapes on MI355X:
-// the 8-wave 256x256 kernel for the forward products with k-contiguous
-// operands (fc, QKV, MLP projection, LM-head logits: the forward runs alone, so
-// holding a CU's LDS costs no other stream anything); the 256x256 4-wave kernel
-// for long-K products whose A is k-contiguous (LM-head data gradient); the
-// 256x128 kernel (two workgroups per CU, so one's epilogue overlaps the other's
-// main loop) for the rest.  Split-K (fp32 outputs only) takes the largest split
-// count that keeps one round of workgroups (2 or 1 per CU) with at least 512 k
-// per split.
+// the 8-wave 256x256 kernel for every bf16 product.  Same-box step A/B against
+// the 256x128 kernel (two workgroups per CU) and the 4-wave 256x256 kernel:
+// forward products -0.28 ms, data gradients -0.2, weight gradients -0.3, the
+// LM-head data gradient and the attention projection -0.1 each.  Tiles 0 and 1
+// stay selectable for tuning runs.  Split-K (fp32 outputs only) takes the
+// largest split count that keeps one round of workgroups (2 or 1 per CU) with
+// at least 512 k per split.
 void choose(int M, int N, int K, bool can_split, int dtype, int a_trans, int b_trans, int* tile_out,
             int* splits_out) {
-  int tile = 2;
-  if (dtype == BF16) {
-    if (!a_trans && !b_trans && K <= 3072 && (N >= 2048 || K >= 3072)) tile = 3;
-    else if (K >= 16384 && !a_trans) tile = 1;
-    else tile = 0;
-  }
+  (void)a_trans;
+  (void)b_trans;
+  const int tile = dtype == BF16 ? 3 : 2;
   int splits = 1;
   if (can_split) {
     const int64_t tiles = (int64_t)cdiv(M, TILE_BM[tile]) * cdiv(N, TILE_BN[tile]);
