@@ -90,99 +90,83 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 // bias gradient of the linear layer that feeds this residual stream).
 constexpr int LNB_ROWS = 32;
 
-template <typename TY, typename T, int NV>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(const TY* __restrict__ dy, const float* __restrict__ x,
-                                                     const float* __restrict__ mu, const float* __restrict__ rs,
-                                                     const float* __restrict__ g, const float* dres_in,
-                                                     float* dres_out, T* __restrict__ dres_T,
-                                                     float* __restrict__ part, int rows, int C) {
+// One wave takes one row at a time with no prefetch of the next, and x-hat and
+// dy*g are recomputed for the output instead of kept: the kernel stays within
+// 120 VGPRs, so one of its workgroups fits on a CU beside an 8-wave GEMM
+// workgroup (2 x 196 VGPRs per SIMD) of the other stream; with the prefetch
+// (182 VGPRs) it waited for whole GEMM workgroups to finish.  A lane past the row
+// (C not a multiple of 256) loads the last column slice and drops it.
+template <typename TY, typename T, int NV, bool DRES>
+__global__ __launch_bounds__(256, 4) void ln_bwd_kernel(const TY* __restrict__ dy, const float* __restrict__ x,
+                                                         const float* __restrict__ mu, const float* __restrict__ rs,
+                                                         const float* __restrict__ g, const float* __restrict__ dres_in,
+                                                         float* __restrict__ dres_out, T* __restrict__ dres_T,
+                                                         float* __restrict__ part, int rows, int C) {
   __shared__ float red[4][NV * 256];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nc = C >> 2;
-  float4 pg[NV], pb[NV], pc[NV], gv[NV];
+  int jj[NV];
+  bool ok[NV];
+  float4 pg[NV], pb[NV], pc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    pg[i] = pb[i] = pc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     const int j = lane + 64 * i;
-    gv[i] = j < nc ? load4(g + 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
+    ok[i] = j < nc;
+    jj[i] = ok[i] ? j : nc - 1;
+    pg[i] = pb[i] = pc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const int r0 = blockIdx.x * LNB_ROWS;
-  // a wave's rows are r0 + w, r0 + w + 4, ...: the next row's x, dy and
-  // incoming residual gradient are loaded before this row's reductions
-  float4 xa[NV], da[NV], qa[NV];
-  auto load_row = [&](int row, float4 (&xv)[NV], float4 (&dv)[NV], float4 (&qv)[NV]) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int j = lane + 64 * i;
-      if (j < nc) {
-        const int64_t o = (int64_t)row * C + 4 * j;
-        xv[i] = load4(x + o);
-        dv[i] = load4(dy + o);
-        qv[i] = dres_in ? load4(dres_in + o) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-  };
-  if (r0 + w < rows) load_row(r0 + w, xa, da, qa);
-#pragma unroll
   for (int k = 0; k < LNB_ROWS / 4; ++k) {
     const int row = r0 + w + 4 * k;
     if (row >= rows) break;
-    float4 xb[NV], db[NV], qb[NV];
-    const bool more = k + 1 < LNB_ROWS / 4 && row + 4 < rows;
-    if (more) load_row(row + 4, xb, db, qb);
+    float4 xv[NV], dv[NV], gv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int64_t o = (int64_t)row * C + 4 * jj[i];
+      xv[i] = load4(x + o);
+      dv[i] = load4(dy + o);
+      gv[i] = load4(g + 4 * jj[i]);
+    }
     const float m = mu[row], r = rs[row];
-    float4 xh[NV], dxh[NV];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int j = lane + 64 * i;
-      if (j < nc) {
-        const float4 xv = xa[i], d = da[i], gg = gv[i];
-        xh[i] = make_float4((xv.x - m) * r, (xv.y - m) * r, (xv.z - m) * r, (xv.w - m) * r);
-        dxh[i] = make_float4(d.x * gg.x, d.y * gg.y, d.z * gg.z, d.w * gg.w);
-        s1 += dxh[i].x + dxh[i].y + dxh[i].z + dxh[i].w;
-        s2 += dxh[i].x * xh[i].x + dxh[i].y * xh[i].y + dxh[i].z * xh[i].z + dxh[i].w * xh[i].w;
-        pg[i].x += d.x * xh[i].x; pg[i].y += d.y * xh[i].y; pg[i].z += d.z * xh[i].z; pg[i].w += d.w * xh[i].w;
-        pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
-      }
+      if (!ok[i]) { dv[i] = make_float4(0.f, 0.f, 0.f, 0.f); }
+      const float4 xq = xv[i], d = dv[i], gg = gv[i];
+      const float4 xh = make_float4((xq.x - m) * r, (xq.y - m) * r, (xq.z - m) * r, (xq.w - m) * r);
+      const float4 dxh = make_float4(d.x * gg.x, d.y * gg.y, d.z * gg.z, d.w * gg.w);
+      s1 += dxh.x + dxh.y + dxh.z + dxh.w;
+      s2 += dxh.x * xh.x + dxh.y * xh.y + dxh.z * xh.z + dxh.w * xh.w;
+      pg[i].x += d.x * xh.x; pg[i].y += d.y * xh.y; pg[i].z += d.z * xh.z; pg[i].w += d.w * xh.w;
+      pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
     }
     const float m1 = wave_sum(s1) / C, m2 = wave_sum(s2) / C;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int j = lane + 64 * i;
-      if (j < nc) {
-        const int64_t o = (int64_t)row * C + 4 * j;
-        const float4 prev = qa[i];
-        const float4 out = make_float4(prev.x + r * (dxh[i].x - m1 - xh[i].x * m2),
-                                       prev.y + r * (dxh[i].y - m1 - xh[i].y * m2),
-                                       prev.z + r * (dxh[i].z - m1 - xh[i].z * m2),
-                                       prev.w + r * (dxh[i].w - m1 - xh[i].w * m2));
+      const int64_t o = (int64_t)row * C + 4 * jj[i];
+      const float4 xq = xv[i], d = dv[i], gg = gv[i];
+      const float4 prev = DRES ? load4(dres_in + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 xh = make_float4((xq.x - m) * r, (xq.y - m) * r, (xq.z - m) * r, (xq.w - m) * r);
+      const float4 dxh = make_float4(d.x * gg.x, d.y * gg.y, d.z * gg.z, d.w * gg.w);
+      const float4 out = make_float4(prev.x + r * (dxh.x - m1 - xh.x * m2), prev.y + r * (dxh.y - m1 - xh.y * m2),
+                                     prev.z + r * (dxh.z - m1 - xh.z * m2), prev.w + r * (dxh.w - m1 - xh.w * m2));
+      if (ok[i]) {
         store4(dres_out + o, out);
         store4(dres_T + o, out);
         pc[i].x += out.x; pc[i].y += out.y; pc[i].z += out.z; pc[i].w += out.w;
       }
     }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        xa[i] = xb[i];
-        da[i] = db[i];
-        qa[i] = qb[i];
-      }
-    }
   }
-  // the 4 waves' partials, added in wave order, one quantity at a time
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    if (k) __syncthreads();
+  for (int q = 0; q < 3; ++q) {
+    if (q) __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int j = lane + 64 * i;
-      if (j < nc) *reinterpret_cast<float4*>(&red[w][4 * j]) = k == 0 ? pg[i] : (k == 1 ? pb[i] : pc[i]);
-    }
+    for (int i = 0; i < NV; ++i)
+      if (ok[i]) *reinterpret_cast<float4*>(&red[w][4 * (lane + 64 * i)]) = q == 0 ? pg[i] : (q == 1 ? pb[i] : pc[i]);
     __syncthreads();
     for (int c = threadIdx.x; c < C; c += 256)
-      part[(int64_t)blockIdx.x * 3 * C + k * C + c] = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+      part[(int64_t)blockIdx.x * 3 * C + q * C + c] = red[0][c] + red[1][c] + red[2][c] + red[3][c];
   }
 }
 
@@ -497,20 +481,29 @@ hipError_t embed_ln_fwd(int dtype, const int32_t* tok, const float* wte, const f
 
 int layernorm_bwd_blocks(int rows) { return cdiv(rows, LNB_ROWS); }
 
+template <int NV, bool DRES>
+hipError_t ln_bwd_nvd(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu, const float* rstd,
+                      const float* g, const float* dres_in, float* dres_out, void* dres_T, float* part, int rows,
+                      int C, int nblk, hipStream_t s) {
+  if (dtype == BF16 && dy_is_t)
+    hipLaunchKernelGGL((ln_bwd_kernel<bf16, bf16, NV, DRES>), dim3(nblk), dim3(256), 0, s, (const bf16*)dy, x, mu,
+                       rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, C);
+  else if (dtype == BF16)
+    hipLaunchKernelGGL((ln_bwd_kernel<float, bf16, NV, DRES>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu,
+                       rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, C);
+  else
+    hipLaunchKernelGGL((ln_bwd_kernel<float, float, NV, DRES>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu,
+                       rstd, g, dres_in, dres_out, (float*)dres_T, part, rows, C);
+  return hipGetLastError();
+}
 template <int NV>
 hipError_t ln_bwd_nv(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu, const float* rstd,
                      const float* g, const float* dres_in, float* dres_out, void* dres_T, float* part, int rows,
                      int C, int nblk, hipStream_t s) {
-  if (dtype == BF16 && dy_is_t)
-    hipLaunchKernelGGL((ln_bwd_kernel<bf16, bf16, NV>), dim3(nblk), dim3(256), 0, s, (const bf16*)dy, x, mu, rstd,
-                       g, dres_in, dres_out, (bf16*)dres_T, part, rows, C);
-  else if (dtype == BF16)
-    hipLaunchKernelGGL((ln_bwd_kernel<float, bf16, NV>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu,
-                       rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, C);
-  else
-    hipLaunchKernelGGL((ln_bwd_kernel<float, float, NV>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu,
-                       rstd, g, dres_in, dres_out, (float*)dres_T, part, rows, C);
-  return hipGetLastError();
+  return dres_in ? ln_bwd_nvd<NV, true>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C,
+                                        nblk, s)
+                 : ln_bwd_nvd<NV, false>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C,
+                                         nblk, s);
 }
 
 hipError_t layernorm_bwd(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu,
