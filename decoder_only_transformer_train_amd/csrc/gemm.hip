@@ -369,21 +369,26 @@ __device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 
   }
 }
 
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+
 // Stage acc through LDS (smem, at least PASS_ROWS * (BN + 4) floats) and run
 // the epilogue.  Waves whose sub-tile rows fall in the current pass write.
-// A thread always handles the same 4 columns (256 is a multiple of BN / 4), so
-// its bias is loaded once; the pass's other inputs are loaded before the
-// accumulators are staged, so their latency overlaps the staging.
+// Thread t handles the column groups g = t + i * NT of a pass (row g / CG,
+// 4 columns at 4 * (g % CG)).  Its groups cycle through NCOL column positions
+// (one when NT is a multiple of CG), whose bias is loaded once; the pass's
+// other inputs are loaded before the accumulators are staged, so their latency
+// overlaps the staging.
 template <typename T, int EPI, int SPLIT, int BM, int BN, int PASS_ROWS, typename ACC, int FM, int FN, int NT = 256,
           int WCOLS = 2>
 __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN], char* smem, int m0, int n0,
                                              int wm, int wn, int lane, int t) {
   using M_ = Mf<T>;
-  constexpr int WM = BM / 2, WN = BN / WCOLS;  // waves: 2 rows x WCOLS columns of sub-tiles
+  constexpr int WROWS = NT / 64 / WCOLS;  // waves: WROWS rows x WCOLS columns of sub-tiles
+  constexpr int WM = BM / WROWS, WN = BN / WCOLS;
   constexpr int LDW = BN + 4;
-  constexpr int CG = BN / 4;           // column groups per row
-  constexpr int RSTEP = NT / CG;       // rows between a thread's groups
-  constexpr int NG = PASS_ROWS / RSTEP;
+  constexpr int CG = BN / 4;                     // column groups per row
+  constexpr int NG = PASS_ROWS * CG / NT;        // a thread's groups per pass
+  constexpr int NCOL = CG / gcd_c(NT % CG, CG);  // distinct column positions of a thread
   // a thread's NG groups of a pass are unrolled and every group uses the bias
   // loaded once above: a load inside the group loop would be waited for after
   // the previous groups' stores, and vmcnt counts stores too, so each group
@@ -391,15 +396,23 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
   // input keep a pass of it in registers, which bounds them to NG <= 16.
   constexpr bool IN = epi_reads<EPI, SPLIT>() && NG <= 16;
   constexpr bool UNR = IN || !epi_reads<EPI, SPLIT>();
-  static_assert(NT % CG == 0 && PASS_ROWS % RSTEP == 0, "epilogue thread mapping");
+  static_assert((PASS_ROWS * CG) % NT == 0 && WROWS * WCOLS * 64 == NT, "epilogue thread mapping");
   float* st = reinterpret_cast<float*>(smem);
-  const int c4 = t % CG, r0 = t / CG;
-  const int n = n0 + c4 * 4;
-  const bool full = n + 3 < p.N && (SPLIT || (p.ldc & 3) == 0);
+  // group i's row in the pass and its column position (index i % NCOL)
+  auto row_of = [&](int i) { return NCOL == 1 ? t / CG + i * (NT / CG) : (t + i * NT) / CG; };
+  int c4[NCOL], n[NCOL];
+  bool full[NCOL];
+  float4 b4[NCOL];
+#pragma unroll
+  for (int j = 0; j < NCOL; ++j) {
+    c4[j] = (t + j * NT) % CG;
+    n[j] = n0 + c4[j] * 4;
+    full[j] = n[j] + 3 < p.N && (SPLIT || (p.ldc & 3) == 0);
+    b4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!SPLIT && full[j] && p.bias) b4[j] = *reinterpret_cast<const float4*>(p.bias + n[j]);
+  }
   // the whole tile inside the output, every group 16-byte aligned
   const bool tile_full = m0 + BM <= p.M && n0 + BN <= p.N && (SPLIT ? (p.N & 3) == 0 : (p.ldc & 3) == 0);
-  float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (!SPLIT && full && p.bias) b4 = *reinterpret_cast<const float4*>(p.bias + n);
   // A 16-bit input (the GELU derivative) is loaded for every pass before the
   // first store, kept as raw bf16 pairs (as many registers as one pass of
   // floats): a later pass's loads would otherwise wait for the earlier passes'
@@ -412,10 +425,10 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
     for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
-        const int m = m0 + ps * PASS_ROWS + r0 + i * RSTEP;
-        raw[ps][i] = (full && m < p.M)
-                         ? *reinterpret_cast<const uint2*>(reinterpret_cast<const T*>(p.aux) + (int64_t)m * p.ldc + n)
-                         : make_uint2(0u, 0u);
+        const int m = m0 + ps * PASS_ROWS + row_of(i), j = i % NCOL;
+        raw[ps][i] = (full[j] && m < p.M) ? *reinterpret_cast<const uint2*>(reinterpret_cast<const T*>(p.aux) +
+                                                                            (int64_t)m * p.ldc + n[j])
+                                          : make_uint2(0u, 0u);
       }
   }
 #pragma unroll
@@ -431,8 +444,9 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
     } else if constexpr (IN) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
-        const int m = m0 + pass * PASS_ROWS + r0 + i * RSTEP;
-        in[i] = (full && m < p.M) ? epi_load<T, EPI, SPLIT>(p, (int64_t)m * p.ldc + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int m = m0 + pass * PASS_ROWS + row_of(i), j = i % NCOL;
+        in[i] = (full[j] && m < p.M) ? epi_load<T, EPI, SPLIT>(p, (int64_t)m * p.ldc + n[j])
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
     __syncthreads();
@@ -453,21 +467,22 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
       if (tile_full) {  // no loads among the stores: nothing makes a group wait for earlier stores
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
-          const int r = r0 + i * RSTEP;
+          const int r = row_of(i), j = i % NCOL;
           float4 x_in = make_float4(0.f, 0.f, 0.f, 0.f);
           if constexpr (IN) x_in = in[i];
-          epi_group_full<T, EPI, SPLIT>(p, m0 + pass * PASS_ROWS + r, n,
-                                        *reinterpret_cast<const float4*>(st + r * LDW + c4 * 4), x_in, b4);
+          epi_group_full<T, EPI, SPLIT>(p, m0 + pass * PASS_ROWS + r, n[j],
+                                        *reinterpret_cast<const float4*>(st + r * LDW + c4[j] * 4), x_in, b4[j]);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
-          const int r = r0 + i * RSTEP;
+          const int r = row_of(i), j = i % NCOL;
           const int m = m0 + pass * PASS_ROWS + r;
-          if (m >= p.M || n >= p.N) continue;
+          if (m >= p.M || n[j] >= p.N) continue;
           float4 x_in = make_float4(0.f, 0.f, 0.f, 0.f);
           if constexpr (IN) x_in = in[i];
-          epi_group<T, EPI, SPLIT>(p, m, n, *reinterpret_cast<const float4*>(st + r * LDW + c4 * 4), full, x_in, b4);
+          epi_group<T, EPI, SPLIT>(p, m, n[j], *reinterpret_cast<const float4*>(st + r * LDW + c4[j] * 4), full[j],
+                                   x_in, b4[j]);
         }
       }
     } else {
@@ -578,11 +593,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Tile configuration: BM = 256 rows x BN columns, BK k per stage, ST stages,
 // OCC workgroups per CU (the register and LDS budget follow from it).
-template <int BN_, int BK_, int ST_, int OCC_, int WAVES_ = 4>
+template <int BN_, int BK_, int ST_, int OCC_, int WAVES_ = 4, int WROWS_ = 2>
 struct DlCfg {
-  static constexpr int BM = 256, BN = BN_, BK = BK_, ST = ST_, OCC = OCC_, WAVES = WAVES_;
-  static constexpr int THREADS = 64 * WAVES, WCOLS = WAVES / 2;
-  static constexpr int WM = BM / 2, WN = BN / WCOLS, FM = WM / 32, FN = WN / 32, KSTEPS = BK / 16;
+  static constexpr int BM = 256, BN = BN_, BK = BK_, ST = ST_, OCC = OCC_, WAVES = WAVES_, WROWS = WROWS_;
+  static constexpr int THREADS = 64 * WAVES, WCOLS = WAVES / WROWS;
+  static constexpr int WM = BM / WROWS, WN = BN / WCOLS, FM = WM / 32, FN = WN / 32, KSTEPS = BK / 16;
+  static_assert(FM * 32 * WROWS == BM && FN * 32 * WCOLS == BN, "whole 32x32 MFMA tiles per wave");
   static constexpr int WAVES_PER_SIMD = OCC * WAVES / 4;  // for the launch bounds
 };
 
@@ -819,6 +835,9 @@ hipError_t launch_tile(const Params& p, int tile, int splits, hipStream_t s) {
     if (tile == 0) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<128, 32, 3, 2>>(p, splits, s);
     if (tile == 1) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1>>(p, splits, s);
     if (tile == 3) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1, 8>>(p, splits, s);
+    if constexpr (TB == 0) {
+      if (tile == 4) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<192, 64, 2, 1, 8, 4>>(p, splits, s);
+    }
   }
   return launch<T, TA, TB, EPI, SPLIT, 128, 128>(p, splits, s);
 }
@@ -847,12 +866,16 @@ hipError_t dispatch(const Gemm& g, const Params& p, int tile, int splits, hipStr
 // tiles: 0 = bf16 256x128 direct-load (2 per CU), 1 = bf16 256x256 direct-load
 // (BK 64, 1 per CU), 2 = 128x128 register-staged (fp32 and the fallback),
 // 3 = bf16 256x256 direct-load with 8 waves (two per SIMD, so one issues its
-// loads while the other keeps the MFMA pipe busy; BK 64, 1 per CU)
-constexpr int TILE_BM[4] = {256, 256, 128, 256};
-constexpr int TILE_BN[4] = {128, 256, 128, 256};
+// loads while the other keeps the MFMA pipe busy; BK 64, 1 per CU), 4 = the
+// same with 192 columns (waves 4 x 2, k-contiguous B only): N = 768 products
+// of 16384 rows make 256 tiles, one per CU, instead of 192
+constexpr int TILE_BM[5] = {256, 256, 128, 256, 256};
+constexpr int TILE_BN[5] = {128, 256, 128, 256, 192};
 
 // Tile and K-split choice from measurements of the step's shapes on MI355X:
-// the 8-wave 256x256 kernel for every bf16 product.  Same-box step A/B against
+// the 8-wave 256x256 kernel for every bf16 product, or its 192-column variant
+// where that fills the CUs better (forward products with N = 768: -10 to -12%
+// alone; QKV, N = 2304: -4 to -12%).  Same-box step A/B against
 // the 256x128 kernel (two workgroups per CU) and the 4-wave 256x256 kernel:
 // forward products -0.28 ms, data gradients -0.2, weight gradients -0.3, the
 // LM-head data gradient and the attention projection -0.1 each.  Tiles 0 and 1
@@ -862,8 +885,14 @@ constexpr int TILE_BN[4] = {128, 256, 128, 256};
 void choose(int M, int N, int K, bool can_split, int dtype, int a_trans, int b_trans, int* tile_out,
             int* splits_out) {
   (void)a_trans;
-  (void)b_trans;
-  const int tile = dtype == BF16 ? 3 : 2;
+  int tile = dtype == BF16 ? 3 : 2;
+  // the 192-column tile where it needs at least 10% fewer tile-columns x rounds
+  // of one workgroup per CU (N = 768: 256 tiles in one round instead of 192;
+  // N = 2304: 768 tiles in three rounds instead of 576 in three)
+  if (tile == 3 && !b_trans && !can_split) {
+    const int64_t r3 = cdiv(cdiv(M, 256) * cdiv(N, 256), 256), r4 = cdiv(cdiv(M, 256) * cdiv(N, 192), 256);
+    if (r4 * 192 * 10 < r3 * 256 * 9) tile = 4;
+  }
   int splits = 1;
   if (can_split) {
     const int64_t tiles = (int64_t)cdiv(M, TILE_BM[tile]) * cdiv(N, TILE_BN[tile]);
@@ -883,11 +912,11 @@ int gemm_pick_splits(int M, int N, int K, int a_trans, int b_trans) {
   return splits;
 }
 
-// GPT_GEMM_TILE=0|1|2 pins the tile (256x256, 256x128, 128x128) for tuning runs.
+// GPT_GEMM_TILE=0..4 pins the tile (TILE_BM x TILE_BN) for tuning runs.
 static int forced_tile() {
   static const int v = [] {
     const char* e = getenv("GPT_GEMM_TILE");
-    return (e && e[0] >= '0' && e[0] <= '3') ? e[0] - '0' : -1;
+    return (e && e[0] >= '0' && e[0] <= '4') ? e[0] - '0' : -1;
   }();
   return v;
 }
@@ -898,6 +927,7 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
   int tile = 2, splits = 1;
   choose(g.M, g.N, g.K, can_split, g.dtype, g.a_trans, g.b_trans, &tile, &splits);
   if (forced_tile() >= 0 && g.dtype == BF16) tile = forced_tile();
+  if (tile == 4 && (g.b_trans || can_split)) tile = 3;  // the 192-column tile reads k-contiguous B only
   // direct-to-LDS loads move 16-byte chunks: rows of other strides take the register-staged kernel
   if (tile != 2 && ((g.lda & 7) || (g.ldb & 7) || ((uintptr_t)g.A & 15) || ((uintptr_t)g.B & 15))) tile = 2;
   if (can_split) splits = std::min(splits, g.splits);
