@@ -611,8 +611,15 @@ __device__ __forceinline__ int swz_nt(int row) {
   else return (row >> 1) & 7;
 }
 // row-contiguous operands: k-row kr's chunks are XOR-permuted so the 4 k-rows
-// a transpose read pass touches do not stack on the same banks
-__device__ __forceinline__ int swz_t(int kr) { return ((kr & 3) << 1) | ((kr & 1) << 3); }
+// a transpose read pass touches do not stack on the same banks.  Rows of 24
+// chunks (192 columns) already alternate between the two 128-byte halves of
+// the banks from one k-row to the next; k-rows two apart are moved by 64
+// bytes, an XOR below 8 so every chunk stays inside the row.
+template <int CPR>
+__device__ __forceinline__ int swz_t(int kr) {
+  if constexpr (CPR == 24) return ((kr >> 1) & 1) << 2;
+  else return ((kr & 3) << 1) | ((kr & 1) << 3);
+}
 
 // one wave instruction: lane i's 16 bytes at voff land at lds + 16 i (kept out of
 // templates: host-side template instantiation drops kernels that call it directly)
@@ -626,20 +633,22 @@ struct DlOperand {
   static constexpr int NI = BYTES / 1024 / WAVES;  // load instructions per wave per stage
   static_assert(NI * 1024 * WAVES == BYTES, "whole load instructions per wave");
   static constexpr int CPR = TRANS ? ROWS / 8 : BK / 8;  // 16-byte chunks per LDS row
-  static constexpr int RPI = 64 / CPR;                   // LDS rows per instruction
+  static_assert(TRANS ? (CPR == 24 || (CPR >= 16 && (CPR & (CPR - 1)) == 0)) : (CPR == 4 || CPR == 8),
+                "chunk permutations stay inside the row");
   uint32_t off[NI];
   uint32_t kstep;  // bytes per BK of k
   __device__ __forceinline__ void init(int64_t ld, int row0, int kb0, int w, int lane) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int inst = w * NI + i;
-      const int r = inst * RPI + lane / CPR;
+      // the instruction's lane writes LDS chunk q: row q / CPR, position q % CPR
+      const int q = (w * NI + i) * 64 + lane;
+      const int r = q / CPR, cq = q % CPR;
       int64_t e;
       if constexpr (TRANS == 0) {
-        const int c = (lane % CPR) ^ swz_nt<CPR>(r);
+        const int c = cq ^ swz_nt<CPR>(r);
         e = (int64_t)(row0 + r) * ld + kb0 + c * 8;
       } else {
-        const int c = (lane % CPR) ^ swz_t(r);
+        const int c = cq ^ swz_t<CPR>(r);
         e = (int64_t)(kb0 + r) * ld + row0 + c * 8;
       }
       off[i] = (uint32_t)(e * 2);
@@ -661,8 +670,8 @@ struct DlOperand {
       const int mm = rb + 16 * (g & 1) + 4 * (s & 3);
       const int kr0 = ks * 16 + 8 * (g >> 1) + (s >> 2);
       const int c = mm >> 3, sub = (mm & 7) * 2;
-      const char* p0 = lds + kr0 * (ROWS * 2) + ((c ^ swz_t(kr0)) * 16) + sub;
-      const char* p1 = lds + (kr0 + 4) * (ROWS * 2) + ((c ^ swz_t(kr0 + 4)) * 16) + sub;
+      const char* p0 = lds + kr0 * (ROWS * 2) + ((c ^ swz_t<CPR>(kr0)) * 16) + sub;
+      const char* p1 = lds + (kr0 + 4) * (ROWS * 2) + ((c ^ swz_t<CPR>(kr0 + 4)) * 16) + sub;
       v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
       v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p1);
       uint2 a = bitcast<uint2>(lo), b = bitcast<uint2>(hi);
@@ -835,7 +844,7 @@ hipError_t launch_tile(const Params& p, int tile, int splits, hipStream_t s) {
     if (tile == 0) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<128, 32, 3, 2>>(p, splits, s);
     if (tile == 1) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1>>(p, splits, s);
     if (tile == 3) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1, 8>>(p, splits, s);
-    if constexpr (TB == 0) {
+    if constexpr (!SPLIT) {
       if (tile == 4) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<192, 64, 2, 1, 8, 4>>(p, splits, s);
     }
   }
@@ -867,7 +876,7 @@ hipError_t dispatch(const Gemm& g, const Params& p, int tile, int splits, hipStr
 // (BK 64, 1 per CU), 2 = 128x128 register-staged (fp32 and the fallback),
 // 3 = bf16 256x256 direct-load with 8 waves (two per SIMD, so one issues its
 // loads while the other keeps the MFMA pipe busy; BK 64, 1 per CU), 4 = the
-// same with 192 columns (waves 4 x 2, k-contiguous B only): N = 768 products
+// same with 192 columns (waves 4 x 2): N = 768 products
 // of 16384 rows make 256 tiles, one per CU, instead of 192
 constexpr int TILE_BM[5] = {256, 256, 128, 256, 256};
 constexpr int TILE_BN[5] = {128, 256, 128, 256, 192};
@@ -888,8 +897,13 @@ void choose(int M, int N, int K, bool can_split, int dtype, int a_trans, int b_t
   int tile = dtype == BF16 ? 3 : 2;
   // the 192-column tile where it needs at least 10% fewer tile-columns x rounds
   // of one workgroup per CU (N = 768: 256 tiles in one round instead of 192;
-  // N = 2304: 768 tiles in three rounds instead of 576 in three)
-  if (tile == 3 && !b_trans && !can_split) {
+  // N = 2304: 768 tiles in three rounds instead of 576 in three).  Forward
+  // (k-contiguous B) products only: the N = 768 data gradients are 10-17%
+  // faster alone with it, but the step was not (same box, 3 x 20 steps: layer
+  // data gradients +0.02 ms, LM-head data gradient +0.2 ms), since the 192
+  // tiles of the 256-column kernel leave 64 CUs to the weight gradients that
+  // run beside them on the second stream.
+  if (tile == 3 && !can_split && !b_trans) {
     const int64_t r3 = cdiv(cdiv(M, 256) * cdiv(N, 256), 256), r4 = cdiv(cdiv(M, 256) * cdiv(N, 192), 256);
     if (r4 * 192 * 10 < r3 * 256 * 9) tile = 4;
   }
@@ -927,7 +941,7 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
   int tile = 2, splits = 1;
   choose(g.M, g.N, g.K, can_split, g.dtype, g.a_trans, g.b_trans, &tile, &splits);
   if (forced_tile() >= 0 && g.dtype == BF16) tile = forced_tile();
-  if (tile == 4 && (g.b_trans || can_split)) tile = 3;  // the 192-column tile reads k-contiguous B only
+  if (tile == 4 && can_split) tile = 3;  // split-K products keep the 256-column tile
   // direct-to-LDS loads move 16-byte chunks: rows of other strides take the register-staged kernel
   if (tile != 2 && ((g.lda & 7) || (g.ldb & 7) || ((uintptr_t)g.A & 15) || ((uintptr_t)g.B & 15))) tile = 2;
   if (can_split) splits = std::min(splits, g.splits);
