@@ -433,7 +433,7 @@ int join_side(gpt_ctx* x) {
 // and into the next chunk's logits (chunks alternate between two dz buffers).
 int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C,
          float scale, float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, void* logits,
-         void* const dzb[2], int64_t ldv, int64_t Nc, int dtype, float* ws) {
+         void* const dzb[2], int64_t ldv, int64_t Nc, int dtype, float* ws, float* loss, float* ring, int slot) {
   const bool side = x->side != nullptr;
   int ci = 0;
   for (int64_t c0 = 0; c0 < N; c0 += Nc, ++ci) {
@@ -454,6 +454,9 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
       HIPCHK(gk::ce_rows(dtype, logits, ldv, (int)V, y + c0, (int)rows, scale, tok_loss + c0, tok_lse + c0,
                          scale > 0 ? dz : nullptr, x->stream));
     }
+    // the mean loss as soon as the last rows' losses exist: one workgroup, which
+    // would otherwise wait behind the dW product's workgroups for a free CU
+    if (c0 + rows >= N) HIPCHK(gk::mean_f32(tok_loss, (int)N, loss, ring, slot, x->stream));
     if (scale > 0) {
       // dW (on the side stream when there is one) and dF both read only dz
       // and operands of the forward, so they run side by side: dF's split-K
@@ -646,10 +649,9 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
   const bool grad = loss_scale > 0.f;
   if (int e = head(x, x->lnf, x->W_(T_WTE), x->Vp, yt, N, C, grad ? scale : 0.f, x->tok_loss, x->tok_lse,
                    grad ? x->dF : nullptr, grad ? x->G_(T_WTE) : nullptr, x->wte_fresh ? 0 : 1, x->logits, x->dz2,
-                   x->ldv, x->Nc, x->dt, x->splitk_ws))
+                   x->ldv, x->Nc, x->dt, x->splitk_ws, x->loss, x->ring, (int)(x->ring_wr % RING)))
     return e;
   if (grad) x->wte_fresh = false;
-  HIPCHK(gk::mean_f32(x->tok_loss, (int)N, x->loss, x->ring, x->ring_wr % RING, s));
   x->ring_wr++;
   x->have_fwd = true;
   x->fwd_grad = grad;
@@ -827,9 +829,8 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
   const bool grad = dX || dW;
   void* const dzb[2] = {dz, dz};  // no side stream here: chunks run in order on one buffer
   if (int e = head(&tmp, X, W, V, y, N, C, grad ? 1.0f / (float)N : 0.f, tl, tlse, dX, dW, 0, logits, dzb, ldv, Nc,
-                   dtype, hws))
+                   dtype, hws, loss_dev, nullptr, 0))
     return e;
-  HIPCHK(gk::mean_f32(tl, (int)N, loss_dev, nullptr, 0, tmp.stream));
   return 0;
 }
 
