@@ -889,8 +889,11 @@ constexpr int TILE_BN[5] = {128, 256, 128, 256, 192};
 // forward products -0.28 ms, data gradients -0.2, weight gradients -0.3, the
 // LM-head data gradient and the attention projection -0.1 each.  Tiles 0 and 1
 // stay selectable for tuning runs.  Split-K (fp32 outputs only) takes the
-// largest split count that keeps one round of workgroups (2 or 1 per CU) with
-// at least 512 k per split.
+// largest split count whose workgroups fill at most 192 of the 256 CUs (512
+// slots for the two-per-CU tile 0) with at least 512 k per split: the weight
+// gradients run beside the data-gradient chain, and leaving it a quarter of the
+// CUs (and a quarter less split-K workspace traffic) was 0.14 ms faster per
+// step than a full round (same box, 3 x 20 steps; 160 and 224 CUs: +0.07, +0.02).
 void choose(int M, int N, int K, bool can_split, int dtype, int a_trans, int b_trans, int* tile_out,
             int* splits_out) {
   (void)a_trans;
@@ -910,7 +913,7 @@ void choose(int M, int N, int K, bool can_split, int dtype, int a_trans, int b_t
   int splits = 1;
   if (can_split) {
     const int64_t tiles = (int64_t)cdiv(M, TILE_BM[tile]) * cdiv(N, TILE_BN[tile]);
-    const int64_t round = tile == 0 ? 512 : 256;
+    const int64_t round = tile == 0 ? 512 : 192;  // workgroup slots split-K may fill
     const int64_t by_round = round / tiles, by_k = K / 512;
     splits = (int)std::max<int64_t>(1, std::min(by_round, by_k));
   }

@@ -170,6 +170,77 @@ __global__ __launch_bounds__(256, 4) void ln_bwd_kernel(const TY* __restrict__ d
   }
 }
 
+// Split-row form for C = 256 * WPR (the 124M width takes WPR = 3): a workgroup
+// of WPR waves takes one row at a time, each lane owning 4 columns, so a lane
+// keeps 12 column partials instead of 12 * NV and the kernel fits in 64 VGPRs:
+// two of its waves fit on a SIMD beside an 8-wave GEMM workgroup of the other
+// stream (the one-wave-per-row kernel above gets one).  The row's two sums
+// cross the waves through LDS, one barrier per row (two slots, alternating by
+// row, so a wave that runs ahead never overwrites sums still being read).  The
+// next row's loads are issued before this row's barrier.  Column partials need
+// no LDS reduction: no two threads of a workgroup own the same column.
+template <typename TY, typename T, int WPR, bool DRES>
+__global__ __launch_bounds__(64 * WPR, 8) void ln_bwd_rows_kernel(
+    const TY* __restrict__ dy, const float* __restrict__ x, const float* __restrict__ mu,
+    const float* __restrict__ rs, const float* __restrict__ g, const float* __restrict__ dres_in,
+    float* __restrict__ dres_out, T* __restrict__ dres_T, float* __restrict__ part, int rows) {
+  constexpr int C = 256 * WPR;
+  __shared__ float2 sums[2][WPR];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = w * 256 + 4 * lane;
+  const float4 gg = load4(g + col);
+  float4 pg = make_float4(0.f, 0.f, 0.f, 0.f), pb = pg, pc = pg;
+  const int r0 = blockIdx.x * LNB_ROWS;
+  const int nr = min(LNB_ROWS, rows - r0);
+  float4 xv = make_float4(0.f, 0.f, 0.f, 0.f), dv = xv, pv = xv;
+  if (nr > 0) {
+    const int64_t o = (int64_t)r0 * C + col;
+    xv = load4(x + o);
+    dv = load4(dy + o);
+    if (DRES) pv = load4(dres_in + o);
+  }
+  for (int k = 0; k < nr; ++k) {
+    const int row = r0 + k;
+    const float m = mu[row], r = rs[row];
+    const float4 xq = xv, d = dv, prev = pv;
+    if (k + 1 < nr) {  // next row's loads ahead of this row's barrier
+      const int64_t o = (int64_t)(row + 1) * C + col;
+      xv = load4(x + o);
+      dv = load4(dy + o);
+      if (DRES) pv = load4(dres_in + o);
+    }
+    const float4 xh = make_float4((xq.x - m) * r, (xq.y - m) * r, (xq.z - m) * r, (xq.w - m) * r);
+    const float4 dxh = make_float4(d.x * gg.x, d.y * gg.y, d.z * gg.z, d.w * gg.w);
+    float s1 = dxh.x + dxh.y + dxh.z + dxh.w;
+    float s2 = dxh.x * xh.x + dxh.y * xh.y + dxh.z * xh.z + dxh.w * xh.w;
+    pg.x += d.x * xh.x; pg.y += d.y * xh.y; pg.z += d.z * xh.z; pg.w += d.w * xh.w;
+    pb.x += d.x; pb.y += d.y; pb.z += d.z; pb.w += d.w;
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    if (lane == 0) sums[k & 1][w] = make_float2(s1, s2);
+    __syncthreads();
+    float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < WPR; ++i) {
+      const float2 v = sums[k & 1][i];
+      t1 += v.x;
+      t2 += v.y;
+    }
+    const float m1 = t1 / C, m2 = t2 / C;
+    const float4 out = make_float4(prev.x + r * (dxh.x - m1 - xh.x * m2), prev.y + r * (dxh.y - m1 - xh.y * m2),
+                                   prev.z + r * (dxh.z - m1 - xh.z * m2), prev.w + r * (dxh.w - m1 - xh.w * m2));
+    const int64_t o = (int64_t)row * C + col;
+    store4(dres_out + o, out);
+    store4(dres_T + o, out);
+    pc.x += out.x; pc.y += out.y; pc.z += out.z; pc.w += out.w;
+  }
+  float* pp = part + (int64_t)blockIdx.x * 3 * C + col;
+  store4(pp, pg);
+  store4(pp + C, pb);
+  store4(pp + 2 * C, pc);
+}
+
 // Batched fixed-order column reductions: job j adds sum_r part[r][c] (rows in
 // order, in 16 interleaved row groups added in order) into out[c], or stores it.
 // Block b belongs to the job with first_block <= b < next job's first_block and
@@ -506,12 +577,37 @@ hipError_t ln_bwd_nv(int dtype, const void* dy, int dy_is_t, const float* x, con
                                          nblk, s);
 }
 
+template <int WPR, bool DRES>
+hipError_t ln_bwd_rows_d(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu, const float* rstd,
+                         const float* g, const float* dres_in, float* dres_out, void* dres_T, float* part, int rows,
+                         int nblk, hipStream_t s) {
+  if (dtype == BF16 && dy_is_t)
+    hipLaunchKernelGGL((ln_bwd_rows_kernel<bf16, bf16, WPR, DRES>), dim3(nblk), dim3(64 * WPR), 0, s,
+                       (const bf16*)dy, x, mu, rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows);
+  else if (dtype == BF16)
+    hipLaunchKernelGGL((ln_bwd_rows_kernel<float, bf16, WPR, DRES>), dim3(nblk), dim3(64 * WPR), 0, s,
+                       (const float*)dy, x, mu, rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows);
+  else
+    hipLaunchKernelGGL((ln_bwd_rows_kernel<float, float, WPR, DRES>), dim3(nblk), dim3(64 * WPR), 0, s,
+                       (const float*)dy, x, mu, rstd, g, dres_in, dres_out, (float*)dres_T, part, rows);
+  return hipGetLastError();
+}
 hipError_t layernorm_bwd(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu,
                          const float* rstd, const float* g, const float* dres_in, float* dres_out, void* dres_T,
                          float* part, int rows, int C, int* nblk_out, hipStream_t s) {
   const int nblk = layernorm_bwd_blocks(rows);
   if (nblk_out) *nblk_out = nblk;
   if (C % 4 || C > 4 * 64 * MAXV) return hipErrorInvalidValue;
+  // the split-row kernel for the final LayerNorm (fp32 dy from the LM head),
+  // which runs beside the head's dW product (2 x 221 VGPRs per SIMD: only a
+  // 64-VGPR wave fits beside it): 377 -> 129 us in the step.  Inside the
+  // layers the one-wave-per-row kernel was faster in the step (same box,
+  // 3 x 20 steps: +0.1 ms with the split-row kernel there).
+  if (!dy_is_t && !dres_in) {
+    if (C == 512) return ln_bwd_rows_d<2, false>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, nblk, s);
+    if (C == 768) return ln_bwd_rows_d<3, false>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, nblk, s);
+    if (C == 1024) return ln_bwd_rows_d<4, false>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, nblk, s);
+  }
   switch ((C / 4 + 63) / 64) {  // float4 slices per lane
     case 1: return ln_bwd_nv<1>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
     case 2: return ln_bwd_nv<2>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
