@@ -68,6 +68,8 @@ struct Params {
   int accumulate;
   int tiles_m, tiles_n;
   float* ws;
+  float* dv;
+  int tn, heads;
 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -220,7 +222,7 @@ __device__ __forceinline__ void epi_group_inline(const Params& p, int m, int n, 
       if (n + k >= p.N) break;
       const float bn = p.bias ? p.bias[n + k] : 0.f;
       const float x = v[k];
-      if constexpr (EPI == EPI_STORE) reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
+      if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_ODOT) reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
       else if constexpr (EPI == EPI_RESID) reinterpret_cast<float*>(p.C)[o + k] = p.R[o + k] + (x + bn);
       else if constexpr (EPI == EPI_GELU) {
         float gg, dg;
@@ -238,7 +240,7 @@ __device__ __forceinline__ void epi_group_inline(const Params& p, int m, int n, 
   }
   float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
   if (p.bias) b4 = *reinterpret_cast<const float4*>(p.bias + n);
-  if constexpr (EPI == EPI_STORE) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_ODOT) {
     store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w));
   } else if constexpr (EPI == EPI_RESID) {
     const float4 r = *reinterpret_cast<const float4*>(p.R + o);
@@ -269,12 +271,12 @@ __device__ __forceinline__ void epi_group_inline(const Params& p, int m, int n, 
 // pre-activation (EPI_GELU_BWD) or the previous output (EPI_F32 accumulating).
 template <int EPI, int SPLIT>
 __device__ __forceinline__ constexpr bool epi_reads() {
-  return !SPLIT && (EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_F32);
+  return !SPLIT && (EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_F32 || EPI == EPI_STORE_ODOT);
 }
 template <typename T, int EPI, int SPLIT>
 __device__ __forceinline__ float4 epi_load(const Params& p, int64_t o) {
   if constexpr (EPI == EPI_RESID) return *reinterpret_cast<const float4*>(p.R + o);
-  else if constexpr (EPI == EPI_GELU_BWD) return load4(reinterpret_cast<const T*>(p.aux) + o);
+  else if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_STORE_ODOT) return load4(reinterpret_cast<const T*>(p.aux) + o);
   else if constexpr (EPI == EPI_F32) {
     if (p.accumulate) return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.C) + o);
   }
@@ -290,7 +292,7 @@ __device__ __forceinline__ void epi_group_full(const Params& p, int m, int n, fl
     return;
   }
   const int64_t o = (int64_t)m * p.ldc + n;
-  if constexpr (EPI == EPI_STORE) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_ODOT) {
     store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w));
   } else if constexpr (EPI == EPI_RESID) {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) =
@@ -332,7 +334,7 @@ __device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 
       if (n + k >= p.N) break;
       const float bn = p.bias ? p.bias[n + k] : 0.f;
       const float x = v[k];
-      if constexpr (EPI == EPI_STORE) reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
+      if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_ODOT) reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(x + bn);
       else if constexpr (EPI == EPI_RESID) reinterpret_cast<float*>(p.C)[o + k] = p.R[o + k] + (x + bn);
       else if constexpr (EPI == EPI_GELU) {
         float gg, dg;
@@ -348,7 +350,7 @@ __device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 
     }
     return;
   }
-  if constexpr (EPI == EPI_STORE) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_ODOT) {
     store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w));
   } else if constexpr (EPI == EPI_RESID) {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) =
@@ -370,6 +372,25 @@ __device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 
 }
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+
+// EPI_STORE_ODOT: one lane's share of a row sum over a head's 64 columns: the
+// group as stored (T-rounded acc + bias) times its aux values; the 16 lanes
+// of the quarter wave (one row, one head) add theirs and the first writes it.
+// valid (row and columns inside the output) is the same for the 16 lanes.
+template <typename T>
+__device__ __forceinline__ void odot_rowsum(const Params& p, int m, int n, float4 a, float4 b4, float4 o, bool valid,
+                                            int lane) {
+  float d = 0.f;
+  if (valid)
+    d = to_f(from_f<T>(a.x + b4.x)) * o.x + to_f(from_f<T>(a.y + b4.y)) * o.y + to_f(from_f<T>(a.z + b4.z)) * o.z +
+        to_f(from_f<T>(a.w + b4.w)) * o.w;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) d += __shfl_xor(d, off, WAVE);
+  if (valid && (lane & 15) == 0) {
+    const int b = m / p.tn, tt = m - b * p.tn;
+    p.dv[((int64_t)b * p.heads + n / 64) * p.tn + tt] = d;
+  }
+}
 
 // Stage acc through LDS (smem, at least PASS_ROWS * (BN + 4) floats) and run
 // the epilogue.  Waves whose sub-tile rows fall in the current pass write.
@@ -418,7 +439,10 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
   // floats): a later pass's loads would otherwise wait for the earlier passes'
   // stores.  Wider inputs are loaded pass by pass (register budget).
   constexpr int NP = BM / PASS_ROWS;
-  constexpr bool PRE = IN && EPI == EPI_GELU_BWD && sizeof(T) == 2;
+  constexpr bool PRE = IN && (EPI == EPI_GELU_BWD || EPI == EPI_STORE_ODOT) && sizeof(T) == 2;
+  // EPI_STORE_ODOT: the 16 lanes of a thread quarter-wave hold one row's 64
+  // columns of one head, which their row sum reduces over
+  constexpr bool ODOT = EPI == EPI_STORE_ODOT && IN && NCOL == 1 && CG % 16 == 0;
   uint2 raw[PRE ? NP : 1][PRE ? NG : 1];
   if constexpr (PRE) {
 #pragma unroll
@@ -470,19 +494,21 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
           const int r = row_of(i), j = i % NCOL;
           float4 x_in = make_float4(0.f, 0.f, 0.f, 0.f);
           if constexpr (IN) x_in = in[i];
-          epi_group_full<T, EPI, SPLIT>(p, m0 + pass * PASS_ROWS + r, n[j],
-                                        *reinterpret_cast<const float4*>(st + r * LDW + c4[j] * 4), x_in, b4[j]);
+          const float4 a = *reinterpret_cast<const float4*>(st + r * LDW + c4[j] * 4);
+          epi_group_full<T, EPI, SPLIT>(p, m0 + pass * PASS_ROWS + r, n[j], a, x_in, b4[j]);
+          if constexpr (ODOT) odot_rowsum<T>(p, m0 + pass * PASS_ROWS + r, n[j], a, b4[j], x_in, true, lane);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
           const int r = row_of(i), j = i % NCOL;
           const int m = m0 + pass * PASS_ROWS + r;
-          if (m >= p.M || n[j] >= p.N) continue;
+          const bool ok = m < p.M && n[j] < p.N;
           float4 x_in = make_float4(0.f, 0.f, 0.f, 0.f);
           if constexpr (IN) x_in = in[i];
-          epi_group<T, EPI, SPLIT>(p, m, n[j], *reinterpret_cast<const float4*>(st + r * LDW + c4[j] * 4), full[j],
-                                   x_in, b4[j]);
+          const float4 a = *reinterpret_cast<const float4*>(st + r * LDW + c4[j] * 4);
+          if (ok) epi_group<T, EPI, SPLIT>(p, m, n[j], a, full[j], x_in, b4[j]);
+          if constexpr (ODOT) odot_rowsum<T>(p, m, n[j], a, b4[j], x_in, ok, lane);  // every lane shuffles
         }
       }
     } else {
@@ -867,6 +893,9 @@ hipError_t dispatch(const Gemm& g, const Params& p, int tile, int splits, hipStr
     case 10 + EPI_F32: return launch_tile<T, 0, 1, EPI_F32, 0>(p, tile, 1, s);
     case 10 + EPI_STORE: return launch_tile<T, 0, 1, EPI_STORE, 0>(p, tile, 1, s);
     case 10 + EPI_GELU_BWD: return launch_tile<T, 0, 1, EPI_GELU_BWD, 0>(p, tile, 1, s);
+    case 10 + EPI_STORE_ODOT:
+      if constexpr (sizeof(T) == 2) return launch_tile<T, 0, 1, EPI_STORE_ODOT, 0>(p, tile, 1, s);
+      return hipErrorInvalidValue;
     case 110 + EPI_F32: return launch_tile<T, 1, 1, EPI_F32, 0>(p, tile, 1, s);
     default: return hipErrorInvalidValue;
   }
@@ -947,6 +976,12 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
   if (tile == 4 && can_split) tile = 3;  // split-K products keep the 256-column tile
   // direct-to-LDS loads move 16-byte chunks: rows of other strides take the register-staged kernel
   if (tile != 2 && ((g.lda & 7) || (g.ldb & 7) || ((uintptr_t)g.A & 15) || ((uintptr_t)g.B & 15))) tile = 2;
+  if (g.epi == EPI_STORE_ODOT) {  // row sums need 16 lanes per head-row: tiles 0, 2, 3 (one column slot per thread)
+    if (g.dtype != BF16 || !g.dv || !g.aux || g.tn <= 0 || g.heads <= 0 || g.N != 64 * g.heads || g.M % g.tn ||
+        (g.ldc & 3))
+      return hipErrorInvalidValue;
+    if (tile == 1 || tile == 4) tile = 3;
+  }
   if (can_split) splits = std::min(splits, g.splits);
   Params p{};
   p.A = g.A;
@@ -963,6 +998,9 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
   p.C2 = g.C2;
   p.aux = g.aux;
   p.accumulate = g.accumulate;
+  p.dv = g.dv;
+  p.tn = g.tn;
+  p.heads = g.heads;
   p.tiles_m = cdiv(g.M, TILE_BM[tile]);
   p.tiles_n = cdiv(g.N, TILE_BN[tile]);
   p.ws = g.ws;

@@ -723,14 +723,27 @@ int gpt_backward(gpt_ctx* x) {
     if (int e = wgrad(x, "gemm_wgrad_attn", T1, C, ly.att, C, C, C, x->G_(tid(l, K_PROJW)), acc)) return e;
     if (int e = done(l, 2)) return e;
     g = mk(x, 0, 1, gk::EPI_STORE, T1, C, x->W_(tid(l, K_PROJW)), C, N, C, C, x->datt, C);
+    // bf16, D = 64: the attention backward's row sums D = rowsum(dO * O) come
+    // out of this product's epilogue, where dO is produced
+    const bool fused_dv = x->dt == GPT_BF16 && x->D == 64;
+    if (fused_dv) {
+      g.epi = gk::EPI_STORE_ODOT;
+      g.aux = ly.att;
+      g.dv = x->Dv;
+      g.tn = (int)x->T;
+      g.heads = (int)x->H;
+    }
     if (int e = run_gemm(x, "gemm_dgrad_attn", g)) return e;
     if (l + 1 < L)
       if (int e = wait_side(l + 1, 3)) return e;  // previous layer's qkv dW finished reading dqkv
     {
       const double pairs = (double)x->B * x->H * x->T * (x->T + 1) / 2.0;
       ProfScope ps(x, "attn_bwd", 8.0 * x->D * pairs, 0.0);
-      HIPCHK(gk::attn_bwd(x->dt, ly.qkv, ly.att, x->datt, ly.lse, x->Dv, x->dqkv, (int)x->B, (int)x->T, (int)x->H,
-                          (int)x->D, s));
+      if (fused_dv)
+        HIPCHK(gk::attn_bwd_bf16_d64(ly.qkv, x->datt, ly.lse, x->Dv, x->dqkv, (int)x->B, (int)x->T, (int)x->H, s));
+      else
+        HIPCHK(gk::attn_bwd(x->dt, ly.qkv, ly.att, x->datt, ly.lse, x->Dv, x->dqkv, (int)x->B, (int)x->T, (int)x->H,
+                            (int)x->D, s));
     }
     // QKV projection
     if (int e = fork(l, 3)) return e;
