@@ -430,7 +430,7 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
     n[j] = n0 + c4[j] * 4;
     full[j] = n[j] + 3 < p.N && (SPLIT || (p.ldc & 3) == 0);
     b4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (!SPLIT && full[j] && p.bias) b4[j] = *reinterpret_cast<const float4*>(p.bias + n[j]);
+    if (!SPLIT && EPI != EPI_STORE_ODOT && full[j] && p.bias) b4[j] = *reinterpret_cast<const float4*>(p.bias + n[j]);
   }
   // the whole tile inside the output, every group 16-byte aligned
   const bool tile_full = m0 + BM <= p.M && n0 + BN <= p.N && (SPLIT ? (p.N & 3) == 0 : (p.ldc & 3) == 0);
@@ -977,8 +977,8 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
   // direct-to-LDS loads move 16-byte chunks: rows of other strides take the register-staged kernel
   if (tile != 2 && ((g.lda & 7) || (g.ldb & 7) || ((uintptr_t)g.A & 15) || ((uintptr_t)g.B & 15))) tile = 2;
   if (g.epi == EPI_STORE_ODOT) {  // row sums need 16 lanes per head-row: tiles 0, 2, 3 (one column slot per thread)
-    if (g.dtype != BF16 || !g.dv || !g.aux || g.tn <= 0 || g.heads <= 0 || g.N != 64 * g.heads || g.M % g.tn ||
-        (g.ldc & 3))
+    if (g.dtype != BF16 || !g.dv || !g.aux || g.bias || g.tn <= 0 || g.heads <= 0 || g.N != 64 * g.heads ||
+        g.M % g.tn || (g.ldc & 3))
       return hipErrorInvalidValue;
     if (tile == 1 || tile == 4) tile = 3;
   }

@@ -16,7 +16,7 @@ enum Epi {
   EPI_GELU = 2,      // u = acc + bias: C(T) = gelu'(u) (kept for the backward), C2(T) = gelu(u)
   EPI_GELU_BWD = 3,  // C(T) = acc * aux(T) (aux = gelu'(u) from the forward)
   EPI_F32 = 4,       // C(f32) = (accumulate ? C : 0) + acc
-  // C(T) = acc + bias, and dv[b][h][t] = sum over head h's 64 columns of row
+  // C(T) = acc (no bias), and dv[b][h][t] = sum over head h's 64 columns of row
   // m = b * tn + t of C(T) * aux(T): attention's D = rowsum(dO * O) computed
   // where dO is produced (bf16, N a multiple of 64, 256- or 128-column tiles)
   EPI_STORE_ODOT = 5,
