@@ -2,6 +2,7 @@
 // fragments, MFMA wrappers, hardware exp2/log2, wavefront reductions.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 typedef __bf16 bf16;

@@ -850,53 +850,67 @@ __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, i
   *c = accumulate ? *c + s : s;
 }
 
+// Timing events of the main kernel: when both are set they are attached to
+// its dispatch (hipExtLaunchKernel), so timing adds no packets to the stream.
+struct Ev {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 template <typename T, int TA, int TB, int EPI, int SPLIT, int BM, int BN>
-hipError_t launch(const Params& p, int splits, hipStream_t s) {
+hipError_t launch(const Params& p, int splits, hipStream_t s, Ev ev) {
   dim3 grid(p.tiles_m * p.tiles_n * splits);
-  hipLaunchKernelGGL((gemm_kernel<T, TA, TB, EPI, SPLIT, BM, BN>), grid, dim3(256), 0, s, p);
+  if (ev.start)
+    hipExtLaunchKernelGGL((gemm_kernel<T, TA, TB, EPI, SPLIT, BM, BN>), grid, dim3(256), 0, s, ev.start, ev.stop, 0,
+                          p);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, TA, TB, EPI, SPLIT, BM, BN>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <int TA, int TB, int EPI, int SPLIT, typename C>
-hipError_t launch_dl(const Params& p, int splits, hipStream_t s) {
+hipError_t launch_dl(const Params& p, int splits, hipStream_t s, Ev ev) {
   dim3 grid(p.tiles_m * p.tiles_n * splits);
-  hipLaunchKernelGGL((gemm_dl_kernel<TA, TB, EPI, SPLIT, C>), grid, dim3(C::THREADS), 0, s, p);
+  if (ev.start)
+    hipExtLaunchKernelGGL((gemm_dl_kernel<TA, TB, EPI, SPLIT, C>), grid, dim3(C::THREADS), 0, s, ev.start, ev.stop, 0,
+                          p);
+  else
+    hipLaunchKernelGGL((gemm_dl_kernel<TA, TB, EPI, SPLIT, C>), grid, dim3(C::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
 template <typename T, int TA, int TB, int EPI, int SPLIT>
-hipError_t launch_tile(const Params& p, int tile, int splits, hipStream_t s) {
+hipError_t launch_tile(const Params& p, int tile, int splits, hipStream_t s, Ev ev) {
   if constexpr (sizeof(T) == 2) {
-    if (tile == 0) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<128, 32, 3, 2>>(p, splits, s);
-    if (tile == 1) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1>>(p, splits, s);
-    if (tile == 3) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1, 8>>(p, splits, s);
+    if (tile == 0) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<128, 32, 3, 2>>(p, splits, s, ev);
+    if (tile == 1) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1>>(p, splits, s, ev);
+    if (tile == 3) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1, 8>>(p, splits, s, ev);
     if constexpr (!SPLIT) {
-      if (tile == 4) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<192, 64, 2, 1, 8, 4>>(p, splits, s);
+      if (tile == 4) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<192, 64, 2, 1, 8, 4>>(p, splits, s, ev);
     }
   }
-  return launch<T, TA, TB, EPI, SPLIT, 128, 128>(p, splits, s);
+  return launch<T, TA, TB, EPI, SPLIT, 128, 128>(p, splits, s, ev);
 }
 
 template <typename T>
-hipError_t dispatch(const Gemm& g, const Params& p, int tile, int splits, hipStream_t s) {
+hipError_t dispatch(const Gemm& g, const Params& p, int tile, int splits, hipStream_t s, Ev ev) {
   const int key = g.a_trans * 100 + g.b_trans * 10 + g.epi;
   if (splits > 1) {
-    if (g.a_trans == 1 && g.b_trans == 1) return launch_tile<T, 1, 1, EPI_F32, 1>(p, tile, splits, s);
-    if (g.a_trans == 0 && g.b_trans == 1) return launch_tile<T, 0, 1, EPI_F32, 1>(p, tile, splits, s);
+    if (g.a_trans == 1 && g.b_trans == 1) return launch_tile<T, 1, 1, EPI_F32, 1>(p, tile, splits, s, ev);
+    if (g.a_trans == 0 && g.b_trans == 1) return launch_tile<T, 0, 1, EPI_F32, 1>(p, tile, splits, s, ev);
     return hipErrorInvalidValue;
   }
   switch (key) {
-    case 0 + EPI_STORE: return launch_tile<T, 0, 0, EPI_STORE, 0>(p, tile, 1, s);
-    case 0 + EPI_RESID: return launch_tile<T, 0, 0, EPI_RESID, 0>(p, tile, 1, s);
-    case 0 + EPI_GELU: return launch_tile<T, 0, 0, EPI_GELU, 0>(p, tile, 1, s);
-    case 0 + EPI_F32: return launch_tile<T, 0, 0, EPI_F32, 0>(p, tile, 1, s);
-    case 10 + EPI_F32: return launch_tile<T, 0, 1, EPI_F32, 0>(p, tile, 1, s);
-    case 10 + EPI_STORE: return launch_tile<T, 0, 1, EPI_STORE, 0>(p, tile, 1, s);
-    case 10 + EPI_GELU_BWD: return launch_tile<T, 0, 1, EPI_GELU_BWD, 0>(p, tile, 1, s);
+    case 0 + EPI_STORE: return launch_tile<T, 0, 0, EPI_STORE, 0>(p, tile, 1, s, ev);
+    case 0 + EPI_RESID: return launch_tile<T, 0, 0, EPI_RESID, 0>(p, tile, 1, s, ev);
+    case 0 + EPI_GELU: return launch_tile<T, 0, 0, EPI_GELU, 0>(p, tile, 1, s, ev);
+    case 0 + EPI_F32: return launch_tile<T, 0, 0, EPI_F32, 0>(p, tile, 1, s, ev);
+    case 10 + EPI_F32: return launch_tile<T, 0, 1, EPI_F32, 0>(p, tile, 1, s, ev);
+    case 10 + EPI_STORE: return launch_tile<T, 0, 1, EPI_STORE, 0>(p, tile, 1, s, ev);
+    case 10 + EPI_GELU_BWD: return launch_tile<T, 0, 1, EPI_GELU_BWD, 0>(p, tile, 1, s, ev);
     case 10 + EPI_STORE_ODOT:
-      if constexpr (sizeof(T) == 2) return launch_tile<T, 0, 1, EPI_STORE_ODOT, 0>(p, tile, 1, s);
+      if constexpr (sizeof(T) == 2) return launch_tile<T, 0, 1, EPI_STORE_ODOT, 0>(p, tile, 1, s, ev);
       return hipErrorInvalidValue;
-    case 110 + EPI_F32: return launch_tile<T, 1, 1, EPI_F32, 0>(p, tile, 1, s);
+    case 110 + EPI_F32: return launch_tile<T, 1, 1, EPI_F32, 0>(p, tile, 1, s, ev);
     default: return hipErrorInvalidValue;
   }
 }
@@ -967,7 +981,7 @@ static int forced_tile() {
   return v;
 }
 
-hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
+hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main, hipEvent_t before_main) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const bool can_split = g.ws != nullptr && g.splits > 1 && g.epi == EPI_F32;
   int tile = 2, splits = 1;
@@ -1017,8 +1031,11 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main) {
   } else {
     p.k_per_split = g.K;
   }
-  hipError_t e = (g.dtype == BF16) ? dispatch<bf16>(g, p, tile, splits, s) : dispatch<float>(g, p, tile, splits, s);
-  if (e == hipSuccess && after_main) e = hipEventRecord(after_main, s);
+  Ev ev;
+  if (before_main && after_main) ev = Ev{before_main, after_main};
+  hipError_t e =
+      (g.dtype == BF16) ? dispatch<bf16>(g, p, tile, splits, s, ev) : dispatch<float>(g, p, tile, splits, s, ev);
+  if (e == hipSuccess && after_main && !ev.start) e = hipEventRecord(after_main, s);
   if (e != hipSuccess || splits <= 1) return e;
   const int64_t total = (int64_t)g.M * g.N;
   hipLaunchKernelGGL(splitk_reduce, dim3(cdiv(total, 256)), dim3(256), 0, s, g.ws, splits, g.M,

@@ -326,7 +326,8 @@ struct ProfScope {
   gpt_ctx* x;
   bool on;
   hipStream_t st;
-  ProfScope(gpt_ctx* x_, const char* cls, double flops, double bytes, hipStream_t s_ = nullptr)
+  // attach: the caller hands start_event() and stop_event() to the launch itself
+  ProfScope(gpt_ctx* x_, const char* cls, double flops, double bytes, hipStream_t s_ = nullptr, bool attach = false)
       : x(x_), st(s_ ? s_ : x_->stream) {
     on = !x->prof.cls.empty() && (x->prof.cls == "any" || x->prof.cls == cls);
     if (!on) return;
@@ -337,12 +338,13 @@ struct ProfScope {
         x->prof.ev.push_back(e);
       }
     }
-    (void)hipEventRecord(x->prof.ev[x->prof.used], st);
+    if (!attach) (void)hipEventRecord(x->prof.ev[x->prof.used], st);
     x->prof.flops += flops;
     x->prof.bytes += bytes;
     x->prof.launches += 1;
   }
-  // the stop event, for a caller that records it itself (nullptr when not profiling)
+  // the events, for a caller that records them itself (nullptr when not profiling)
+  hipEvent_t start_event() { return on ? x->prof.ev[x->prof.used] : nullptr; }
   hipEvent_t stop_event() { return on ? x->prof.ev[x->prof.used + 1] : nullptr; }
   ~ProfScope() {
     if (!on) return;
@@ -352,12 +354,14 @@ struct ProfScope {
   bool stopped = false;
 };
 
-// GEMM classes time only the main kernel (a split-K reduction is not included)
+// GEMM classes time only the main kernel (a split-K reduction is not
+// included), with the events attached to its dispatch: no marker packets
+// between it and its neighbours
 int run_gemm(gpt_ctx* x, const char* cls, const gk::Gemm& g, hipStream_t st = nullptr) {
   if (!st) st = x->stream;
-  ProfScope ps(x, cls, 2.0 * g.M * g.N * (double)g.K, 0.0, st);
+  ProfScope ps(x, cls, 2.0 * g.M * g.N * (double)g.K, 0.0, st, true);
   hipEvent_t stop = ps.stop_event();
-  HIPCHK(gk::gemm(g, st, stop));
+  HIPCHK(gk::gemm(g, st, stop, ps.start_event()));
   ps.stopped = stop != nullptr;
   return 0;
 }

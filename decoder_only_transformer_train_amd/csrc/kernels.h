@@ -42,8 +42,9 @@ struct Gemm {
   int splits = 1;
   float* ws = nullptr;
 };
-// after_main (nullable) is recorded right after the main kernel, before any split-K reduction
-hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main = nullptr);
+// after_main (nullable) is recorded right after the main kernel, before any split-K reduction;
+// with before_main too, both are attached to the main kernel's dispatch (its start and end)
+hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main = nullptr, hipEvent_t before_main = nullptr);
 // split count and workspace floats a wgrad GEMM of this shape would use
 int gemm_pick_splits(int M, int N, int K, int a_trans, int b_trans);
 
