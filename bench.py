@@ -165,9 +165,13 @@ def main():
         g.read_losses()
 
     torch.cuda.synchronize()
-    g.profile_begin(args.roofline_kernel)
     t0 = time.perf_counter()
-    for _ in range(K):
+    for i in range(K):
+        # the roofline kernel is timed in the last timed step: its events put
+        # barrier packets around each launch (a few us of idle GPU each), which
+        # the other steps are spared
+        if i == K - 1:
+            g.profile_begin(args.roofline_kernel)
         pos = step(pos)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
