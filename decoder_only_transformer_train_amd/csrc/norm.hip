@@ -16,7 +16,10 @@ namespace {
 constexpr float LN_EPS = 1e-5f;
 constexpr int MAXV = 8;  // float4 slices per lane: C <= 2048
 
-template <typename T, bool EMBED>
+// NV float4 slices per lane (C <= 256 NV): the registers, and so the
+// occupancy, follow the row width (with a fixed 8 slots: 132 VGPRs, 3 waves
+// per SIMD at C = 768)
+template <typename T, bool EMBED, int NV>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x, const int32_t* __restrict__ tok,
                                                      const float* __restrict__ wte, const float* __restrict__ wpe,
                                                      int Tn, float* __restrict__ res0, const float* __restrict__ g,
@@ -28,11 +31,11 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
   const int nc = C >> 2;
   // every load (row, gain, shift) is issued before the first store: a load
   // issued after a store would wait for it (the vector memory counter counts both)
-  float4 v[MAXV], gv[MAXV], bv[MAXV];
+  float4 v[NV], gv[NV], bv[NV];
   int64_t wrow = 0;
   if constexpr (EMBED) wrow = (int64_t)tok[row] * C;
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int j = lane + 64 * i;
     if (j < nc) {
       if constexpr (EMBED) {
@@ -48,7 +51,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
   }
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int j = lane + 64 * i;
     if (j < nc) {
       if constexpr (EMBED) store4(res0 + (int64_t)row * C + 4 * j, v[i]);
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
   const float mean = wave_sum(s) / C;
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int j = lane + 64 * i;
     if (j < nc) {
       const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
   }
   const float r = rsqrtf(wave_sum(ss) / C + LN_EPS);
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int j = lane + 64 * i;
     if (j < nc) {
       const float4 gg = gv[i], b4 = bv[i];
@@ -525,29 +528,39 @@ __global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x,
 
 }  // namespace
 
+template <typename T, bool EMBED, int NV>
+void ln_fwd_launch(const float* x, const int32_t* tok, const float* wte, const float* wpe, int Tn, float* res0,
+                   const float* g, const float* b, void* y, float* mu, float* rstd, int rows, int C, hipStream_t s) {
+  hipLaunchKernelGGL((ln_fwd_kernel<T, EMBED, NV>), dim3(cdiv(rows, 4)), dim3(256), 0, s, x, tok, wte, wpe, Tn, res0,
+                     g, b, (T*)y, mu, rstd, rows, C);
+}
+template <typename T, bool EMBED>
+hipError_t ln_fwd_nv(const float* x, const int32_t* tok, const float* wte, const float* wpe, int Tn, float* res0,
+                     const float* g, const float* b, void* y, float* mu, float* rstd, int rows, int C, hipStream_t s) {
+  if (C % 4 || C > 4 * 64 * MAXV) return hipErrorInvalidValue;
+  switch ((C / 4 + 63) / 64) {  // float4 slices per lane
+    case 1: ln_fwd_launch<T, EMBED, 1>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
+    case 2: ln_fwd_launch<T, EMBED, 2>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
+    case 3: ln_fwd_launch<T, EMBED, 3>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
+    case 4: ln_fwd_launch<T, EMBED, 4>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
+    case 5:
+    case 6: ln_fwd_launch<T, EMBED, 6>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
+    default: ln_fwd_launch<T, EMBED, 8>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t layernorm_fwd(int dtype, const float* x, const float* g, const float* b, void* y, float* mu,
                          float* rstd, int rows, int C, hipStream_t s) {
-  dim3 grid(cdiv(rows, 4));
-  if (dtype == BF16)
-    hipLaunchKernelGGL((ln_fwd_kernel<bf16, false>), grid, dim3(256), 0, s, x, nullptr, nullptr, nullptr, 1,
-                       nullptr, g, b, (bf16*)y, mu, rstd, rows, C);
-  else
-    hipLaunchKernelGGL((ln_fwd_kernel<float, false>), grid, dim3(256), 0, s, x, nullptr, nullptr, nullptr, 1,
-                       nullptr, g, b, (float*)y, mu, rstd, rows, C);
-  return hipGetLastError();
+  if (dtype == BF16) return ln_fwd_nv<bf16, false>(x, nullptr, nullptr, nullptr, 1, nullptr, g, b, y, mu, rstd, rows, C, s);
+  return ln_fwd_nv<float, false>(x, nullptr, nullptr, nullptr, 1, nullptr, g, b, y, mu, rstd, rows, C, s);
 }
 
 hipError_t embed_ln_fwd(int dtype, const int32_t* tok, const float* wte, const float* wpe, int Tn, float* res0,
                         const float* g, const float* b, void* y, float* mu, float* rstd, int rows, int C,
                         hipStream_t s) {
-  dim3 grid(cdiv(rows, 4));
-  if (dtype == BF16)
-    hipLaunchKernelGGL((ln_fwd_kernel<bf16, true>), grid, dim3(256), 0, s, nullptr, tok, wte, wpe, Tn, res0, g, b,
-                       (bf16*)y, mu, rstd, rows, C);
-  else
-    hipLaunchKernelGGL((ln_fwd_kernel<float, true>), grid, dim3(256), 0, s, nullptr, tok, wte, wpe, Tn, res0, g,
-                       b, (float*)y, mu, rstd, rows, C);
-  return hipGetLastError();
+  if (dtype == BF16) return ln_fwd_nv<bf16, true>(nullptr, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s);
+  return ln_fwd_nv<float, true>(nullptr, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s);
 }
 
 int layernorm_bwd_blocks(int rows) { return cdiv(rows, LNB_ROWS); }
