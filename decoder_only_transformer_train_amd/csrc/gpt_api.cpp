@@ -110,6 +110,13 @@ struct gpt_ctx {
   std::vector<hipEvent_t> sev;
   hipEvent_t head_ready[2] = {nullptr, nullptr}, head_done[2] = {nullptr, nullptr}, side_tail = nullptr;
   hipEvent_t fwd_start = nullptr;  // the forward's start, for side-stream work that needs only the batch
+  // AdamW runs on the side stream in pieces (all vectors, wte + wpe, then each
+  // layer's matrices); the next forward waits for each piece where it first
+  // reads it.  adam_ev[k] marks piece k done; adam_pending: pieces queued
+  // since the last forward (the side stream holds nothing else then)
+  std::vector<hipEvent_t> adam_ev;
+  hipEvent_t norm_done = nullptr;
+  bool adam_pending = false;
   bool dz_busy[2] = {false, false};
   float *Dv, *lnf_part, *splitk_ws;
   gk::RedJob* jobs_dev;
@@ -552,6 +559,9 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
   }
   chk(hipEventCreateWithFlags(&x->side_tail, hipEventDisableTiming));
   chk(hipEventCreateWithFlags(&x->fwd_start, hipEventDisableTiming));
+  chk(hipEventCreateWithFlags(&x->norm_done, hipEventDisableTiming));
+  x->adam_ev.assign((size_t)x->L + 2, nullptr);
+  for (auto& e : x->adam_ev) chk(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   if (rc) {
     gpt_destroy(x);
     return rc;
@@ -566,7 +576,10 @@ int gpt_destroy(gpt_ctx* x) {
   if (x->side) (void)hipStreamSynchronize(x->side);
   for (auto e : x->sev)
     if (e) (void)hipEventDestroy(e);
-  for (hipEvent_t e : {x->head_ready[0], x->head_ready[1], x->head_done[0], x->head_done[1], x->side_tail, x->fwd_start})
+  for (auto e : x->adam_ev)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : {x->head_ready[0], x->head_ready[1], x->head_done[0], x->head_done[1], x->side_tail, x->fwd_start,
+                       x->norm_done})
     if (e) (void)hipEventDestroy(e);
   if (x->side) (void)hipStreamDestroy(x->side);
   delete x;
@@ -582,7 +595,10 @@ int gpt_make_batch(gpt_ctx* x, const int32_t* host_tokens, int64_t n_tokens, int
     if (t < 0 || t >= x->V)
       return fail(GPT_ERANGE, "token " + std::to_string(t) + " at " + std::to_string(start + i) + " outside [0, vocab)");
   }
-  if (int e = join_side(x)) return e;  // the side stream's token sort may still read the previous batch
+  // the side stream's token sort may still read the previous batch (not when
+  // it holds only AdamW pieces: the update joined everything queued before them)
+  if (!x->adam_pending)
+    if (int e = join_side(x)) return e;
   HIPCHK(hipMemcpyAsync(x->win, host_tokens + start, need * 4, hipMemcpyHostToDevice, x->stream));
   HIPCHK(hipStreamSynchronize(x->stream));
   return 0;
@@ -604,8 +620,12 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
   const int64_t N = x->N, C = x->C;
   const int32_t* xt = x->win;
   const int32_t* yt = x->win + 1;
-  // a previous call's head dW may still read lnf / dz and write G(wte)
-  if (int e = join_side(x)) return e;
+  // a previous call's head dW may still read lnf / dz and write G(wte); after
+  // an update the side stream holds only AdamW pieces, waited for piece by piece
+  const bool adam = x->adam_pending;
+  x->adam_pending = false;
+  if (adam) HIPCHK(hipStreamWaitEvent(s, x->adam_ev[1], 0));  // vectors, then wte and wpe
+  else if (int e = join_side(x)) return e;
   if (loss_scale > 0.f) {
     // the embedding backward's token sort needs only the batch: it runs on the
     // side stream beside the forward (its keys are read after backward's join)
@@ -621,6 +641,8 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
   }
   for (int l = 0; l < x->L; ++l) {
     Layer& ly = x->layers[l];
+    // layer 0 and 1's matrices, then all the rest (they finish long before layer 2)
+    if (adam && l <= 2) HIPCHK(hipStreamWaitEvent(s, x->adam_ev[l < 2 ? 2 + l : x->L + 1], 0));
     gk::Gemm g = mk(x, 0, 0, gk::EPI_STORE, ly.ln1, C, x->W_(tid(l, K_ATTW)), C, N, 3 * C, C, ly.qkv, 3 * C);
     g.bias = x->P_(tid(l, K_ATTB));
     if (int e = run_gemm(x, "gemm_qkv_fwd", g)) return e;
@@ -795,12 +817,37 @@ int gpt_adamw_step(gpt_ctx* x, float lr, float beta1, float beta2, float eps, fl
   }
   hipStream_t s = x->stream;
   int nblk = 0;
-  {
+  if (!x->side) {
     ProfScope ps(x, "adamw", 0.0, (double)x->P * (4.0 + (x->shadow ? 30.0 : 28.0)));
     HIPCHK(gk::sumsq_partial(x->grads, x->P, x->norm_part, &nblk, s));
     HIPCHK(gk::norm_finish(x->norm_part, nblk, grad_clip, x->scal, s));
     HIPCHK(gk::adamw(x->params, x->grads, x->m, x->v, x->shadow, x->P, x->P_decay, x->scal, lr, beta1, beta2, eps,
                      weight_decay, x->step_dev, s));
+  } else {
+    // the gradient norm on s; the update on the side stream in pieces, in the
+    // order the next forward reads them (memory order: every matrix - wte,
+    // wpe, then each layer's - before the vectors): the vectors, wte + wpe,
+    // then layer by layer.  The forward waits for each piece (adam_ev) instead
+    // of the whole update, so most of it runs beside the forward's products.
+    ProfScope ps(x, "adamw", 0.0, (double)x->P * (4.0 + (x->shadow ? 30.0 : 28.0)), x->side);
+    HIPCHK(gk::sumsq_partial(x->grads, x->P, x->norm_part, &nblk, s));
+    HIPCHK(gk::norm_finish(x->norm_part, nblk, grad_clip, x->scal, s));
+    HIPCHK(hipEventRecord(x->norm_done, s));
+    HIPCHK(hipStreamWaitEvent(x->side, x->norm_done, 0));
+    HIPCHK(gk::adamw_prep(x->scal, lr, beta1, beta2, x->step_dev, x->side));
+    auto piece = [&](int64_t lo, int64_t hi, int k) -> int {
+      HIPCHK(gk::adamw_range(x->params, x->grads, x->m, x->v, x->shadow, lo, hi, x->P_decay, x->scal, lr, beta1,
+                             beta2, eps, weight_decay, x->side));
+      HIPCHK(hipEventRecord(x->adam_ev[k], x->side));
+      return 0;
+    };
+    const int L = (int)x->L;
+    auto first = [&](int l) { return l < L ? x->tensors[tid(l, K_ATTW)].off : x->P_decay; };  // layer l's matrices
+    if (int e = piece(x->P_decay, x->P, 0)) return e;  // LayerNorm gains/shifts and biases of every layer
+    if (int e = piece(0, first(0), 1)) return e;       // wte, wpe
+    for (int l = 0; l < L; ++l)
+      if (int e = piece(first(l), first(l + 1), 2 + l)) return e;
+    x->adam_pending = true;
   }
   x->wte_fresh = x->others_fresh = true;
   x->have_fwd = false;

@@ -122,6 +122,12 @@ hipError_t norm_finish(const float* part, int nblk, float clip, float* scal, hip
 hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow, int64_t n,
                  int64_t n_decay, float* scal, float lr, float b1, float b2, float eps, float wd,
                  int* step_dev, hipStream_t s);
+// the same in pieces: adamw_prep once (advances step_dev, sets scal[3]), then
+// adamw_range over [lo, hi) (multiples of 4; decay below n_decay) in any order
+hipError_t adamw_prep(float* scal, float lr, float b1, float b2, int* step_dev, hipStream_t s);
+hipError_t adamw_range(float* p, const float* g, float* m, float* v, void* shadow, int64_t lo, int64_t hi,
+                       int64_t n_decay, const float* scal, float lr, float b1, float b2, float eps, float wd,
+                       hipStream_t s);
 // fp32 -> bf16 copy
 hipError_t to_bf16(const float* x, void* y, int64_t n, hipStream_t s);
 // x[i] = value

@@ -12,6 +12,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace gk {
 namespace {
 
@@ -250,16 +252,30 @@ hipError_t norm_finish(const float* part, int nblk, float clip, float* scal, hip
   return hipGetLastError();
 }
 
-hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow, int64_t n, int64_t n_decay,
-                 float* scal, float lr, float b1, float b2, float eps, float wd, int* step_dev, hipStream_t s) {
+hipError_t adamw_prep(float* scal, float lr, float b1, float b2, int* step_dev, hipStream_t s) {
   hipLaunchKernelGGL(adamw_prep_kernel, dim3(1), dim3(1), 0, s, scal, step_dev, lr, b1, b2);
-  const int64_t n4 = n / 4;
+  return hipGetLastError();
+}
+
+hipError_t adamw_range(float* p, const float* g, float* m, float* v, void* shadow, int64_t lo, int64_t hi,
+                       int64_t n_decay, const float* scal, float lr, float b1, float b2, float eps, float wd,
+                       hipStream_t s) {
+  if ((lo | hi) & 3 || hi < lo) return hipErrorInvalidValue;
+  const int64_t n4 = (hi - lo) / 4;
   const int64_t blocks = cdiv(n4, 256 * ADAMW_U);
-  if (blocks == 0) return hipGetLastError();
+  if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, g, m, v, (bf16*)shadow, n4, n_decay / 4,
+  const int64_t d4 = std::min(std::max<int64_t>(n_decay - lo, 0), hi - lo) / 4;  // decayed prefix of the range
+  bf16* sh = shadow ? (bf16*)shadow + lo : nullptr;
+  hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p + lo, g + lo, m + lo, v + lo, sh, n4, d4,
                      scal, lr, b1, b2, eps, wd);
   return hipGetLastError();
+}
+
+hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow, int64_t n, int64_t n_decay,
+                 float* scal, float lr, float b1, float b2, float eps, float wd, int* step_dev, hipStream_t s) {
+  if (hipError_t e = adamw_prep(scal, lr, b1, b2, step_dev, s)) return e;
+  return adamw_range(p, g, m, v, shadow, 0, n, n_decay, scal, lr, b1, b2, eps, wd, s);
 }
 
 hipError_t to_bf16(const float* x, void* y, int64_t n, hipStream_t s) {
