@@ -21,14 +21,19 @@
  *     ordinary process memory borrowed for the duration of the call only;
  *   - all GPU work is enqueued on the context's HIP stream (hipStream_t
  *     passed as void*; NULL means the default stream), except the weight-
- *     gradient products of the backward and of the tied head (and the token sort
- *     of the embedding gradient), which run on a second stream the context owns.  That stream starts from events on the
+ *     gradient products of the backward and of the tied head, the token sort
+ *     of the embedding gradient and the AdamW update itself, which run on a
+ *     second stream the context owns.  That stream starts from events on the
  *     context stream and is joined back into it (the context stream waits
  *     for it) before gpt_backward's embedding step and at the start of
- *     gpt_make_batch, gpt_forward_loss, gpt_adamw_step, gpt_get_tensor and gpt_set_tensor,
- *     so work later enqueued on the context stream sees every gradient.
- *     Only calls that are given a non-NULL host result pointer synchronise
- *     the context stream.
+ *     gpt_make_batch, gpt_forward_loss, gpt_adamw_step, gpt_get_tensor and
+ *     gpt_set_tensor; after gpt_adamw_step the next gpt_forward_loss waits
+ *     for the update piece by piece (vectors, wte and wpe, then each layer's
+ *     matrices) before it first reads them, and gpt_make_batch does not wait
+ *     for it.  Work the caller enqueues on the context stream sees every
+ *     gradient and updated parameter only after one of these joins (or
+ *     gpt_get_tensor).  Only calls that are given a non-NULL host result
+ *     pointer synchronise the context stream.
  *   - the library never allocates device memory: the caller owns the
  *     arena and every buffer passed in.
  */
