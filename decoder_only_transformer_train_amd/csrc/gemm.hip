@@ -8,11 +8,13 @@
 // k with XOR-permuted 16-byte chunks and are read with ds_read_b128;
 // row-contiguous operands (the weight- and data-gradient products) sit as rows
 // of k-rows and are read with the LDS transpose read ds_read_b64_tr_b16, so no
-// operand is ever transposed in registers.  Two tiles: 256x128 with 3 stages
-// of 32 k and two workgroups per CU (one's epilogue overlaps the other's main
-// loop), and 256x256 with 2 stages of 64 k for very large outputs.  Workgroup:
-// 4 waves in 2x2, each owning a (BM/2) x (BN/2) sub-tile.  fp32 products (16x16x4
-// f32 MFMA) use a register-staged 128x128 kernel with padded LDS rows.
+// operand is ever transposed in registers.  Every bf16 product runs a 256x256
+// tile of 8 waves (2 x 4 sub-tiles of 128 x 64, two waves per SIMD, so one
+// issues its loads while the other keeps the MFMA pipe busy) with 2 stages of
+// 64 k and one workgroup per CU, or its 256x192 variant (4 x 2 sub-tiles of
+// 64 x 96) where that fills the CUs better; 4-wave 256x128 and 256x256 tiles
+// stay selectable for tuning.  fp32 products (16x16x4 f32 MFMA) use a
+// register-staged 128x128 kernel with padded LDS rows.
 // Operands are read through buffer descriptors whose range ends at the
 // operand, so loads past M, N or K return zeros without a branch.  Epilogues
 // stage the accumulators through LDS so bias, residual and GELU work uses
