@@ -832,9 +832,10 @@ int gpt_adamw_step(gpt_ctx* x, float lr, float beta1, float beta2, float eps, fl
     ProfScope ps(x, "adamw", 0.0, (double)x->P * (4.0 + (x->shadow ? 30.0 : 28.0)), x->side);
     HIPCHK(gk::sumsq_partial(x->grads, x->P, x->norm_part, &nblk, s));
     HIPCHK(gk::norm_finish(x->norm_part, nblk, grad_clip, x->scal, s));
+    // the step counter and step size on s too: gpt_step_count reads them there
+    HIPCHK(gk::adamw_prep(x->scal, lr, beta1, beta2, x->step_dev, s));
     HIPCHK(hipEventRecord(x->norm_done, s));
     HIPCHK(hipStreamWaitEvent(x->side, x->norm_done, 0));
-    HIPCHK(gk::adamw_prep(x->scal, lr, beta1, beta2, x->step_dev, x->side));
     auto piece = [&](int64_t lo, int64_t hi, int k) -> int {
       HIPCHK(gk::adamw_range(x->params, x->grads, x->m, x->v, x->shadow, lo, hi, x->P_decay, x->scal, lr, beta1,
                              beta2, eps, weight_decay, x->side));
