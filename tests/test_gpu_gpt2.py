@@ -101,6 +101,8 @@ def test_bf16_adamw_update_matches_oracle():
     stream = synthetic.zipf_eot_stream(257, cfg.vocab, seed=4)
     g, p, G = check_step(cfg, stream, seed=4)
     g.adamw_step(**configs.ADAMW)
+    # read straight after the update, before any call that joins the second stream
+    assert g.step_count() == 1
     ref = oracle.adamw_step(p, G, {k: 0 * v for k, v in G.items()}, {k: 0 * v for k, v in G.items()}, 1,
                             6e-4, 0.9, 0.95, 1e-8, 0.1)
     for k in g.names:
