@@ -851,6 +851,25 @@ __global__ void splitk_reduce(const float* __restrict__ ws, int splits, int M, i
   float* c = out + m * ldc + n;
   *c = accumulate ? *c + s : s;
 }
+// the same four columns at a time (N and ldc multiples of 4, 16-byte aligned rows)
+__global__ void splitk_reduce4(const float* __restrict__ ws, int splits, int M, int N, float* out, int64_t ldc,
+                               int accumulate) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
+  const int64_t total = (int64_t)M * N;
+  if (4 * i >= total) return;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int z = 0; z < splits; ++z) {
+    const float4 v = *reinterpret_cast<const float4*>(ws + (int64_t)z * total + 4 * i);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  const int64_t m = 4 * i / N, n = 4 * i % N;
+  float4* c = reinterpret_cast<float4*>(out + m * ldc + n);
+  if (accumulate) {
+    const float4 o = *c;
+    s = make_float4(o.x + s.x, o.y + s.y, o.z + s.z, o.w + s.w);
+  }
+  *c = s;
+}
 
 // Timing events of the main kernel: when both are set they are attached to
 // its dispatch (hipExtLaunchKernel), so timing adds no packets to the stream.
@@ -1040,8 +1059,12 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main, hipEvent_t 
   if (e == hipSuccess && after_main && !ev.start) e = hipEventRecord(after_main, s);
   if (e != hipSuccess || splits <= 1) return e;
   const int64_t total = (int64_t)g.M * g.N;
-  hipLaunchKernelGGL(splitk_reduce, dim3(cdiv(total, 256)), dim3(256), 0, s, g.ws, splits, g.M,
-                     g.N, reinterpret_cast<float*>(g.C), g.ldc, g.accumulate);
+  if ((g.N & 3) == 0 && (g.ldc & 3) == 0 && ((uintptr_t)g.C & 15) == 0 && ((uintptr_t)g.ws & 15) == 0)
+    hipLaunchKernelGGL(splitk_reduce4, dim3(cdiv(total / 4, 256)), dim3(256), 0, s, g.ws, splits, g.M, g.N,
+                       reinterpret_cast<float*>(g.C), g.ldc, g.accumulate);
+  else
+    hipLaunchKernelGGL(splitk_reduce, dim3(cdiv(total, 256)), dim3(256), 0, s, g.ws, splits, g.M,
+                       g.N, reinterpret_cast<float*>(g.C), g.ldc, g.accumulate);
   return hipGetLastError();
 }
 
