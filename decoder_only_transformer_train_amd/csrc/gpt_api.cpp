@@ -785,15 +785,22 @@ int gpt_backward(gpt_ctx* x) {
   // join: every side product (the head's dW among them) is done before the
   // embedding backward adds into G(wte), the parameter reduction and AdamW
   if (int e = join_side(x)) return e;
-  // embeddings: token rows (deterministic segmented sum) and positions
+  // embeddings: token rows (deterministic segmented sum) on s; positions and
+  // the batched reduction of the bias / LayerNorm partials (which write other
+  // tensors) beside it on the side stream, which every later reader joins
+  if (ss) {
+    HIPCHK(hipEventRecord(x->fwd_start, s));
+    HIPCHK(hipStreamWaitEvent(ss, x->fwd_start, 0));
+  }
+  hipStream_t s2 = ss ? ss : s;
   {
     ProfScope ps(x, "embed_bwd", 0.0, (double)N * C * 12);
     HIPCHK(gk::embed_bwd_ws(x->keys, (int)N, x->dres, (int)C, x->dln, x->G_(T_WTE), s));
-    HIPCHK(gk::wpe_bwd(x->dres, (int)x->B, (int)x->T, (int)C, x->G_(T_WPE), acc, s));
+    HIPCHK(gk::wpe_bwd(x->dres, (int)x->B, (int)x->T, (int)C, x->G_(T_WPE), acc, s2));
   }
   {
-    ProfScope ps(x, "param_reduce", 0.0, 0.0);
-    HIPCHK(gk::reduce_jobs(x->jobs_dev, (int)x->jobs.size(), x->nred_blocks, acc, s));
+    ProfScope ps(x, "param_reduce", 0.0, 0.0, s2);
+    HIPCHK(gk::reduce_jobs(x->jobs_dev, (int)x->jobs.size(), x->nred_blocks, acc, s2));
   }
   x->others_fresh = false;
   x->fwd_grad = false;

@@ -22,8 +22,9 @@
  *   - all GPU work is enqueued on the context's HIP stream (hipStream_t
  *     passed as void*; NULL means the default stream), except the weight-
  *     gradient products of the backward and of the tied head, the token sort
- *     of the embedding gradient and the AdamW update itself, which run on a
- *     second stream the context owns.  That stream starts from events on the
+ *     of the embedding gradient, the position-embedding gradient, the final
+ *     reduction of the bias and LayerNorm gradients, and the AdamW update
+ *     itself, which run on a second stream the context owns.  That stream starts from events on the
  *     context stream and is joined back into it (the context stream waits
  *     for it) before gpt_backward's embedding step and at the start of
  *     gpt_make_batch, gpt_forward_loss, gpt_adamw_step, gpt_get_tensor and
