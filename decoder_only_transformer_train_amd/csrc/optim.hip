@@ -190,29 +190,17 @@ __global__ __launch_bounds__(256) void embed_bwd_chunk_kernel(const uint32_t* __
   const int i0 = blockIdx.x * 64, i1 = min(n, i0 + 64);
   const uint32_t pmask = (1u << shift) - 1u;
   const int nc = C >> 2;
-  constexpr int U = 8;  // rows whose loads are in flight together (the adds stay in row order)
   for (int j = threadIdx.x; j < nc; j += 256) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     int run = i0;
-    for (int ib = i0; ib < i1; ib += U) {
-      uint32_t k[U];
-      float4 v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (ib + u < i1) {
-          k[u] = keys[ib + u];
-          v[u] = load4(dres + (int64_t)(k[u] & pmask) * C + 4 * j);
-        }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = ib + u;
-        if (i >= i1) break;
-        acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
-        if (i == i1 - 1 || (keys[i + 1] >> shift) != (k[u] >> shift)) {
-          store4(part + (int64_t)run * C + 4 * j, acc);
-          acc = make_float4(0.f, 0.f, 0.f, 0.f);
-          run = i + 1;
-        }
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t k = keys[i];
+      const float4 v = load4(dres + (int64_t)(k & pmask) * C + 4 * j);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      if (i == i1 - 1 || (keys[i + 1] >> shift) != (k >> shift)) {
+        store4(part + (int64_t)run * C + 4 * j, acc);
+        acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        run = i + 1;
       }
     }
   }
