@@ -1,13 +1,22 @@
-"""Training throughput of the GPT-2 124M step on one MI355X.
+"""Training throughput of the GPT-2 training step on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--breakdown]
-                [--roofline-kernel CLASS] [--copy-calibration BYTES]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--repeats R] [--config NAME]
+                [--no-cpu-baseline] [--breakdown] [--roofline-kernel CLASS]
+                [--copy-calibration BYTES]
 
-One step = make_batch (B*T+1 tokens of a seeded synthetic Zipf(1.1) stream
-with end-of-text separators) -> forward + fused head/CE -> backward -> AdamW,
-all through libgpt.so.  Prints one JSON line with tokens/s, MFU, the
-roofline of one kernel (timed with HIP events on the library's stream inside
-the timed region) and the fp64 CPU oracle timed on a bounded sample.
+--config gpt2-124m (default, the headline workload: B=16, T=1024), gpt2-350m
+(B=8), gpt2-1.5b (B=4 x 4 accumulation micro-steps) or lmhead (the isolated
+LM head + cross-entropy, N=65536, V=50257, C=768).
+
+One step = per micro-step make_batch (B*T+1 tokens of a seeded synthetic
+Zipf(1.1) stream with end-of-text separators) -> forward + head/CE ->
+backward, then AdamW, all through libgpt.so.  W warm-up steps, then R loops
+of K timed steps, each between torch.cuda.synchronize() calls; the line
+reports the median loop.  It carries tokens/s, MFU, the roofline of the
+dominant kernel (timed with HIP events on the library's stream in the last
+step of the last loop), the rates of a few more kernel classes (timed in
+extra steps after the loops) and the fp64 CPU oracle timed on the GPU's own
+step-1 weights and window.
 
 The roofline's "traffic" (HBM bytes per launch of that kernel) comes from
 profiles/traffic.json, written from two rocprofv3 --pmc runs (FETCH_SIZE,
@@ -21,8 +30,8 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
+import statistics
 import sys
 import time
 
@@ -36,8 +45,18 @@ PROFILE_CLASSES = ["gemm_qkv_fwd", "gemm_proj_fwd", "gemm_fc_fwd", "gemm_mlpproj
                    "gemm_dgrad_attn", "gemm_wgrad_mlp", "gemm_wgrad_attn", "attn_fwd", "attn_bwd",
                    "layernorm_fwd", "layernorm_bwd", "head_logits", "head_ce", "head_dx", "head_dw",
                    "bias_colsum", "param_reduce", "embed_bwd", "adamw"]
+# further classes reported beside the dominant one (one extra step each)
+MORE_CLASSES = ["gemm_fc_fwd", "attn_fwd", "head_logits", "layernorm_fwd", "adamw"]
 METRIC = "train tokens/sec + MFU, GPT-2 124M B=16 T=1024 bf16, 1×MI355X"
 
+WORKLOADS = {
+    "gpt2-124m": "GPT-2 124M training step: L=12, C=768, H=12, V=50257 padded to 50304, T=1024, B=16",
+    "gpt2-350m": "GPT-2 350M training step: L=24, C=1024, H=16, V=50257 padded to 50304, T=1024, B=8",
+    "gpt2-1.5b": ("GPT-2 1.5B training step: L=48, C=1600, H=25, V=50257 padded to 50304, T=1024, "
+                  "B=4 x 4 gradient-accumulation micro-steps"),
+}
+WORKLOAD_TAIL = (", bf16 GEMM/attention operands with fp32 master weights and AdamW state; Zipf(1.1) tokens "
+                 "with end-of-text every Geometric(1/600), random init")
 
 # sources whose change invalidates stored counter readings of a kernel class
 KERNEL_SOURCES = {
@@ -55,90 +74,119 @@ def sources_sha(kernel_class):
     return h.hexdigest()
 
 
-def stored_traffic(kernel_class):
+def stored_traffic(kernel_class, workload):
     """HBM bytes per launch measured by counters, or None when absent or stale."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f)
+            recs = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel") != kernel_class or rec.get("sources_sha256") != sources_sha(kernel_class):
-        return None
-    return rec.get("bytes_per_launch")
+    for rec in recs if isinstance(recs, list) else [recs]:
+        if (rec.get("kernel") == kernel_class and rec.get("workload", "gpt2-124m") == workload
+                and rec.get("sources_sha256") == sources_sha(kernel_class)):
+            return rec.get("bytes_per_launch")
+    return None
 
 
-def model_flops_per_token(L, C, T, Vp):
-    """3 x forward matmul FLOPs per token; attention counts the causal pairs only."""
-    fwd = 2 * 12 * C * C * L + 2 * 2 * C * L * (T + 1) / 2 + 2 * C * Vp
-    return 3.0 * fwd
-
-
-def cpu_baseline(cfg, seconds_cap=30.0):
-    """fp64 oracle on one 1024-token sequence (fwd + bwd) plus AdamW over all parameters."""
-    import numpy as np
-    import oracle
-    from decoder_only_transformer_train_amd import synthetic
+def host_info():
+    """CPU model, usable cores, BLAS library and its thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", None
     try:
         from threadpoolctl import threadpool_info
-        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer')})"
+                threads = int(i.get("num_threads", 1))
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    p = synthetic.init_params(cfg.n_layer, cfg.n_embd, cfg.padded_vocab, cfg.max_seq, seed=0)
-    toks = synthetic.zipf_eot_stream(cfg.seq + 1, cfg.vocab, seed=0)
-    x, y = oracle.make_batch(toks, 0, 1, cfg.seq)
-    t0 = time.perf_counter()
-    loss, _, G = oracle.loss_and_grads(p, x, y, cfg.n_head)
-    t_row = time.perf_counter() - t0
-    m = {k: np.zeros(a.shape) for k, a in p.items()}
-    v = {k: np.zeros(a.shape) for k, a in p.items()}
-    t0 = time.perf_counter()
-    oracle.adamw_step(p, G, m, v, 1, 6e-4, 0.9, 0.95, 1e-8, 0.1)
-    t_adam = time.perf_counter() - t0
-    step_s = cfg.batch * t_row + t_adam
-    return {"value": round(cfg.batch * cfg.seq / step_s, 2), "unit": "tokens/s", "cores": threads,
+        pass
+    cores = len(os.sched_getaffinity(0))
+    return model, cores, blas, threads if threads else cores
+
+
+def cpu_baseline(cfg, params, stream, repeats):
+    """fp64 oracle: forward+backward of the first sequence of the GPU's first window, on the
+    GPU's own initial weights, plus AdamW over all parameters; median of `repeats` runs."""
+    import numpy as np
+    import oracle
+    model, cores, blas, threads = host_info()
+    x, y = oracle.make_batch(stream, 0, cfg.batch, cfg.seq)
+    rows, adams = [], []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        _, _, G = oracle.loss_and_grads(params, x[:1], y[:1], cfg.n_head)
+        rows.append(time.perf_counter() - t0)
+        m = {k: np.zeros(a.shape) for k, a in params.items()}
+        v = {k: np.zeros(a.shape) for k, a in params.items()}
+        t0 = time.perf_counter()
+        oracle.adamw_step(params, G, m, v, 1, 6e-4, 0.9, 0.95, 1e-8, 0.1)
+        adams.append(time.perf_counter() - t0)
+        del G, m, v
+    t_row, t_adam = statistics.median(rows), statistics.median(adams)
+    n_rows = cfg.batch * cfg.accum
+    step_s = n_rows * t_row + t_adam
+    return {"value": round(n_rows * cfg.seq / step_s, 2), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": (f"fp64 NumPy oracle: forward+backward of 1 of the {cfg.batch} sequences "
-                       f"({cfg.seq} tokens) in {t_row:.2f} s and AdamW over all parameters in "
-                       f"{t_adam:.2f} s, scaled to one {cfg.batch}x{cfg.seq} step"),
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "sample": (f"fp64 NumPy oracle on the GPU's own initial weights and first window: forward+backward "
+                       f"of sequence 0 ({cfg.seq} tokens) in {t_row:.2f} s and AdamW over all parameters in "
+                       f"{t_adam:.2f} s (medians of {repeats}), scaled to one step of {n_rows} sequences"),
+            "cpu_model": model, "host_cpus": cores, "blas": blas, "blas_threads": threads}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", action="store_true")
-    # the largest kernel class that runs alone: the backward's two streams and the head's dW share the GPU
-    ap.add_argument("--roofline-kernel", default="gemm_fc_fwd", choices=PROFILE_CLASSES)
-    ap.add_argument("--copy-calibration", type=int, default=0,
-                    help="after the timed steps, copy this many bytes device-to-device once")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
-              file=sys.stderr)
-        sys.exit(2)
+def rate(r):
+    """Algorithmic rate of a profiled class against its roofline."""
+    if r["launches"] == 0 or r["ms"] <= 0:
+        return None
+    avg_ms = r["ms"] / r["launches"]
+    if r["flops"] > 0:
+        a = r["flops"] / r["launches"] / (avg_ms / 1e3)
+        return {"bound": "mfma", "achieved": round(a / 1e12, 2), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": round(a / PEAK_BF16, 4), "avg_launch_ms": round(avg_ms, 4), "launches": r["launches"]}
+    a = r["bytes"] / r["launches"] / (avg_ms / 1e3)
+    return {"bound": "hbm", "achieved": round(a / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM, 4), "avg_launch_ms": round(avg_ms, 4), "launches": r["launches"]}
 
+
+def copy_calibration(nbytes):
     import torch
-    from decoder_only_transformer_train_amd import binding, configs, synthetic
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
 
-    cfg = configs.GPT2_124M
-    B, T = cfg.batch, cfg.seq
-    W, K = args.warmup, args.steps
-    n_tok = (W + K) * B * T + 1
+
+def bench_model(args, name):
+    import torch
+    from decoder_only_transformer_train_amd import accounting, binding, configs, synthetic
+
+    cfg = configs.PRESETS[name]
+    B, T, A = cfg.batch, cfg.seq, cfg.accum
+    W, K, R = args.warmup, args.steps, args.repeats
+    n_tok = (W + K * R + 2 + len(MORE_CLASSES)) * A * B * T + 1
     stream = synthetic.zipf_eot_stream(n_tok, cfg.vocab, seed=0)
     g = binding.GPT(cfg, seed=0, device="cuda:0")
-    s = g.stream
+    init_params = None if args.no_cpu_baseline else g.get_all(binding.PARAM)  # the step-1 weights
     adam = configs.ADAMW
 
     def step(pos):
-        g.make_batch(stream, pos)
-        g.forward_loss(1.0, sync=False)
-        g.backward()
+        for _ in range(A):
+            g.make_batch(stream, pos)
+            g.forward_loss(1.0 / A, sync=False)
+            g.backward()
+            pos = binding.next_start(pos, len(stream), B, T)
         g.adamw_step(**adam, grad_clip=0.0, sync=False)
-        return binding.next_start(pos, len(stream), B, T)
+        return pos
 
     pos = 0
     for _ in range(W):
@@ -146,7 +194,7 @@ def main():
     torch.cuda.synchronize()
     g.read_losses()
 
-    breakdown = None
+    breakdown = rates = None
     if args.breakdown:
         # per kernel class: time per step and the class's algorithmic rate against its peak
         # (classes on the backward's second stream share the GPU with the first stream)
@@ -156,69 +204,144 @@ def main():
             step(0)
             r = g.profile_end()
             breakdown[cls] = round(r["ms"], 3)
-            if r["ms"] > 0 and r["flops"] > 0:
-                a = r["flops"] / (r["ms"] / 1e3)
-                rates[cls] = {"TFLOP/s": round(a / 1e12, 1), "frac": round(a / PEAK_BF16, 3)}
-            elif r["ms"] > 0 and r["bytes"] > 0:
-                a = r["bytes"] / (r["ms"] / 1e3)
-                rates[cls] = {"GB/s": round(a / 1e9, 1), "frac": round(a / PEAK_HBM, 3)}
+            rates[cls] = rate(r)
         g.read_losses()
 
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        # the roofline kernel is timed in the last timed step: its events put
-        # barrier packets around each launch (a few us of idle GPU each), which
-        # the other steps are spared
-        if i == K - 1:
-            g.profile_begin(args.roofline_kernel)
-        pos = step(pos)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    prof = g.profile_end()
+    loops = []
+    prof = None
+    for rep in range(R):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            # the roofline kernel is timed in the last step of the last loop: its events put
+            # barrier packets around each launch (a few us of idle GPU each), which the other
+            # steps are spared
+            if rep == R - 1 and i == K - 1:
+                g.profile_begin(args.roofline_kernel)
+            pos = step(pos)
+        torch.cuda.synchronize()
+        loops.append(time.perf_counter() - t0)
+        if rep == R - 1:
+            prof = g.profile_end()
     losses = g.read_losses()
+    more = {}
+    for cls in MORE_CLASSES:
+        if cls == args.roofline_kernel:
+            continue
+        g.profile_begin(cls)
+        pos = step(pos)
+        more[cls] = rate(g.profile_end())
+    g.read_losses()
 
-    tokens = K * B * T
+    dt = statistics.median(loops)
+    tokens = K * A * B * T
     tps = tokens / dt
-    fpt = model_flops_per_token(cfg.n_layer, cfg.n_embd, T, cfg.padded_vocab)
+    fpt = accounting.training_flops_per_token(cfg.n_layer, cfg.n_embd, T, cfg.padded_vocab)
     mfu = tps * fpt / PEAK_BF16
-    avg_ms = prof["ms"] / max(1, prof["launches"])
-    if prof["flops"] > 0:
-        achieved = prof["flops"] / max(1, prof["launches"]) / (avg_ms / 1e3)
-        roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_BF16 / 1e12,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4), "traffic": None}
-    else:
-        achieved = prof["bytes"] / max(1, prof["launches"]) / (avg_ms / 1e3)
-        roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4), "traffic": None}
-    roof["traffic"] = stored_traffic(args.roofline_kernel)
-    roof.update({"kernel": args.roofline_kernel, "avg_launch_ms": round(avg_ms, 4),
-                 "launches": prof["launches"]})
+    roof = rate(prof)
+    roof["traffic"] = stored_traffic(args.roofline_kernel, name)
+    roof["kernel"] = args.roofline_kernel
     if args.copy_calibration > 0:
-        n = args.copy_calibration // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_calibration(args.copy_calibration)
     out = {
-        "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "metric": METRIC if name == "gpt2-124m" else f"train tokens/sec + MFU, {WORKLOADS[name].split(':')[0]}, 1×MI355X",
+        "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(dt / K * 1e3, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": ("GPT-2 124M training step: L=12, C=768, H=12, V=50257 padded to 50304, "
-                                "T=1024, B=16, bf16 GEMM/attention operands with fp32 master weights "
-                                "and AdamW state; Zipf(1.1) tokens with end-of-text every "
-                                "Geometric(1/600), random init"),
-                   "global_batch": B, "seq_len": T, "tokens_per_step": B * T},
-        "mfu": round(mfu, 4), "model_tflop_per_step": round(fpt * B * T / 1e12, 3),
+        "config": {"workload": WORKLOADS[name] + WORKLOAD_TAIL, "global_batch": B * A, "seq_len": T,
+                   "tokens_per_step": A * B * T, "accumulation": A},
+        "mfu": round(mfu, 4), "model_tflop_per_step": round(fpt * A * B * T / 1e12, 3),
+        "repeats_ms_per_step": [round(x / K * 1e3, 3) for x in loops],
         "final_loss": float(losses[-1]) if len(losses) else None,
         "roofline": roof,
+        "kernel_rates": more,
     }
     if breakdown is not None:
         out["breakdown_ms"] = breakdown
         out["breakdown_rate"] = rates
+    g.close()
+    del g
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg)
+        out["cpu_baseline"] = cpu_baseline(cfg, init_params, stream, 3 if name == "gpt2-124m" else 1)
+    return out
+
+
+def bench_lmhead(args):
+    """The isolated LM head + cross-entropy: loss, dX and dW of N=65536 rows, V=50257, C=768."""
+    import numpy as np
+    import torch
+    from decoder_only_transformer_train_amd import accounting, binding, synthetic
+
+    N, V, C = 65536, 50257, 768
+    X, Wt, y = synthetic.lmhead_inputs(N, V, C, seed=1)
+    Xd = torch.from_numpy(synthetic.bf16_bits(X).view(np.int16)).cuda()
+    Wd = torch.from_numpy(synthetic.bf16_bits(Wt).view(np.int16)).cuda()
+    yd = torch.from_numpy(np.ascontiguousarray(y, np.int32)).cuda()
+    run = binding.LMHead(N, V, C, binding.GPT_BF16)
+    for _ in range(args.warmup):
+        run(Xd, Wd, yd)
+    loops = []
+    s = torch.cuda.current_stream()
+    for _ in range(args.repeats):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run(Xd, Wd, yd)
+        torch.cuda.synchronize()
+        loops.append(time.perf_counter() - t0)
+    # one more call between HIP events on the stream the call runs on
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    run(Xd, Wd, yd)
+    e1.record(s)
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1)
+    dt = statistics.median(loops) / args.steps
+    flops = accounting.lmhead_flops(N, V, C)
+    roof = {"bound": "mfma", "achieved": round(flops / (call_ms / 1e3) / 1e12, 2), "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s", "frac": round(flops / (call_ms / 1e3) / PEAK_BF16, 4),
+            "traffic": stored_traffic("lmhead", "lmhead"), "kernel": "lmhead (whole call)",
+            "avg_launch_ms": round(call_ms, 4), "launches": 1}
+    out = {
+        "metric": "LM head + cross-entropy tokens/sec (loss, dX, dW), N=65536 V=50257 C=768 bf16, 1×MI355X",
+        "value": round(N / dt, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": ("LM head + cross-entropy in isolation: X [65536, 768] ~ N(0,1), W [50257, 768] "
+                                "~ N(0, 0.02), bf16, Zipf(1.1) targets, seed 1; loss, dX and dW")},
+        "model_tflop_per_step": round(flops / 1e12, 3), "tflops": round(flops / dt / 1e12, 2),
+        "repeats_ms_per_step": [round(x / args.steps * 1e3, 3) for x in loops],
+        "loss": float(run.loss.item()),
+        "roofline": roof,
+    }
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--repeats", type=int, default=3)
+    ap.add_argument("--config", default="gpt2-124m", choices=list(WORKLOADS) + ["lmhead"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true")
+    # the dominant kernel class of the step (largest share of the step's kernel time)
+    ap.add_argument("--roofline-kernel", default="attn_bwd", choices=PROFILE_CLASSES)
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="after the timed steps, copy this many bytes device-to-device once")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.repeats < 1 or args.warmup < 0:
+        print("need --steps >= 1, --repeats >= 1, --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+    out = bench_lmhead(args) if args.config == "lmhead" else bench_model(args, args.config)
     print(json.dumps(out), flush=True)
 
 

@@ -210,27 +210,37 @@ class GPT:
         return dict(ms=ms.value, launches=n.value, flops=fl.value, bytes=by.value)
 
 
+class LMHead:
+    """Buffers for repeated gpt_lmhead_ce calls of one shape: workspace, loss [1], dX [N, C], dW [V, C]."""
+
+    def __init__(self, N: int, V: int, C: int, dtype: int, want_grads: bool = True, device="cuda:0"):
+        import torch
+        lib = load()
+        self.N, self.V, self.C, self.dtype = N, V, C, dtype
+        self.ws_n = int(lib.gpt_lmhead_ce_ws_bytes(N, V, C, dtype))
+        if self.ws_n == 0:
+            raise GPTError(GPT_EINVAL, "bad lmhead_ce shape")
+        self.ws = torch.empty(self.ws_n, dtype=torch.uint8, device=device)
+        self.loss = torch.empty(1, dtype=torch.float32, device=device)
+        self.dX = torch.empty((N, C), dtype=torch.float32, device=device) if want_grads else None
+        self.dW = torch.empty((V, C), dtype=torch.float32, device=device) if want_grads else None
+
+    def __call__(self, X, W, y, stream=None):
+        import torch
+        if tuple(X.shape) != (self.N, self.C) or tuple(W.shape) != (self.V, self.C) or y.numel() != self.N:
+            raise ValueError("lmhead_ce: shapes do not match the buffers")
+        s = stream if stream is not None else torch.cuda.current_stream(X.device)
+        ptr = lambda t: c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+        _check(load().gpt_lmhead_ce(ptr(X), ptr(W), ptr(y), self.N, self.V, self.C, self.dtype, ptr(self.loss),
+                                    ptr(self.dX), ptr(self.dW), ptr(self.ws), self.ws_n, c_void_p(s.cuda_stream)))
+        return self.loss, self.dX, self.dW
+
+
 def lmhead_ce(X, W, y, dtype: int, want_grads: bool = True, stream=None):
     """Fused LM head + CE on device tensors X [N, C], W [V, C] (fp32, or bf16 bits as int16/bf16), y int32 [N].
 
     Returns (loss tensor [1], dX [N, C] or None, dW [V, C] or None), all fp32 device tensors.
     """
-    import torch
-    lib = load()
     N, C = X.shape
     V = W.shape[0]
-    dev = X.device
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
-    ws_n = int(lib.gpt_lmhead_ce_ws_bytes(N, V, C, dtype))
-    if ws_n == 0:
-        raise GPTError(GPT_EINVAL, "bad lmhead_ce shape")
-    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
-    loss = torch.empty(1, dtype=torch.float32, device=dev)
-    dX = torch.empty((N, C), dtype=torch.float32, device=dev) if want_grads else None
-    dW = torch.empty((V, C), dtype=torch.float32, device=dev) if want_grads else None
-    _check(lib.gpt_lmhead_ce(c_void_p(X.data_ptr()), c_void_p(W.data_ptr()), c_void_p(y.data_ptr()),
-                             N, V, C, dtype, c_void_p(loss.data_ptr()),
-                             c_void_p(dX.data_ptr()) if dX is not None else None,
-                             c_void_p(dW.data_ptr()) if dW is not None else None,
-                             c_void_p(ws.data_ptr()), ws_n, c_void_p(s.cuda_stream)))
-    return loss, dX, dW
+    return LMHead(N, V, C, dtype, want_grads, device=X.device)(X, W, y, stream)

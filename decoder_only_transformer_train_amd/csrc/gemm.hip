@@ -1046,9 +1046,15 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main, hipEvent_t 
   if ((!g.a_trans && g.lda < kpad) || (!g.b_trans && g.ldb < kpad)) return hipErrorInvalidValue;
 
   if (splits > 1) {
+    // never more partial slices than the workspace holds
+    const int64_t fit = g.ws_floats / ((int64_t)g.M * g.N);
+    if (fit < splits) splits = (int)std::max<int64_t>(1, fit);
+  }
+  if (splits > 1) {
     const int kps = cdiv(cdiv(g.K, splits), bk) * bk;
     p.k_per_split = kps;
     splits = cdiv(g.K, kps);
+    if ((int64_t)splits * g.M * g.N > g.ws_floats) return hipErrorInvalidValue;
   } else {
     p.k_per_split = g.K;
   }

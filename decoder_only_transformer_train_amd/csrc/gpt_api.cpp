@@ -119,6 +119,7 @@ struct gpt_ctx {
   bool adam_pending = false;
   bool dz_busy[2] = {false, false};
   float *Dv, *lnf_part, *splitk_ws;
+  int64_t splitk_n = 0;  // floats in splitk_ws
   gk::RedJob* jobs_dev;
   std::vector<gk::RedJob> jobs;
   int nred_blocks = 0;
@@ -199,10 +200,17 @@ std::vector<TensorDesc> make_tensors(const gpt_config* c, int64_t* P, int64_t* P
   return t;
 }
 
-// split-K partial sums of the head's data gradient for a row chunk of Nc rows
-int64_t head_splitk_floats(int64_t Nc, int64_t C, int64_t V) {
-  const int sp = gk::gemm_pick_splits((int)Nc, (int)C, (int)V, 0, 1);
-  return sp > 1 ? (int64_t)sp * Nc * C : 0;
+// split-K partial sums of the head's data gradient over N rows in chunks of
+// Nc: the largest need of the chunk sizes that occur (Nc, and the ragged last
+// chunk N % Nc, which has fewer tiles and may take more splits)
+int64_t head_splitk_floats(int64_t N, int64_t Nc, int64_t C, int64_t V) {
+  int64_t best = 0;
+  for (int64_t rows : {std::min(Nc, N), N % Nc}) {
+    if (rows <= 0) continue;
+    const int sp = gk::gemm_pick_splits((int)rows, (int)C, (int)V, 0, 1);
+    if (sp > 1) best = std::max(best, (int64_t)sp * rows * C);
+  }
+  return best;
 }
 
 int64_t splitk_floats(int64_t N, int64_t C) {
@@ -270,8 +278,8 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->Dv = cv.take<float>(nh * 4);
   x->lnf_part = cv.take<float>(nlnb * 3 * C * 4);
   x->jobs_dev = cv.take<gk::RedJob>((8 * x->L + 3) * (int64_t)sizeof(gk::RedJob));
-  x->splitk_ws = cv.take<float>(
-      std::max<int64_t>(1, std::max(splitk_floats(N, C), head_splitk_floats(x->Nc, C, x->Vp))) * 4);
+  x->splitk_n = std::max<int64_t>(1, std::max(splitk_floats(N, C), head_splitk_floats(N, x->Nc, C, x->Vp)));
+  x->splitk_ws = cv.take<float>(x->splitk_n * 4);
   x->keys = cv.take<uint32_t>(N * 4);
   x->norm_part = cv.take<float>(gk::sumsq_blocks(x->P) * 4);
   x->scal = cv.take<float>(64);
@@ -402,6 +410,7 @@ int wgrad(gpt_ctx* x, const char* cls, const void* dY, int64_t ldy, const void* 
   g.accumulate = acc;
   g.splits = gk::gemm_pick_splits((int)M, (int)Nn, (int)x->N, 1, 1);
   g.ws = x->splitk_ws;
+  g.ws_floats = x->splitk_n;
   return run_gemm(x, cls, g, x->side);
 }
 
@@ -444,7 +453,8 @@ int join_side(gpt_ctx* x) {
 // and into the next chunk's logits (chunks alternate between two dz buffers).
 int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C,
          float scale, float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, void* logits,
-         void* const dzb[2], int64_t ldv, int64_t Nc, int dtype, float* ws, float* loss, float* ring, int slot) {
+         void* const dzb[2], int64_t ldv, int64_t Nc, int dtype, float* ws, int64_t ws_floats, float* loss, float* ring,
+         int slot, int* bad) {
   const bool side = x->side != nullptr;
   int ci = 0;
   for (int64_t c0 = 0; c0 < N; c0 += Nc, ++ci) {
@@ -463,7 +473,7 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
       const int es = dtype == GPT_BF16 ? 2 : 4;
       ProfScope ps(x, "head_ce", 0.0, (double)rows * V * (es + (scale > 0 ? es : 0)));
       HIPCHK(gk::ce_rows(dtype, logits, ldv, (int)V, y + c0, (int)rows, scale, tok_loss + c0, tok_lse + c0,
-                         scale > 0 ? dz : nullptr, x->stream));
+                         scale > 0 ? dz : nullptr, bad, x->stream));
     }
     // the mean loss as soon as the last rows' losses exist: one workgroup, which
     // would otherwise wait behind the dW product's workgroups for a free CU
@@ -493,6 +503,7 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
         d.dtype = dtype;
         d.splits = gk::gemm_pick_splits((int)rows, (int)C, (int)V, 0, 1);  // few output tiles, long K
         d.ws = ws;
+        d.ws_floats = ws_floats;
         if (run_gemm(x, "head_dx", d)) return GPT_EHIP;
       }
       if (dw_here && run_gemm(x, "head_dw", w)) return GPT_EHIP;
@@ -675,7 +686,8 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
   const bool grad = loss_scale > 0.f;
   if (int e = head(x, x->lnf, x->W_(T_WTE), x->Vp, yt, N, C, grad ? scale : 0.f, x->tok_loss, x->tok_lse,
                    grad ? x->dF : nullptr, grad ? x->G_(T_WTE) : nullptr, x->wte_fresh ? 0 : 1, x->logits, x->dz2,
-                   x->ldv, x->Nc, x->dt, x->splitk_ws, x->loss, x->ring, (int)(x->ring_wr % RING)))
+                   x->ldv, x->Nc, x->dt, x->splitk_ws, x->splitk_n, x->loss, x->ring, (int)(x->ring_wr % RING),
+                   nullptr))
     return e;
   if (grad) x->wte_fresh = false;
   x->ring_wr++;
@@ -875,10 +887,11 @@ int gpt_adamw_step(gpt_ctx* x, float lr, float beta1, float beta2, float eps, fl
 
 size_t gpt_lmhead_ce_ws_bytes(int64_t N, int64_t V, int64_t C, int32_t dtype) {
   if (N < 1 || V < 1 || C < 64 || C % 64 || (dtype != GPT_F32 && dtype != GPT_BF16)) return 0;
+  if (N > 0x7fffffff || V > 0x7fffffff) return 0;
   const int64_t es = dtype == GPT_BF16 ? 2 : 4;
   const int64_t ldv = align_up(V, 64), Nc = std::min<int64_t>(N, 4096);
-  return (size_t)(2 * align_up(Nc * ldv * es, ALIGN) + 2 * align_up(N * 4, ALIGN) +
-                  align_up(std::max<int64_t>(1, head_splitk_floats(Nc, C, V)) * 4, ALIGN));
+  return (size_t)(2 * align_up(Nc * ldv * es, ALIGN) + 2 * align_up(N * 4, ALIGN) + ALIGN +
+                  align_up(std::max<int64_t>(1, head_splitk_floats(N, Nc, C, V)) * 4, ALIGN));
 }
 
 int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int64_t V, int64_t C, int32_t dtype,
@@ -886,7 +899,6 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
   const size_t need = gpt_lmhead_ce_ws_bytes(N, V, C, dtype);
   if (!need || !X || !W || !y || !loss_dev) return fail(GPT_EINVAL, "bad lmhead_ce arguments");
   if (!ws || ws_bytes < need) return fail(GPT_ENOMEM, "lmhead_ce workspace too small");
-  if (N > 0x7fffffff || V > 0x7fffffff) return fail(GPT_EINVAL, "N, V too large");
   gpt_ctx tmp;  // launch helpers only use the stream, dtype and profiling fields
   tmp.stream = (hipStream_t)hip_stream;
   tmp.dt = dtype;
@@ -897,12 +909,20 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
   void* dz = cv.take<void>(Nc * ldv * tmp.es);
   float* tl = cv.take<float>(N * 4);
   float* tlse = cv.take<float>(N * 4);
-  float* hws = cv.take<float>(std::max<int64_t>(1, head_splitk_floats(Nc, C, V)) * 4);
+  int* bad = cv.take<int>(ALIGN);
+  const int64_t hn = std::max<int64_t>(1, head_splitk_floats(N, Nc, C, V));
+  float* hws = cv.take<float>(hn * 4);
   const bool grad = dX || dW;
   void* const dzb[2] = {dz, dz};  // no side stream here: chunks run in order on one buffer
+  HIPCHK(gk::fill_f32((float*)bad, 1, 0.f, tmp.stream));
   if (int e = head(&tmp, X, W, V, y, N, C, grad ? 1.0f / (float)N : 0.f, tl, tlse, dX, dW, 0, logits, dzb, ldv, Nc,
-                   dtype, hws, loss_dev, nullptr, 0))
+                   dtype, hws, hn, loss_dev, nullptr, 0, bad))
     return e;
+  // out-of-range targets were clamped on the device; report them here
+  int flag = 0;
+  HIPCHK(hipMemcpyAsync(&flag, bad, 4, hipMemcpyDeviceToHost, tmp.stream));
+  HIPCHK(hipStreamSynchronize(tmp.stream));
+  if (flag) return fail(GPT_ERANGE, "a target id is outside [0, V)");
   return 0;
 }
 

@@ -38,14 +38,17 @@ struct Gemm {
   int accumulate = 0;
   float* dv = nullptr;  // EPI_STORE_ODOT: [rows / tn][heads][tn] row sums
   int tn = 0, heads = 0;
-  // split-K (EPI_F32 only): when > 1, partial sums go to ws [splits][M][N] and are reduced in order
+  // split-K (EPI_F32 only): when > 1, partial sums go to ws [splits][M][N] and are reduced in order;
+  // ws holds ws_floats floats and the split count is lowered until splits * M * N fits
   int splits = 1;
   float* ws = nullptr;
+  int64_t ws_floats = 0;
 };
 // after_main (nullable) is recorded right after the main kernel, before any split-K reduction;
 // with before_main too, both are attached to the main kernel's dispatch (its start and end)
 hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main = nullptr, hipEvent_t before_main = nullptr);
-// split count and workspace floats a wgrad GEMM of this shape would use
+// split count a GEMM of this shape with an fp32 output would use (its split-K
+// workspace is gemm_pick_splits(...) * M * N floats when that is > 1)
 int gemm_pick_splits(int M, int N, int K, int a_trans, int b_trans);
 
 // ---- LayerNorm ----
@@ -93,9 +96,11 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, c
 
 // ---- cross-entropy rows over a chunk of logits ----
 // z T [rows][ldz] (first V columns valid) -> loss[r] = lse - z[y]; lse_out[r];
-// if dz != null: dz T [rows][ldz] = (softmax - onehot) * scale, zero in [V, ldz)
+// if dz != null: dz T [rows][ldz] = (softmax - onehot) * scale, zero in [V, ldz).
+// A target outside [0, V) is clamped into the row (never read out of it) and,
+// when bad != null, sets *bad = 1 (the caller clears it first).
 hipError_t ce_rows(int dtype, const void* z, int64_t ldz, int V, const int32_t* y, int rows,
-                   float scale, float* loss, float* lse_out, void* dz, hipStream_t s);
+                   float scale, float* loss, float* lse_out, void* dz, int* bad, hipStream_t s);
 // mean of n floats in fixed order -> out[0] (and ring[slot] if ring != null)
 hipError_t mean_f32(const float* x, int n, float* out, float* ring, int slot, hipStream_t s);
 

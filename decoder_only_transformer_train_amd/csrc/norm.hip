@@ -327,6 +327,14 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict
 
 // Cross-entropy over one row of logits (CS336 page, section 1: subtract the
 // row maximum, log-sum-exp, minus the target logit).  One workgroup per row.
+// A target id outside [0, V) is clamped into the row before any load (the
+// row's loss is then meaningless) and flagged in *bad when bad is given.
+__device__ __forceinline__ int target_in_range(int yy, int V, int* bad, int t) {
+  if (yy >= 0 && yy < V) return yy;
+  if (bad != nullptr && t == 0) *bad = 1;
+  return yy < 0 ? 0 : V - 1;
+}
+
 // Logits z and dz are both T (bf16 logits are widened to fp32, as the page's
 // loss does, before any arithmetic).
 // With dz: dz = (softmax - onehot(y)) * scale, zero in the padding [V, ldz).
@@ -334,7 +342,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void ce_rows_kernel(const T* __restrict__ z, int64_t ldz, int V,
                                                       const int32_t* __restrict__ y, float scale,
                                                       float* __restrict__ loss, float* __restrict__ lse_out,
-                                                      T* __restrict__ dz) {
+                                                      T* __restrict__ dz, int* __restrict__ bad) {
   __shared__ float sm[4], ss[4];
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -378,7 +386,7 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const T* __restrict__ z, i
 #pragma unroll
   for (int i = 0; i < 4; ++i) S += ss[i] * hw_exp2((sm[i] - M) * LOG2E);
   const float lse = M + hw_log2(S) * LN2;
-  const int yy = y[row];
+  const int yy = target_in_range(y[row], V, bad, t);
   if (t == 0) {
     loss[row] = lse - to_f(zr[yy]);
     if (lse_out) lse_out[row] = lse;
@@ -433,7 +441,7 @@ template <typename T, int NV>
 __global__ __launch_bounds__(1024, sizeof(T) == 2 ? 8 : 4) void ce_reg_kernel(const T* __restrict__ z, int64_t ldz, int V,
                                                          const int32_t* __restrict__ y, float scale,
                                                          float* __restrict__ loss, float* __restrict__ lse_out,
-                                                         T* __restrict__ dz) {
+                                                         T* __restrict__ dz, int* __restrict__ bad) {
   using R = CeRow<T>;
   __shared__ float red[2][16];
   const int row = blockIdx.x;
@@ -481,7 +489,7 @@ __global__ __launch_bounds__(1024, sizeof(T) == 2 ? 8 : 4) void ce_reg_kernel(co
 #pragma unroll
   for (int i = 0; i < 16; ++i) S += red[1][i];
   const float lse = M + hw_log2(S) * LN2;
-  const int yy = y[row];
+  const int yy = target_in_range(y[row], V, bad, t);
   if (t == 0) {
     loss[row] = lse - to_f(zr[yy]);
     if (lse_out) lse_out[row] = lse;
@@ -657,33 +665,33 @@ hipError_t colsum_partial(int dtype, const void* x, int rows, int cols, float* p
 
 template <int NV>
 hipError_t ce_reg(int dtype, const void* z, int64_t ldz, int V, const int32_t* y, int rows, float scale, float* loss,
-                  float* lse_out, void* dz, hipStream_t s) {
+                  float* lse_out, void* dz, int* bad, hipStream_t s) {
   if (dtype == BF16)
     hipLaunchKernelGGL((ce_reg_kernel<bf16, NV>), dim3(rows), dim3(1024), 0, s, (const bf16*)z, ldz, V, y, scale,
-                       loss, lse_out, (bf16*)dz);
+                       loss, lse_out, (bf16*)dz, bad);
   else
     hipLaunchKernelGGL((ce_reg_kernel<float, NV>), dim3(rows), dim3(1024), 0, s, (const float*)z, ldz, V, y, scale,
-                       loss, lse_out, (float*)dz);
+                       loss, lse_out, (float*)dz, bad);
   return hipGetLastError();
 }
 
 hipError_t ce_rows(int dtype, const void* z, int64_t ldz, int V, const int32_t* y, int rows, float scale,
-                   float* loss, float* lse_out, void* dz, hipStream_t s) {
+                   float* loss, float* lse_out, void* dz, int* bad, hipStream_t s) {
   // rows of up to 64K columns are held in registers (one read of the logits)
   if (ldz % 4 == 0) {
     const int64_t nv = (ldz / 4 + 1023) / 1024;
-    if (nv <= 2) return ce_reg<2>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, s);
-    if (nv <= 4) return ce_reg<4>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, s);
-    if (nv <= 8) return ce_reg<8>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, s);
-    if (nv <= 13) return ce_reg<13>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, s);
-    if (nv <= 16) return ce_reg<16>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, s);
+    if (nv <= 2) return ce_reg<2>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, bad, s);
+    if (nv <= 4) return ce_reg<4>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, bad, s);
+    if (nv <= 8) return ce_reg<8>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, bad, s);
+    if (nv <= 13) return ce_reg<13>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, bad, s);
+    if (nv <= 16) return ce_reg<16>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, bad, s);
   }
   if (dtype == BF16)
     hipLaunchKernelGGL(ce_rows_kernel<bf16>, dim3(rows), dim3(256), 0, s, (const bf16*)z, ldz, V, y, scale, loss,
-                       lse_out, (bf16*)dz);
+                       lse_out, (bf16*)dz, bad);
   else
     hipLaunchKernelGGL(ce_rows_kernel<float>, dim3(rows), dim3(256), 0, s, (const float*)z, ldz, V, y, scale, loss,
-                       lse_out, (float*)dz);
+                       lse_out, (float*)dz, bad);
   return hipGetLastError();
 }
 

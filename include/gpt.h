@@ -168,17 +168,22 @@ int gpt_adamw_step(gpt_ctx* ctx, float lr, float beta1, float beta2, float eps,
                    float weight_decay, float grad_clip, float* grad_norm_host);
 
 /*
- * Fused LM head + cross-entropy on caller buffers, no model context
- * (Zero page, output layer: projection and cross-entropy in one operator so
- * that the [N, V] logits are never kept).
+ * LM head + cross-entropy on caller buffers, no model context (Zero page,
+ * output layer: the projection and the cross-entropy as one operator).
  *   X  device [N, C] rows (dtype: fp32 or bf16 bits), W device [V, C],
- *   y  device int32 [N] in [0, V).
+ *   y  device int32 [N], target ids in [0, V).
  *   loss_dev  device fp32 [1]: mean over N of logsumexp(X W^T)_n - (X W^T)_n,y_n.
  *   dX  device fp32 [N, C] (nullable): gradient of the mean loss w.r.t. X.
  *   dW  device fp32 [V, C] (nullable): gradient w.r.t. W (overwritten).
- *   ws  device workspace of at least gpt_lmhead_ce_ws_bytes(N, V, C, dtype).
- * C must be a multiple of 64.
- * Errors: EINVAL, ENOMEM (ws too small), EHIP.  Target ids are not checked.
+ *   ws  device workspace of at least gpt_lmhead_ce_ws_bytes(N, V, C, dtype)
+ *       bytes (0 for an invalid shape).  It holds the logits of one chunk of
+ *       at most 4096 rows and their gradient, both [rows, V] in dtype; rows
+ *       are processed chunk after chunk, so [N, V] is never kept at once.
+ * C must be a multiple of 64; N and V below 2^31.
+ * The call synchronises the stream at its end.  A target id outside [0, V)
+ * is clamped on the device (never read out of bounds) and the call returns
+ * ERANGE; loss and gradients are then not meaningful.
+ * Errors: EINVAL (shape, null pointer), ENOMEM (ws too small), ERANGE, EHIP.
  */
 size_t gpt_lmhead_ce_ws_bytes(int64_t N, int64_t V, int64_t C, int32_t dtype);
 int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int64_t V,

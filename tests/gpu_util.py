@@ -1,4 +1,7 @@
 """Helpers shared by the GPU tests (device contexts, comparison metrics)."""
+import os
+import time
+
 import numpy as np
 
 from decoder_only_transformer_train_amd import binding, synthetic
@@ -33,5 +36,17 @@ def init_for(cfg, seed=0):
     return synthetic.init_params(cfg.n_layer, cfg.n_embd, cfg.padded_vocab, cfg.max_seq, seed=seed)
 
 
+_PROGRESS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
+                         "gpu_test_progress.log")
+
+
 def announce(msg):
-    print(f"[gpu-test] {msg}", flush=True)
+    """Print a progress line, and append it to a log that shows a long test is alive."""
+    line = f"[gpu-test {time.strftime('%H:%M:%S')}] {msg}"
+    print(line, flush=True)
+    try:
+        os.makedirs(os.path.dirname(_PROGRESS), exist_ok=True)
+        with open(_PROGRESS, "a") as f:
+            f.write(line + "\n")
+    except OSError:
+        pass

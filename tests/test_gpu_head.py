@@ -1,11 +1,10 @@
 """The fused LM head + cross-entropy (gpt_lmhead_ce) against the oracle.
 
-The isolated-kernel workload: X [65536, 768] ~ N(0,1), W [50257, 768] ~
-N(0, 0.02), both bf16, Zipf(1.1) targets (seed 1); smaller sizes of the same
-problem are compared in full, the full size on sampled rows and invariants.
+The isolated-kernel workload: X [N, 768] ~ N(0,1), W [V, 768] ~ N(0, 0.02),
+both bf16, Zipf(1.1) targets (seed 1), compared in full at smaller sizes here
+(the full N=65536, V=50257 size is in test_gpu_stated.py), plus ragged row
+chunks at wide rows and out-of-range targets.
 """
-import math
-
 import numpy as np
 import pytest
 
@@ -52,24 +51,31 @@ def test_head_fp32_vs_oracle(N, V, C):
     assert rel_err(dW.cpu().numpy(), rdW) <= 1e-4
 
 
-def test_head_full_size_sampled():
-    N, V, C = 65536, 50257, 768
-    announce("head full size")
-    X, W, y = synthetic.lmhead_inputs(N, V, C, seed=1)
+@pytest.mark.parametrize("N,V,C", [(4352, 300, 1600), (4352, 300, 1280), (4100, 257, 2048)])
+def test_head_ragged_last_chunk_wide_rows(N, V, C):
+    # more rows than one 4096-row chunk with a short last chunk, at widths whose data-gradient
+    # product takes more K-splits for the short chunk: its partial sums must fit the workspace
+    announce(f"head bf16 N={N} V={V} C={C}")
+    X, W, y = synthetic.lmhead_inputs(N, V, C, seed=2)
     loss, dX, dW = binding.lmhead_ce(*to_dev(X, W, y, binding.GPT_BF16), binding.GPT_BF16)
-    loss = loss.item()
-    # Gaussian logits of variance C * 0.02^2 (unit X): E[loss] ~ ln V + sigma^2 / 2
-    assert abs(loss - (math.log(V) + C * 0.02 ** 2 / 2)) < 0.05
-    rows = np.random.default_rng(0).choice(N, 256, replace=False)
-    dXh = dX[rows].cpu().numpy()
-    rl, per, rdX, _ = oracle.lmhead_ce(X[rows], W, y[rows])
-    # dX rows of the full problem carry 1/N instead of 1/len(rows)
-    assert cosine(dXh * N / len(rows), rdX) >= 0.999
-    # the sampled rows' losses reproduce the oracle's mean over those rows
-    announce("head full size: property checks")
-    dWh = dW.cpu().numpy()
-    # every row of dz sums to zero, so the columns of dW sum to (almost) zero
-    col = dWh.sum(axis=0)
-    assert np.linalg.norm(col) <= 1e-3 * np.linalg.norm(dWh)
-    # rows of classes never targeted only get the softmax part: dW[v] = sum_n p_nv X_n / N
-    assert np.isfinite(dWh).all() and np.isfinite(dX.cpu().numpy()).all()
+    rl, _, rdX, rdW = oracle.lmhead_ce(X, W, y)
+    assert abs(loss.item() - rl) <= 2e-2
+    assert cosine(dX.cpu().numpy(), rdX) >= 0.999
+    assert cosine(dW.cpu().numpy(), rdW) >= 0.999
+
+
+def test_head_target_out_of_range_is_erange():
+    import torch
+    N, V, C = 256, 100, 64
+    X, W, y = synthetic.lmhead_inputs(N, V, C, seed=3)
+    for bad in (V, -1, 1 << 30):
+        yb = y.copy()
+        yb[37] = bad
+        with pytest.raises(binding.GPTError) as e:
+            binding.lmhead_ce(*to_dev(X, W, yb, binding.GPT_BF16), binding.GPT_BF16)
+        assert e.value.code == binding.GPT_ERANGE
+    # a valid call on the same buffers afterwards is clean
+    loss, _, _ = binding.lmhead_ce(*to_dev(X, W, y, binding.GPT_BF16), binding.GPT_BF16)
+    rl, _, _, _ = oracle.lmhead_ce(X, W, y)
+    assert abs(loss.item() - rl) <= 2e-2
+    torch.cuda.synchronize()
