@@ -23,7 +23,8 @@ EXPORTS = [
     "gpt_arena_bytes", "gpt_init", "gpt_destroy", "gpt_make_batch", "gpt_next_start",
     "gpt_forward_loss", "gpt_backward", "gpt_adamw_step", "gpt_lmhead_ce_ws_bytes", "gpt_lmhead_ce",
     "gpt_num_tensors", "gpt_tensor_info", "gpt_get_tensor", "gpt_set_tensor",
-    "gpt_get_batch", "gpt_get_token_losses", "gpt_read_losses", "gpt_step_count", "gpt_profile_begin",
+    "gpt_get_batch", "gpt_get_token_losses", "gpt_read_losses", "gpt_step_count", "gpt_set_step_count",
+    "gpt_profile_begin",
     "gpt_profile_end", "gpt_last_error",
 ]
 
@@ -72,6 +73,7 @@ def load():
         "gpt_get_token_losses": (c_int, [c_void_p, c_void_p, c_int64]),
         "gpt_read_losses": (c_int, [c_void_p, c_void_p, c_int]),
         "gpt_step_count": (c_int64, [c_void_p]),
+        "gpt_set_step_count": (c_int, [c_void_p, c_int64]),
         "gpt_profile_begin": (c_int, [c_void_p, c_char_p]),
         "gpt_profile_end": (c_int, [c_void_p, P(c_double), P(c_int64), P(c_double), P(c_double)]),
         "gpt_last_error": (c_char_p, []),
@@ -199,6 +201,9 @@ class GPT:
 
     def step_count(self) -> int:
         return _check(load().gpt_step_count(self._ctx))
+
+    def set_step_count(self, t: int):
+        _check(load().gpt_set_step_count(self._ctx, int(t)))
 
     # ---- timing ----
     def profile_begin(self, cls: str):

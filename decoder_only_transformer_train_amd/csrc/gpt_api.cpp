@@ -1032,6 +1032,16 @@ int64_t gpt_step_count(const gpt_ctx* xc) {
   return t;
 }
 
+int gpt_set_step_count(gpt_ctx* x, int64_t t) {
+  if (!x) return fail(GPT_EINVAL, "null context");
+  if (t < 0 || t > 0x7fffffff) return fail(GPT_EINVAL, "step count outside [0, 2^31)");
+  if (int e = join_side(x)) return e;  // an update still queued on the side stream reads the counter's step size
+  const int v = (int)t;
+  HIPCHK(hipMemcpyAsync(x->step_dev, &v, 4, hipMemcpyHostToDevice, x->stream));
+  HIPCHK(hipStreamSynchronize(x->stream));
+  return 0;
+}
+
 int gpt_profile_begin(gpt_ctx* x, const char* cls) {
   if (!x || !cls) return fail(GPT_EINVAL, "null argument");
   x->prof.cls = cls;

@@ -223,6 +223,17 @@ int gpt_read_losses(gpt_ctx* ctx, float* host, int max);
 int64_t gpt_step_count(const gpt_ctx* ctx);
 
 /*
+ * Set the AdamW step counter t, so that a context restored from a checkpoint
+ * (parameters, m and v through gpt_set_tensor) applies the bias corrections
+ * of the next update exactly as the uninterrupted run would ("Chapter 28
+ * Data, evaluation and resume", 28.6: exact resume needs the optimiser's
+ * internal state and the index of the next update; CS336 page, section 3,
+ * Checkpoint).  t in [0, 2^31).  Synchronises the stream.
+ * Errors: EINVAL, EHIP.
+ */
+int gpt_set_step_count(gpt_ctx* ctx, int64_t t);
+
+/*
  * Kernel timing for measurement.  gpt_profile_begin(ctx, cls) starts
  * recording HIP events around every launch of kernel class `cls` on the
  * context stream (classes: "gemm_fc_fwd", "attn_fwd", "attn_bwd",

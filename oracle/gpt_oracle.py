@@ -15,8 +15,9 @@ beyond what that definition states.  Sources, by page title and section:
   [D]  "Chapter 28 Data, evaluation and resume", section 28.3 (how B x T + 1
        tokens become one batch).
   [C]  "Implementing an LLM from scratch (CS336) - pretraining", section 1
-       (training objective, cross-entropy), section 2 (AdamW, gradient
-       clipping), section 4 (resource accounting, FLOPs and MFU).
+       (training objective, cross-entropy), section 2 (AdamW, learning-rate
+       schedule, gradient clipping), section 4 (resource accounting, FLOPs
+       and MFU).
   [Z]  "GPT training" (Zero framework), sections autoregressive objective,
        Embedding, Attention, Transformer Block and output layer.
 
@@ -335,6 +336,27 @@ def train_step(params, x, y, n_head, lr=6e-4, betas=(0.9, 0.95), eps=1e-8,
         v = {k: np.zeros(np.shape(a)) for k, a in params.items()}
     P2, M2, V2 = adamw_step(params, G, m, v, t, lr, betas[0], betas[1], eps, weight_decay)
     return dict(loss=loss, per_row=per_row, grads=G, params=P2, m=M2, v=V2, grad_norm=norm)
+
+
+# --------------------------------------------------------------------------
+# Learning-rate schedule ([C] section 2 learning-rate schedule; [R] LR schedule)
+# --------------------------------------------------------------------------
+
+def lr_schedule(step: int, max_lr: float, min_lr: float, warmup: int, total: int) -> float:
+    """Learning rate at schedule step `step` (counted from 0).
+
+    Linear warm-up from 0 to max_lr over the first `warmup` steps, then a
+    half cosine from max_lr down to min_lr, reached at step `total`; from
+    there on it stays at min_lr.  Requires 0 <= warmup < total.
+    """
+    if not (0 <= warmup < total):
+        raise ValueError("need 0 <= warmup < total")
+    if step < warmup:
+        return max_lr * step / warmup
+    if step >= total:
+        return min_lr
+    frac = (step - warmup) / (total - warmup)
+    return min_lr + (max_lr - min_lr) * 0.5 * (1.0 + math.cos(math.pi * frac))
 
 
 # --------------------------------------------------------------------------

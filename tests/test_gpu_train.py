@@ -1,0 +1,102 @@
+"""The multi-step driver on the GPU: overfitting one batch, the first steps against the
+oracle's loop (schedule and clipping on), the fixed-window validation loss, and exact
+resume from a checkpoint ("Chapter 28", 28.6: after restoring, every parameter matches
+the uninterrupted run with maximum error 0)."""
+import numpy as np
+import pytest
+
+import oracle
+from decoder_only_transformer_train_amd import binding, configs, synthetic, train
+from gpu_util import announce, context, init_for, rel_err
+
+pytestmark = pytest.mark.gpu
+
+CFG = configs.TINY_F32
+
+
+def test_overfit_one_batch_loss_falls():
+    announce("driver: overfit one batch")
+    p = init_for(CFG)
+    toks = synthetic.uniform_tokens(CFG.batch * CFG.seq + 1, CFG.vocab, seed=0)  # one window: the cursor stays
+    g = context(CFG, p)
+    tr = train.Trainer(g, toks, toks, train.Schedule(3e-3, 3e-4, 5, 100), val_batches=1)
+    recs = tr.run(100, val_every=50)
+    losses = [r["train_loss"] for r in recs]
+    assert losses[0] > 5.0
+    assert losses[-1] < 0.2 * losses[0], losses[-1]
+    assert recs[-1]["val_loss"] < recs[49]["val_loss"] < losses[0]
+    assert g.step_count() == 100
+    assert recs[0]["lr"] == 0.0 and recs[5]["lr"] == pytest.approx(3e-3)
+
+
+def test_driver_first_steps_match_oracle_loop():
+    announce("driver: 6 steps with schedule and clipping vs oracle")
+    p = init_for(CFG, seed=2)
+    n = 4 * CFG.batch * CFG.seq + 1
+    toks = synthetic.uniform_tokens(n, CFG.vocab, seed=2)
+    sched = train.Schedule(2e-3, 2e-4, 2, 6)
+    g = context(CFG, p)
+    tr = train.Trainer(g, toks, schedule=sched, optim=train.OptimConfig(grad_clip=1.0))
+    recs = tr.run(6)
+    P, m, v, pos = p, None, None, 0
+    for t in range(6):
+        x, y = oracle.make_batch(toks, pos, CFG.batch, CFG.seq)
+        r = oracle.train_step(P, x, y, CFG.n_head, lr=oracle.lr_schedule(t, 2e-3, 2e-4, 2, 6), grad_clip=1.0,
+                              m=m, v=v, t=t + 1)
+        assert abs(recs[t]["train_loss"] - r["loss"]) <= 1e-4 * r["loss"], (t, recs[t]["train_loss"], r["loss"])
+        assert abs(recs[t]["grad_norm"] - r["grad_norm"]) <= 1e-4 * r["grad_norm"]
+        P, m, v = r["params"], r["m"], r["v"]
+        pos = oracle.next_start(pos, n, CFG.batch, CFG.seq)
+    for k in g.names:
+        assert rel_err(g.get(k) - p[k], P[k] - p[k]) <= 2e-3, k
+
+
+def test_validation_loss_fixed_windows():
+    announce("driver: validation loss")
+    p = init_for(CFG, seed=4)
+    toks = synthetic.uniform_tokens(2 * CFG.batch * CFG.seq + 1, CFG.vocab, seed=4)
+    val = synthetic.uniform_tokens(5 * CFG.batch * CFG.seq + 1, CFG.vocab, seed=5)
+    g = context(CFG, p)
+    tr = train.Trainer(g, toks, val, train.Schedule(1e-3, 1e-4, 1, 10), val_batches=3)
+    tr.run(2)
+    params = g.get_all(binding.PARAM)
+    vl = tr.validate()
+    assert tr.validate() == vl  # the same windows every time
+    ref, pos = [], 0
+    for _ in range(3):
+        x, y = oracle.make_batch(val, pos, CFG.batch, CFG.seq)
+        ref.append(oracle.forward(params, x, y, CFG.n_head, keep=False)[0])
+        pos = oracle.next_start(pos, len(val), CFG.batch, CFG.seq)
+    assert abs(vl - np.mean(ref)) <= 1e-4 * np.mean(ref)
+    # forward-only validation left the optimiser state alone
+    assert g.step_count() == 2
+
+
+@pytest.mark.parametrize("cfg", [CFG, configs.GPT2_124M.with_(n_layer=1, batch=2, seq=128, max_seq=128)],
+                         ids=["tiny-fp32", "124m-shaped-bf16"])
+def test_checkpoint_exact_resume(cfg, tmp_path):
+    announce(f"driver: exact resume ({cfg.n_layer}L C={cfg.n_embd})")
+    p = init_for(cfg, seed=6)
+    if cfg.vocab > 1000:
+        toks = synthetic.zipf_eot_stream(7 * cfg.batch * cfg.seq + 1, cfg.vocab, seed=6)
+    else:
+        toks = synthetic.uniform_tokens(7 * cfg.batch * cfg.seq + 1, cfg.vocab, seed=6)
+    sched = train.Schedule(1e-3, 1e-4, 2, 8)
+    ck = str(tmp_path / "ck.npz")
+    a = train.Trainer(context(cfg, p), toks, schedule=sched, accum=2)
+    a.run(3)
+    a.save(ck)
+    ra = a.run(2)
+    b = train.Trainer(context(cfg, init_for(cfg, seed=9)), toks, schedule=train.Schedule(), accum=1)
+    meta = b.load(ck)
+    assert meta["adam_t"] == 3 and meta["next_step"] == 3 and b.accum == 2
+    rb = b.run(2)
+    assert [r["train_loss"] for r in ra] == [r["train_loss"] for r in rb]
+    assert [r["lr"] for r in ra] == [r["lr"] for r in rb]
+    assert a.gpt.step_count() == b.gpt.step_count() == 5
+    for kind in (binding.PARAM, binding.ADAM_M, binding.ADAM_V):
+        A, Bv = a.gpt.get_all(kind), b.gpt.get_all(kind)
+        for k in A:
+            assert np.max(np.abs(A[k] - Bv[k])) == 0.0, (kind, k)
+    with pytest.raises(ValueError):
+        train.Trainer(context(cfg, p), toks[:-1]).load(ck)  # another stream

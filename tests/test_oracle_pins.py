@@ -304,3 +304,29 @@ def test_bench_flops_at_124m_match_oracle():
     a = accounting.training_flops_per_token(12, 768, 1024, 50304)
     assert a == pytest.approx(oracle.training_flops_per_token(12, 768, 1024, 50304), rel=1e-14)
     assert a * 16 * 1024 == pytest.approx(13.0756e12, rel=1e-4)
+
+
+# ---- CS336 page, section 2 (learning-rate schedule); lecture, LR schedule ----
+
+def test_lr_schedule_boundaries_and_shape():
+    mx, mn, wu, tot = 6e-4, 6e-5, 10, 100  # lecture: decays to about 10% of the 6e-4 peak
+    # warm-up starts from zero and reaches the peak exactly at its end
+    assert oracle.lr_schedule(0, mx, mn, wu, tot) == 0.0
+    assert oracle.lr_schedule(wu, mx, mn, wu, tot) == mx
+    assert oracle.lr_schedule(wu // 2, mx, mn, wu, tot) == pytest.approx(mx / 2, rel=1e-15)
+    # the decay ends at the minimum at the total step and stays there
+    assert oracle.lr_schedule(tot, mx, mn, wu, tot) == mn
+    assert oracle.lr_schedule(10 * tot, mx, mn, wu, tot) == mn
+    # half-way through the decay the half cosine is at the mean of peak and floor
+    assert oracle.lr_schedule((wu + tot) // 2, mx, mn, wu, tot) == pytest.approx((mx + mn) / 2, rel=1e-12)
+    # the last decay step is just above the floor: cosine of (1 - 1/90) pi
+    last = oracle.lr_schedule(tot - 1, mx, mn, wu, tot)
+    assert mn < last < mn + (mx - mn) * 1e-3
+    # rising during warm-up, falling during the decay
+    lrs = [oracle.lr_schedule(t, mx, mn, wu, tot) for t in range(tot + 1)]
+    assert all(a < b for a, b in zip(lrs[:wu], lrs[1:wu + 1]))
+    assert all(a > b for a, b in zip(lrs[wu:tot], lrs[wu + 1:tot + 1]))
+    with pytest.raises(ValueError):
+        oracle.lr_schedule(0, mx, mn, 10, 10)
+    # no warm-up: the schedule starts at the peak
+    assert oracle.lr_schedule(0, mx, mn, 0, tot) == mx
