@@ -94,10 +94,7 @@ struct gpt_ctx {
   std::vector<Layer> layers;
   void* lnf;
   float *muf, *rsf;
-  // head
-  int64_t ldv, Nc;
-  void* logits;   // T [Nc][ldv]
-  void* dz2[2];   // T [Nc][ldv], alternating per chunk (the head's dW runs on the side stream)
+  // head: per-row losses and log-sum-exps, the gradient at the final LayerNorm output
   float *tok_loss, *tok_lse, *dF, *loss;
   float* ring;
   int ring_wr = 0, ring_rd = 0;
@@ -108,7 +105,7 @@ struct gpt_ctx {
   // weight-gradient products run on a second stream, ordered by events
   hipStream_t side = nullptr;
   std::vector<hipEvent_t> sev;
-  hipEvent_t head_ready[2] = {nullptr, nullptr}, head_done[2] = {nullptr, nullptr}, side_tail = nullptr;
+  hipEvent_t head_fork = nullptr, side_tail = nullptr;  // head_fork: pass 1 done, the tied dW may start
   hipEvent_t fwd_start = nullptr;  // the forward's start, for side-stream work that needs only the batch
   // AdamW runs on the side stream in pieces (all vectors, wte + wpe, then each
   // layer's matrices); the next forward waits for each piece where it first
@@ -117,7 +114,6 @@ struct gpt_ctx {
   std::vector<hipEvent_t> adam_ev;
   hipEvent_t norm_done = nullptr;
   bool adam_pending = false;
-  bool dz_busy[2] = {false, false};
   float *Dv, *lnf_part, *splitk_ws;
   int64_t splitk_n = 0;  // floats in splitk_ws
   gk::RedJob* jobs_dev;
@@ -149,7 +145,8 @@ int check_cfg(const gpt_config* c) {
   if (c->dtype != GPT_F32 && c->dtype != GPT_BF16) return fail(GPT_EINVAL, "dtype must be GPT_F32 or GPT_BF16");
   if (c->n_layer < 1 || c->n_embd < 64 || c->n_head < 1 || c->vocab < 1 || c->batch < 1 || c->seq < 1)
     return fail(GPT_EINVAL, "sizes must be positive (n_embd >= 64)");
-  if (c->n_embd % 64 != 0 || c->n_embd > 2048) return fail(GPT_EINVAL, "n_embd must be a multiple of 64, <= 2048");
+  if (c->n_embd % 64 != 0 || c->n_embd > gk::lmhead_max_embd(c->dtype))
+    return fail(GPT_EINVAL, "n_embd must be a multiple of 64, <= 1792 (bf16) or 1024 (fp32)");
   if (c->n_embd % c->n_head != 0) return fail(GPT_EINVAL, "n_embd % n_head != 0");
   const int D = c->n_embd / c->n_head;
   if (c->dtype == GPT_BF16 && D != 64) return fail(GPT_EINVAL, "bf16 head size must be 64");
@@ -200,19 +197,6 @@ std::vector<TensorDesc> make_tensors(const gpt_config* c, int64_t* P, int64_t* P
   return t;
 }
 
-// split-K partial sums of the head's data gradient over N rows in chunks of
-// Nc: the largest need of the chunk sizes that occur (Nc, and the ragged last
-// chunk N % Nc, which has fewer tiles and may take more splits)
-int64_t head_splitk_floats(int64_t N, int64_t Nc, int64_t C, int64_t V) {
-  int64_t best = 0;
-  for (int64_t rows : {std::min(Nc, N), N % Nc}) {
-    if (rows <= 0) continue;
-    const int sp = gk::gemm_pick_splits((int)rows, (int)C, (int)V, 0, 1);
-    if (sp > 1) best = std::max(best, (int64_t)sp * rows * C);
-  }
-  return best;
-}
-
 int64_t splitk_floats(int64_t N, int64_t C) {
   int64_t best = 0;
   const int64_t shapes[4][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}};
@@ -259,9 +243,6 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->lnf = cv.take<void>(N * C * es);
   x->muf = cv.take<float>(N * 4);
   x->rsf = cv.take<float>(N * 4);
-  x->logits = cv.take<void>(x->Nc * x->ldv * es);
-  x->dz2[0] = cv.take<void>(x->Nc * x->ldv * es);
-  x->dz2[1] = x->N > x->Nc ? cv.take<void>(x->Nc * x->ldv * es) : x->dz2[0];  // a second chunk alternates
   x->tok_loss = cv.take<float>(N * 4);
   x->tok_lse = cv.take<float>(N * 4);
   x->dF = cv.take<float>(N * C * 4);
@@ -278,7 +259,7 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->Dv = cv.take<float>(nh * 4);
   x->lnf_part = cv.take<float>(nlnb * 3 * C * 4);
   x->jobs_dev = cv.take<gk::RedJob>((8 * x->L + 3) * (int64_t)sizeof(gk::RedJob));
-  x->splitk_n = std::max<int64_t>(1, std::max(splitk_floats(N, C), head_splitk_floats(N, x->Nc, C, x->Vp)));
+  x->splitk_n = std::max<int64_t>(1, splitk_floats(N, C));
   x->splitk_ws = cv.take<float>(x->splitk_n * 4);
   x->keys = cv.take<uint32_t>(N * 4);
   x->norm_part = cv.take<float>(gk::sumsq_blocks(x->P) * 4);
@@ -329,10 +310,6 @@ void setup_dims(gpt_ctx* x, const gpt_config* c) {
   x->T = c->seq;
   x->B = c->batch;
   x->N = x->B * x->T;
-  x->ldv = align_up(x->Vp, 64);
-  // the head runs as one chunk of all N <= 16384 rows: measured faster than 4096- or
-  // 8192-row chunks (fewer, fuller launches; the dW product overlaps the backward instead)
-  x->Nc = x->N;
   x->tensors = make_tensors(c, &x->P, &x->P_decay);
 }
 
@@ -442,72 +419,31 @@ int join_side(gpt_ctx* x) {
   if (!x->side) return 0;
   HIPCHK(hipEventRecord(x->side_tail, x->side));
   HIPCHK(hipStreamWaitEvent(x->stream, x->side_tail, 0));
-  x->dz_busy[0] = x->dz_busy[1] = false;
   return 0;
 }
 
-// The fused tied head + cross-entropy over row chunks: logits of a chunk (in
-// the compute type, as the bf16 matrix product of the pages' mixed precision
-// leaves them) live only in the chunk buffer; loss, dF and dW come out of the same pass.  With a
-// side stream, a chunk's dW product runs there, beside the chunk's dF product
-// and into the next chunk's logits (chunks alternate between two dz buffers).
-int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C,
-         float scale, float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, void* logits,
-         void* const dzb[2], int64_t ldv, int64_t Nc, int dtype, float* ws, int64_t ws_floats, float* loss, float* ring,
+// The tied head fused with the cross-entropy (no [N, V] logits anywhere):
+// pass 1 - per-row loss and log-sum-exp and, with gradients, dF - on the
+// context stream, then the fixed-order mean of the row losses; pass 2 - the
+// head's part of the tied weight's gradient, which only the embedding step of
+// the backward reads - on the side stream when there is one, beside the
+// backward of the blocks.
+int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C, float scale,
+         float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, int dtype, float* loss, float* ring,
          int slot, int* bad) {
-  const bool side = x->side != nullptr;
-  int ci = 0;
-  for (int64_t c0 = 0; c0 < N; c0 += Nc, ++ci) {
-    const int b = ci & 1;
-    void* dz = dzb[b];
-    const int64_t rows = std::min(Nc, N - c0);
-    const void* Fc = (const char*)Fin + c0 * C * (dtype == GPT_BF16 ? 2 : 4);
-    gk::Gemm g = mk(x, 0, 0, gk::EPI_STORE, Fc, C, W, C, rows, V, C, logits, ldv);  // T logits, no bias
-    g.dtype = dtype;
-    if (run_gemm(x, "head_logits", g)) return GPT_EHIP;
-    if (side && x->dz_busy[b]) {  // an earlier chunk's dW still reads this dz buffer
-      HIPCHK(hipStreamWaitEvent(x->stream, x->head_done[b], 0));
-      x->dz_busy[b] = false;
+  {
+    ProfScope ps(x, "head_fwd", (dF ? 4.0 : 2.0) * N * V * C, 0.0);
+    HIPCHK(gk::lmhead_fwd(dtype, Fin, W, (int)N, (int)V, (int)C, y, scale, tok_loss, tok_lse, dF, bad, x->stream));
+  }
+  HIPCHK(gk::mean_f32(tok_loss, (int)N, loss, ring, slot, x->stream));
+  if (dW) {
+    hipStream_t ds = x->side ? x->side : x->stream;
+    if (x->side) {
+      HIPCHK(hipEventRecord(x->head_fork, x->stream));
+      HIPCHK(hipStreamWaitEvent(x->side, x->head_fork, 0));
     }
-    {
-      const int es = dtype == GPT_BF16 ? 2 : 4;
-      ProfScope ps(x, "head_ce", 0.0, (double)rows * V * (es + (scale > 0 ? es : 0)));
-      HIPCHK(gk::ce_rows(dtype, logits, ldv, (int)V, y + c0, (int)rows, scale, tok_loss + c0, tok_lse + c0,
-                         scale > 0 ? dz : nullptr, bad, x->stream));
-    }
-    // the mean loss as soon as the last rows' losses exist: one workgroup, which
-    // would otherwise wait behind the dW product's workgroups for a free CU
-    if (c0 + rows >= N) HIPCHK(gk::mean_f32(tok_loss, (int)N, loss, ring, slot, x->stream));
-    if (scale > 0) {
-      // dW (on the side stream when there is one) and dF both read only dz
-      // and operands of the forward, so they run side by side: dF's split-K
-      // product has few output tiles and leaves most of the chip to dW.
-      bool dw_here = false;
-      gk::Gemm w;
-      if (dW) {
-        w = mk(x, 1, 1, gk::EPI_F32, dz, ldv, Fc, C, V, C, rows, dW, C);
-        w.dtype = dtype;
-        w.accumulate = (c0 > 0) || dW_acc;
-        if (side) {
-          HIPCHK(hipEventRecord(x->head_ready[b], x->stream));
-          HIPCHK(hipStreamWaitEvent(x->side, x->head_ready[b], 0));
-          if (run_gemm(x, "head_dw", w, x->side)) return GPT_EHIP;
-          HIPCHK(hipEventRecord(x->head_done[b], x->side));
-          x->dz_busy[b] = true;
-        } else {
-          dw_here = true;
-        }
-      }
-      if (dF) {
-        gk::Gemm d = mk(x, 0, 1, gk::EPI_F32, dz, ldv, W, C, rows, C, V, dF + c0 * C, C);
-        d.dtype = dtype;
-        d.splits = gk::gemm_pick_splits((int)rows, (int)C, (int)V, 0, 1);  // few output tiles, long K
-        d.ws = ws;
-        d.ws_floats = ws_floats;
-        if (run_gemm(x, "head_dx", d)) return GPT_EHIP;
-      }
-      if (dw_here && run_gemm(x, "head_dw", w)) return GPT_EHIP;
-    }
+    ProfScope ps(x, "head_dw", 2.0 * N * V * C, 0.0, ds);
+    HIPCHK(gk::lmhead_dw(dtype, Fin, W, (int)N, (int)V, (int)C, y, tok_lse, scale, dW, dW_acc, ds));
   }
   return 0;
 }
@@ -564,10 +500,7 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
   chk(hipStreamCreateWithFlags(&x->side, hipStreamNonBlocking));
   x->sev.assign((size_t)x->L * 8, nullptr);
   for (auto& e : x->sev) chk(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-  for (int b = 0; b < 2; ++b) {
-    chk(hipEventCreateWithFlags(&x->head_ready[b], hipEventDisableTiming));
-    chk(hipEventCreateWithFlags(&x->head_done[b], hipEventDisableTiming));
-  }
+  chk(hipEventCreateWithFlags(&x->head_fork, hipEventDisableTiming));
   chk(hipEventCreateWithFlags(&x->side_tail, hipEventDisableTiming));
   chk(hipEventCreateWithFlags(&x->fwd_start, hipEventDisableTiming));
   chk(hipEventCreateWithFlags(&x->norm_done, hipEventDisableTiming));
@@ -589,8 +522,7 @@ int gpt_destroy(gpt_ctx* x) {
     if (e) (void)hipEventDestroy(e);
   for (auto e : x->adam_ev)
     if (e) (void)hipEventDestroy(e);
-  for (hipEvent_t e : {x->head_ready[0], x->head_ready[1], x->head_done[0], x->head_done[1], x->side_tail, x->fwd_start,
-                       x->norm_done})
+  for (hipEvent_t e : {x->head_fork, x->side_tail, x->fwd_start, x->norm_done})
     if (e) (void)hipEventDestroy(e);
   if (x->side) (void)hipStreamDestroy(x->side);
   delete x;
@@ -631,8 +563,9 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
   const int64_t N = x->N, C = x->C;
   const int32_t* xt = x->win;
   const int32_t* yt = x->win + 1;
-  // a previous call's head dW may still read lnf / dz and write G(wte); after
-  // an update the side stream holds only AdamW pieces, waited for piece by piece
+  // a previous call's head dW may still read lnf and the log-sum-exps and write
+  // G(wte); after an update the side stream holds only AdamW pieces, waited for
+  // piece by piece
   const bool adam = x->adam_pending;
   x->adam_pending = false;
   if (adam) HIPCHK(hipStreamWaitEvent(s, x->adam_ev[1], 0));  // vectors, then wte and wpe
@@ -685,9 +618,8 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
   const float scale = loss_scale / (float)N;
   const bool grad = loss_scale > 0.f;
   if (int e = head(x, x->lnf, x->W_(T_WTE), x->Vp, yt, N, C, grad ? scale : 0.f, x->tok_loss, x->tok_lse,
-                   grad ? x->dF : nullptr, grad ? x->G_(T_WTE) : nullptr, x->wte_fresh ? 0 : 1, x->logits, x->dz2,
-                   x->ldv, x->Nc, x->dt, x->splitk_ws, x->splitk_n, x->loss, x->ring, (int)(x->ring_wr % RING),
-                   nullptr))
+                   grad ? x->dF : nullptr, grad ? x->G_(T_WTE) : nullptr, x->wte_fresh ? 0 : 1, x->dt, x->loss, x->ring,
+                   (int)(x->ring_wr % RING), nullptr))
     return e;
   if (grad) x->wte_fresh = false;
   x->ring_wr++;
@@ -887,11 +819,10 @@ int gpt_adamw_step(gpt_ctx* x, float lr, float beta1, float beta2, float eps, fl
 
 size_t gpt_lmhead_ce_ws_bytes(int64_t N, int64_t V, int64_t C, int32_t dtype) {
   if (N < 1 || V < 1 || C < 64 || C % 64 || (dtype != GPT_F32 && dtype != GPT_BF16)) return 0;
-  if (N > 0x7fffffff || V > 0x7fffffff) return 0;
-  const int64_t es = dtype == GPT_BF16 ? 2 : 4;
-  const int64_t ldv = align_up(V, 64), Nc = std::min<int64_t>(N, 4096);
-  return (size_t)(2 * align_up(Nc * ldv * es, ALIGN) + 2 * align_up(N * 4, ALIGN) + ALIGN +
-                  align_up(std::max<int64_t>(1, head_splitk_floats(N, Nc, C, V)) * 4, ALIGN));
+  if (N > 0x7fffffff || V > 0x7fffffff || C > gk::lmhead_max_embd(dtype)) return 0;
+  if (dtype == GPT_BF16 && ((N + 32) * C * 2 >= (1ll << 32) || (V + 32) * C * 2 >= (1ll << 32))) return 0;
+  // per-row losses and log-sum-exps, and the out-of-range target flag
+  return (size_t)(2 * align_up(N * 4, ALIGN) + ALIGN);
 }
 
 int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int64_t V, int64_t C, int32_t dtype,
@@ -899,24 +830,15 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
   const size_t need = gpt_lmhead_ce_ws_bytes(N, V, C, dtype);
   if (!need || !X || !W || !y || !loss_dev) return fail(GPT_EINVAL, "bad lmhead_ce arguments");
   if (!ws || ws_bytes < need) return fail(GPT_ENOMEM, "lmhead_ce workspace too small");
-  gpt_ctx tmp;  // launch helpers only use the stream, dtype and profiling fields
+  if (((uintptr_t)ws) % ALIGN) return fail(GPT_EINVAL, "lmhead_ce workspace must be 256-byte aligned");
+  gpt_ctx tmp;  // launch helpers only use the stream and the profiling fields; no side stream
   tmp.stream = (hipStream_t)hip_stream;
-  tmp.dt = dtype;
-  tmp.es = dtype == GPT_BF16 ? 2 : 4;
-  const int64_t ldv = align_up(V, 64), Nc = std::min<int64_t>(N, 4096);
   Carver cv(ws);
-  void* logits = cv.take<void>(Nc * ldv * tmp.es);
-  void* dz = cv.take<void>(Nc * ldv * tmp.es);
   float* tl = cv.take<float>(N * 4);
   float* tlse = cv.take<float>(N * 4);
   int* bad = cv.take<int>(ALIGN);
-  const int64_t hn = std::max<int64_t>(1, head_splitk_floats(N, Nc, C, V));
-  float* hws = cv.take<float>(hn * 4);
-  const bool grad = dX || dW;
-  void* const dzb[2] = {dz, dz};  // no side stream here: chunks run in order on one buffer
   HIPCHK(gk::fill_f32((float*)bad, 1, 0.f, tmp.stream));
-  if (int e = head(&tmp, X, W, V, y, N, C, grad ? 1.0f / (float)N : 0.f, tl, tlse, dX, dW, 0, logits, dzb, ldv, Nc,
-                   dtype, hws, hn, loss_dev, nullptr, 0, bad))
+  if (int e = head(&tmp, X, W, V, y, N, C, 1.0f / (float)N, tl, tlse, dX, dW, 0, dtype, loss_dev, nullptr, 0, bad))
     return e;
   // out-of-range targets were clamped on the device; report them here
   int flag = 0;

@@ -1,0 +1,798 @@
+// The tied LM head fused with next-token cross-entropy, forward and backward,
+// without ever storing a [rows, vocabulary] logits matrix ("GPT training"
+// (Zero) page, output layer: the projection and the loss as one operator so
+// that the [B*T, V] logits are not kept; CS336 page, section 1: the loss is
+// the mean over rows of logsumexp(z) - z[y] with the row maximum taken out).
+//
+// With F the final-LayerNorm rows [N, C] and W the tied embedding [V, C],
+// z = F W^T, p = softmax(z) per row, g = scale (p - onehot(y)):
+//   dF = g W = scale (sum_v p_v W_v - W_y),   dW = g^T F.
+// Two passes over the vocabulary, both streaming 32-row blocks of one operand
+// through LDS while the other operand stays in registers:
+//   pass 1 (per block of F rows): z tiles against every W block, a softmax
+//     in one sweep (exponentials against a per-row reference, their running
+//     sum), and sum_v p_v W_v accumulated - the forward pass of attention with
+//     keys = values = W.  Its end gives the log-sum-exp, the row loss and dF.
+//   pass 2 (per block of W rows): z tiles against every F block, recomputed,
+//     g from the saved log-sum-exp, and dW accumulated.
+// 8 N V C FLOPs against the algorithmic 6 N V C (the logits are computed
+// twice); HBM traffic is F, W, dF, dW and per-row scalars.
+//
+// gfx950 layout of one workgroup (4 waves, one per SIMD):
+//  * the contraction over C is split across the waves: wave w owns the
+//    columns [c_lo, c_lo + 64 ng) (C / 64 column groups dealt out in order)
+//    for both products, so it only ever reads its own slice of a streamed
+//    block: it loads that slice itself (buffer_load ... lds, one wave
+//    instruction = 1 KB) and refills its stage without waiting for the
+//    other waves;
+//  * z tiles are computed transposed (rows = streamed rows, columns = fixed
+//    rows) so that a tile's accumulators are directly the B operand of the
+//    second product; each wave's partial tile over its columns is summed with
+//    the others' through LDS (each wave reduces one quarter of the tile's
+//    accumulators in a fixed order, then every wave reads the whole sum), so
+//    all waves hold the same bits of z and take the same softmax decisions;
+//  * the second product reads the streamed block transposed with
+//    ds_read_b64_tr_b16, so no transposed copy is stored;
+//  * LDS rows of a slice are 128 ng bytes; their 16-byte chunks are
+//    XOR-permuted by row so that the 16 rows of a ds_read_b128 pass and the
+//    4 rows x 4 chunks of a transpose-read pass hit distinct banks.
+#include "common.h"
+#include "kernels.h"
+#include "mfma_lds.h"
+
+namespace gk {
+namespace hd {
+using namespace mx;
+
+constexpr int BV = 32;          // streamed rows per block
+constexpr float HEADROOM = 64.f; // pass 1: p = 2^(z log2e - m) may reach 2^64 before a sweep is redone
+
+struct Args {
+  const bf16* fix;   // rows kept in registers: F (pass 1) or W (pass 2), [n_fix][C]
+  const bf16* str;   // streamed rows: W (pass 1) or F (pass 2), [n_str][C]
+  int n_fix, n_str, C;
+  const int32_t* y;  // [N] targets
+  const float* lse;  // pass 2: [N] natural-log log-sum-exp from pass 1
+  float* loss;       // pass 1: [N] row losses
+  float* lse_out;    // pass 1: [N]
+  float* out;        // pass 1: dF [N][C]; pass 2: dW [V][C]
+  int accumulate;    // pass 2: dW += instead of =
+  float scale;       // gradients are those of scale * (sum of row losses)
+  int* bad;          // pass 1: set to 1 when a target lies outside [0, V)
+};
+
+// Column groups of 64 dealt to the 4 waves in order: wave w gets ng of them from column c_lo.
+__device__ __forceinline__ void wave_range(int C, int w, int& ng, int& c_lo) {
+  const int G = C >> 6, q = G >> 2, r = G & 3;
+  ng = q + (w < r ? 1 : 0);
+  c_lo = (w * q + min(w, r)) * 64;
+}
+
+// Physical 16-byte chunk of logical chunk ch in LDS row `row` of a slice whose
+// rows are NG * 128 bytes.  NG odd: consecutive rows alternate between the two
+// 128-byte halves of a 256-byte bank window, and the low 3 bits are XORed by a
+// permutation of (row / 2) % 8; NG even: rows alias in the window and the low
+// 4 bits are XORed by a permutation of row % 16.  Either way the 16 rows of a
+// row-fragment pass and the 4 rows x 4 chunks of a transpose-read pass land on
+// distinct 16-byte slots.  The map is its own inverse.
+template <int NG>
+__device__ __forceinline__ int phys(int ch, int row) {
+  if constexpr (NG & 1) {
+    const int i = (row >> 1) & 7;
+    return ch ^ (((i & 1) << 2) | (i >> 1));
+  } else {
+    const int r = row & 15;
+    return ch ^ (((r & 3) << 2) | (r >> 2));
+  }
+}
+
+template <int NG>
+struct Slice {
+  static constexpr int RS = NG * 128;   // bytes per LDS row
+  static constexpr int BYTES = BV * RS;  // one block's slice
+  static constexpr int NLD = BYTES / 1024;  // wave load instructions per block
+};
+
+// row fragment (A operand of the z product): block row `row`, k-step ks (16 columns), lane half g
+template <int NG>
+__device__ __forceinline__ uint4 frag_row(const char* s, int row, int ks, int g) {
+  const int ch = phys<NG>(ks * 2 + g, row);
+  return *reinterpret_cast<const uint4*>(s + row * Slice<NG>::RS + ch * 16);
+}
+// transposed fragment (A operand of the second product): lane l holds column
+// c0 + l % 32 of the slice and block rows r0 + 4 (l / 32) + j, then
+// r0 + 8 + 4 (l / 32) + j (j = 0..3): the k order of pack_half over rows
+// r0 .. r0 + 15.  In each 16-lane group G, lane s reads 4 consecutive columns
+// of one row; the transpose read gives lane i element i % 4 of the row read by
+// lane i / 4 + 4 j.
+template <int NG>
+__device__ __forceinline__ uint4 frag_tr(const char* s, int c0, int r0, int lane) {
+  const int G = lane >> 4, sl = lane & 15;
+  const int cc = c0 + 16 * (G & 1) + 4 * (sl & 3);
+  const int ch = cc >> 3, sub = (cc & 7) * 2;
+  const int ra = r0 + 4 * (G >> 1) + (sl >> 2), rb = ra + 8;
+  constexpr int RS = Slice<NG>::RS;
+  v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(s + ra * RS + phys<NG>(ch, ra) * 16 + sub));
+  v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(s + rb * RS + phys<NG>(ch, rb) * 16 + sub));
+  const uint2 a = bitcast<uint2>(lo), b = bitcast<uint2>(hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// LDS of a workgroup: per wave ST stages of its slice (+ 512 bytes of per-row
+// scalars in pass 2), then the partial z tiles [4 waves][NQT][4][64 lanes]
+// (float4) and their reduced quarters [NQT][4][64 lanes].
+template <int NG, int NQT, int ST, int MODE>
+struct Lds {
+  static constexpr int STAGE = Slice<NG>::BYTES + (MODE ? 512 : 0);
+  static constexpr int PER_WAVE = ST * STAGE;
+  static constexpr int PART = 4 * PER_WAVE;
+  static constexpr int RED = PART + 4 * NQT * 4 * 64 * 16;
+  static constexpr int TOTAL = RED + NQT * 4 * 64 * 16;
+};
+
+// Per-lane state of a workgroup's pass (the same row statistics in every wave).
+template <int NG, int NQT>
+struct State {
+  uint4 qf[NQT][NG * 4];    // fixed rows: B fragments of the z product over this wave's columns
+  f32x16 O[NQT][NG * 2];    // second-product accumulators over this wave's columns
+  float m[NQT], l[NQT], zy[NQT];  // pass 1: reference max (log2 units), this lane half's sum, target logit
+  int yq[NQT];              // pass 1: the fixed row's target
+  int ng, f0, lane, w, g, c32;
+};
+
+// z^T tiles of one streamed block: partials over this wave's columns, summed
+// across the waves through part/red.  rd holds the block's slice; the
+// pointers are distinct and __restrict__, so the compiler need not wait for
+// outstanding direct-to-LDS loads (into other stages) before these accesses.
+// z[qt][e]: streamed row r0 + crow(e, g), fixed row f0 + 32 qt + c32.
+template <int NG, int NQT>
+__device__ __forceinline__ void z_tiles(const char* __restrict__ rd, float4* __restrict__ part,
+                                        float4* __restrict__ red, const State<NG, NQT>& S, f32x16 (&z)[NQT]) {
+  const int lane = S.lane, w = S.w, g = S.g, c32 = S.c32;
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) zero16(z[qt]);
+  // Every k-step runs in every wave, also past a wave's own columns (fewer
+  // groups than NG): those k-steps have zero fixed fragments, and the slot data
+  // there is real memory from the loads, so it is finite; the waves meet at
+  // every block and wait for the widest one anyway.
+#pragma unroll
+  for (int ks = 0; ks < NG * 4; ++ks) {
+    const uint4 af = frag_row<NG>(rd, c32, ks, g);  // serves every fixed tile
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) mma32(z[qt], af, S.qf[qt][ks]);
+    // keep at most 4 k-steps of fragment reads ahead of their products (registers)
+    if ((ks & 3) == 3) asm volatile("" ::: "memory");
+  }
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4)
+      part[((w * NQT + qt) * 4 + e4) * 64 + lane] =
+          make_float4(z[qt][4 * e4], z[qt][4 * e4 + 1], z[qt][4 * e4 + 2], z[qt][4 * e4 + 3]);
+  __syncthreads();
+  // wave w adds accumulator quarter w of every tile over the 4 waves, in wave order
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    float4 s4 = part[(qt * 4 + w) * 64 + lane];
+#pragma unroll
+    for (int v = 1; v < 4; ++v) {
+      const float4 p4 = part[((v * NQT + qt) * 4 + w) * 64 + lane];
+      s4.x += p4.x;
+      s4.y += p4.y;
+      s4.z += p4.z;
+      s4.w += p4.w;
+    }
+    red[(qt * 4 + w) * 64 + lane] = s4;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const float4 s4 = red[(qt * 4 + e4) * 64 + lane];
+      z[qt][4 * e4] = s4.x;
+      z[qt][4 * e4 + 1] = s4.y;
+      z[qt][4 * e4 + 2] = s4.z;
+      z[qt][4 * e4 + 3] = s4.w;
+    }
+}
+
+// second product over this wave's columns: O^T[c][fixed] += (block^T)[c][streamed] P^T[streamed][fixed]
+// (the tiles past a wave's own columns are computed too and never stored)
+template <int NG, int NQT>
+__device__ __forceinline__ void second_product(const char* __restrict__ rd, const uint4 (&pb)[NQT][2],
+                                               State<NG, NQT>& S) {
+#pragma unroll
+  for (int ct = 0; ct < NG * 2; ++ct) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint4 af = frag_tr<NG>(rd, ct * 32, hh * 16, S.lane);
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) mma32(S.O[qt][ct], af, pb[qt][hh]);
+    }
+    if (ct & 1) asm volatile("" ::: "memory");
+  }
+}
+
+// pass 1, one block: p = 2^(z log2e - m) against the row's reference m (bf16,
+// as the product uses it), the running sums, and the second product
+template <int NG, int NQT>
+__device__ __forceinline__ void fwd_consume(const char* __restrict__ rd, const f32x16 (&z)[NQT], State<NG, NQT>& S) {
+  uint4 pb[NQT][2];
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    float ls = S.l[qt];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      bf16x8 v;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const bf16 p = (bf16)hw_exp2(fmaf(z[qt][8 * hh + jj], LOG2E, -S.m[qt]));
+        v[jj] = p;
+        ls += (float)p;  // the sum of the rounded p the product uses
+      }
+      pb[qt][hh] = bitcast<uint4>(v);
+    }
+    S.l[qt] = ls;
+  }
+  second_product<NG, NQT>(rd, pb, S);
+}
+
+// pass 1: mask W rows past V, note the target logit, and return each fixed
+// row's block maximum in log2 units
+template <int NG, int NQT>
+__device__ __forceinline__ void fwd_block_max(f32x16 (&z)[NQT], int r0, int n_str, State<NG, NQT>& S,
+                                              float (&mx)[NQT]) {
+  const int g = S.g;
+  if (r0 + BV > n_str) {  // the last block of a ragged vocabulary: rows past V are not classes
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (r0 + crow(e, g) >= n_str) z[qt][e] = NEG_INF;
+  }
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    float v = NEG_INF;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      v = fmaxf(v, z[qt][e]);
+      if (r0 + crow(e, g) == S.yq[qt]) S.zy[qt] = z[qt][e];
+    }
+    mx[qt] = halves_max(v) * LOG2E;
+  }
+}
+
+// pass 2, one block: g = scale (exp(z - lse) - [y == v]) for the block's F rows
+// (rows past N load as zeros and give 0), then the second product
+template <int NG, int NQT>
+__device__ __forceinline__ void bwd_consume(const char* __restrict__ rd, const f32x16 (&z)[NQT], int r0, const Args& a,
+                                            State<NG, NQT>& S) {
+  const int g = S.g, c32 = S.c32;
+  const float* sl = reinterpret_cast<const float*>(rd + Slice<NG>::BYTES);
+  const int* sy = reinterpret_cast<const int*>(rd + Slice<NG>::BYTES + 256);
+  float lv[16];
+  int yv[16];
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const int k0 = r4 * 8 + g * 4;  // rows crow(4 r4 .. 4 r4 + 3, g)
+    const float4 l4 = *reinterpret_cast<const float4*>(sl + k0);
+    const int4 y4 = *reinterpret_cast<const int4*>(sy + k0);
+    lv[4 * r4] = l4.x * LOG2E;
+    lv[4 * r4 + 1] = l4.y * LOG2E;
+    lv[4 * r4 + 2] = l4.z * LOG2E;
+    lv[4 * r4 + 3] = l4.w * LOG2E;
+    yv[4 * r4] = y4.x;
+    yv[4 * r4 + 1] = y4.y;
+    yv[4 * r4 + 2] = y4.z;
+    yv[4 * r4 + 3] = y4.w;
+  }
+  uint4 pb[NQT][2];
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    const int vq = S.f0 + qt * 32 + c32;  // this lane's W row
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      bf16x8 v;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int e = 8 * hh + jj;
+        float p = hw_exp2(fmaf(z[qt][e], LOG2E, -lv[e])) - (yv[e] == vq ? 1.f : 0.f);
+        if (r0 + crow(e, g) >= a.n_str) p = 0.f;
+        v[jj] = (bf16)(p * a.scale);
+      }
+      pb[qt][hh] = bitcast<uint4>(v);
+    }
+  }
+  second_product<NG, NQT>(rd, pb, S);
+}
+
+template <int NG, int NQT, int ST, int MODE>
+__global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
+  using L = Lds<NG, NQT, ST, MODE>;
+  using SL = Slice<NG>;
+  static_assert(L::TOTAL <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  State<NG, NQT> S;
+  const int t = threadIdx.x;
+  S.lane = t & 63;
+  S.w = t >> 6;
+  S.g = S.lane >> 5;
+  S.c32 = S.lane & 31;
+  const int lane = S.lane, w = S.w, g = S.g, c32 = S.c32;
+  const int C = a.C;
+  int c_lo, ng;
+  wave_range(C, w, ng, c_lo);
+  S.ng = __builtin_amdgcn_readfirstlane(ng);  // uniform in the wave: scalar branches
+  c_lo = __builtin_amdgcn_readfirstlane(c_lo);
+  S.f0 = blockIdx.x * (32 * NQT);  // first fixed row of the workgroup
+  const int nblk = (a.n_str + BV - 1) / BV;
+
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    const int fr = S.f0 + qt * 32 + c32;
+    const bf16* src = a.fix + (int64_t)min(fr, a.n_fix - 1) * C + c_lo + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < NG * 4; ++ks)
+      S.qf[qt][ks] =
+          (ks < S.ng * 4 && fr < a.n_fix) ? *reinterpret_cast<const uint4*>(src + ks * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int ct = 0; ct < NG * 2; ++ct) zero16(S.O[qt][ct]);
+    S.m[qt] = NEG_INF;
+    S.l[qt] = 0.f;
+    S.zy[qt] = 0.f;
+    S.yq[qt] = 0;
+    if constexpr (MODE == 0) {
+      int yy = fr < a.n_fix ? a.y[fr] : 0;
+      if (yy < 0 || yy >= a.n_str) {  // clamped into the row; reported through a.bad
+        if (fr < a.n_fix && a.bad) *a.bad = 1;
+        yy = yy < 0 ? 0 : a.n_str - 1;
+      }
+      S.yq[qt] = yy;
+    }
+  }
+
+  // this wave's slice loads: instruction i, lane -> (block row, logical chunk) -> source byte offset
+  const rsrc_t rs = make_rsrc(a.str, (int64_t)a.n_str * C * 2);
+  uint32_t off[SL::NLD];
+#pragma unroll
+  for (int i = 0; i < SL::NLD; ++i) {
+    const int q = i * 1024 + 16 * lane;
+    const int row = q / SL::RS, pc = (q % SL::RS) >> 4;
+    off[i] = (uint32_t)(((int64_t)row * C + c_lo + phys<NG>(pc, row) * 8) * 2);
+  }
+  const uint32_t blk_bytes = (uint32_t)(BV * C * 2);
+  char* wbase = smem + w * L::PER_WAVE;
+  const rsrc_t rl = make_rsrc(MODE == 1 ? (const void*)a.lse : nullptr, MODE == 1 ? (int64_t)a.n_str * 4 : 0);
+  const rsrc_t ry = make_rsrc(MODE == 1 ? (const void*)a.y : nullptr, MODE == 1 ? (int64_t)a.n_str * 4 : 0);
+  auto issue = [&](int blk, char* st) {
+#pragma unroll
+    for (int i = 0; i < SL::NLD; ++i) dma16(rs, st + i * 1024, off[i] + (uint32_t)blk * blk_bytes);
+    if constexpr (MODE == 1) {
+      dma4(rl, st + SL::BYTES, (uint32_t)(blk * BV + lane) * 4);
+      dma4(ry, st + SL::BYTES + 256, (uint32_t)(blk * BV + lane) * 4);
+    }
+  };
+  constexpr int LPB = SL::NLD + (MODE ? 2 : 0);  // load instructions per block
+  float4* part = reinterpret_cast<float4*>(smem + L::PART);
+  float4* red = reinterpret_cast<float4*>(smem + L::RED);
+
+  // Block j lives in stage j % ST.  With ST > 1, block j + ST - 1 goes into the
+  // stage block j - 1 used (this wave alone reads its slice, and it is done with
+  // it) before waiting for block j; with one stage the next block is loaded
+  // after the current one is consumed.
+  auto fetch = [&](int j, int sc) {
+    if constexpr (ST == 1) {
+      if (j == 0) issue(0, wbase);
+      wait_vm<0>();
+    } else {
+      if (j == 0) {
+#pragma unroll
+        for (int s2 = 0; s2 < ST - 1; ++s2)
+          if (s2 < nblk) issue(s2, wbase + s2 * L::STAGE);
+      }
+      const int sw = sc == 0 ? ST - 1 : sc - 1;
+      if (j + ST - 1 < nblk) issue(j + ST - 1, wbase + sw * L::STAGE);
+      const int later = min(ST - 1, nblk - 1 - j);  // blocks after j whose loads may stay outstanding
+      if constexpr (ST == 2) {
+        if (later >= 1) wait_vm<LPB>();
+        else wait_vm<0>();
+      } else {
+        if (later >= 2) wait_vm<2 * LPB>();
+        else if (later == 1) wait_vm<LPB>();
+        else wait_vm<0>();
+      }
+    }
+  };
+  auto after = [&](int j) {
+    if constexpr (ST == 1)
+      if (j + 1 < nblk) issue(j + 1, wbase);
+  };
+
+  f32x16 z[NQT];
+  if constexpr (MODE == 0) {
+    // Softmax against a fixed reference per row instead of a running maximum:
+    // m is the row's maximum over the first W block (so p <= 2^(max - m)), and
+    // the accumulators are never rescaled inside the sweep.  A row whose later
+    // maximum exceeds m by more than HEADROOM (p could overflow) has the whole
+    // sweep redone with m = that maximum; every wave holds the same z, so the
+    // decision is the same in all of them.
+    for (int attempt = 0;; ++attempt) {
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) {
+#pragma unroll
+        for (int ct = 0; ct < NG * 2; ++ct) zero16(S.O[qt][ct]);
+        S.l[qt] = 0.f;
+      }
+      float seen[NQT];
+      int sc = 0;
+      for (int j = 0; j < nblk; ++j) {
+        const char* st = wbase + sc * L::STAGE;
+        fetch(j, sc);
+        z_tiles<NG, NQT>(st, part, red, S, z);
+        float mx[NQT];
+        fwd_block_max<NG, NQT>(z, j * BV, a.n_str, S, mx);
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+          if (j == 0) {
+            if (attempt == 0) S.m[qt] = mx[qt];
+            seen[qt] = mx[qt];
+          }
+          seen[qt] = fmaxf(seen[qt], mx[qt]);
+        }
+        fwd_consume<NG, NQT>(st, z, S);
+        after(j);
+        sc = sc + 1 == ST ? 0 : sc + 1;
+      }
+      bool redo = false;
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) redo |= seen[qt] > S.m[qt] + HEADROOM;
+      if (!__any(redo)) break;
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) S.m[qt] = fmaxf(S.m[qt], seen[qt]);
+    }
+  } else {
+    int sc = 0;
+    for (int j = 0; j < nblk; ++j) {
+      const char* st = wbase + sc * L::STAGE;
+      fetch(j, sc);
+      z_tiles<NG, NQT>(st, part, red, S, z);
+      bwd_consume<NG, NQT>(st, z, j * BV, a, S);
+      after(j);
+      sc = sc + 1 == ST ? 0 : sc + 1;
+    }
+  }
+
+  // epilogue: tile ct of fixed tile qt holds columns c_lo + 32 ct + crow(e, g) of fixed row f0 + 32 qt + c32
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    const int fr = S.f0 + qt * 32 + c32;
+    if (fr >= a.n_fix) continue;
+    float* orow = a.out + (int64_t)fr * C + c_lo;
+    if constexpr (MODE == 0) {
+      const float lt = halves_sum(S.l[qt]);
+      const float zt = halves_sum(S.zy[qt]);  // exactly one lane half saw the target
+      const float lse = (S.m[qt] + hw_log2(lt)) * LN2;
+      if (w == 0 && g == 0) {
+        a.loss[fr] = lse - zt;
+        a.lse_out[fr] = lse;
+      }
+      if (a.out == nullptr) continue;  // forward only
+      const float inv = 1.f / lt, sc2 = a.scale;
+      const bf16* wy = a.str + (int64_t)S.yq[qt] * C + c_lo;
+#pragma unroll
+      for (int ct = 0; ct < NG * 2; ++ct) {
+        if (ct >= S.ng * 2) continue;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int c = ct * 32 + r4 * 8 + g * 4;
+          const float4 wv = load4(wy + c);
+          const f32x16& o = S.O[qt][ct];
+          store4(orow + c, make_float4((o[4 * r4] * inv - wv.x) * sc2, (o[4 * r4 + 1] * inv - wv.y) * sc2,
+                                       (o[4 * r4 + 2] * inv - wv.z) * sc2, (o[4 * r4 + 3] * inv - wv.w) * sc2));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < NG * 2; ++ct) {
+        if (ct >= S.ng * 2) continue;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int c = ct * 32 + r4 * 8 + g * 4;
+          const f32x16& o = S.O[qt][ct];
+          float4 v = make_float4(o[4 * r4], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]);
+          if (a.accumulate) {
+            const float4 p = load4(orow + c);
+            v.x += p.x;
+            v.y += p.y;
+            v.z += p.z;
+            v.w += p.w;
+          }
+          store4(orow + c, v);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32: the same two passes in plain fp32 FMAs (the tiny fp32 model; no
+// tensor-core path), 256 threads and 8 rows per workgroup.
+constexpr int FR = 8;      // rows per workgroup
+constexpr int FCH = 256;   // streamed rows per chunk (one per thread)
+
+// pass 1: per row, lse by an online max/sum over all W rows, then
+// dF = scale (sum_v p_v W_v - W_y) from a second sweep.
+__global__ __launch_bounds__(256) void head_f32_fwd(const float* __restrict__ F, const float* __restrict__ W, int N, int V,
+                                                    int C, const int32_t* __restrict__ y, float scale,
+                                                    float* __restrict__ loss, float* __restrict__ lse_out,
+                                                    float* __restrict__ dF, int* bad) {
+  extern __shared__ float fsm[];  // [FR][C] rows of F, then [FR][FCH] gradients of a chunk
+  float* rowsF = fsm;
+  float* gch = fsm + FR * C;
+  __shared__ float rm[FR][4], rsum[FR][4], rzy[FR];
+  const int t = threadIdx.x, n0 = blockIdx.x * FR;
+  for (int i = t; i < FR * C; i += 256) {
+    const int r = i / C;
+    rowsF[i] = (n0 + r < N) ? F[(int64_t)(n0 + r) * C + i % C] : 0.f;
+  }
+  if (t < FR) rzy[t] = 0.f;
+  int yr[FR];
+#pragma unroll
+  for (int r = 0; r < FR; ++r) {
+    int yy = (n0 + r < N) ? y[n0 + r] : 0;
+    if (yy < 0 || yy >= V) {
+      if (n0 + r < N && bad && t == 0) *bad = 1;
+      yy = yy < 0 ? 0 : V - 1;
+    }
+    yr[r] = yy;
+  }
+  __syncthreads();
+  float m[FR], s[FR];
+#pragma unroll
+  for (int r = 0; r < FR; ++r) {
+    m[r] = -__builtin_huge_valf();
+    s[r] = 0.f;
+  }
+  for (int v = t; v < V; v += 256) {
+    float z[FR];
+#pragma unroll
+    for (int r = 0; r < FR; ++r) z[r] = 0.f;
+    for (int c = 0; c < C; ++c) {
+      const float wv = W[(int64_t)v * C + c];
+#pragma unroll
+      for (int r = 0; r < FR; ++r) z[r] = fmaf(rowsF[r * C + c], wv, z[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < FR; ++r) {
+      if (v == yr[r]) rzy[r] = z[r];
+      if (z[r] > m[r]) {
+        s[r] = s[r] * hw_exp2((m[r] - z[r]) * LOG2E);
+        m[r] = z[r];
+      }
+      s[r] += hw_exp2((z[r] - m[r]) * LOG2E);
+    }
+  }
+  // combine the threads' (max, sum) pairs: across the wave, then the 4 waves
+  const int lane = t & 63, wv = t >> 6;
+#pragma unroll
+  for (int r = 0; r < FR; ++r) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float mo = __shfl_xor(m[r], o, WAVE), so = __shfl_xor(s[r], o, WAVE);
+      const float mn = fmaxf(m[r], mo);
+      s[r] = (mn == -__builtin_huge_valf()) ? 0.f : s[r] * hw_exp2((m[r] - mn) * LOG2E) + so * hw_exp2((mo - mn) * LOG2E);
+      m[r] = mn;
+    }
+    if (lane == 0) {
+      rm[r][wv] = m[r];
+      rsum[r][wv] = s[r];
+    }
+  }
+  __syncthreads();
+  float lse[FR];
+#pragma unroll
+  for (int r = 0; r < FR; ++r) {
+    const float M = fmaxf(fmaxf(rm[r][0], rm[r][1]), fmaxf(rm[r][2], rm[r][3]));
+    float S = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) S += rsum[r][k] * hw_exp2((rm[r][k] - M) * LOG2E);
+    lse[r] = M + hw_log2(S) * LN2;
+  }
+  if (t < FR && n0 + t < N) {
+    loss[n0 + t] = lse[t] - rzy[t];
+    lse_out[n0 + t] = lse[t];
+  }
+  if (dF == nullptr) return;  // forward only (the whole workgroup leaves together)
+  // second sweep: chunk of FCH W rows -> g[r][v] in LDS -> dF[r][c] += sum_v g[r][v] W[v][c]
+  constexpr int CMAX = 4;  // columns per thread: C <= 1024
+  float acc[FR][CMAX];
+#pragma unroll
+  for (int r = 0; r < FR; ++r)
+#pragma unroll
+    for (int k = 0; k < CMAX; ++k) acc[r][k] = 0.f;
+  for (int v0 = 0; v0 < V; v0 += FCH) {
+    const int v = v0 + t;
+    float z[FR];
+#pragma unroll
+    for (int r = 0; r < FR; ++r) z[r] = 0.f;
+    if (v < V)
+      for (int c = 0; c < C; ++c) {
+        const float wv2 = W[(int64_t)v * C + c];
+#pragma unroll
+        for (int r = 0; r < FR; ++r) z[r] = fmaf(rowsF[r * C + c], wv2, z[r]);
+      }
+    __syncthreads();  // the previous chunk's gradients are consumed
+#pragma unroll
+    for (int r = 0; r < FR; ++r)
+      gch[r * FCH + t] = (v < V) ? (hw_exp2((z[r] - lse[r]) * LOG2E) - (v == yr[r] ? 1.f : 0.f)) * scale : 0.f;
+    __syncthreads();
+    const int nv = min(FCH, V - v0);
+    for (int k = 0; k < nv; ++k) {
+      const float* wr = W + (int64_t)(v0 + k) * C;
+#pragma unroll
+      for (int kc = 0; kc < CMAX; ++kc) {
+        const int c = t + 256 * kc;
+        if (c < C) {
+          const float wv2 = wr[c];
+#pragma unroll
+          for (int r = 0; r < FR; ++r) acc[r][kc] = fmaf(gch[r * FCH + k], wv2, acc[r][kc]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < FR; ++r) {
+    if (n0 + r >= N) continue;
+#pragma unroll
+    for (int kc = 0; kc < CMAX; ++kc) {
+      const int c = t + 256 * kc;
+      if (c < C) dF[(int64_t)(n0 + r) * C + c] = acc[r][kc];
+    }
+  }
+}
+
+// pass 2: per W row v, dW[v] (+)= sum_n scale (exp(z_nv - lse_n) - [y_n == v]) F_n
+__global__ __launch_bounds__(256) void head_f32_dw(const float* __restrict__ F, const float* __restrict__ W, int N, int V,
+                                                   int C, const int32_t* __restrict__ y, const float* __restrict__ lse,
+                                                   float scale, float* __restrict__ dW, int accumulate) {
+  extern __shared__ float fsm[];  // [FR][C] rows of W, then [FR][FCH] gradients of a chunk
+  float* rowsW = fsm;
+  float* gch = fsm + FR * C;
+  const int t = threadIdx.x, v0 = blockIdx.x * FR;
+  for (int i = t; i < FR * C; i += 256) {
+    const int r = i / C;
+    rowsW[i] = (v0 + r < V) ? W[(int64_t)(v0 + r) * C + i % C] : 0.f;
+  }
+  constexpr int CMAX = 4;
+  float acc[FR][CMAX];
+#pragma unroll
+  for (int r = 0; r < FR; ++r)
+#pragma unroll
+    for (int k = 0; k < CMAX; ++k) acc[r][k] = 0.f;
+  __syncthreads();
+  for (int n0 = 0; n0 < N; n0 += FCH) {
+    const int n = n0 + t;
+    float z[FR];
+#pragma unroll
+    for (int r = 0; r < FR; ++r) z[r] = 0.f;
+    if (n < N)
+      for (int c = 0; c < C; ++c) {
+        const float fv = F[(int64_t)n * C + c];
+#pragma unroll
+        for (int r = 0; r < FR; ++r) z[r] = fmaf(rowsW[r * C + c], fv, z[r]);
+      }
+    const float ln = n < N ? lse[n] : 0.f;
+    const int yn = n < N ? y[n] : -1;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < FR; ++r)
+      gch[r * FCH + t] = (n < N) ? (hw_exp2((z[r] - ln) * LOG2E) - (yn == v0 + r ? 1.f : 0.f)) * scale : 0.f;
+    __syncthreads();
+    const int nn = min(FCH, N - n0);
+    for (int k = 0; k < nn; ++k) {
+      const float* fr = F + (int64_t)(n0 + k) * C;
+#pragma unroll
+      for (int kc = 0; kc < CMAX; ++kc) {
+        const int c = t + 256 * kc;
+        if (c < C) {
+          const float fv = fr[c];
+#pragma unroll
+          for (int r = 0; r < FR; ++r) acc[r][kc] = fmaf(gch[r * FCH + k], fv, acc[r][kc]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < FR; ++r) {
+    if (v0 + r >= V) continue;
+#pragma unroll
+    for (int kc = 0; kc < CMAX; ++kc) {
+      const int c = t + 256 * kc;
+      if (c < C) {
+        float* o = dW + (int64_t)(v0 + r) * C + c;
+        *o = accumulate ? *o + acc[r][kc] : acc[r][kc];
+      }
+    }
+  }
+}
+
+// launch a bf16 pass with the register/LDS shape for C
+template <int MODE>
+hipError_t launch_bf16(const Args& a, hipStream_t s) {
+  const int G = a.C / 64;
+  const int ngmax = (G + 3) / 4;
+  // fixed rows per workgroup: 64 (two 32-row tiles) while a wave's 64-column groups are <= 3, else 32
+  auto grid = [&](int rows) { return dim3((a.n_fix + rows - 1) / rows); };
+  switch (ngmax) {
+    case 1: hipLaunchKernelGGL((head_kernel<1, 2, 3, MODE>), grid(64), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((head_kernel<2, 2, 3, MODE>), grid(64), dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((head_kernel<3, 2, 2, MODE>), grid(64), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((head_kernel<4, 1, 2, MODE>), grid(32), dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((head_kernel<5, 1, 1, MODE>), grid(32), dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((head_kernel<6, 1, 1, MODE>), grid(32), dim3(256), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((head_kernel<7, 1, 1, MODE>), grid(32), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hd
+
+// bf16: up to 7 column groups of 64 per wave; fp32: the plain kernels keep 8 rows of C floats
+// plus a 256-row gradient chunk in LDS (40 KB at C = 1024)
+int lmhead_max_embd(int dtype) { return dtype == BF16 ? 7 * 4 * 64 : 1024; }
+
+hipError_t lmhead_fwd(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, float scale,
+                      float* loss, float* lse, float* dF, int* bad, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  if (V <= 0 || C <= 0 || C % 64 || C > lmhead_max_embd(dtype)) return hipErrorInvalidValue;
+  if (dtype == BF16) {
+    // 32-bit buffer offsets into the streamed W (the last block's rows run up to 31 past V)
+    if ((int64_t)(V + 32) * C * 2 >= (1ll << 32)) return hipErrorInvalidValue;
+    hd::Args a{};
+    a.fix = (const bf16*)F;
+    a.str = (const bf16*)W;
+    a.n_fix = N;
+    a.n_str = V;
+    a.C = C;
+    a.y = y;
+    a.loss = loss;
+    a.lse_out = lse;
+    a.out = dF;
+    a.scale = scale;
+    a.bad = bad;
+    return hd::launch_bf16<0>(a, s);
+  }
+  const size_t sh = (size_t)(hd::FR * C + hd::FR * hd::FCH) * 4;
+  hipLaunchKernelGGL(hd::head_f32_fwd, dim3((N + hd::FR - 1) / hd::FR), dim3(256), sh, s, (const float*)F,
+                     (const float*)W, N, V, C, y, scale, loss, lse, dF, bad);
+  return hipGetLastError();
+}
+
+hipError_t lmhead_dw(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, const float* lse,
+                     float scale, float* dW, int accumulate, hipStream_t s) {
+  if (V <= 0) return hipSuccess;
+  if (N <= 0 || C <= 0 || C % 64 || C > lmhead_max_embd(dtype)) return hipErrorInvalidValue;
+  if (dtype == BF16) {
+    if ((int64_t)(N + 32) * C * 2 >= (1ll << 32)) return hipErrorInvalidValue;
+    hd::Args a{};
+    a.fix = (const bf16*)W;
+    a.str = (const bf16*)F;
+    a.n_fix = V;
+    a.n_str = N;
+    a.C = C;
+    a.y = y;
+    a.lse = lse;
+    a.out = dW;
+    a.accumulate = accumulate;
+    a.scale = scale;
+    return hd::launch_bf16<1>(a, s);
+  }
+  const size_t sh = (size_t)(hd::FR * C + hd::FR * hd::FCH) * 4;
+  hipLaunchKernelGGL(hd::head_f32_dw, dim3((V + hd::FR - 1) / hd::FR), dim3(256), sh, s, (const float*)F,
+                     (const float*)W, N, V, C, y, lse, scale, dW, accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace gk

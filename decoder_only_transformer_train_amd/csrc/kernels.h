@@ -94,13 +94,20 @@ hipError_t attn_bwd_bf16_d64(const void* qkv, const void* dO, const float* lse, 
 hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse,
                     float* Dv, void* dqkv, int B, int T, int H, int D, hipStream_t s);
 
-// ---- cross-entropy rows over a chunk of logits ----
-// z T [rows][ldz] (first V columns valid) -> loss[r] = lse - z[y]; lse_out[r];
-// if dz != null: dz T [rows][ldz] = (softmax - onehot) * scale, zero in [V, ldz).
-// A target outside [0, V) is clamped into the row (never read out of it) and,
-// when bad != null, sets *bad = 1 (the caller clears it first).
-hipError_t ce_rows(int dtype, const void* z, int64_t ldz, int V, const int32_t* y, int rows,
-                   float scale, float* loss, float* lse_out, void* dz, int* bad, hipStream_t s);
+// ---- LM head fused with cross-entropy (head.hip) ----
+// F T [N][C] rows, W T [V][C], y int32 [N]; nothing of size [N][V] is stored.
+// Pass 1: loss[n] = lse_n - z_n,y_n, lse[n] (natural log), and, when dF != null,
+// dF [N][C] (f32) = scale (softmax(z_n) W - W_y).  A target outside [0, V) is
+// clamped into the row (never read out of it) and, when bad != null, sets
+// *bad = 1 (the caller clears it first).
+// Pass 2 (needs pass 1's lse): dW [V][C] (f32) (+)= scale (softmax(z) - onehot(y))^T F.
+// C a multiple of 64, at most lmhead_max_embd(dtype); bf16 needs V*C*2 and
+// N*C*2 below 4 GB (32-bit buffer offsets).
+int lmhead_max_embd(int dtype);
+hipError_t lmhead_fwd(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, float scale,
+                      float* loss, float* lse, float* dF, int* bad, hipStream_t s);
+hipError_t lmhead_dw(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, const float* lse,
+                     float scale, float* dW, int accumulate, hipStream_t s);
 // mean of n floats in fixed order -> out[0] (and ring[slot] if ring != null)
 hipError_t mean_f32(const float* x, int n, float* out, float* ring, int slot, hipStream_t s);
 

@@ -1,6 +1,6 @@
 // HBM-bound row kernels for gfx950: LayerNorm forward / backward (fused with
 // the embedding gather and the residual-gradient add), column reductions and
-// the cross-entropy row pass of the LM head.
+// the fixed-order mean of the per-row losses.
 //
 // LayerNorm (lecture, pre-LN blocks and final LayerNorm; Zero page,
 // Transformer Block): y = (x - mu) / sqrt(var + 1e-5) * g + b over the C
@@ -325,192 +325,6 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict
   }
 }
 
-// Cross-entropy over one row of logits (CS336 page, section 1: subtract the
-// row maximum, log-sum-exp, minus the target logit).  One workgroup per row.
-// A target id outside [0, V) is clamped into the row before any load (the
-// row's loss is then meaningless) and flagged in *bad when bad is given.
-__device__ __forceinline__ int target_in_range(int yy, int V, int* bad, int t) {
-  if (yy >= 0 && yy < V) return yy;
-  if (bad != nullptr && t == 0) *bad = 1;
-  return yy < 0 ? 0 : V - 1;
-}
-
-// Logits z and dz are both T (bf16 logits are widened to fp32, as the page's
-// loss does, before any arithmetic).
-// With dz: dz = (softmax - onehot(y)) * scale, zero in the padding [V, ldz).
-template <typename T>
-__global__ __launch_bounds__(256) void ce_rows_kernel(const T* __restrict__ z, int64_t ldz, int V,
-                                                      const int32_t* __restrict__ y, float scale,
-                                                      float* __restrict__ loss, float* __restrict__ lse_out,
-                                                      T* __restrict__ dz, int* __restrict__ bad) {
-  __shared__ float sm[4], ss[4];
-  const int row = blockIdx.x;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const T* zr = z + (int64_t)row * ldz;
-  // running max and sum of 2^((z - max) log2 e), rescaled when the max grows
-  float m = -__builtin_huge_valf(), s = 0.f;
-  const int V4 = V >> 2;
-  for (int j = t; j < V4; j += 256) {
-    const float4 v = load4(zr + 4 * j);
-    const float mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
-    if (mx > m) {
-      s *= hw_exp2((m - mx) * LOG2E);
-      m = mx;
-    }
-    s += hw_exp2((v.x - m) * LOG2E) + hw_exp2((v.y - m) * LOG2E) + hw_exp2((v.z - m) * LOG2E) +
-         hw_exp2((v.w - m) * LOG2E);
-  }
-  for (int j = 4 * V4 + t; j < V; j += 256) {
-    const float v = to_f(zr[j]);
-    if (v > m) {
-      s *= hw_exp2((m - v) * LOG2E);
-      m = v;
-    }
-    s += hw_exp2((v - m) * LOG2E);
-  }
-  // combine (m, s) pairs across the wave, then across the 4 waves
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float mo = __shfl_xor(m, o, WAVE), so = __shfl_xor(s, o, WAVE);
-    const float mn = fmaxf(m, mo);
-    s = (mn == -__builtin_huge_valf()) ? 0.f : s * hw_exp2((m - mn) * LOG2E) + so * hw_exp2((mo - mn) * LOG2E);
-    m = mn;
-  }
-  if (lane == 0) {
-    sm[w] = m;
-    ss[w] = s;
-  }
-  __syncthreads();
-  const float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-  float S = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) S += ss[i] * hw_exp2((sm[i] - M) * LOG2E);
-  const float lse = M + hw_log2(S) * LN2;
-  const int yy = target_in_range(y[row], V, bad, t);
-  if (t == 0) {
-    loss[row] = lse - to_f(zr[yy]);
-    if (lse_out) lse_out[row] = lse;
-  }
-  if (dz != nullptr) {
-    T* dr = dz + (int64_t)row * ldz;
-    const int L4 = (int)(ldz >> 2);
-    for (int j = t; j < L4; j += 256) {
-      const int c = 4 * j;
-      float d[4] = {0.f, 0.f, 0.f, 0.f};
-      if (c + 3 < V) {
-        const float4 v = load4(zr + c);
-        d[0] = hw_exp2((v.x - lse) * LOG2E);
-        d[1] = hw_exp2((v.y - lse) * LOG2E);
-        d[2] = hw_exp2((v.z - lse) * LOG2E);
-        d[3] = hw_exp2((v.w - lse) * LOG2E);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (c + k < V) d[k] = hw_exp2((to_f(zr[c + k]) - lse) * LOG2E);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (c + k == yy) d[k] -= 1.f;
-      store4(dr + c, make_float4(d[0] * scale, d[1] * scale, d[2] * scale, d[3] * scale));
-    }
-  }
-}
-
-// The same cross-entropy row with the row held in registers: 1024 threads
-// load the row once (NV groups of 4 each), reduce the maximum, then the sum of
-// exp(z - max), and write dz from the same registers - one read of the logits
-// instead of two.  Columns in [V, ldz) are padding: excluded, dz = 0 there.
-// the row's values as loaded (bf16 stays packed: half the registers, so two
-// rows' workgroups fit on a CU and one's loads overlap the other's reductions)
-template <typename T> struct CeRow;
-template <> struct CeRow<float> {
-  typedef float4 raw;
-  static __device__ __forceinline__ raw ld(const float* p) { return load4(p); }
-  static __device__ __forceinline__ float4 f(const raw& r) { return r; }
-};
-template <> struct CeRow<bf16> {
-  typedef bf16x4 raw;
-  static __device__ __forceinline__ raw ld(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
-  static __device__ __forceinline__ float4 f(const raw& r) {
-    return make_float4((float)r[0], (float)r[1], (float)r[2], (float)r[3]);
-  }
-};
-
-// (bf16: at most 64 registers, eight waves per SIMD = two rows per CU)
-template <typename T, int NV>
-__global__ __launch_bounds__(1024, sizeof(T) == 2 ? 8 : 4) void ce_reg_kernel(const T* __restrict__ z, int64_t ldz, int V,
-                                                         const int32_t* __restrict__ y, float scale,
-                                                         float* __restrict__ loss, float* __restrict__ lse_out,
-                                                         T* __restrict__ dz, int* __restrict__ bad) {
-  using R = CeRow<T>;
-  __shared__ float red[2][16];
-  const int row = blockIdx.x;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const T* zr = z + (int64_t)row * ldz;
-  const int L4 = (int)(ldz >> 2);
-  constexpr float NINF = -__builtin_huge_valf();
-  typename R::raw v[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int j = t + 1024 * i;
-    if (j < L4) v[i] = R::ld(zr + 4 * j);
-  }
-  // columns in [V, ldz) are padding: excluded from the statistics, dz = 0 there
-  auto val = [&](int i) {
-    const int c = 4 * (t + 1024 * i);
-    const float4 a = R::f(v[i]);
-    return make_float4(c < V ? a.x : NINF, c + 1 < V ? a.y : NINF, c + 2 < V ? a.z : NINF, c + 3 < V ? a.w : NINF);
-  };
-  float mx = NINF;
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if (t + 1024 * i < L4) {
-      const float4 a = val(i);
-      mx = fmaxf(mx, fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)));
-    }
-  mx = wave_max(mx);
-  if (lane == 0) red[0][w] = mx;
-  __syncthreads();
-  float M = red[0][0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) M = fmaxf(M, red[0][i]);
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if (t + 1024 * i < L4) {
-      const float4 a = val(i);
-      sum += hw_exp2((a.x - M) * LOG2E) + hw_exp2((a.y - M) * LOG2E) + hw_exp2((a.z - M) * LOG2E) +
-             hw_exp2((a.w - M) * LOG2E);
-    }
-  sum = wave_sum(sum);
-  if (lane == 0) red[1][w] = sum;
-  __syncthreads();
-  float S = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) S += red[1][i];
-  const float lse = M + hw_log2(S) * LN2;
-  const int yy = target_in_range(y[row], V, bad, t);
-  if (t == 0) {
-    loss[row] = lse - to_f(zr[yy]);
-    if (lse_out) lse_out[row] = lse;
-  }
-  if (dz != nullptr) {
-    T* dr = dz + (int64_t)row * ldz;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int j = t + 1024 * i, c = 4 * j;
-      if (j >= L4) break;
-      const float4 a = val(i);
-      float d[4] = {hw_exp2((a.x - lse) * LOG2E), hw_exp2((a.y - lse) * LOG2E), hw_exp2((a.z - lse) * LOG2E),
-                    hw_exp2((a.w - lse) * LOG2E)};
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (c + k == yy) d[k] -= 1.f;
-      store4(dr + c, make_float4(d[0] * scale, d[1] * scale, d[2] * scale, d[3] * scale));
-    }
-  }
-}
-
 // out[0] = mean of x[0..n) summed in a fixed order; also ring[slot].  1024
 // threads; thread t adds x[t], x[t + 1024], ... in order, then the waves' sums
 // are added in wave order.
@@ -663,37 +477,6 @@ hipError_t colsum_partial(int dtype, const void* x, int rows, int cols, float* p
   return hipGetLastError();
 }
 
-template <int NV>
-hipError_t ce_reg(int dtype, const void* z, int64_t ldz, int V, const int32_t* y, int rows, float scale, float* loss,
-                  float* lse_out, void* dz, int* bad, hipStream_t s) {
-  if (dtype == BF16)
-    hipLaunchKernelGGL((ce_reg_kernel<bf16, NV>), dim3(rows), dim3(1024), 0, s, (const bf16*)z, ldz, V, y, scale,
-                       loss, lse_out, (bf16*)dz, bad);
-  else
-    hipLaunchKernelGGL((ce_reg_kernel<float, NV>), dim3(rows), dim3(1024), 0, s, (const float*)z, ldz, V, y, scale,
-                       loss, lse_out, (float*)dz, bad);
-  return hipGetLastError();
-}
-
-hipError_t ce_rows(int dtype, const void* z, int64_t ldz, int V, const int32_t* y, int rows, float scale,
-                   float* loss, float* lse_out, void* dz, int* bad, hipStream_t s) {
-  // rows of up to 64K columns are held in registers (one read of the logits)
-  if (ldz % 4 == 0) {
-    const int64_t nv = (ldz / 4 + 1023) / 1024;
-    if (nv <= 2) return ce_reg<2>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, bad, s);
-    if (nv <= 4) return ce_reg<4>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, bad, s);
-    if (nv <= 8) return ce_reg<8>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, bad, s);
-    if (nv <= 13) return ce_reg<13>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, bad, s);
-    if (nv <= 16) return ce_reg<16>(dtype, z, ldz, V, y, rows, scale, loss, lse_out, dz, bad, s);
-  }
-  if (dtype == BF16)
-    hipLaunchKernelGGL(ce_rows_kernel<bf16>, dim3(rows), dim3(256), 0, s, (const bf16*)z, ldz, V, y, scale, loss,
-                       lse_out, (bf16*)dz, bad);
-  else
-    hipLaunchKernelGGL(ce_rows_kernel<float>, dim3(rows), dim3(256), 0, s, (const float*)z, ldz, V, y, scale, loss,
-                       lse_out, (float*)dz, bad);
-  return hipGetLastError();
-}
 
 hipError_t mean_f32(const float* x, int n, float* out, float* ring, int slot, hipStream_t s) {
   hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, s, x, n, out, ring, slot);

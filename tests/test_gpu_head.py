@@ -51,10 +51,11 @@ def test_head_fp32_vs_oracle(N, V, C):
     assert rel_err(dW.cpu().numpy(), rdW) <= 1e-4
 
 
-@pytest.mark.parametrize("N,V,C", [(4352, 300, 1600), (4352, 300, 1280), (4100, 257, 2048)])
-def test_head_ragged_last_chunk_wide_rows(N, V, C):
-    # more rows than one 4096-row chunk with a short last chunk, at widths whose data-gradient
-    # product takes more K-splits for the short chunk: its partial sums must fit the workspace
+@pytest.mark.parametrize("N,V,C", [(4352, 300, 1600), (4352, 300, 1280), (4100, 257, 1792), (333, 129, 1024),
+                                   (97, 33, 192)])
+def test_head_ragged_rows_wide_rows(N, V, C):
+    # row counts and vocabularies that are not multiples of the 32- or 64-row blocks, at every
+    # register/LDS shape of the kernel (64-column groups per wave: 1, 3, 4, 5, 7)
     announce(f"head bf16 N={N} V={V} C={C}")
     X, W, y = synthetic.lmhead_inputs(N, V, C, seed=2)
     loss, dX, dW = binding.lmhead_ce(*to_dev(X, W, y, binding.GPT_BF16), binding.GPT_BF16)
