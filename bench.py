@@ -43,7 +43,7 @@ PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
 # kernel classes the library can time (each GEMM class times its main kernel only)
 PROFILE_CLASSES = ["gemm_qkv_fwd", "gemm_proj_fwd", "gemm_fc_fwd", "gemm_mlpproj_fwd", "gemm_dgrad_mlp",
                    "gemm_dgrad_attn", "gemm_wgrad_mlp", "gemm_wgrad_attn", "attn_fwd", "attn_bwd",
-                   "layernorm_fwd", "layernorm_bwd", "head_fwd", "head_dw",
+                   "layernorm_fwd", "layernorm_bwd", "head_fwd", "head_dz", "head_dw",
                    "bias_colsum", "param_reduce", "embed_bwd", "adamw"]
 # further classes reported beside the dominant one (one extra step each)
 MORE_CLASSES = ["gemm_fc_fwd", "attn_fwd", "head_fwd", "head_dw", "layernorm_fwd", "adamw"]
@@ -68,7 +68,7 @@ KERNEL_SOURCES = {
 
 def sources_sha(kernel_class):
     fam = ("attn" if kernel_class.startswith("attn") else
-           "head" if kernel_class.startswith(("head", "lmhead")) else "gemm")
+           "head" if kernel_class in ("head_fwd", "lmhead") else "gemm")
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[fam]:
         with open(os.path.join(ROOT, "decoder_only_transformer_train_amd", rel), "rb") as f:

@@ -72,7 +72,17 @@ struct Params {
   float* ws;
   float* dv;
   int tn, heads;
+  const float* lse;     // EPI_CE_GRAD: per-row log-sum-exp (natural log)
+  const int32_t* rowi;  // EPI_CE_GRAD: per-row target class
+  int col0;             // EPI_CE_GRAD: class of output column 0
+  float scale;          // EPI_CE_GRAD
 };
+
+// EPI_CE_GRAD: the cross-entropy gradient at logit x of class `cls` in a row
+// with log-sum-exp lse and target y: scale (exp(x - lse) - [cls == y]).
+__device__ __forceinline__ float ce_grad(float x, float lse, int y, int cls, float scale) {
+  return (hw_exp2((x - lse) * LOG2E) - (cls == y ? 1.f : 0.f)) * scale;
+}
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -219,6 +229,13 @@ __device__ __forceinline__ void epi_group_inline(const Params& p, int m, int n, 
     return;
   }
   const int64_t o = (int64_t)m * p.ldc + n;
+  if constexpr (EPI == EPI_CE_GRAD) {
+    const float l = p.lse[m];
+    const int y = p.rowi[m];
+    for (int k = 0; k < 4; ++k)
+      if (n + k < p.N) reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(ce_grad(v[k], l, y, p.col0 + n + k, p.scale));
+    return;
+  }
   if (!full || (p.ldc & 3)) {  // ragged edge: element by element
     for (int k = 0; k < 4; ++k) {
       if (n + k >= p.N) break;
@@ -273,11 +290,14 @@ __device__ __forceinline__ void epi_group_inline(const Params& p, int m, int n, 
 // pre-activation (EPI_GELU_BWD) or the previous output (EPI_F32 accumulating).
 template <int EPI, int SPLIT>
 __device__ __forceinline__ constexpr bool epi_reads() {
-  return !SPLIT && (EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_F32 || EPI == EPI_STORE_ODOT);
+  return !SPLIT && (EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_F32 || EPI == EPI_STORE_ODOT ||
+                    EPI == EPI_CE_GRAD);
 }
+// (EPI_CE_GRAD: the row's log-sum-exp and target, as (lse, bits of y, 0, 0))
 template <typename T, int EPI, int SPLIT>
-__device__ __forceinline__ float4 epi_load(const Params& p, int64_t o) {
-  if constexpr (EPI == EPI_RESID) return *reinterpret_cast<const float4*>(p.R + o);
+__device__ __forceinline__ float4 epi_load(const Params& p, int m, int64_t o) {
+  if constexpr (EPI == EPI_CE_GRAD) return make_float4(p.lse[m], __int_as_float(p.rowi[m]), 0.f, 0.f);
+  else if constexpr (EPI == EPI_RESID) return *reinterpret_cast<const float4*>(p.R + o);
   else if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_STORE_ODOT) return load4(reinterpret_cast<const T*>(p.aux) + o);
   else if constexpr (EPI == EPI_F32) {
     if (p.accumulate) return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.C) + o);
@@ -294,7 +314,12 @@ __device__ __forceinline__ void epi_group_full(const Params& p, int m, int n, fl
     return;
   }
   const int64_t o = (int64_t)m * p.ldc + n;
-  if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_ODOT) {
+  if constexpr (EPI == EPI_CE_GRAD) {
+    const int y = __float_as_int(in.y), c = p.col0 + n;
+    store4(reinterpret_cast<T*>(p.C) + o, make_float4(ce_grad(a.x, in.x, y, c, p.scale), ce_grad(a.y, in.x, y, c + 1, p.scale),
+                                                      ce_grad(a.z, in.x, y, c + 2, p.scale),
+                                                      ce_grad(a.w, in.x, y, c + 3, p.scale)));
+  } else if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_ODOT) {
     store4(reinterpret_cast<T*>(p.C) + o, make_float4(a.x + b4.x, a.y + b4.y, a.z + b4.z, a.w + b4.w));
   } else if constexpr (EPI == EPI_RESID) {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) =
@@ -331,6 +356,17 @@ __device__ __forceinline__ void epi_group(const Params& p, int m, int n, float4 
     return;
   }
   const int64_t o = (int64_t)m * p.ldc + n;
+  if constexpr (EPI == EPI_CE_GRAD) {
+    if (!full) {  // ragged edge: element by element, the row's values loaded here
+      const float l = p.lse[m];
+      const int y = p.rowi[m];
+      for (int k = 0; k < 4; ++k)
+        if (n + k < p.N) reinterpret_cast<T*>(p.C)[o + k] = from_f<T>(ce_grad(v[k], l, y, p.col0 + n + k, p.scale));
+    } else {
+      epi_group_full<T, EPI, SPLIT>(p, m, n, a, in, b4);
+    }
+    return;
+  }
   if (!full) {  // ragged edge: element by element
     for (int k = 0; k < 4; ++k) {
       if (n + k >= p.N) break;
@@ -471,7 +507,7 @@ __device__ __forceinline__ void epilogue_lds(const Params& p, ACC (&acc)[FM][FN]
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const int m = m0 + pass * PASS_ROWS + row_of(i), j = i % NCOL;
-        in[i] = (full[j] && m < p.M) ? epi_load<T, EPI, SPLIT>(p, (int64_t)m * p.ldc + n[j])
+        in[i] = (full[j] && m < p.M) ? epi_load<T, EPI, SPLIT>(p, m, (int64_t)m * p.ldc + n[j])
                                      : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
@@ -925,6 +961,7 @@ hipError_t dispatch(const Gemm& g, const Params& p, int tile, int splits, hipStr
     case 0 + EPI_RESID: return launch_tile<T, 0, 0, EPI_RESID, 0>(p, tile, 1, s, ev);
     case 0 + EPI_GELU: return launch_tile<T, 0, 0, EPI_GELU, 0>(p, tile, 1, s, ev);
     case 0 + EPI_F32: return launch_tile<T, 0, 0, EPI_F32, 0>(p, tile, 1, s, ev);
+    case 0 + EPI_CE_GRAD: return launch_tile<T, 0, 0, EPI_CE_GRAD, 0>(p, tile, 1, s, ev);
     case 10 + EPI_F32: return launch_tile<T, 0, 1, EPI_F32, 0>(p, tile, 1, s, ev);
     case 10 + EPI_STORE: return launch_tile<T, 0, 1, EPI_STORE, 0>(p, tile, 1, s, ev);
     case 10 + EPI_GELU_BWD: return launch_tile<T, 0, 1, EPI_GELU_BWD, 0>(p, tile, 1, s, ev);
@@ -1017,6 +1054,7 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main, hipEvent_t 
       return hipErrorInvalidValue;
     if (tile == 1 || tile == 4) tile = 3;
   }
+  if (g.epi == EPI_CE_GRAD && (!g.lse || !g.rowi || g.bias)) return hipErrorInvalidValue;
   if (can_split) splits = std::min(splits, g.splits);
   Params p{};
   p.A = g.A;
@@ -1036,6 +1074,10 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main, hipEvent_t 
   p.dv = g.dv;
   p.tn = g.tn;
   p.heads = g.heads;
+  p.lse = g.lse;
+  p.rowi = g.rowi;
+  p.col0 = g.col0;
+  p.scale = g.scale;
   p.tiles_m = cdiv(g.M, TILE_BM[tile]);
   p.tiles_n = cdiv(g.N, TILE_BN[tile]);
   p.ws = g.ws;

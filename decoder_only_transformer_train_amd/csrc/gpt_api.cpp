@@ -96,6 +96,8 @@ struct gpt_ctx {
   float *muf, *rsf;
   // head: per-row losses and log-sum-exps, the gradient at the final LayerNorm output
   float *tok_loss, *tok_lse, *dF, *loss;
+  void* gchunk;         // T [N][head_cols]: the logit gradient of one block of vocabulary columns
+  int64_t head_cols = 0;
   float* ring;
   int ring_wr = 0, ring_rd = 0;
   // backward
@@ -114,7 +116,7 @@ struct gpt_ctx {
   std::vector<hipEvent_t> adam_ev;
   hipEvent_t norm_done = nullptr;
   bool adam_pending = false;
-  float *Dv, *lnf_part, *splitk_ws;
+  float *Dv, *lnf_part, *splitk_ws = nullptr;
   int64_t splitk_n = 0;  // floats in splitk_ws
   gk::RedJob* jobs_dev;
   std::vector<gk::RedJob> jobs;
@@ -207,6 +209,20 @@ int64_t splitk_floats(int64_t N, int64_t C) {
   return best;
 }
 
+// Vocabulary columns per block of the head's weight gradient: the block's
+// logit gradient [N][cols] (T) is about 64 MB, a multiple of 256 columns (the
+// GEMM tile) between 256 and V rounded up.  GPT_HEAD_COLS overrides it for
+// tuning runs.
+int64_t head_block_cols(int64_t N, int64_t V, int64_t es) {
+  static const int64_t forced = [] {
+    const char* e = getenv("GPT_HEAD_COLS");
+    return e ? std::max<int64_t>(0, atoll(e)) : 0;
+  }();
+  const int64_t vmax = (V + 255) / 256 * 256;
+  int64_t c = forced ? forced : (64ll << 20) / (N * es) / 256 * 256;
+  return std::min(vmax, std::max<int64_t>(256, c / 256 * 256));
+}
+
 // Lays out (base == nullptr: measures) everything the context needs.
 int64_t carve(gpt_ctx* x, void* base) {
   Carver cv(base);
@@ -246,6 +262,8 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->tok_loss = cv.take<float>(N * 4);
   x->tok_lse = cv.take<float>(N * 4);
   x->dF = cv.take<float>(N * C * 4);
+  x->head_cols = head_block_cols(N, x->Vp, es);
+  x->gchunk = cv.take<void>(N * x->head_cols * es);
   x->loss = cv.take<float>(64);
   x->ring = cv.take<float>(RING * 4);
   x->dres = cv.take<float>(N * C * 4);
@@ -423,11 +441,18 @@ int join_side(gpt_ctx* x) {
 }
 
 // The tied head fused with the cross-entropy (no [N, V] logits anywhere):
-// pass 1 - per-row loss and log-sum-exp and, with gradients, dF - on the
-// context stream, then the fixed-order mean of the row losses; pass 2 - the
+// one pass gives the per-row loss and log-sum-exp and, with gradients, dF -
+// on the context stream - then the fixed-order mean of the row losses.  The
 // head's part of the tied weight's gradient, which only the embedding step of
-// the backward reads - on the side stream when there is one, beside the
-// backward of the blocks.
+// the backward reads, runs on the side stream when there is one, beside the
+// backward of the blocks: per block of head_cols vocabulary columns, one
+// product recomputes the block's logits and turns them into their gradient
+// (exp(z - lse) - onehot) * scale in its epilogue (T, [N][cols]), and a second
+// one contracts it with F over the rows into those columns' rows of dW.
+// Short tiles of the two products interleave with the backward's kernels on
+// the CUs.  GPT_HEAD_DW=fused selects the single-kernel variant instead (the
+// same recomputation and contraction with the block never leaving the CU; its
+// long-lived workgroups hold CUs away from the backward).
 int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C, float scale,
          float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, int dtype, float* loss, float* ring,
          int slot, int* bad) {
@@ -436,14 +461,40 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
     HIPCHK(gk::lmhead_fwd(dtype, Fin, W, (int)N, (int)V, (int)C, y, scale, tok_loss, tok_lse, dF, bad, x->stream));
   }
   HIPCHK(gk::mean_f32(tok_loss, (int)N, loss, ring, slot, x->stream));
-  if (dW) {
-    hipStream_t ds = x->side ? x->side : x->stream;
-    if (x->side) {
-      HIPCHK(hipEventRecord(x->head_fork, x->stream));
-      HIPCHK(hipStreamWaitEvent(x->side, x->head_fork, 0));
-    }
+  if (!dW) return 0;
+  hipStream_t ds = x->side ? x->side : x->stream;
+  if (x->side) {
+    HIPCHK(hipEventRecord(x->head_fork, x->stream));
+    HIPCHK(hipStreamWaitEvent(x->side, x->head_fork, 0));
+  }
+  static const bool fused = [] {
+    const char* e = getenv("GPT_HEAD_DW");
+    return e && std::string(e) == "fused";
+  }();
+  if (fused) {
     ProfScope ps(x, "head_dw", 2.0 * N * V * C, 0.0, ds);
     HIPCHK(gk::lmhead_dw(dtype, Fin, W, (int)N, (int)V, (int)C, y, tok_lse, scale, dW, dW_acc, ds));
+    return 0;
+  }
+  const int64_t es = dtype == GPT_BF16 ? 2 : 4, cols = x->head_cols;
+  for (int64_t v0 = 0; v0 < V; v0 += cols) {
+    const int64_t n = std::min(cols, V - v0);
+    gk::Gemm g = mk(x, 0, 0, gk::EPI_CE_GRAD, Fin, C, (const char*)W + v0 * C * es, C, N, n, C, x->gchunk, cols);
+    g.dtype = dtype;
+    g.lse = tok_lse;
+    g.rowi = y;
+    g.col0 = (int)v0;
+    g.scale = scale;
+    if (int e = run_gemm(x, "head_dz", g, ds)) return e;
+    g = mk(x, 1, 1, gk::EPI_F32, x->gchunk, cols, Fin, C, n, C, N, dW + v0 * C, C);
+    g.dtype = dtype;
+    g.accumulate = dW_acc;
+    if (x->splitk_ws) {
+      g.splits = gk::gemm_pick_splits((int)n, (int)C, (int)N, 1, 1);
+      g.ws = x->splitk_ws;
+      g.ws_floats = x->splitk_n;
+    }
+    if (int e = run_gemm(x, "head_dw", g, ds)) return e;
   }
   return 0;
 }
@@ -821,8 +872,14 @@ size_t gpt_lmhead_ce_ws_bytes(int64_t N, int64_t V, int64_t C, int32_t dtype) {
   if (N < 1 || V < 1 || C < 64 || C % 64 || (dtype != GPT_F32 && dtype != GPT_BF16)) return 0;
   if (N > 0x7fffffff || V > 0x7fffffff || C > gk::lmhead_max_embd(dtype)) return 0;
   if (dtype == GPT_BF16 && ((N + 32) * C * 2 >= (1ll << 32) || (V + 32) * C * 2 >= (1ll << 32))) return 0;
-  // per-row losses and log-sum-exps, and the out-of-range target flag
-  return (size_t)(2 * align_up(N * 4, ALIGN) + ALIGN);
+  // per-row losses and log-sum-exps, the out-of-range target flag, with dW the
+  // logit gradient of one block of vocabulary columns and a split-K workspace
+  size_t b = (size_t)(2 * align_up(N * 4, ALIGN) + ALIGN);
+  const int64_t es = dtype == GPT_BF16 ? 2 : 4, cols = head_block_cols(N, V, es);
+  b += (size_t)align_up(N * cols * es, ALIGN);
+  const int sp = gk::gemm_pick_splits((int)cols, (int)C, (int)N, 1, 1);
+  if (sp > 1) b += (size_t)align_up((int64_t)sp * cols * C * 4, ALIGN);
+  return b;
 }
 
 int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int64_t V, int64_t C, int32_t dtype,
@@ -837,6 +894,14 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
   float* tl = cv.take<float>(N * 4);
   float* tlse = cv.take<float>(N * 4);
   int* bad = cv.take<int>(ALIGN);
+  const int64_t es = dtype == GPT_BF16 ? 2 : 4;
+  tmp.head_cols = head_block_cols(N, V, es);
+  tmp.gchunk = cv.take<void>(N * tmp.head_cols * es);
+  const int sp = gk::gemm_pick_splits((int)tmp.head_cols, (int)C, (int)N, 1, 1);
+  if (sp > 1) {
+    tmp.splitk_n = (int64_t)sp * tmp.head_cols * C;
+    tmp.splitk_ws = cv.take<float>(tmp.splitk_n * 4);
+  }
   HIPCHK(gk::fill_f32((float*)bad, 1, 0.f, tmp.stream));
   if (int e = head(&tmp, X, W, V, y, N, C, 1.0f / (float)N, tl, tlse, dX, dW, 0, dtype, loss_dev, nullptr, 0, bad))
     return e;

@@ -119,15 +119,17 @@ __device__ __forceinline__ uint4 frag_tr(const char* s, int c0, int r0, int lane
 }
 
 // LDS of a workgroup: per wave ST stages of its slice (+ 512 bytes of per-row
-// scalars in pass 2), then the partial z tiles [4 waves][NQT][4][64 lanes]
-// (float4) and their reduced quarters [NQT][4][64 lanes].
+// scalars in pass 2); the partial z tiles [4 waves][NQT][4 quarters][64 lanes]
+// (float4); the bf16 probabilities or gradients [NQT][4 quarters][64 lanes]
+// (4 bf16 each); and per-wave column values [NQT][4 waves][64 lanes] (float).
 template <int NG, int NQT, int ST, int MODE>
 struct Lds {
   static constexpr int STAGE = Slice<NG>::BYTES + (MODE ? 512 : 0);
   static constexpr int PER_WAVE = ST * STAGE;
   static constexpr int PART = 4 * PER_WAVE;
-  static constexpr int RED = PART + 4 * NQT * 4 * 64 * 16;
-  static constexpr int TOTAL = RED + NQT * 4 * 64 * 16;
+  static constexpr int PQ = PART + 4 * NQT * 4 * 64 * 16;
+  static constexpr int COLV = PQ + NQT * 4 * 64 * 8;
+  static constexpr int TOTAL = COLV + NQT * 4 * 64 * 4;
 };
 
 // Per-lane state of a workgroup's pass (the same row statistics in every wave).
@@ -135,42 +137,114 @@ template <int NG, int NQT>
 struct State {
   uint4 qf[NQT][NG * 4];    // fixed rows: B fragments of the z product over this wave's columns
   f32x16 O[NQT][NG * 2];    // second-product accumulators over this wave's columns
-  float m[NQT], l[NQT], zy[NQT];  // pass 1: reference max (log2 units), this lane half's sum, target logit
+  float m[NQT], l[NQT], zy[NQT];  // pass 1: reference max (log2 units); this wave's quarter: sum of p, target logit
+  float seen[NQT];                // pass 1: this wave's quarter: maximum so far (log2 units)
   int yq[NQT];              // pass 1: the fixed row's target
   int ng, f0, lane, w, g, c32;
 };
 
-// z^T tiles of one streamed block: partials over this wave's columns, summed
-// across the waves through part/red.  rd holds the block's slice; the
-// pointers are distinct and __restrict__, so the compiler need not wait for
-// outstanding direct-to-LDS loads (into other stages) before these accesses.
-// z[qt][e]: streamed row r0 + crow(e, g), fixed row f0 + 32 qt + c32.
-template <int NG, int NQT>
-__device__ __forceinline__ void z_tiles(const char* __restrict__ rd, float4* __restrict__ part,
-                                        float4* __restrict__ red, const State<NG, NQT>& S, f32x16 (&z)[NQT]) {
-  const int lane = S.lane, w = S.w, g = S.g, c32 = S.c32;
-#pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) zero16(z[qt]);
-  // Every k-step runs in every wave, also past a wave's own columns (fewer
-  // groups than NG): those k-steps have zero fixed fragments, and the slot data
-  // there is real memory from the loads, so it is finite; the waves meet at
-  // every block and wait for the widest one anyway.
-#pragma unroll
-  for (int ks = 0; ks < NG * 4; ++ks) {
-    const uint4 af = frag_row<NG>(rd, c32, ks, g);  // serves every fixed tile
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) mma32(z[qt], af, S.qf[qt][ks]);
-    // keep at most 4 k-steps of fragment reads ahead of their products (registers)
-    if ((ks & 3) == 3) asm volatile("" ::: "memory");
+// This wave's slice loads of a streamed block: instruction i, lane -> (block
+// row, logical chunk) -> source byte offset; pass 2 also loads the block rows'
+// log-sum-exps and targets (one dword instruction each, into the stage tail).
+template <int NG, int MODE>
+struct Loader {
+  rsrc_t rs, rl, ry;
+  uint32_t off[Slice<NG>::NLD];
+  uint32_t blk_bytes;
+  int lane;
+  // load instruction i of block blk into stage st
+  __device__ __forceinline__ void one(int i, int blk, char* st) const {
+    dma16(rs, st + i * 1024, off[i] + (uint32_t)blk * blk_bytes);
   }
+  __device__ __forceinline__ void tail(int blk, char* st) const {
+    if constexpr (MODE == 1) {
+      dma4(rl, st + Slice<NG>::BYTES, (uint32_t)(blk * BV + lane) * 4);
+      dma4(ry, st + Slice<NG>::BYTES + 256, (uint32_t)(blk * BV + lane) * 4);
+    }
+  }
+  __device__ __forceinline__ void all(int blk, char* st) const {
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt)
+    for (int i = 0; i < Slice<NG>::NLD; ++i) one(i, blk, st);
+    tail(blk, st);
+  }
+  static constexpr int PER_BLOCK = Slice<NG>::NLD + (MODE ? 2 : 0);  // load instructions per block
+};
+
+// second product over this wave's columns: O^T[c][fixed] += (block^T)[c][streamed] P^T[streamed][fixed]
+// (the tiles past a wave's own columns are computed too and never stored)
+// Both halves of the streamed rows (hh) go over all column tiles in turn, so
+// the two products into one accumulator are 2 NG NQT products apart (an MFMA
+// result is not ready for a dependent product for several issue slots).  A
+// ring of three fragments keeps the reads two (hh, ct) steps ahead of their
+// products; the empty asm statements keep the compiler from hoisting every
+// read to the top (registers).
+template <int NG, int NQT>
+__device__ __forceinline__ void second_product(const char* __restrict__ rd, const uint4 (&pb)[NQT][2],
+                                               State<NG, NQT>& S) {
+  constexpr int NT = NG * 2;
+  uint4 f[3];
+  f[0] = frag_tr<NG>(rd, 0, 0, S.lane);
+  f[1] = frag_tr<NG>(rd, (1 % NT) * 32, (1 / NT) * 16, S.lane);
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4)
-      part[((w * NQT + qt) * 4 + e4) * 64 + lane] =
-          make_float4(z[qt][4 * e4], z[qt][4 * e4 + 1], z[qt][4 * e4 + 2], z[qt][4 * e4 + 3]);
-  __syncthreads();
-  // wave w adds accumulator quarter w of every tile over the 4 waves, in wave order
+  for (int i = 0; i < 2 * NT; ++i) {
+    const int hh = i / NT, ct = i % NT;
+    if (i + 2 < 2 * NT) f[(i + 2) % 3] = frag_tr<NG>(rd, ((i + 2) % NT) * 32, ((i + 2) / NT) * 16, S.lane);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) mma32(S.O[qt][ct], f[i % 3], pb[qt][hh]);
+  }
+}
+
+// One streamed block (its slice in rd, streamed rows r0 ..):
+//  1. partial z^T tiles over this wave's columns (z[qt][e]: streamed row
+//     r0 + crow(e, g), fixed row f0 + 32 qt + c32); meanwhile, when refill >= 0,
+//     block `refill` is loaded into wr (one instruction per k-step: a wave that
+//     issues its loads back to back stalls at issue);
+//  2. through LDS, wave w adds accumulator quarter w (e = 4 w .. 4 w + 3, the
+//     streamed rows 8 w + 4 g + i) over the 4 waves, in wave order, and turns
+//     it into bf16 probabilities (pass 1, against the row's reference m) or
+//     gradients (pass 2); the quarters go back through LDS and every wave
+//     assembles the B fragments of the second product from them.
+// At block 0 of pass 1 (first), the reference m of each fixed row is set to
+// the block's maximum, exchanged through LDS.  The pointers are distinct and
+// __restrict__, so the compiler need not wait for the loads into wr before
+// the LDS accesses here.
+template <int NG, int NQT, int MODE>
+__device__ __forceinline__ void block_p(const char* __restrict__ rd, char* __restrict__ wr, int refill,
+                                        const Loader<NG, MODE>& ld, float4* __restrict__ part,
+                                        uint2* __restrict__ pq, float* __restrict__ colv, const Args& a, int r0,
+                                        bool first, State<NG, NQT>& S, uint4 (&pb)[NQT][2]) {
+  const int lane = S.lane, w = S.w, g = S.g, c32 = S.c32;
+  {
+    f32x16 z[NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) zero16(z[qt]);
+    // Every k-step runs in every wave, also past a wave's own columns (fewer
+    // groups than NG): those k-steps have zero fixed fragments, and the slot
+    // data there is real memory from the loads, so it is finite; the waves meet
+    // at every block and wait for the widest one anyway.
+    // the fragment of k-step ks + 2 is read while k-step ks's products run
+    uint4 af[3];
+    af[0] = frag_row<NG>(rd, c32, 0, g);
+    af[1] = frag_row<NG>(rd, c32, 1, g);
+#pragma unroll
+    for (int ks = 0; ks < NG * 4; ++ks) {
+      if (ks + 2 < NG * 4) af[(ks + 2) % 3] = frag_row<NG>(rd, c32, ks + 2, g);
+      if (refill >= 0) ld.one(ks, refill, wr);  // NLD == 4 NG == the number of k-steps
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) mma32(z[qt], af[ks % 3], S.qf[qt][ks]);  // serves every fixed tile
+    }
+    if (refill >= 0) ld.tail(refill, wr);
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        part[((w * NQT + qt) * 4 + e4) * 64 + lane] =
+            make_float4(z[qt][4 * e4], z[qt][4 * e4 + 1], z[qt][4 * e4 + 2], z[qt][4 * e4 + 3]);
+  }
+  lds_barrier();
+  float q[NQT][4];  // this wave's quarter of z: streamed rows r0 + 8 w + 4 g + i
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     float4 s4 = part[(qt * 4 + w) * 64 + lane];
@@ -182,129 +256,93 @@ __device__ __forceinline__ void z_tiles(const char* __restrict__ rd, float4* __r
       s4.z += p4.z;
       s4.w += p4.w;
     }
-    red[(qt * 4 + w) * 64 + lane] = s4;
+    q[qt][0] = s4.x;
+    q[qt][1] = s4.y;
+    q[qt][2] = s4.z;
+    q[qt][3] = s4.w;
   }
-  __syncthreads();
+  const int rq = r0 + 8 * w + 4 * g;  // streamed row of q[.][0]
+  if constexpr (MODE == 0) {
+    float mx[NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      float v = NEG_INF;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (rq + i >= a.n_str) q[qt][i] = NEG_INF;  // W rows past V are not classes
+        v = fmaxf(v, q[qt][i]);
+        if (rq + i == S.yq[qt]) S.zy[qt] = q[qt][i];
+      }
+      mx[qt] = v * LOG2E;
+      S.seen[qt] = fmaxf(S.seen[qt], mx[qt]);
+    }
+    if (first) {  // the reference: each fixed row's maximum over this block
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) colv[(qt * 4 + w) * 64 + lane] = mx[qt];
+      lds_barrier();
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) {
+        float v = colv[(qt * 4) * 64 + lane];
+#pragma unroll
+        for (int u = 1; u < 4; ++u) v = fmaxf(v, colv[(qt * 4 + u) * 64 + lane]);
+        S.m[qt] = halves_max(v);
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      bf16x4 v;
+      float ls = S.l[qt];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16 p = (bf16)hw_exp2(fmaf(q[qt][i], LOG2E, -S.m[qt]));
+        v[i] = p;
+        ls += (float)p;  // the sum of the rounded p the product uses
+      }
+      S.l[qt] = ls;
+      pq[(qt * 4 + w) * 64 + lane] = bitcast<uint2>(v);
+    }
+  } else {
+    // pass 2: g = scale (exp(z - lse) - [y == v]); F rows past N (loaded as zeros) give 0
+    const float* sl = reinterpret_cast<const float*>(rd + Slice<NG>::BYTES);
+    const int* sy = reinterpret_cast<const int*>(rd + Slice<NG>::BYTES + 256);
+    const float4 l4 = *reinterpret_cast<const float4*>(sl + 8 * w + 4 * g);
+    const int4 y4 = *reinterpret_cast<const int4*>(sy + 8 * w + 4 * g);
+    const float lv[4] = {l4.x * LOG2E, l4.y * LOG2E, l4.z * LOG2E, l4.w * LOG2E};
+    const int yv[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int vq = S.f0 + qt * 32 + c32;  // this lane's W row
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = hw_exp2(fmaf(q[qt][i], LOG2E, -lv[i])) - (yv[i] == vq ? 1.f : 0.f);
+        if (rq + i >= a.n_str) p = 0.f;
+        v[i] = (bf16)(p * a.scale);
+      }
+      pq[(qt * 4 + w) * 64 + lane] = bitcast<uint2>(v);
+    }
+  }
+  lds_barrier();
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const float4 s4 = red[(qt * 4 + e4) * 64 + lane];
-      z[qt][4 * e4] = s4.x;
-      z[qt][4 * e4 + 1] = s4.y;
-      z[qt][4 * e4 + 2] = s4.z;
-      z[qt][4 * e4 + 3] = s4.w;
-    }
-}
-
-// second product over this wave's columns: O^T[c][fixed] += (block^T)[c][streamed] P^T[streamed][fixed]
-// (the tiles past a wave's own columns are computed too and never stored)
-template <int NG, int NQT>
-__device__ __forceinline__ void second_product(const char* __restrict__ rd, const uint4 (&pb)[NQT][2],
-                                               State<NG, NQT>& S) {
-#pragma unroll
-  for (int ct = 0; ct < NG * 2; ++ct) {
-#pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const uint4 af = frag_tr<NG>(rd, ct * 32, hh * 16, S.lane);
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) mma32(S.O[qt][ct], af, pb[qt][hh]);
+      const uint2 lo = pq[(qt * 4 + 2 * hh) * 64 + lane], hi = pq[(qt * 4 + 2 * hh + 1) * 64 + lane];
+      pb[qt][hh] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
-    if (ct & 1) asm volatile("" ::: "memory");
-  }
 }
 
-// pass 1, one block: p = 2^(z log2e - m) against the row's reference m (bf16,
-// as the product uses it), the running sums, and the second product
-template <int NG, int NQT>
-__device__ __forceinline__ void fwd_consume(const char* __restrict__ rd, const f32x16 (&z)[NQT], State<NG, NQT>& S) {
-  uint4 pb[NQT][2];
+// Sum (or max) of a per-lane value over the 4 waves and the two lane halves,
+// through LDS (after a barrier every wave holds the same result).
+template <bool MAX>
+__device__ __forceinline__ float wg_column(float v, float* __restrict__ colv, int w, int lane) {
+  colv[w * 64 + lane] = v;
+  lds_barrier();
+  float t = colv[lane];
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    float ls = S.l[qt];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      bf16x8 v;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const bf16 p = (bf16)hw_exp2(fmaf(z[qt][8 * hh + jj], LOG2E, -S.m[qt]));
-        v[jj] = p;
-        ls += (float)p;  // the sum of the rounded p the product uses
-      }
-      pb[qt][hh] = bitcast<uint4>(v);
-    }
-    S.l[qt] = ls;
-  }
-  second_product<NG, NQT>(rd, pb, S);
-}
-
-// pass 1: mask W rows past V, note the target logit, and return each fixed
-// row's block maximum in log2 units
-template <int NG, int NQT>
-__device__ __forceinline__ void fwd_block_max(f32x16 (&z)[NQT], int r0, int n_str, State<NG, NQT>& S,
-                                              float (&mx)[NQT]) {
-  const int g = S.g;
-  if (r0 + BV > n_str) {  // the last block of a ragged vocabulary: rows past V are not classes
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (r0 + crow(e, g) >= n_str) z[qt][e] = NEG_INF;
-  }
-#pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    float v = NEG_INF;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      v = fmaxf(v, z[qt][e]);
-      if (r0 + crow(e, g) == S.yq[qt]) S.zy[qt] = z[qt][e];
-    }
-    mx[qt] = halves_max(v) * LOG2E;
-  }
-}
-
-// pass 2, one block: g = scale (exp(z - lse) - [y == v]) for the block's F rows
-// (rows past N load as zeros and give 0), then the second product
-template <int NG, int NQT>
-__device__ __forceinline__ void bwd_consume(const char* __restrict__ rd, const f32x16 (&z)[NQT], int r0, const Args& a,
-                                            State<NG, NQT>& S) {
-  const int g = S.g, c32 = S.c32;
-  const float* sl = reinterpret_cast<const float*>(rd + Slice<NG>::BYTES);
-  const int* sy = reinterpret_cast<const int*>(rd + Slice<NG>::BYTES + 256);
-  float lv[16];
-  int yv[16];
-#pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4) {
-    const int k0 = r4 * 8 + g * 4;  // rows crow(4 r4 .. 4 r4 + 3, g)
-    const float4 l4 = *reinterpret_cast<const float4*>(sl + k0);
-    const int4 y4 = *reinterpret_cast<const int4*>(sy + k0);
-    lv[4 * r4] = l4.x * LOG2E;
-    lv[4 * r4 + 1] = l4.y * LOG2E;
-    lv[4 * r4 + 2] = l4.z * LOG2E;
-    lv[4 * r4 + 3] = l4.w * LOG2E;
-    yv[4 * r4] = y4.x;
-    yv[4 * r4 + 1] = y4.y;
-    yv[4 * r4 + 2] = y4.z;
-    yv[4 * r4 + 3] = y4.w;
-  }
-  uint4 pb[NQT][2];
-#pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    const int vq = S.f0 + qt * 32 + c32;  // this lane's W row
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      bf16x8 v;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int e = 8 * hh + jj;
-        float p = hw_exp2(fmaf(z[qt][e], LOG2E, -lv[e])) - (yv[e] == vq ? 1.f : 0.f);
-        if (r0 + crow(e, g) >= a.n_str) p = 0.f;
-        v[jj] = (bf16)(p * a.scale);
-      }
-      pb[qt][hh] = bitcast<uint4>(v);
-    }
-  }
-  second_product<NG, NQT>(rd, pb, S);
+  for (int u = 1; u < 4; ++u) t = MAX ? fmaxf(t, colv[u * 64 + lane]) : t + colv[u * 64 + lane];
+  lds_barrier();  // every wave has read colv before it is written again
+  return MAX ? halves_max(t) : halves_sum(t);
 }
 
 template <int NG, int NQT, int ST, int MODE>
@@ -341,6 +379,7 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
     S.m[qt] = NEG_INF;
     S.l[qt] = 0.f;
     S.zy[qt] = 0.f;
+    S.seen[qt] = NEG_INF;
     S.yq[qt] = 0;
     if constexpr (MODE == 0) {
       int yy = fr < a.n_fix ? a.y[fr] : 0;
@@ -352,113 +391,116 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
     }
   }
 
-  // this wave's slice loads: instruction i, lane -> (block row, logical chunk) -> source byte offset
-  const rsrc_t rs = make_rsrc(a.str, (int64_t)a.n_str * C * 2);
-  uint32_t off[SL::NLD];
+  Loader<NG, MODE> ld;
+  ld.rs = make_rsrc(a.str, (int64_t)a.n_str * C * 2);
+  ld.rl = make_rsrc(MODE == 1 ? (const void*)a.lse : nullptr, MODE == 1 ? (int64_t)a.n_str * 4 : 0);
+  ld.ry = make_rsrc(MODE == 1 ? (const void*)a.y : nullptr, MODE == 1 ? (int64_t)a.n_str * 4 : 0);
+  ld.lane = lane;
+  ld.blk_bytes = (uint32_t)(BV * C * 2);
 #pragma unroll
   for (int i = 0; i < SL::NLD; ++i) {
     const int q = i * 1024 + 16 * lane;
     const int row = q / SL::RS, pc = (q % SL::RS) >> 4;
-    off[i] = (uint32_t)(((int64_t)row * C + c_lo + phys<NG>(pc, row) * 8) * 2);
+    ld.off[i] = (uint32_t)(((int64_t)row * C + c_lo + phys<NG>(pc, row) * 8) * 2);
   }
-  const uint32_t blk_bytes = (uint32_t)(BV * C * 2);
+  constexpr int LPB = Loader<NG, MODE>::PER_BLOCK;
   char* wbase = smem + w * L::PER_WAVE;
-  const rsrc_t rl = make_rsrc(MODE == 1 ? (const void*)a.lse : nullptr, MODE == 1 ? (int64_t)a.n_str * 4 : 0);
-  const rsrc_t ry = make_rsrc(MODE == 1 ? (const void*)a.y : nullptr, MODE == 1 ? (int64_t)a.n_str * 4 : 0);
-  auto issue = [&](int blk, char* st) {
-#pragma unroll
-    for (int i = 0; i < SL::NLD; ++i) dma16(rs, st + i * 1024, off[i] + (uint32_t)blk * blk_bytes);
-    if constexpr (MODE == 1) {
-      dma4(rl, st + SL::BYTES, (uint32_t)(blk * BV + lane) * 4);
-      dma4(ry, st + SL::BYTES + 256, (uint32_t)(blk * BV + lane) * 4);
-    }
-  };
-  constexpr int LPB = SL::NLD + (MODE ? 2 : 0);  // load instructions per block
   float4* part = reinterpret_cast<float4*>(smem + L::PART);
-  float4* red = reinterpret_cast<float4*>(smem + L::RED);
+  uint2* pq = reinterpret_cast<uint2*>(smem + L::PQ);
+  float* colv = reinterpret_cast<float*>(smem + L::COLV);
+  static_assert(SL::NLD == NG * 4, "one slice load per k-step");
 
-  // Block j lives in stage j % ST.  With ST > 1, block j + ST - 1 goes into the
-  // stage block j - 1 used (this wave alone reads its slice, and it is done with
-  // it) before waiting for block j; with one stage the next block is loaded
-  // after the current one is consumed.
-  auto fetch = [&](int j, int sc) {
-    if constexpr (ST == 1) {
-      if (j == 0) issue(0, wbase);
-      wait_vm<0>();
+  // Block j lives in stage j % ST.  Before block j is used, the stage block
+  // j - 1 used (this wave alone reads its slice, and it is done with it) gets
+  // block j + ST - 1, issued during block j's z product; so the loads still
+  // outstanding when block j is needed are those of blocks j + 1 .. j + ST - 2.
+  // With one stage the next block is loaded after the current one is consumed.
+  auto wait_block = [&](int j) {
+    if constexpr (ST == 3) {
+      if (j + 1 < nblk) wait_vm<LPB>();
+      else wait_vm<0>();
     } else {
-      if (j == 0) {
-#pragma unroll
-        for (int s2 = 0; s2 < ST - 1; ++s2)
-          if (s2 < nblk) issue(s2, wbase + s2 * L::STAGE);
-      }
-      const int sw = sc == 0 ? ST - 1 : sc - 1;
-      if (j + ST - 1 < nblk) issue(j + ST - 1, wbase + sw * L::STAGE);
-      const int later = min(ST - 1, nblk - 1 - j);  // blocks after j whose loads may stay outstanding
-      if constexpr (ST == 2) {
-        if (later >= 1) wait_vm<LPB>();
-        else wait_vm<0>();
-      } else {
-        if (later >= 2) wait_vm<2 * LPB>();
-        else if (later == 1) wait_vm<LPB>();
-        else wait_vm<0>();
-      }
+      wait_vm<0>();
     }
   };
-  auto after = [&](int j) {
-    if constexpr (ST == 1)
-      if (j + 1 < nblk) issue(j + 1, wbase);
+  auto stage = [&](int sc) { return wbase + sc * L::STAGE; };
+  auto prologue = [&]() {
+    if constexpr (ST == 1) {
+      ld.all(0, wbase);
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < ST - 1; ++s2)
+        if (s2 < nblk) ld.all(s2, stage(s2));
+    }
+  };
+  prologue();
+  // the stage to refill while block j (in stage sc) is used, and the block it gets (-1: none)
+  auto refill_of = [&](int j, int sc, char*& wr) {
+    if constexpr (ST == 1) {
+      wr = wbase + L::STAGE;  // unused: the single stage is refilled after the block
+      return -1;
+    } else {
+      wr = stage(sc == 0 ? ST - 1 : sc - 1);
+      return j + ST - 1 < nblk ? j + ST - 1 : -1;
+    }
   };
 
-  f32x16 z[NQT];
+  uint4 pb[NQT][2];
   if constexpr (MODE == 0) {
     // Softmax against a fixed reference per row instead of a running maximum:
     // m is the row's maximum over the first W block (so p <= 2^(max - m)), and
     // the accumulators are never rescaled inside the sweep.  A row whose later
     // maximum exceeds m by more than HEADROOM (p could overflow) has the whole
-    // sweep redone with m = that maximum; every wave holds the same z, so the
-    // decision is the same in all of them.
+    // sweep redone with m = that maximum; the maxima are combined over the
+    // waves, so the decision is the same in all of them.
     for (int attempt = 0;; ++attempt) {
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) {
 #pragma unroll
         for (int ct = 0; ct < NG * 2; ++ct) zero16(S.O[qt][ct]);
         S.l[qt] = 0.f;
+        S.seen[qt] = NEG_INF;
       }
-      float seen[NQT];
+      if (attempt > 0) prologue();  // the sweep starts over: reload the first blocks
       int sc = 0;
       for (int j = 0; j < nblk; ++j) {
-        const char* st = wbase + sc * L::STAGE;
-        fetch(j, sc);
-        z_tiles<NG, NQT>(st, part, red, S, z);
-        float mx[NQT];
-        fwd_block_max<NG, NQT>(z, j * BV, a.n_str, S, mx);
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-          if (j == 0) {
-            if (attempt == 0) S.m[qt] = mx[qt];
-            seen[qt] = mx[qt];
-          }
-          seen[qt] = fmaxf(seen[qt], mx[qt]);
-        }
-        fwd_consume<NG, NQT>(st, z, S);
-        after(j);
+        char* wr;
+        const int rf = refill_of(j, sc, wr);
+        wait_block(j);
+        block_p<NG, NQT, MODE>(stage(sc), wr, rf, ld, part, pq, colv, a, j * BV, j == 0 && attempt == 0,
+                               S, pb);
+        second_product<NG, NQT>(stage(sc), pb, S);
+        if constexpr (ST == 1)
+          if (j + 1 < nblk) ld.all(j + 1, wbase);
         sc = sc + 1 == ST ? 0 : sc + 1;
       }
       bool redo = false;
+      float seen[NQT];
 #pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) redo |= seen[qt] > S.m[qt] + HEADROOM;
+      for (int qt = 0; qt < NQT; ++qt) {
+        seen[qt] = wg_column<true>(S.seen[qt], colv, w, lane);
+        redo |= seen[qt] > S.m[qt] + HEADROOM;
+      }
       if (!__any(redo)) break;
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) S.m[qt] = fmaxf(S.m[qt], seen[qt]);
     }
+    // totals over the waves' quarters and the lane halves
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      S.l[qt] = wg_column<false>(S.l[qt], colv, w, lane);
+      S.zy[qt] = wg_column<false>(S.zy[qt], colv, w, lane);  // exactly one quarter saw the target
+    }
   } else {
     int sc = 0;
     for (int j = 0; j < nblk; ++j) {
-      const char* st = wbase + sc * L::STAGE;
-      fetch(j, sc);
-      z_tiles<NG, NQT>(st, part, red, S, z);
-      bwd_consume<NG, NQT>(st, z, j * BV, a, S);
-      after(j);
+      char* wr;
+      const int rf = refill_of(j, sc, wr);
+      wait_block(j);
+      block_p<NG, NQT, MODE>(stage(sc), wr, rf, ld, part, pq, colv, a, j * BV, false, S, pb);
+      second_product<NG, NQT>(stage(sc), pb, S);
+      if constexpr (ST == 1)
+        if (j + 1 < nblk) ld.all(j + 1, wbase);
       sc = sc + 1 == ST ? 0 : sc + 1;
     }
   }
@@ -470,8 +512,7 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
     if (fr >= a.n_fix) continue;
     float* orow = a.out + (int64_t)fr * C + c_lo;
     if constexpr (MODE == 0) {
-      const float lt = halves_sum(S.l[qt]);
-      const float zt = halves_sum(S.zy[qt]);  // exactly one lane half saw the target
+      const float lt = S.l[qt], zt = S.zy[qt];
       const float lse = (S.m[qt] + hw_log2(lt)) * LN2;
       if (w == 0 && g == 0) {
         a.loss[fr] = lse - zt;

@@ -20,6 +20,9 @@ enum Epi {
   // m = b * tn + t of C(T) * aux(T): attention's D = rowsum(dO * O) computed
   // where dO is produced (bf16, N a multiple of 64, 256- or 128-column tiles)
   EPI_STORE_ODOT = 5,
+  // C(T) = scale (exp(acc - lse[m]) - [col0 + n == rowi[m]]): the softmax
+  // cross-entropy gradient of a block of logit columns col0 .. col0 + N - 1
+  EPI_CE_GRAD = 6,
 };
 
 struct Gemm {
@@ -38,6 +41,10 @@ struct Gemm {
   int accumulate = 0;
   float* dv = nullptr;  // EPI_STORE_ODOT: [rows / tn][heads][tn] row sums
   int tn = 0, heads = 0;
+  const float* lse = nullptr;     // EPI_CE_GRAD: [M] per-row log-sum-exp
+  const int32_t* rowi = nullptr;  // EPI_CE_GRAD: [M] per-row target class
+  int col0 = 0;                   // EPI_CE_GRAD
+  float scale = 1.f;              // EPI_CE_GRAD
   // split-K (EPI_F32 only): when > 1, partial sums go to ws [splits][M][N] and are reduced in order;
   // ws holds ws_floats floats and the split count is lowered until splits * M * N fits
   int splits = 1;

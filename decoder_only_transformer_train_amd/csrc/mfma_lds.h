@@ -33,6 +33,18 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier for data exchanged through LDS: this wave's LDS reads and
+// writes are complete, then s_barrier.  Unlike __syncthreads() it does not wait
+// for outstanding direct-to-LDS loads (vmcnt), so blocks prefetched into other
+// stages stay in flight; the empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima (gfx9 encoding)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void mma32(f32x16& c, const uint4& a, const uint4& b) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(a), bitcast<bf16x8>(b), c, 0, 0, 0);
 }
