@@ -941,6 +941,8 @@ hipError_t launch_tile(const Params& p, int tile, int splits, hipStream_t s, Ev 
     if (tile == 0) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<128, 32, 3, 2>>(p, splits, s, ev);
     if (tile == 1) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1>>(p, splits, s, ev);
     if (tile == 3) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 64, 2, 1, 8>>(p, splits, s, ev);
+    if (tile == 5) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 32, 4, 1, 8>>(p, splits, s, ev);
+    if (tile == 6) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<256, 32, 3, 1, 8>>(p, splits, s, ev);
     if constexpr (!SPLIT) {
       if (tile == 4) return launch_dl<TA, TB, EPI, SPLIT, dl::DlCfg<192, 64, 2, 1, 8, 4>>(p, splits, s, ev);
     }
@@ -979,8 +981,8 @@ hipError_t dispatch(const Gemm& g, const Params& p, int tile, int splits, hipStr
 // loads while the other keeps the MFMA pipe busy; BK 64, 1 per CU), 4 = the
 // same with 192 columns (waves 4 x 2): N = 768 products
 // of 16384 rows make 256 tiles, one per CU, instead of 192
-constexpr int TILE_BM[5] = {256, 256, 128, 256, 256};
-constexpr int TILE_BN[5] = {128, 256, 128, 256, 192};
+constexpr int TILE_BM[7] = {256, 256, 128, 256, 256, 256, 256};
+constexpr int TILE_BN[7] = {128, 256, 128, 256, 192, 256, 256};
 
 // Tile and K-split choice from measurements of the step's shapes on MI355X:
 // the 8-wave 256x256 kernel for every bf16 product, or its 192-column variant
@@ -1030,11 +1032,11 @@ int gemm_pick_splits(int M, int N, int K, int a_trans, int b_trans) {
   return splits;
 }
 
-// GPT_GEMM_TILE=0..4 pins the tile (TILE_BM x TILE_BN) for tuning runs.
+// GPT_GEMM_TILE=0..6 pins the tile (TILE_BM x TILE_BN) for tuning runs.
 static int forced_tile() {
   static const int v = [] {
     const char* e = getenv("GPT_GEMM_TILE");
-    return (e && e[0] >= '0' && e[0] <= '4') ? e[0] - '0' : -1;
+    return (e && e[0] >= '0' && e[0] <= '6') ? e[0] - '0' : -1;
   }();
   return v;
 }

@@ -98,6 +98,8 @@ struct gpt_ctx {
   float *tok_loss, *tok_lse, *dF, *loss;
   void* gchunk;         // T [N][head_cols]: the logit gradient of one block of vocabulary columns
   int64_t head_cols = 0;
+  float* head_skws = nullptr;  // split-K workspace of the head's dW blocks (head_skn floats)
+  int64_t head_skn = 0;
   float* ring;
   int ring_wr = 0, ring_rd = 0;
   // backward
@@ -108,6 +110,11 @@ struct gpt_ctx {
   hipStream_t side = nullptr;
   std::vector<hipEvent_t> sev;
   hipEvent_t head_fork = nullptr, side_tail = nullptr;  // head_fork: pass 1 done, the tied dW may start
+  // the head's tied-weight gradient blocks run on a stream of their own, so
+  // they never queue in front of the layers' weight gradients on `side`
+  // (whose completion the data-gradient chain waits for)
+  hipStream_t hside = nullptr;
+  hipEvent_t hside_tail = nullptr;
   hipEvent_t fwd_start = nullptr;  // the forward's start, for side-stream work that needs only the batch
   // AdamW runs on the side stream in pieces (all vectors, wte + wpe, then each
   // layer's matrices); the next forward waits for each piece where it first
@@ -210,16 +217,17 @@ int64_t splitk_floats(int64_t N, int64_t C) {
 }
 
 // Vocabulary columns per block of the head's weight gradient: the block's
-// logit gradient [N][cols] (T) is about 64 MB, a multiple of 256 columns (the
-// GEMM tile) between 256 and V rounded up.  GPT_HEAD_COLS overrides it for
-// tuning runs.
+// logit gradient [N][cols] (T) is about 128 MB, a multiple of 256 columns (the
+// GEMM tile) between 256 and V rounded up (4096 columns at N = 16384 in bf16:
+// 19.9 ms per 124M step against 20.7 ms with 2048, same box).  GPT_HEAD_COLS
+// overrides it for tuning runs.
 int64_t head_block_cols(int64_t N, int64_t V, int64_t es) {
   static const int64_t forced = [] {
     const char* e = getenv("GPT_HEAD_COLS");
     return e ? std::max<int64_t>(0, atoll(e)) : 0;
   }();
   const int64_t vmax = (V + 255) / 256 * 256;
-  int64_t c = forced ? forced : (64ll << 20) / (N * es) / 256 * 256;
+  int64_t c = forced ? forced : (128ll << 20) / (N * es) / 256 * 256;
   return std::min(vmax, std::max<int64_t>(256, c / 256 * 256));
 }
 
@@ -264,6 +272,11 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->dF = cv.take<float>(N * C * 4);
   x->head_cols = head_block_cols(N, x->Vp, es);
   x->gchunk = cv.take<void>(N * x->head_cols * es);
+  {
+    const int sp = gk::gemm_pick_splits((int)x->head_cols, (int)C, (int)N, 1, 1);
+    x->head_skn = sp > 1 ? (int64_t)sp * x->head_cols * C : 0;
+    x->head_skws = x->head_skn ? cv.take<float>(x->head_skn * 4) : nullptr;
+  }
   x->loss = cv.take<float>(64);
   x->ring = cv.take<float>(RING * 4);
   x->dres = cv.take<float>(N * C * 4);
@@ -432,11 +445,16 @@ int ln_fwd(gpt_ctx* x, const float* in, int g_id, int b_id, void* out, float* mu
   return 0;
 }
 
-// main stream waits for all work queued on the side stream so far
+// main stream waits for all work queued on the side streams so far
 int join_side(gpt_ctx* x) {
-  if (!x->side) return 0;
-  HIPCHK(hipEventRecord(x->side_tail, x->side));
-  HIPCHK(hipStreamWaitEvent(x->stream, x->side_tail, 0));
+  if (x->side) {
+    HIPCHK(hipEventRecord(x->side_tail, x->side));
+    HIPCHK(hipStreamWaitEvent(x->stream, x->side_tail, 0));
+  }
+  if (x->hside) {
+    HIPCHK(hipEventRecord(x->hside_tail, x->hside));
+    HIPCHK(hipStreamWaitEvent(x->stream, x->hside_tail, 0));
+  }
   return 0;
 }
 
@@ -462,10 +480,10 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
   }
   HIPCHK(gk::mean_f32(tok_loss, (int)N, loss, ring, slot, x->stream));
   if (!dW) return 0;
-  hipStream_t ds = x->side ? x->side : x->stream;
-  if (x->side) {
+  hipStream_t ds = x->hside ? x->hside : x->stream;
+  if (x->hside) {
     HIPCHK(hipEventRecord(x->head_fork, x->stream));
-    HIPCHK(hipStreamWaitEvent(x->side, x->head_fork, 0));
+    HIPCHK(hipStreamWaitEvent(x->hside, x->head_fork, 0));
   }
   static const bool fused = [] {
     const char* e = getenv("GPT_HEAD_DW");
@@ -489,10 +507,10 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
     g = mk(x, 1, 1, gk::EPI_F32, x->gchunk, cols, Fin, C, n, C, N, dW + v0 * C, C);
     g.dtype = dtype;
     g.accumulate = dW_acc;
-    if (x->splitk_ws) {
+    if (x->head_skws) {
       g.splits = gk::gemm_pick_splits((int)n, (int)C, (int)N, 1, 1);
-      g.ws = x->splitk_ws;
-      g.ws_floats = x->splitk_n;
+      g.ws = x->head_skws;
+      g.ws_floats = x->head_skn;
     }
     if (int e = run_gemm(x, "head_dw", g, ds)) return e;
   }
@@ -549,6 +567,8 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
   chk(hipMemcpyAsync(x->jobs_dev, x->jobs.data(), x->jobs.size() * sizeof(gk::RedJob), hipMemcpyHostToDevice, s));
   // side stream (default priority) and its ordering events
   chk(hipStreamCreateWithFlags(&x->side, hipStreamNonBlocking));
+  chk(hipStreamCreateWithFlags(&x->hside, hipStreamNonBlocking));
+  chk(hipEventCreateWithFlags(&x->hside_tail, hipEventDisableTiming));
   x->sev.assign((size_t)x->L * 8, nullptr);
   for (auto& e : x->sev) chk(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   chk(hipEventCreateWithFlags(&x->head_fork, hipEventDisableTiming));
@@ -569,13 +589,15 @@ int gpt_destroy(gpt_ctx* x) {
   if (!x) return 0;
   for (auto e : x->prof.ev) (void)hipEventDestroy(e);
   if (x->side) (void)hipStreamSynchronize(x->side);
+  if (x->hside) (void)hipStreamSynchronize(x->hside);
   for (auto e : x->sev)
     if (e) (void)hipEventDestroy(e);
   for (auto e : x->adam_ev)
     if (e) (void)hipEventDestroy(e);
-  for (hipEvent_t e : {x->head_fork, x->side_tail, x->fwd_start, x->norm_done})
+  for (hipEvent_t e : {x->head_fork, x->side_tail, x->hside_tail, x->fwd_start, x->norm_done})
     if (e) (void)hipEventDestroy(e);
   if (x->side) (void)hipStreamDestroy(x->side);
+  if (x->hside) (void)hipStreamDestroy(x->hside);
   delete x;
   return 0;
 }
@@ -899,8 +921,8 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
   tmp.gchunk = cv.take<void>(N * tmp.head_cols * es);
   const int sp = gk::gemm_pick_splits((int)tmp.head_cols, (int)C, (int)N, 1, 1);
   if (sp > 1) {
-    tmp.splitk_n = (int64_t)sp * tmp.head_cols * C;
-    tmp.splitk_ws = cv.take<float>(tmp.splitk_n * 4);
+    tmp.head_skn = (int64_t)sp * tmp.head_cols * C;
+    tmp.head_skws = cv.take<float>(tmp.head_skn * 4);
   }
   HIPCHK(gk::fill_f32((float*)bad, 1, 0.f, tmp.stream));
   if (int e = head(&tmp, X, W, V, y, N, C, 1.0f / (float)N, tl, tlse, dX, dW, 0, dtype, loss_dev, nullptr, 0, bad))
@@ -1042,6 +1064,7 @@ int gpt_profile_end(gpt_ctx* x, double* total_ms, int64_t* launches, double* flo
   if (!x) return fail(GPT_EINVAL, "null context");
   HIPCHK(hipStreamSynchronize(x->stream));
   if (x->side) HIPCHK(hipStreamSynchronize(x->side));
+  if (x->hside) HIPCHK(hipStreamSynchronize(x->hside));
   double ms = 0;
   for (size_t i = 0; i + 1 < x->prof.used; i += 2) {
     float t = 0;

@@ -179,7 +179,7 @@ int gpt_adamw_step(gpt_ctx* ctx, float lr, float beta1, float beta2, float eps,
  *       bytes (0 for an invalid shape), 256-byte aligned.  It holds the
  *       per-row losses and log-sum-exps, the out-of-range flag and, for dW,
  *       the logit gradient of one block of vocabulary columns ([N, cols] in
- *       dtype, cols about 64 MB / (N * element size), a multiple of 256) with
+ *       dtype, cols about 128 MB / (N * element size), a multiple of 256) with
  *       a split-K workspace for its contraction.  The loss, the log-sum-exps
  *       and dX come from one pass that streams W through each workgroup and
  *       never stores a logit; dW recomputes one column block of logits at a
