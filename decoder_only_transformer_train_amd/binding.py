@@ -22,6 +22,7 @@ PARAM, GRAD, ADAM_M, ADAM_V = 0, 1, 2, 3
 EXPORTS = [
     "gpt_arena_bytes", "gpt_init", "gpt_destroy", "gpt_make_batch", "gpt_next_start",
     "gpt_forward_loss", "gpt_backward", "gpt_adamw_step", "gpt_lmhead_ce_ws_bytes", "gpt_lmhead_ce",
+    "gpt_lmhead_ce_noalloc",
     "gpt_num_tensors", "gpt_tensor_info", "gpt_get_tensor", "gpt_set_tensor",
     "gpt_get_batch", "gpt_get_token_losses", "gpt_read_losses", "gpt_step_count", "gpt_set_step_count",
     "gpt_profile_begin",
@@ -65,6 +66,8 @@ def load():
         "gpt_lmhead_ce_ws_bytes": (c_size_t, [c_int64, c_int64, c_int64, c_int32]),
         "gpt_lmhead_ce": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int32,
                                   c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "gpt_lmhead_ce_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int32,
+                                          c_void_p, c_void_p, c_void_p, c_void_p]),
         "gpt_num_tensors": (c_int, [c_void_p]),
         "gpt_tensor_info": (c_int, [c_void_p, c_int, P(c_char_p), P(c_int64), P(c_int)]),
         "gpt_get_tensor": (c_int, [c_void_p, c_int, c_int, c_void_p, c_int64]),
@@ -239,6 +242,22 @@ class LMHead:
         _check(load().gpt_lmhead_ce(ptr(X), ptr(W), ptr(y), self.N, self.V, self.C, self.dtype, ptr(self.loss),
                                     ptr(self.dX), ptr(self.dW), ptr(self.ws), self.ws_n, c_void_p(s.cuda_stream)))
         return self.loss, self.dX, self.dW
+
+
+def lmhead_ce_noalloc(X, W, y, dtype: int, loss, dX=None, dW=None, stream=None):
+    """gpt_lmhead_ce_noalloc on caller tensors: X [N, C], W [V, C], y int32 [N] and the
+    fp32 outputs loss [1], dX [N, C] (or None), dW [V, C] (or None); nothing is allocated."""
+    import torch
+    N, C = X.shape
+    V = W.shape[0]
+    if y.numel() != N or loss.numel() < 1 or (dX is not None and tuple(dX.shape) != (N, C)) or \
+            (dW is not None and tuple(dW.shape) != (V, C)):
+        raise ValueError("lmhead_ce_noalloc: shapes do not match")
+    s = stream if stream is not None else torch.cuda.current_stream(X.device)
+    ptr = lambda t: c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    _check(load().gpt_lmhead_ce_noalloc(ptr(X), ptr(W), ptr(y), N, V, C, dtype, ptr(loss), ptr(dX), ptr(dW),
+                                        c_void_p(s.cuda_stream)))
+    return loss, dX, dW
 
 
 def lmhead_ce(X, W, y, dtype: int, want_grads: bool = True, stream=None):

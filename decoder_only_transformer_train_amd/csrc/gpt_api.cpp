@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -473,7 +474,7 @@ int join_side(gpt_ctx* x) {
 // long-lived workgroups hold CUs away from the backward).
 int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C, float scale,
          float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, int dtype, float* loss, float* ring,
-         int slot, int* bad) {
+         int slot, int* bad, bool fused_dw = false) {
   {
     ProfScope ps(x, "head_fwd", (dF ? 4.0 : 2.0) * N * V * C, 0.0);
     HIPCHK(gk::lmhead_fwd(dtype, Fin, W, (int)N, (int)V, (int)C, y, scale, tok_loss, tok_lse, dF, bad, x->stream));
@@ -485,11 +486,11 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
     HIPCHK(hipEventRecord(x->head_fork, x->stream));
     HIPCHK(hipStreamWaitEvent(x->hside, x->head_fork, 0));
   }
-  static const bool fused = [] {
+  static const bool fused_env = [] {
     const char* e = getenv("GPT_HEAD_DW");
     return e && std::string(e) == "fused";
   }();
-  if (fused) {
+  if (fused_dw || fused_env) {
     ProfScope ps(x, "head_dw", 2.0 * N * V * C, 0.0, ds);
     HIPCHK(gk::lmhead_dw(dtype, Fin, W, (int)N, (int)V, (int)C, y, tok_lse, scale, dW, dW_acc, ds));
     return 0;
@@ -928,6 +929,63 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
   if (int e = head(&tmp, X, W, V, y, N, C, 1.0f / (float)N, tl, tlse, dX, dW, 0, dtype, loss_dev, nullptr, 0, bad))
     return e;
   // out-of-range targets were clamped on the device; report them here
+  int flag = 0;
+  HIPCHK(hipMemcpyAsync(&flag, bad, 4, hipMemcpyDeviceToHost, tmp.stream));
+  HIPCHK(hipStreamSynchronize(tmp.stream));
+  if (flag) return fail(GPT_ERANGE, "a target id is outside [0, V)");
+  return 0;
+}
+
+}  // extern "C"
+
+// ---- gpt_lmhead_ce without allocation: a file-scope device scratch array ----
+namespace {
+constexpr int64_t NOALLOC_MAX_ROWS = 65536;
+// per-row losses [NOALLOC_MAX_ROWS], per-row log-sum-exps [NOALLOC_MAX_ROWS], the out-of-range flag
+constexpr size_t NOALLOC_BYTES = 2 * NOALLOC_MAX_ROWS * 4 + 256;
+__device__ __align__(256) char scratch[NOALLOC_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[MAX_DEVICES] = {};
+
+// The current device's copy of `scratch`, looked up once per device with that
+// device current.  Host code uses this address, never the array's name.
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(GPT_EINVAL, "device index out of range");
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return 0;
+}
+}  // namespace
+
+extern "C" {
+
+int gpt_lmhead_ce_noalloc(const void* X, const void* W, const int32_t* y, int64_t N, int64_t V, int64_t C,
+                          int32_t dtype, float* loss_dev, float* dX, float* dW, void* hip_stream) {
+  if (!X || !W || !y || !loss_dev || gpt_lmhead_ce_ws_bytes(N, V, C, dtype) == 0)
+    return fail(GPT_EINVAL, "bad lmhead_ce arguments");
+  if (N > NOALLOC_MAX_ROWS)
+    return fail(GPT_EINVAL, "gpt_lmhead_ce_noalloc: N = " + std::to_string(N) + " rows exceeds its scratch of " +
+                                std::to_string(NOALLOC_MAX_ROWS) + " rows (use gpt_lmhead_ce with a workspace)");
+  void* sp = nullptr;
+  if (int e = scratch_for_current_device(&sp)) return e;
+  gpt_ctx tmp;  // stream and profiling fields only; no side stream, no workspace
+  tmp.stream = (hipStream_t)hip_stream;
+  float* tl = (float*)sp;
+  float* tlse = tl + NOALLOC_MAX_ROWS;
+  int* bad = (int*)(tlse + NOALLOC_MAX_ROWS);
+  HIPCHK(gk::fill_f32((float*)bad, 1, 0.f, tmp.stream));  // the scratch keeps the previous call's flag
+  // dW by the single-kernel recompute, which needs only the per-row log-sum-exps
+  if (int e = head(&tmp, X, W, V, y, N, C, 1.0f / (float)N, tl, tlse, dX, dW, 0, dtype, loss_dev, nullptr, 0, bad,
+                   /*fused_dw=*/true))
+    return e;
   int flag = 0;
   HIPCHK(hipMemcpyAsync(&flag, bad, 4, hipMemcpyDeviceToHost, tmp.stream));
   HIPCHK(hipStreamSynchronize(tmp.stream));

@@ -196,6 +196,24 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
                   int64_t C, int32_t dtype, float* loss_dev, float* dX, float* dW, void* ws,
                   size_t ws_bytes, void* hip_stream);
 
+/*
+ * gpt_lmhead_ce without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments, results, synchronisation and errors as
+ * gpt_lmhead_ce; dW, when asked for, comes from the single-kernel recompute
+ * (each workgroup streams all N rows for its vocabulary rows), which needs
+ * only the per-row log-sum-exps.  Its per-row losses, log-sum-exps and
+ * out-of-range flag live in a static device array of 512 KB + 256 B inside
+ * the library (one copy per GPU, held until the process ends), so N is at
+ * most 65536; larger N returns EINVAL.  Every call on a GPU shares that
+ * GPU's copy and it keeps the last call's contents: calls that overlap on one
+ * GPU (other streams, other threads) race, and must be serialised by the
+ * caller.  No allocation of any kind is made.
+ */
+int gpt_lmhead_ce_noalloc(const void* X, const void* W, const int32_t* y, int64_t N,
+                          int64_t V, int64_t C, int32_t dtype, float* loss_dev, float* dX,
+                          float* dW, void* hip_stream);
+
 /* ---- harness and parity helpers ---- */
 
 /* Number of parameter tensors (2 + 12 L + 2), in the order
