@@ -1009,7 +1009,11 @@ void choose(int M, int N, int K, bool can_split, int dtype, int a_trans, int b_t
   // data gradients +0.02 ms, LM-head data gradient +0.2 ms), since the 192
   // tiles of the 256-column kernel leave 64 CUs to the weight gradients that
   // run beside them on the second stream.
-  if (tile == 3 && !can_split && !b_trans) {
+  static const bool dgrad192 = [] {
+    const char* e = getenv("GPT_GEMM_DGRAD192");
+    return e && e[0] == '1';
+  }();
+  if (tile == 3 && !can_split && (!b_trans || dgrad192)) {
     const int64_t r3 = cdiv(cdiv(M, 256) * cdiv(N, 256), 256), r4 = cdiv(cdiv(M, 256) * cdiv(N, 192), 256);
     if (r4 * 192 * 10 < r3 * 256 * 9) tile = 4;
   }

@@ -97,7 +97,7 @@ struct gpt_ctx {
   float *muf, *rsf;
   // head: per-row losses and log-sum-exps, the gradient at the final LayerNorm output
   float *tok_loss, *tok_lse, *dF, *loss;
-  void* gchunk;         // T [N][head_cols]: the logit gradient of one block of vocabulary columns
+  void* gchunk = nullptr;  // GEMM form of the head dW: T [N][head_cols], one column block's logit gradient
   int64_t head_cols = 0;
   float* head_skws = nullptr;  // split-K workspace of the head's dW blocks (head_skn floats)
   int64_t head_skn = 0;
@@ -217,11 +217,20 @@ int64_t splitk_floats(int64_t N, int64_t C) {
   return best;
 }
 
-// Vocabulary columns per block of the head's weight gradient: the block's
-// logit gradient [N][cols] (T) is about 128 MB, a multiple of 256 columns (the
-// GEMM tile) between 256 and V rounded up (4096 columns at N = 16384 in bf16:
-// 19.9 ms per 124M step against 20.7 ms with 2048, same box).  GPT_HEAD_COLS
-// overrides it for tuning runs.
+// The head's weight gradient by column-block GEMMs instead of the single
+// recompute kernel: GPT_HEAD_DW=gemm, read at every use (contexts and
+// workspaces sized under one setting keep working under the other: without a
+// block buffer the single kernel runs).
+bool head_gemm_mode() {
+  const char* e = getenv("GPT_HEAD_DW");
+  return e && std::string(e) == "gemm";
+}
+
+// Vocabulary columns per block of the GEMM form of the head's weight gradient:
+// the block's logit gradient [N][cols] (T) is about 128 MB, a multiple of 256
+// columns (the GEMM tile) between 256 and V rounded up (4096 columns at N =
+// 16384 in bf16: 19.9 ms per 124M step against 20.7 ms with 2048, same box).
+// GPT_HEAD_COLS overrides it for tuning runs.
 int64_t head_block_cols(int64_t N, int64_t V, int64_t es) {
   static const int64_t forced = [] {
     const char* e = getenv("GPT_HEAD_COLS");
@@ -271,12 +280,16 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->tok_loss = cv.take<float>(N * 4);
   x->tok_lse = cv.take<float>(N * 4);
   x->dF = cv.take<float>(N * C * 4);
-  x->head_cols = head_block_cols(N, x->Vp, es);
-  x->gchunk = cv.take<void>(N * x->head_cols * es);
-  {
+  if (head_gemm_mode()) {
+    x->head_cols = head_block_cols(N, x->Vp, es);
+    x->gchunk = cv.take<void>(N * x->head_cols * es);
     const int sp = gk::gemm_pick_splits((int)x->head_cols, (int)C, (int)N, 1, 1);
     x->head_skn = sp > 1 ? (int64_t)sp * x->head_cols * C : 0;
     x->head_skws = x->head_skn ? cv.take<float>(x->head_skn * 4) : nullptr;
+  } else {
+    x->gchunk = nullptr;
+    x->head_skws = nullptr;
+    x->head_cols = x->head_skn = 0;
   }
   x->loss = cv.take<float>(64);
   x->ring = cv.take<float>(RING * 4);
@@ -463,15 +476,17 @@ int join_side(gpt_ctx* x) {
 // one pass gives the per-row loss and log-sum-exp and, with gradients, dF -
 // on the context stream - then the fixed-order mean of the row losses.  The
 // head's part of the tied weight's gradient, which only the embedding step of
-// the backward reads, runs on the side stream when there is one, beside the
-// backward of the blocks: per block of head_cols vocabulary columns, one
-// product recomputes the block's logits and turns them into their gradient
-// (exp(z - lse) - onehot) * scale in its epilogue (T, [N][cols]), and a second
-// one contracts it with F over the rows into those columns' rows of dW.
-// Short tiles of the two products interleave with the backward's kernels on
-// the CUs.  GPT_HEAD_DW=fused selects the single-kernel variant instead (the
-// same recomputation and contraction with the block never leaving the CU; its
-// long-lived workgroups hold CUs away from the backward).
+// the backward reads, runs on a stream of its own when there is one, beside
+// the backward of the blocks.  By default one kernel recomputes each vocabulary
+// block's logits from the row log-sum-exps and contracts their gradient with F
+// without it leaving the CU.  The GEMM form (GPT_HEAD_DW=gemm, when a block
+// buffer exists) instead runs, per block of head_cols vocabulary columns, one
+// product that recomputes the block's logits and turns them into their
+// gradient (exp(z - lse) - onehot) * scale in its epilogue (T, [N][cols]), and a
+// second that contracts it with F over the rows into those rows of dW.  Same
+// box, 124M step: 20.25 ms with the single kernel against 20.47 ms with the
+// GEMM form, which also moves the [N, V] logit gradient through memory once
+// each way (about 6 GB per step).
 int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C, float scale,
          float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, int dtype, float* loss, float* ring,
          int slot, int* bad, bool fused_dw = false) {
@@ -486,11 +501,7 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
     HIPCHK(hipEventRecord(x->head_fork, x->stream));
     HIPCHK(hipStreamWaitEvent(x->hside, x->head_fork, 0));
   }
-  static const bool fused_env = [] {
-    const char* e = getenv("GPT_HEAD_DW");
-    return e && std::string(e) == "fused";
-  }();
-  if (fused_dw || fused_env) {
+  if (fused_dw || !x->gchunk || !head_gemm_mode()) {
     ProfScope ps(x, "head_dw", 2.0 * N * V * C, 0.0, ds);
     HIPCHK(gk::lmhead_dw(dtype, Fin, W, (int)N, (int)V, (int)C, y, tok_lse, scale, dW, dW_acc, ds));
     return 0;
@@ -895,13 +906,16 @@ size_t gpt_lmhead_ce_ws_bytes(int64_t N, int64_t V, int64_t C, int32_t dtype) {
   if (N < 1 || V < 1 || C < 64 || C % 64 || (dtype != GPT_F32 && dtype != GPT_BF16)) return 0;
   if (N > 0x7fffffff || V > 0x7fffffff || C > gk::lmhead_max_embd(dtype)) return 0;
   if (dtype == GPT_BF16 && ((N + 32) * C * 2 >= (1ll << 32) || (V + 32) * C * 2 >= (1ll << 32))) return 0;
-  // per-row losses and log-sum-exps, the out-of-range target flag, with dW the
-  // logit gradient of one block of vocabulary columns and a split-K workspace
+  // per-row losses and log-sum-exps, the out-of-range target flag; for the GEMM
+  // form of dW also the logit gradient of one block of vocabulary columns and a
+  // split-K workspace
   size_t b = (size_t)(2 * align_up(N * 4, ALIGN) + ALIGN);
-  const int64_t es = dtype == GPT_BF16 ? 2 : 4, cols = head_block_cols(N, V, es);
-  b += (size_t)align_up(N * cols * es, ALIGN);
-  const int sp = gk::gemm_pick_splits((int)cols, (int)C, (int)N, 1, 1);
-  if (sp > 1) b += (size_t)align_up((int64_t)sp * cols * C * 4, ALIGN);
+  if (head_gemm_mode()) {
+    const int64_t es = dtype == GPT_BF16 ? 2 : 4, cols = head_block_cols(N, V, es);
+    b += (size_t)align_up(N * cols * es, ALIGN);
+    const int sp = gk::gemm_pick_splits((int)cols, (int)C, (int)N, 1, 1);
+    if (sp > 1) b += (size_t)align_up((int64_t)sp * cols * C * 4, ALIGN);
+  }
   return b;
 }
 
@@ -917,13 +931,15 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
   float* tl = cv.take<float>(N * 4);
   float* tlse = cv.take<float>(N * 4);
   int* bad = cv.take<int>(ALIGN);
-  const int64_t es = dtype == GPT_BF16 ? 2 : 4;
-  tmp.head_cols = head_block_cols(N, V, es);
-  tmp.gchunk = cv.take<void>(N * tmp.head_cols * es);
-  const int sp = gk::gemm_pick_splits((int)tmp.head_cols, (int)C, (int)N, 1, 1);
-  if (sp > 1) {
-    tmp.head_skn = (int64_t)sp * tmp.head_cols * C;
-    tmp.head_skws = cv.take<float>(tmp.head_skn * 4);
+  if (head_gemm_mode()) {
+    const int64_t es = dtype == GPT_BF16 ? 2 : 4;
+    tmp.head_cols = head_block_cols(N, V, es);
+    tmp.gchunk = cv.take<void>(N * tmp.head_cols * es);
+    const int sp = gk::gemm_pick_splits((int)tmp.head_cols, (int)C, (int)N, 1, 1);
+    if (sp > 1) {
+      tmp.head_skn = (int64_t)sp * tmp.head_cols * C;
+      tmp.head_skws = cv.take<float>(tmp.head_skn * 4);
+    }
   }
   HIPCHK(gk::fill_f32((float*)bad, 1, 0.f, tmp.stream));
   if (int e = head(&tmp, X, W, V, y, N, C, 1.0f / (float)N, tl, tlse, dX, dW, 0, dtype, loss_dev, nullptr, 0, bad))
@@ -982,7 +998,8 @@ int gpt_lmhead_ce_noalloc(const void* X, const void* W, const int32_t* y, int64_
   float* tlse = tl + NOALLOC_MAX_ROWS;
   int* bad = (int*)(tlse + NOALLOC_MAX_ROWS);
   HIPCHK(gk::fill_f32((float*)bad, 1, 0.f, tmp.stream));  // the scratch keeps the previous call's flag
-  // dW by the single-kernel recompute, which needs only the per-row log-sum-exps
+  // dW by the single-kernel recompute (whatever GPT_HEAD_DW says), which needs
+  // only the per-row log-sum-exps
   if (int e = head(&tmp, X, W, V, y, N, C, 1.0f / (float)N, tl, tlse, dX, dW, 0, dtype, loss_dev, nullptr, 0, bad,
                    /*fused_dw=*/true))
     return e;

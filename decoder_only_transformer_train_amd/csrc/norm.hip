@@ -94,13 +94,17 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 constexpr int LNB_ROWS = 32;
 
 // One wave takes one row at a time with no prefetch of the next, and x-hat and
-// dy*g are recomputed for the output instead of kept: the kernel stays within
-// 120 VGPRs, so one of its workgroups fits on a CU beside an 8-wave GEMM
-// workgroup (2 x 196 VGPRs per SIMD) of the other stream; with the prefetch
-// (182 VGPRs) it waited for whole GEMM workgroups to finish.  A lane past the row
-// (C not a multiple of 256) loads the last column slice and drops it.
+// dy*g are recomputed for the output instead of kept: at C <= 768 (NV <= 3) the
+// kernel stays within 120 VGPRs, so one of its workgroups fits on a CU beside an
+// 8-wave GEMM workgroup (2 x 196 VGPRs per SIMD) of the other stream; with the
+// prefetch (182 VGPRs) it waited for whole GEMM workgroups to finish.  Wider rows
+// keep 24 NV floats per lane live (row data and column partials), so they take
+// two workgroups per CU and up to 256 VGPRs (one and 512 above C = 1792)
+// instead of spilling to scratch (C = 1024: 28-84 bytes per lane, C = 1600:
+// 520-592 at four per CU; C = 1600 takes NV = 7).  A lane
+// past the row (C not a multiple of 256) loads the last column slice and drops it.
 template <typename TY, typename T, int NV, bool DRES>
-__global__ __launch_bounds__(256, 4) void ln_bwd_kernel(const TY* __restrict__ dy, const float* __restrict__ x,
+__global__ __launch_bounds__(256, NV <= 3 ? 4 : (NV <= 7 ? 2 : 1)) void ln_bwd_kernel(const TY* __restrict__ dy, const float* __restrict__ x,
                                                          const float* __restrict__ mu, const float* __restrict__ rs,
                                                          const float* __restrict__ g, const float* __restrict__ dres_in,
                                                          float* __restrict__ dres_out, T* __restrict__ dres_T,
@@ -450,6 +454,7 @@ hipError_t layernorm_bwd(int dtype, const void* dy, int dy_is_t, const float* x,
     case 4: return ln_bwd_nv<4>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
     case 5:
     case 6: return ln_bwd_nv<6>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
+    case 7: return ln_bwd_nv<7>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
     default: return ln_bwd_nv<8>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
   }
 }

@@ -177,13 +177,16 @@ int gpt_adamw_step(gpt_ctx* ctx, float lr, float beta1, float beta2, float eps,
  *   dW  device fp32 [V, C] (nullable): gradient w.r.t. W (overwritten).
  *   ws  device workspace of at least gpt_lmhead_ce_ws_bytes(N, V, C, dtype)
  *       bytes (0 for an invalid shape), 256-byte aligned.  It holds the
- *       per-row losses and log-sum-exps, the out-of-range flag and, for dW,
- *       the logit gradient of one block of vocabulary columns ([N, cols] in
- *       dtype, cols about 128 MB / (N * element size), a multiple of 256) with
- *       a split-K workspace for its contraction.  The loss, the log-sum-exps
- *       and dX come from one pass that streams W through each workgroup and
- *       never stores a logit; dW recomputes one column block of logits at a
- *       time.  [N, V] is never held.
+ *       per-row losses and log-sum-exps and the out-of-range flag.  The loss,
+ *       the log-sum-exps and dX come from one pass that streams W through each
+ *       workgroup and never stores a logit; dW comes from a second kernel that
+ *       streams the rows of X past each block of W rows, recomputing the
+ *       logits from the log-sum-exps.  [N, V] is never held.  With the
+ *       environment variable GPT_HEAD_DW=gemm (set when both the size and the
+ *       call are made) dW instead comes from GEMMs over blocks of vocabulary
+ *       columns, and the workspace also holds one block's logit gradient
+ *       ([N, cols] in dtype, cols about 128 MB / (N * element size), a
+ *       multiple of 256) and a split-K workspace.
  * C must be a multiple of 64 and at most 1792 (bf16) or 1024 (fp32); N and V
  * below 2^31 (bf16: (N + 32) C and (V + 32) C below 2^31).
  * The call synchronises the stream at its end.  A target id outside [0, V)

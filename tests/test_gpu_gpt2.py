@@ -47,6 +47,15 @@ def test_gpt2_124m_step_b2():
     check_step(cfg, stream)
 
 
+def test_gpt2_124m_step_b2_head_gemm_form(monkeypatch):
+    # the head's weight gradient by column-block GEMMs (GPT_HEAD_DW=gemm) instead of the single kernel
+    monkeypatch.setenv("GPT_HEAD_DW", "gemm")
+    cfg = configs.GPT2_124M.with_(batch=2)
+    stream = synthetic.zipf_eot_stream(2 * 1024 + 1, cfg.vocab, seed=0)
+    announce("124M B=2 step, GEMM-form head dW")
+    check_step(cfg, stream)
+
+
 def test_gpt2_124m_bench_batch_sampled_rows():
     # the bench's launch configuration: B=16, T=1024; per-row losses of sampled rows
     cfg = configs.GPT2_124M

@@ -37,6 +37,33 @@ def test_head_bf16_vs_oracle(N, V):
     assert cosine(dW.cpu().numpy(), rdW) >= 0.999
 
 
+@pytest.mark.parametrize("N,V,dtype", [(2048, 50257, binding.GPT_BF16), (333, 1000, binding.GPT_BF16),
+                                       (256, 1000, binding.GPT_F32)])
+def test_head_gemm_form_vs_oracle_and_single_kernel(N, V, dtype, monkeypatch):
+    # dW by column-block GEMMs (GPT_HEAD_DW=gemm: 13 blocks with a ragged last one at V=50257)
+    announce(f"head GEMM-form dW dtype={dtype} N={N} V={V}")
+    C = 768 if dtype == binding.GPT_BF16 else 64
+    if dtype == binding.GPT_BF16:
+        X, W, y = synthetic.lmhead_inputs(N, V, C, seed=4)
+    else:
+        rng = np.random.default_rng(4)
+        X = rng.standard_normal((N, C)).astype(np.float32)
+        W = (rng.standard_normal((V, C)) * 0.3).astype(np.float32)
+        y = rng.integers(0, V, N).astype(np.int32)
+    dev = to_dev(X, W, y, dtype)
+    _, _, dW1 = binding.lmhead_ce(*dev, dtype)
+    monkeypatch.setenv("GPT_HEAD_DW", "gemm")
+    loss, dX, dW = binding.lmhead_ce(*dev, dtype)
+    rl, _, rdX, rdW = oracle.lmhead_ce(X, W, y)
+    if dtype == binding.GPT_BF16:
+        assert abs(loss.item() - rl) <= 2e-2
+        assert cosine(dW.cpu().numpy(), rdW) >= 0.999
+        assert rel_err(dW.cpu().numpy(), dW1.cpu().numpy()) <= 1e-2
+    else:
+        assert rel_err(dW.cpu().numpy(), rdW) <= 1e-4
+        assert rel_err(dW.cpu().numpy(), dW1.cpu().numpy()) <= 1e-5
+
+
 @pytest.mark.parametrize("N,V,C", [(256, 1000, 64), (200, 77, 128)])
 def test_head_fp32_vs_oracle(N, V, C):
     announce(f"head fp32 N={N} V={V} C={C}")
