@@ -503,7 +503,11 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
   }
   if (fused_dw || !x->gchunk || !head_gemm_mode()) {
     ProfScope ps(x, "head_dw", 2.0 * N * V * C, 0.0, ds);
-    HIPCHK(gk::lmhead_dw(dtype, Fin, W, (int)N, (int)V, (int)C, y, tok_lse, scale, dW, dW_acc, ds));
+    // GPT_HEAD_DW_WGS caps its grid (tuning runs): fewer resident workgroups
+    // leave more CUs to the backward running beside it
+    const char* cap = x->hside ? getenv("GPT_HEAD_DW_WGS") : nullptr;
+    HIPCHK(gk::lmhead_dw(dtype, Fin, W, (int)N, (int)V, (int)C, y, tok_lse, scale, dW, dW_acc, ds,
+                         cap ? atoi(cap) : 0));
     return 0;
   }
   const int64_t es = dtype == GPT_BF16 ? 2 : 4, cols = x->head_cols;

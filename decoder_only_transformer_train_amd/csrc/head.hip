@@ -59,6 +59,7 @@ struct Args {
   int accumulate;    // pass 2: dW += instead of =
   float scale;       // gradients are those of scale * (sum of row losses)
   int* bad;          // pass 1: set to 1 when a target lies outside [0, V)
+  int blk0;          // index of the launch's first block of fixed rows
 };
 
 // Column groups of 64 dealt to the 4 waves in order: wave w gets ng of them from column c_lo.
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
   wave_range(C, w, ng, c_lo);
   S.ng = __builtin_amdgcn_readfirstlane(ng);  // uniform in the wave: scalar branches
   c_lo = __builtin_amdgcn_readfirstlane(c_lo);
-  S.f0 = blockIdx.x * (32 * NQT);  // first fixed row of the workgroup
+  S.f0 = (a.blk0 + blockIdx.x) * (32 * NQT);  // first fixed row of the workgroup
   const int nblk = (a.n_str + BV - 1) / BV;
 
 #pragma unroll
@@ -760,19 +761,37 @@ __global__ __launch_bounds__(256) void head_f32_dw(const float* __restrict__ F, 
 
 // launch a bf16 pass with the register/LDS shape for C
 template <int MODE>
-hipError_t launch_bf16(const Args& a, hipStream_t s) {
+hipError_t launch_bf16_range(const Args& a, int ngmax, dim3 grid, hipStream_t s);
+
+template <int MODE>
+hipError_t launch_bf16(const Args& a, hipStream_t s, int max_wgs) {
   const int G = a.C / 64;
   const int ngmax = (G + 3) / 4;
-  // fixed rows per workgroup: 64 (two 32-row tiles) while a wave's 64-column groups are <= 3, else 32
-  auto grid = [&](int rows) { return dim3((a.n_fix + rows - 1) / rows); };
+  // fixed rows per workgroup: 64 (two 32-row tiles) while a wave's 64-column groups are <= 3, else 32.
+  // max_wgs > 0 splits the pass into launches of at most that many workgroups
+  // (blocks blk0 .. blk0 + grid - 1 each), queued one after another on s, so
+  // no more than max_wgs of them are resident at once
+  const int rows = ngmax <= 3 ? 64 : 32;
+  const int nfix = (a.n_fix + rows - 1) / rows;
+  const int step = max_wgs > 0 && max_wgs < nfix ? max_wgs : nfix;
+  for (int b0 = 0; b0 < nfix; b0 += step) {
+    Args ab = a;
+    ab.blk0 = b0;
+    if (hipError_t e = launch_bf16_range<MODE>(ab, ngmax, dim3(std::min(step, nfix - b0)), s)) return e;
+  }
+  return hipSuccess;
+}
+
+template <int MODE>
+hipError_t launch_bf16_range(const Args& a, int ngmax, dim3 grid, hipStream_t s) {
   switch (ngmax) {
-    case 1: hipLaunchKernelGGL((head_kernel<1, 2, 3, MODE>), grid(64), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((head_kernel<2, 2, 3, MODE>), grid(64), dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((head_kernel<3, 2, 2, MODE>), grid(64), dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((head_kernel<4, 1, 2, MODE>), grid(32), dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((head_kernel<5, 1, 1, MODE>), grid(32), dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((head_kernel<6, 1, 1, MODE>), grid(32), dim3(256), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((head_kernel<7, 1, 1, MODE>), grid(32), dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((head_kernel<1, 2, 3, MODE>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((head_kernel<2, 2, 3, MODE>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((head_kernel<3, 2, 2, MODE>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((head_kernel<4, 1, 2, MODE>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((head_kernel<5, 1, 1, MODE>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((head_kernel<6, 1, 1, MODE>), grid, dim3(256), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((head_kernel<7, 1, 1, MODE>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -803,7 +822,7 @@ hipError_t lmhead_fwd(int dtype, const void* F, const void* W, int N, int V, int
     a.out = dF;
     a.scale = scale;
     a.bad = bad;
-    return hd::launch_bf16<0>(a, s);
+    return hd::launch_bf16<0>(a, s, 0);
   }
   const size_t sh = (size_t)(hd::FR * C + hd::FR * hd::FCH) * 4;
   hipLaunchKernelGGL(hd::head_f32_fwd, dim3((N + hd::FR - 1) / hd::FR), dim3(256), sh, s, (const float*)F,
@@ -812,7 +831,7 @@ hipError_t lmhead_fwd(int dtype, const void* F, const void* W, int N, int V, int
 }
 
 hipError_t lmhead_dw(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, const float* lse,
-                     float scale, float* dW, int accumulate, hipStream_t s) {
+                     float scale, float* dW, int accumulate, hipStream_t s, int max_wgs) {
   if (V <= 0) return hipSuccess;
   if (N <= 0 || C <= 0 || C % 64 || C > lmhead_max_embd(dtype)) return hipErrorInvalidValue;
   if (dtype == BF16) {
@@ -828,7 +847,7 @@ hipError_t lmhead_dw(int dtype, const void* F, const void* W, int N, int V, int 
     a.out = dW;
     a.accumulate = accumulate;
     a.scale = scale;
-    return hd::launch_bf16<1>(a, s);
+    return hd::launch_bf16<1>(a, s, max_wgs);
   }
   const size_t sh = (size_t)(hd::FR * C + hd::FR * hd::FCH) * 4;
   hipLaunchKernelGGL(hd::head_f32_dw, dim3((V + hd::FR - 1) / hd::FR), dim3(256), sh, s, (const float*)F,

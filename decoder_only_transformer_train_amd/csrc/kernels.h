@@ -113,8 +113,9 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, c
 int lmhead_max_embd(int dtype);
 hipError_t lmhead_fwd(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, float scale,
                       float* loss, float* lse, float* dF, int* bad, hipStream_t s);
+// max_wgs > 0 (bf16): at most that many workgroups, each looping over blocks of W rows
 hipError_t lmhead_dw(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, const float* lse,
-                     float scale, float* dW, int accumulate, hipStream_t s);
+                     float scale, float* dW, int accumulate, hipStream_t s, int max_wgs = 0);
 // mean of n floats in fixed order -> out[0] (and ring[slot] if ring != null)
 hipError_t mean_f32(const float* x, int n, float* out, float* ring, int slot, hipStream_t s);
 

@@ -127,3 +127,21 @@ def test_bf16_adamw_update_matches_oracle():
         if sel.any():
             np.testing.assert_allclose(du[sel], dr[sel], rtol=0.02, atol=2e-6, err_msg=k)
     assert g.step_count() == 1
+
+
+def test_head_dw_capped_grid_is_bit_identical(monkeypatch):
+    # the head's second pass with fewer workgroups than W-row blocks (each loops over blocks)
+    cfg = configs.GPT2_124M.with_(n_layer=1, batch=2)
+    stream = synthetic.zipf_eot_stream(2 * 1024 + 1, cfg.vocab, seed=3)
+    p = init_for(cfg, seed=3)
+    out = []
+    for cap in (None, "37"):
+        if cap:
+            monkeypatch.setenv("GPT_HEAD_DW_WGS", cap)
+        announce(f"head dW grid cap {cap}")
+        g = context(cfg, p)
+        g.make_batch(stream, 0)
+        g.forward_loss(1.0)
+        g.backward()
+        out.append(g.get("wte", binding.GRAD))
+    assert np.array_equal(out[0], out[1])
