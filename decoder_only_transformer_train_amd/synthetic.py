@@ -109,6 +109,44 @@ def init_params(n_layer: int, n_embd: int, vocab_padded: int, max_seq: int,
     return params
 
 
+def tensor_layout_cs336(n_layer: int, n_embd: int, d_ff: int, vocab_padded: int):
+    """Ordered (name, shape, std_kind) list of the RMSNorm / RoPE / SwiGLU block variant.
+
+    No biases and no position table; w1 (gate) and w3 (up) are [d_ff, C], w2 is
+    [C, d_ff]; lm_head [V_pad, C] is the output projection, separate from wte.
+    """
+    C, L, F = n_embd, n_layer, d_ff
+    out = [("wte", (vocab_padded, C), "w")]
+    for l in range(L):
+        p = f"h{l}."
+        out += [
+            (p + "rms1.g", (C,), "one"), (p + "attn.w", (3 * C, C), "w"), (p + "proj.w", (C, C), "wr"),
+            (p + "rms2.g", (C,), "one"), (p + "w1", (F, C), "w"), (p + "w3", (F, C), "w"),
+            (p + "w2", (C, F), "wr"),
+        ]
+    out += [("rmsf.g", (C,), "one"), ("lm_head", (vocab_padded, C), "w")]
+    return out
+
+
+def init_params_cs336(n_layer: int, n_embd: int, d_ff: int, vocab_padded: int, seed: int = 0,
+                      gain_jitter: float = 0.0) -> dict[str, np.ndarray]:
+    """Initial weights of the variant as float32 arrays (same scheme as init_params);
+    gain_jitter > 0 draws the RMSNorm gains as 1 + gain_jitter * N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    std = 0.02
+    std_r = 0.02 / np.sqrt(2.0 * n_layer)
+    params: dict[str, np.ndarray] = {}
+    for name, shape, kind in tensor_layout_cs336(n_layer, n_embd, d_ff, vocab_padded):
+        if kind == "w":
+            a = rng.standard_normal(shape) * std
+        elif kind == "wr":
+            a = rng.standard_normal(shape) * std_r
+        else:
+            a = 1.0 + gain_jitter * rng.standard_normal(shape) if gain_jitter else np.ones(shape)
+        params[name] = a.astype(np.float32)
+    return params
+
+
 def round_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
     bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)

@@ -276,6 +276,160 @@ def loss_and_grads(params, x, y, n_head: int, loss_scale: float = 1.0):
 
 
 # --------------------------------------------------------------------------
+# The second block variant ([C] sections 4 and 6): two RMSNorms per block and
+# one at the end, RoPE on Q and K, a SwiGLU feed-forward with three matrices,
+# no biases, no learned positions, and an output projection of its own
+# (untied from the token embedding).  Readings where the page is silent:
+#   * RMSNorm(h) = h / sqrt(mean(h^2) + eps) * g, eps 1e-5 as for LayerNorm;
+#   * RoPE rotates each pair of channels (2i, 2i+1) of a head by the angle
+#     t * theta^(-2i/D) at position t (t from 0 in every row), theta = 10000;
+#   * SiLU(u) = u * sigmoid(u); FFN(x) = (SiLU(x W1^T) * (x W3^T)) W2^T.
+# --------------------------------------------------------------------------
+
+def rmsnorm(h, g):
+    """RMSNorm over the last axis; returns (y, (xhat, rstd))."""
+    rstd = 1.0 / np.sqrt((h * h).mean(axis=-1, keepdims=True) + LN_EPS)
+    xhat = h * rstd
+    return xhat * g, (xhat, rstd)
+
+
+def rmsnorm_backward(dout, xhat, rstd, g):
+    """Chain rule of rmsnorm: returns dx, dg."""
+    dxhat = dout * g
+    dg = (dout * xhat).reshape(-1, xhat.shape[-1]).sum(axis=0)
+    m2 = (dxhat * xhat).mean(axis=-1, keepdims=True)
+    return rstd * (dxhat - xhat * m2), dg
+
+
+def rope_angles(T: int, D: int, theta: float):
+    """[T, D/2] angles t * theta^(-2i/D)."""
+    inv = theta ** (-np.arange(0, D, 2, dtype=np.float64) / D)
+    return np.arange(T, dtype=np.float64)[:, None] * inv[None, :]
+
+
+def rope(x, theta: float, inverse: bool = False):
+    """Rotate channel pairs (2i, 2i+1) of x [B, H, T, D] by their angles (inverse: by minus them)."""
+    T, D = x.shape[-2], x.shape[-1]
+    a = rope_angles(T, D, theta)
+    c, s = np.cos(a), np.sin(a)
+    if inverse:
+        s = -s
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def silu(u):
+    return u / (1.0 + np.exp(-u))
+
+
+def silu_backward(dout, u):
+    sg = 1.0 / (1.0 + np.exp(-u))
+    return dout * sg * (1.0 + u * (1.0 - sg))
+
+
+def _n_layer_cs336(params):
+    L = 0
+    while f"h{L}.rms1.g" in params:
+        L += 1
+    return L
+
+
+def cs336_forward(params, x, y, n_head: int, theta: float = 10000.0, keep=True):
+    """Forward pass and mean next-token loss of the variant; as forward()."""
+    P = {k: np.asarray(v, dtype=np.float64) for k, v in params.items()}
+    L = _n_layer_cs336(P)
+    B, T = x.shape
+    C = P["wte"].shape[1]
+    H = n_head
+    D = C // H
+    N = B * T
+    cache = {"x": x, "y": y, "B": B, "T": T, "H": H, "L": L, "theta": theta}
+    h = P["wte"][x].reshape(N, C)
+    layers = []
+    for l in range(L):
+        p = f"h{l}."
+        a, r1 = rmsnorm(h, P[p + "rms1.g"])
+        qkv = a @ P[p + "attn.w"].T
+        q, k, v = (qkv[:, i * C:(i + 1) * C].reshape(B, T, H, D).transpose(0, 2, 1, 3)
+                   for i in range(3))
+        qr, kr = rope(q, theta), rope(k, theta)
+        o, Pm = causal_attention(qr, kr, v)
+        o = o.transpose(0, 2, 1, 3).reshape(N, C)
+        h_mid = h + o @ P[p + "proj.w"].T
+        m, r2 = rmsnorm(h_mid, P[p + "rms2.g"])
+        u1 = m @ P[p + "w1"].T
+        u3 = m @ P[p + "w3"].T
+        s = silu(u1) * u3
+        h_out = h_mid + s @ P[p + "w2"].T
+        if keep:
+            layers.append(dict(a=a, r1=r1, qr=qr, kr=kr, v=v, P=Pm, o=o, m=m, r2=r2, u1=u1, u3=u3, s=s))
+        h = h_out
+    f, rf = rmsnorm(h, P["rmsf.g"])
+    z = f @ P["lm_head"].T
+    per_row, lse = cross_entropy_rows(z, y.reshape(-1))
+    loss = per_row.mean()
+    if keep:
+        cache.update(layers=layers, f=f, rf=rf, z=z, lse=lse, P64=P)
+    return loss, per_row.reshape(B, T), cache
+
+
+def cs336_backward(cache, loss_scale: float = 1.0):
+    """Gradients of loss_scale * loss for every parameter of the variant."""
+    P = cache["P64"]
+    L, B, T, H, theta = cache["L"], cache["B"], cache["T"], cache["H"], cache["theta"]
+    x, y = cache["x"], cache["y"].reshape(-1)
+    N = B * T
+    C = P["wte"].shape[1]
+    D = C // H
+    G = {k: np.zeros_like(v) for k, v in P.items()}
+    dz = np.exp(cache["z"] - cache["lse"][:, None])
+    dz[np.arange(N), y] -= 1.0
+    dz *= loss_scale / N
+    G["lm_head"] = dz.T @ cache["f"]
+    df = dz @ P["lm_head"]
+    dh, G["rmsf.g"] = rmsnorm_backward(df, *cache["rf"], P["rmsf.g"])
+    for l in reversed(range(L)):
+        p = f"h{l}."
+        c = cache["layers"][l]
+        # feed-forward: h_out = h_mid + (silu(u1) * u3) W2^T
+        G[p + "w2"] = dh.T @ c["s"]
+        ds = dh @ P[p + "w2"]
+        du1 = silu_backward(ds * c["u3"], c["u1"])
+        du3 = ds * silu(c["u1"])
+        G[p + "w1"] = du1.T @ c["m"]
+        G[p + "w3"] = du3.T @ c["m"]
+        dm = du1 @ P[p + "w1"] + du3 @ P[p + "w3"]
+        dx2, G[p + "rms2.g"] = rmsnorm_backward(dm, *c["r2"], P[p + "rms2.g"])
+        dh = dh + dx2
+        # attention: h_mid = h + o Wo^T, with q and k rotated before the scores
+        G[p + "proj.w"] = dh.T @ c["o"]
+        do = (dh @ P[p + "proj.w"]).reshape(B, T, H, D).transpose(0, 2, 1, 3)
+        dqr, dkr, dv = causal_attention_backward(do, c["qr"], c["kr"], c["v"], c["P"])
+        dq, dk = rope(dqr, theta, inverse=True), rope(dkr, theta, inverse=True)
+        dqkv = np.concatenate([t.transpose(0, 2, 1, 3).reshape(N, C) for t in (dq, dk, dv)], axis=1)
+        G[p + "attn.w"] = dqkv.T @ c["a"]
+        da = dqkv @ P[p + "attn.w"]
+        dx1, G[p + "rms1.g"] = rmsnorm_backward(da, *c["r1"], P[p + "rms1.g"])
+        dh = dh + dx1
+    np.add.at(G["wte"], x.reshape(-1), dh.reshape(N, C))
+    return G
+
+
+def cs336_loss_and_grads(params, x, y, n_head: int, theta: float = 10000.0, loss_scale: float = 1.0):
+    loss, per_row, cache = cs336_forward(params, x, y, n_head, theta)
+    return loss, per_row, cs336_backward(cache, loss_scale)
+
+
+def cs336_param_count(vocab: int, d_model: int, n_layer: int, d_ff: int, tied: bool = False) -> int:
+    """Parameters of the variant: embedding (+ untied head), per block 4 D^2 + 3 D d_ff + 2 D, final norm."""
+    per_layer = 4 * d_model * d_model + 3 * d_model * d_ff + 2 * d_model
+    return vocab * d_model * (1 if tied else 2) + n_layer * per_layer + d_model
+
+
+# --------------------------------------------------------------------------
 # Optimiser ([C] section 2 AdamW and gradient clipping; [R] AdamW, groups)
 # --------------------------------------------------------------------------
 
