@@ -33,7 +33,11 @@ EXPORTS = [
 class GPTConfigC(ctypes.Structure):
     _fields_ = [("n_layer", c_int32), ("n_embd", c_int32), ("n_head", c_int32),
                 ("vocab", c_int32), ("padded_vocab", c_int32),
-                ("max_seq", c_int32), ("batch", c_int32), ("seq", c_int32), ("dtype", c_int32)]
+                ("max_seq", c_int32), ("batch", c_int32), ("seq", c_int32), ("dtype", c_int32),
+                ("block", c_int32), ("d_ff", c_int32), ("rope_theta", ctypes.c_float)]
+
+
+GPT_BLOCK_GPT2, GPT_BLOCK_RMS_ROPE_SWIGLU = 0, 1
 
 
 class GPTError(RuntimeError):

@@ -86,6 +86,10 @@ struct gpt_ctx {
   hipStream_t stream;
   int dt, es;  // dtype, element size of T
   int64_t N, C, L, H, D, V, Vp, T, B;
+  int blk = GPT_BLOCK_GPT2;  // block type
+  int64_t F = 0;             // SwiGLU width (GPT_BLOCK_RMS_ROPE_SWIGLU)
+  float2* rope_tab = nullptr;  // [max_seq][D/2] (cos, sin) of the RoPE angles
+  void* dh = nullptr;          // T [N][F]: gradient at the SwiGLU output
   std::vector<TensorDesc> tensors;  // logical (ABI) order
   int64_t P, P_decay;               // flat parameter floats
   float *params, *grads, *m, *v;
@@ -149,6 +153,11 @@ enum { T_WTE = 0, T_WPE = 1 };
 inline int tid(int l, int k) { return 2 + 12 * l + k; }  // k: 0 ln1.g .. 11 mlp_proj.b
 enum { K_LN1G, K_LN1B, K_ATTW, K_ATTB, K_PROJW, K_PROJB, K_LN2G, K_LN2B, K_FCW, K_FCB, K_MPW, K_MPB };
 inline int tid_lnf(int L, int k) { return 2 + 12 * L + k; }
+// GPT_BLOCK_RMS_ROPE_SWIGLU: wte, 7 tensors per block, rmsf.g, lm_head
+enum { VK_RMS1, VK_ATTW, VK_PROJW, VK_RMS2, VK_W1, VK_W3, VK_W2 };
+inline int vt(int l, int k) { return 1 + 7 * l + k; }
+inline int vt_rmsf(int L) { return 1 + 7 * L; }
+inline int vt_head(int L) { return 2 + 7 * L; }
 
 int check_cfg(const gpt_config* c) {
   if (!c) return fail(GPT_EINVAL, "null config");
@@ -162,6 +171,11 @@ int check_cfg(const gpt_config* c) {
   if (c->dtype == GPT_BF16 && D != 64) return fail(GPT_EINVAL, "bf16 head size must be 64");
   if (c->dtype == GPT_F32 && D != 16 && D != 32 && D != 64) return fail(GPT_EINVAL, "fp32 head size must be 16, 32 or 64");
   if (c->padded_vocab < c->vocab) return fail(GPT_EINVAL, "padded_vocab < vocab");
+  if (c->block != GPT_BLOCK_GPT2 && c->block != GPT_BLOCK_RMS_ROPE_SWIGLU) return fail(GPT_EINVAL, "unknown block type");
+  if (c->block == GPT_BLOCK_RMS_ROPE_SWIGLU) {
+    if (c->d_ff < 64 || c->d_ff % 64) return fail(GPT_EINVAL, "d_ff must be a positive multiple of 64");
+    if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) return fail(GPT_EINVAL, "rope_theta must be > 0");
+  }
   if (c->seq > c->max_seq) return fail(GPT_EINVAL, "seq > max_seq");
   const int64_t N = (int64_t)c->batch * c->seq;
   if (N > 16384) return fail(GPT_EINVAL, "batch * seq must be <= 16384");
@@ -178,6 +192,21 @@ std::vector<TensorDesc> make_tensors(const gpt_config* c, int64_t* P, int64_t* P
     t.push_back(TensorDesc{n, r, cc, dec, kind, 0});
   };
   add("wte", c->padded_vocab, C, 1, 0);
+  if (c->block == GPT_BLOCK_RMS_ROPE_SWIGLU) {
+    const int64_t F = c->d_ff;
+    for (int64_t l = 0; l < L; ++l) {  // w1 and w3 adjacent: one [2F, C] operand
+      const std::string p = "h" + std::to_string(l) + ".";
+      add(p + "rms1.g", C, 0, 0, 3);
+      add(p + "attn.w", 3 * C, C, 1, 0);
+      add(p + "proj.w", C, C, 1, 1);
+      add(p + "rms2.g", C, 0, 0, 3);
+      add(p + "w1", F, C, 1, 0);
+      add(p + "w3", F, C, 1, 0);
+      add(p + "w2", C, F, 1, 1);
+    }
+    add("rmsf.g", C, 0, 0, 3);
+    add("lm_head", c->padded_vocab, C, 1, 0);
+  } else {
   add("wpe", c->max_seq, C, 1, 0);
   for (int64_t l = 0; l < L; ++l) {
     const std::string p = "h" + std::to_string(l) + ".";
@@ -196,6 +225,7 @@ std::vector<TensorDesc> make_tensors(const gpt_config* c, int64_t* P, int64_t* P
   }
   add("lnf.g", C, 0, 0, 3);
   add("lnf.b", C, 0, 0, 2);
+  }
   // memory order: every decayed (2-D) tensor first, then the vectors
   int64_t off = 0;
   for (auto& d : t)
@@ -207,9 +237,10 @@ std::vector<TensorDesc> make_tensors(const gpt_config* c, int64_t* P, int64_t* P
   return t;
 }
 
-int64_t splitk_floats(int64_t N, int64_t C) {
+int64_t splitk_floats(int64_t N, int64_t C, int64_t F) {
   int64_t best = 0;
-  const int64_t shapes[4][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}};
+  // weight-gradient shapes: qkv, projection, MLP in and out ([2F, C] and [C, F] for SwiGLU)
+  const int64_t shapes[6][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}, {2 * F, C}, {C, F}};
   for (auto& s : shapes) {
     const int sp = gk::gemm_pick_splits((int)s[0], (int)s[1], (int)N, 1, 1);
     if (sp > 1) best = std::max(best, (int64_t)sp * s[0] * s[1]);
@@ -259,8 +290,9 @@ int64_t carve(gpt_ctx* x, void* base) {
   for (auto& l : x->layers) {
     l.ln1_part = cv.take<float>(nlnb * 3 * C * 4);
     l.ln2_part = cv.take<float>(nlnb * 3 * C * 4);
-    l.fcb_part = cv.take<float>(ncs * 4 * C * 4);
-    l.attb_part = cv.take<float>(ncs * 3 * C * 4);
+    const bool gpt2 = x->blk == GPT_BLOCK_GPT2;
+    l.fcb_part = cv.take<float>(gpt2 ? ncs * 4 * C * 4 : 0);
+    l.attb_part = cv.take<float>(gpt2 ? ncs * 3 * C * 4 : 0);
     l.ln1 = cv.take<void>(N * C * es);
     l.mu1 = cv.take<float>(N * 4);
     l.rs1 = cv.take<float>(N * 4);
@@ -271,8 +303,9 @@ int64_t carve(gpt_ctx* x, void* base) {
     l.ln2 = cv.take<void>(N * C * es);
     l.mu2 = cv.take<float>(N * 4);
     l.rs2 = cv.take<float>(N * 4);
-    l.fcdg = cv.take<void>(N * 4 * C * es);
-    l.fcact = cv.take<void>(N * 4 * C * es);
+    // GPT-2: GELU' and GELU output [N][4C]; SwiGLU: [gate | up] [N][2F] and its output [N][F]
+    l.fcdg = cv.take<void>(N * (gpt2 ? 4 * C : 2 * x->F) * es);
+    l.fcact = cv.take<void>(N * (gpt2 ? 4 * C : x->F) * es);
   }
   x->lnf = cv.take<void>(N * C * es);
   x->muf = cv.take<float>(N * 4);
@@ -298,13 +331,15 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->dlnT = cv.take<void>(N * C * es);
   x->dresT2[0] = cv.take<void>(N * C * es);
   x->dresT2[1] = cv.take<void>(N * C * es);
-  x->dfc = cv.take<void>(N * 4 * C * es);
+  x->dfc = cv.take<void>(N * std::max(4 * C, 2 * x->F) * es);
+  x->dh = x->blk == GPT_BLOCK_RMS_ROPE_SWIGLU ? cv.take<void>(N * x->F * es) : nullptr;
+  x->rope_tab = x->blk == GPT_BLOCK_RMS_ROPE_SWIGLU ? cv.take<float2>(x->cfg.max_seq * (x->D / 2) * 8) : nullptr;
   x->datt = cv.take<void>(N * C * es);
   x->dqkv = cv.take<void>(N * 3 * C * es);
   x->Dv = cv.take<float>(nh * 4);
   x->lnf_part = cv.take<float>(nlnb * 3 * C * 4);
   x->jobs_dev = cv.take<gk::RedJob>((8 * x->L + 3) * (int64_t)sizeof(gk::RedJob));
-  x->splitk_n = std::max<int64_t>(1, splitk_floats(N, C));
+  x->splitk_n = std::max<int64_t>(1, splitk_floats(N, C, x->F));
   x->splitk_ws = cv.take<float>(x->splitk_n * 4);
   x->keys = cv.take<uint32_t>(N * 4);
   x->norm_part = cv.take<float>(gk::sumsq_blocks(x->P) * 4);
@@ -324,6 +359,15 @@ void build_jobs(gpt_ctx* x) {
     x->jobs.push_back(gk::RedJob{part, out, nrows, cols, ld, blocks});
     blocks += (cols + 15) / 16;
   };
+  if (x->blk == GPT_BLOCK_RMS_ROPE_SWIGLU) {  // RMSNorm gains only (no shifts, no biases)
+    add(x->lnf_part, nlnb, C, 3 * C, x->G_(vt_rmsf(L)));
+    for (int l = 0; l < L; ++l) {
+      add(x->layers[l].ln2_part, nlnb, C, 3 * C, x->G_(vt(l, VK_RMS2)));
+      add(x->layers[l].ln1_part, nlnb, C, 3 * C, x->G_(vt(l, VK_RMS1)));
+    }
+    x->nred_blocks = blocks;
+    return;
+  }
   // final LayerNorm; its residual-gradient column sums are the last MLP output bias gradient
   add(x->lnf_part, nlnb, C, 3 * C, x->G_(tid_lnf(L, 0)));
   add(x->lnf_part + C, nlnb, C, 3 * C, x->G_(tid_lnf(L, 1)));
@@ -355,6 +399,8 @@ void setup_dims(gpt_ctx* x, const gpt_config* c) {
   x->T = c->seq;
   x->B = c->batch;
   x->N = x->B * x->T;
+  x->blk = c->block;
+  x->F = c->block == GPT_BLOCK_RMS_ROPE_SWIGLU ? c->d_ff : 4 * c->n_embd;
   x->tensors = make_tensors(c, &x->P, &x->P_decay);
 }
 
@@ -449,13 +495,15 @@ int ln_bwd(gpt_ctx* x, const void* dy, bool dy_is_t, const float* xin, const flo
            const float* dres_in, float* part, void* dresT) {
   ProfScope ps(x, "layernorm_bwd", 0.0, (double)x->N * x->C * ((dy_is_t ? x->es : 4) + 4 + 4 + 4 + x->es) + 8.0 * x->N);
   HIPCHK(gk::layernorm_bwd(x->dt, dy, dy_is_t ? 1 : 0, xin, mu, rs, x->P_(g_id), dres_in, x->dres, dresT, part,
-                           (int)x->N, (int)x->C, nullptr, x->stream));
+                           (int)x->N, (int)x->C, nullptr, x->stream, x->blk == GPT_BLOCK_RMS_ROPE_SWIGLU ? 1 : 0));
   return 0;
 }
 
+// LayerNorm (GPT_BLOCK_GPT2) or RMSNorm (b_id < 0: GPT_BLOCK_RMS_ROPE_SWIGLU) forward
 int ln_fwd(gpt_ctx* x, const float* in, int g_id, int b_id, void* out, float* mu, float* rs) {
   ProfScope ps(x, "layernorm_fwd", 0.0, (double)x->N * x->C * (4 + x->es) + 8.0 * x->N);
-  HIPCHK(gk::layernorm_fwd(x->dt, in, x->P_(g_id), x->P_(b_id), out, mu, rs, (int)x->N, (int)x->C, x->stream));
+  HIPCHK(gk::layernorm_fwd(x->dt, in, x->P_(g_id), b_id >= 0 ? x->P_(b_id) : nullptr, out, mu, rs, (int)x->N,
+                           (int)x->C, x->stream, b_id < 0 ? 1 : 0));
   return 0;
 }
 
@@ -533,6 +581,170 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
   return 0;
 }
 
+// ---- GPT_BLOCK_RMS_ROPE_SWIGLU (CS336 pretraining page, the second block variant) ----
+
+// Forward of the embedding and the blocks into lnf: embedding + RMSNorm, then
+// per block QKV (no bias) -> RoPE on q and k (in place) -> causal attention ->
+// out-projection + residual -> RMSNorm -> [gate | up] = x [W1; W3]^T ->
+// SwiGLU -> down-projection + residual; the final RMSNorm.
+int forward_variant(gpt_ctx* x, bool adam) {
+  hipStream_t s = x->stream;
+  const int64_t N = x->N, C = x->C, F = x->F;
+  const int L = (int)x->L;
+  {
+    ProfScope ps(x, "layernorm_fwd", 0.0, (double)N * C * (4 + 4 + x->es) + 8.0 * N);
+    HIPCHK(gk::embed_ln_fwd(x->dt, x->win, x->P_(0), nullptr, (int)x->T, x->res[0], x->P_(vt(0, VK_RMS1)), nullptr,
+                            x->layers[0].ln1, x->layers[0].mu1, x->layers[0].rs1, (int)N, (int)C, s, 1));
+  }
+  for (int l = 0; l < L; ++l) {
+    Layer& ly = x->layers[l];
+    if (adam && l <= 2) HIPCHK(hipStreamWaitEvent(s, x->adam_ev[l < 2 ? 2 + l : L + 1], 0));
+    gk::Gemm g = mk(x, 0, 0, gk::EPI_STORE, ly.ln1, C, x->W_(vt(l, VK_ATTW)), C, N, 3 * C, C, ly.qkv, 3 * C);
+    if (int e = run_gemm(x, "gemm_qkv_fwd", g)) return e;
+    {
+      ProfScope ps(x, "rope", 0.0, (double)N * 2 * C * 2 * x->es);
+      HIPCHK(gk::rope_qk(x->dt, ly.qkv, (int)N, (int)C, (int)x->T, (int)x->D, x->rope_tab, 0, s));
+    }
+    {
+      const double pairs = (double)x->B * x->H * x->T * (x->T + 1) / 2.0;
+      ProfScope ps(x, "attn_fwd", 4.0 * x->D * pairs, 0.0);
+      HIPCHK(gk::attn_fwd(x->dt, ly.qkv, ly.att, ly.lse, (int)x->B, (int)x->T, (int)x->H, (int)x->D, s));
+    }
+    g = mk(x, 0, 0, gk::EPI_RESID, ly.att, C, x->W_(vt(l, VK_PROJW)), C, N, C, C, ly.res_mid, C);
+    g.R = x->res[l];
+    if (int e = run_gemm(x, "gemm_proj_fwd", g)) return e;
+    if (int e = ln_fwd(x, ly.res_mid, vt(l, VK_RMS2), -1, ly.ln2, ly.mu2, ly.rs2)) return e;
+    g = mk(x, 0, 0, gk::EPI_STORE, ly.ln2, C, x->W_(vt(l, VK_W1)), C, N, 2 * F, C, ly.fcdg, 2 * F);
+    if (int e = run_gemm(x, "gemm_fc_fwd", g)) return e;
+    {
+      ProfScope ps(x, "swiglu", 0.0, (double)N * F * 3 * x->es);
+      HIPCHK(gk::swiglu_fwd(x->dt, ly.fcdg, ly.fcact, (int)N, (int)F, s));
+    }
+    g = mk(x, 0, 0, gk::EPI_RESID, ly.fcact, F, x->W_(vt(l, VK_W2)), F, N, C, F, x->res[l + 1], C);
+    g.R = ly.res_mid;
+    if (int e = run_gemm(x, "gemm_mlpproj_fwd", g)) return e;
+    if (l + 1 < L) {
+      Layer& nx = x->layers[l + 1];
+      if (int e = ln_fwd(x, x->res[l + 1], vt(l + 1, VK_RMS1), -1, nx.ln1, nx.mu1, nx.rs1)) return e;
+    } else {
+      if (int e = ln_fwd(x, x->res[l + 1], vt_rmsf(L), -1, x->lnf, x->muf, x->rsf)) return e;
+    }
+  }
+  return 0;
+}
+
+// Backward of the blocks and the embedding (the head already wrote dF and
+// G(lm_head)).  Same two-stream schedule as the GPT-2 blocks: weight
+// gradients on the side stream, started by events on the data-gradient chain,
+// which waits for them before reusing their inputs.  dqkv is rotated back
+// (RoPE's transpose) before the QKV products read it.
+int backward_variant(gpt_ctx* x) {
+  hipStream_t s = x->stream, ss = x->side;
+  const int64_t N = x->N, C = x->C, F = x->F;
+  const int acc = x->others_fresh ? 0 : 1;
+  const int L = (int)x->L;
+  auto ev = [&](int l, int k) { return x->sev[(size_t)l * 8 + k]; };
+  auto fork = [&](int l, int k) -> int {
+    HIPCHK(hipEventRecord(ev(l, k), s));
+    HIPCHK(hipStreamWaitEvent(ss, ev(l, k), 0));
+    return 0;
+  };
+  auto done = [&](int l, int k) -> int {
+    HIPCHK(hipEventRecord(ev(l, 4 + k), ss));
+    return 0;
+  };
+  auto wait_side = [&](int l, int k) -> int {
+    HIPCHK(hipStreamWaitEvent(s, ev(l, 4 + k), 0));
+    return 0;
+  };
+  void* T0 = x->dresT2[0];
+  void* T1 = x->dresT2[1];
+  if (int e = ln_bwd(x, x->dF, false, x->res[L], x->muf, x->rsf, vt_rmsf(L), nullptr, x->lnf_part, T0)) return e;
+  for (int l = L - 1; l >= 0; --l) {
+    Layer& ly = x->layers[l];
+    // SwiGLU down-projection: dW2 on the side stream, dh = dY W2 on s
+    if (int e = fork(l, 0)) return e;
+    if (int e = wgrad(x, "gemm_wgrad_mlp", T0, C, ly.fcact, F, C, F, x->G_(vt(l, VK_W2)), acc)) return e;
+    if (int e = done(l, 0)) return e;
+    gk::Gemm g = mk(x, 0, 1, gk::EPI_STORE, T0, C, x->W_(vt(l, VK_W2)), F, N, F, C, x->dh, F);
+    if (int e = run_gemm(x, "gemm_dgrad_mlp", g)) return e;
+    if (l + 1 < L)
+      if (int e = wait_side(l + 1, 1)) return e;  // previous layer's W1/W3 dW finished reading dfc
+    {
+      ProfScope ps(x, "swiglu", 0.0, (double)N * F * 5 * x->es);
+      HIPCHK(gk::swiglu_bwd(x->dt, ly.fcdg, x->dh, x->dfc, (int)N, (int)F, s));
+    }
+    // [W1; W3]: one [2F, C] product each way
+    if (int e = fork(l, 1)) return e;
+    if (int e = wgrad(x, "gemm_wgrad_mlp", x->dfc, 2 * F, ly.ln2, C, 2 * F, C, x->G_(vt(l, VK_W1)), acc)) return e;
+    if (int e = done(l, 1)) return e;
+    g = mk(x, 0, 1, gk::EPI_STORE, x->dfc, 2 * F, x->W_(vt(l, VK_W1)), C, N, C, 2 * F, x->dlnT, C);
+    if (int e = run_gemm(x, "gemm_dgrad_mlp", g)) return e;
+    if (l + 1 < L)
+      if (int e = wait_side(l + 1, 2)) return e;  // previous layer's proj dW finished reading T1
+    if (int e = ln_bwd(x, x->dlnT, true, ly.res_mid, ly.mu2, ly.rs2, vt(l, VK_RMS2), x->dres, ly.ln2_part, T1))
+      return e;
+    // attention output projection
+    if (int e = fork(l, 2)) return e;
+    if (int e = wgrad(x, "gemm_wgrad_attn", T1, C, ly.att, C, C, C, x->G_(vt(l, VK_PROJW)), acc)) return e;
+    if (int e = done(l, 2)) return e;
+    g = mk(x, 0, 1, gk::EPI_STORE, T1, C, x->W_(vt(l, VK_PROJW)), C, N, C, C, x->datt, C);
+    const bool fused_dv = x->dt == GPT_BF16 && x->D == 64;
+    if (fused_dv) {
+      g.epi = gk::EPI_STORE_ODOT;
+      g.aux = ly.att;
+      g.dv = x->Dv;
+      g.tn = (int)x->T;
+      g.heads = (int)x->H;
+    }
+    if (int e = run_gemm(x, "gemm_dgrad_attn", g)) return e;
+    if (l + 1 < L)
+      if (int e = wait_side(l + 1, 3)) return e;  // previous layer's qkv dW finished reading dqkv
+    {
+      const double pairs = (double)x->B * x->H * x->T * (x->T + 1) / 2.0;
+      ProfScope ps(x, "attn_bwd", 8.0 * x->D * pairs, 0.0);
+      if (fused_dv)
+        HIPCHK(gk::attn_bwd_bf16_d64(ly.qkv, x->datt, ly.lse, x->Dv, x->dqkv, (int)x->B, (int)x->T, (int)x->H, s));
+      else
+        HIPCHK(gk::attn_bwd(x->dt, ly.qkv, ly.att, x->datt, ly.lse, x->Dv, x->dqkv, (int)x->B, (int)x->T, (int)x->H,
+                            (int)x->D, s));
+    }
+    {
+      ProfScope ps(x, "rope", 0.0, (double)N * 2 * C * 2 * x->es);
+      HIPCHK(gk::rope_qk(x->dt, x->dqkv, (int)N, (int)C, (int)x->T, (int)x->D, x->rope_tab, 1, s));
+    }
+    // QKV projection
+    if (int e = fork(l, 3)) return e;
+    if (int e = wgrad(x, "gemm_wgrad_attn", x->dqkv, 3 * C, ly.ln1, C, 3 * C, C, x->G_(vt(l, VK_ATTW)), acc)) return e;
+    if (int e = done(l, 3)) return e;
+    g = mk(x, 0, 1, gk::EPI_STORE, x->dqkv, 3 * C, x->W_(vt(l, VK_ATTW)), C, N, C, 3 * C, x->dlnT, C);
+    if (int e = run_gemm(x, "gemm_dgrad_attn", g)) return e;
+    if (int e = wait_side(l, 0)) return e;  // this layer's W2 dW finished reading T0
+    if (int e = ln_bwd(x, x->dlnT, true, x->res[l], ly.mu1, ly.rs1, vt(l, VK_RMS1), x->dres, ly.ln1_part, T0))
+      return e;
+  }
+  if (int e = join_side(x)) return e;
+  if (ss) {
+    HIPCHK(hipEventRecord(x->fwd_start, s));
+    HIPCHK(hipStreamWaitEvent(ss, x->fwd_start, 0));
+  }
+  hipStream_t s2 = ss ? ss : s;
+  {
+    // the token rows are the only gradient of wte here (the head has its own tensor)
+    ProfScope ps(x, "embed_bwd", 0.0, (double)N * C * 12);
+    if (x->wte_fresh) HIPCHK(gk::fill_f32(x->G_(0), x->tensors[0].numel(), 0.f, s));
+    HIPCHK(gk::embed_bwd_ws(x->keys, (int)N, x->dres, (int)C, x->dln, x->G_(0), s));
+    x->wte_fresh = false;
+  }
+  {
+    ProfScope ps(x, "param_reduce", 0.0, 0.0, s2);
+    HIPCHK(gk::reduce_jobs(x->jobs_dev, (int)x->jobs.size(), x->nred_blocks, acc, s2));
+  }
+  x->others_fresh = false;
+  x->fwd_grad = false;
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -581,6 +793,19 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
   if (x->shadow) chk(gk::to_bf16(x->params, x->shadow, x->P, s));
   build_jobs(x);
   chk(hipMemcpyAsync(x->jobs_dev, x->jobs.data(), x->jobs.size() * sizeof(gk::RedJob), hipMemcpyHostToDevice, s));
+  if (x->rope_tab) {
+    // RoPE angles t * theta^(-2i/D) for every position the context can see, in
+    // double, stored as fp32 (cos, sin) pairs
+    const int64_t Tm = x->cfg.max_seq, half = x->D / 2;
+    std::vector<float2> tab((size_t)(Tm * half));
+    for (int64_t t = 0; t < Tm; ++t)
+      for (int64_t i = 0; i < half; ++i) {
+        const double a = (double)t * std::pow((double)x->cfg.rope_theta, -2.0 * (double)i / (double)x->D);
+        tab[(size_t)(t * half + i)] = make_float2((float)std::cos(a), (float)std::sin(a));
+      }
+    chk(hipMemcpyAsync(x->rope_tab, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice, s));
+    chk(hipStreamSynchronize(s));
+  }
   // side stream (default priority) and its ordering events
   chk(hipStreamCreateWithFlags(&x->side, hipStreamNonBlocking));
   chk(hipStreamCreateWithFlags(&x->hside, hipStreamNonBlocking));
@@ -666,6 +891,9 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
     HIPCHK(hipStreamWaitEvent(x->side, x->fwd_start, 0));
     HIPCHK(gk::sort_tokens(x->win, (int)N, x->keys, x->side));
   }
+  if (x->blk == GPT_BLOCK_RMS_ROPE_SWIGLU) {
+    if (int e = forward_variant(x, adam)) return e;
+  } else {
   {
     ProfScope ps(x, "layernorm_fwd", 0.0, (double)N * C * (4 + 4 + 4 + x->es) + 8.0 * N);
     HIPCHK(gk::embed_ln_fwd(x->dt, xt, x->P_(T_WTE), x->P_(T_WPE), (int)x->T, x->res[0], x->P_(tid(0, K_LN1G)),
@@ -704,13 +932,18 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
       if (int e = ln_fwd(x, x->res[l + 1], tid_lnf(x->L, 0), tid_lnf(x->L, 1), x->lnf, x->muf, x->rsf)) return e;
     }
   }
+  }
   const float scale = loss_scale / (float)N;
   const bool grad = loss_scale > 0.f;
-  if (int e = head(x, x->lnf, x->W_(T_WTE), x->Vp, yt, N, C, grad ? scale : 0.f, x->tok_loss, x->tok_lse,
-                   grad ? x->dF : nullptr, grad ? x->G_(T_WTE) : nullptr, x->wte_fresh ? 0 : 1, x->dt, x->loss, x->ring,
+  // the GPT-2 head is tied to wte; the variant's head is a tensor of its own
+  const bool tied = x->blk == GPT_BLOCK_GPT2;
+  const int hw = tied ? T_WTE : vt_head((int)x->L);
+  const bool fresh = tied ? x->wte_fresh : x->others_fresh;
+  if (int e = head(x, x->lnf, x->W_(hw), x->Vp, yt, N, C, grad ? scale : 0.f, x->tok_loss, x->tok_lse,
+                   grad ? x->dF : nullptr, grad ? x->G_(hw) : nullptr, fresh ? 0 : 1, x->dt, x->loss, x->ring,
                    (int)(x->ring_wr % RING), nullptr))
     return e;
-  if (grad) x->wte_fresh = false;
+  if (grad && tied) x->wte_fresh = false;
   x->ring_wr++;
   x->have_fwd = true;
   x->fwd_grad = grad;
@@ -726,6 +959,7 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
 int gpt_backward(gpt_ctx* x) {
   if (!x) return fail(GPT_EINVAL, "null context");
   if (!x->have_fwd || !x->fwd_grad) return fail(GPT_EINVAL, "gpt_backward needs a gpt_forward_loss with loss_scale > 0");
+  if (x->blk == GPT_BLOCK_RMS_ROPE_SWIGLU) return backward_variant(x);
   hipStream_t s = x->stream, ss = x->side;
   const int64_t N = x->N, C = x->C;
   const int acc = x->others_fresh ? 0 : 1;
@@ -851,8 +1085,9 @@ int gpt_adamw_step(gpt_ctx* x, float lr, float beta1, float beta2, float eps, fl
     // some gradients were never written since the last update: they are zero
     if (x->wte_fresh) HIPCHK(gk::fill_f32(x->G_(T_WTE), x->tensors[T_WTE].numel(), 0.f, x->stream));
     if (x->others_fresh) {
-      HIPCHK(gk::fill_f32(x->grads + x->tensors[T_WPE].off, x->P - x->tensors[T_WPE].off, 0.f, x->stream));
-      // wte precedes wpe in memory; anything between is padding
+      // wte comes first in memory; every other tensor (and padding) follows it
+      const int64_t rest = align_up(x->tensors[T_WTE].numel(), 64);
+      HIPCHK(gk::fill_f32(x->grads + rest, x->P - rest, 0.f, x->stream));
     }
   }
   hipStream_t s = x->stream;
@@ -883,9 +1118,11 @@ int gpt_adamw_step(gpt_ctx* x, float lr, float beta1, float beta2, float eps, fl
       return 0;
     };
     const int L = (int)x->L;
-    auto first = [&](int l) { return l < L ? x->tensors[tid(l, K_ATTW)].off : x->P_decay; };  // layer l's matrices
+    auto first = [&](int l) {  // layer l's matrices (the variant's lm_head rides with the last layer's)
+      return l < L ? x->tensors[x->blk == GPT_BLOCK_GPT2 ? tid(l, K_ATTW) : vt(l, VK_ATTW)].off : x->P_decay;
+    };
     if (int e = piece(x->P_decay, x->P, 0)) return e;  // LayerNorm gains/shifts and biases of every layer
-    if (int e = piece(0, first(0), 1)) return e;       // wte, wpe
+    if (int e = piece(0, first(0), 1)) return e;       // wte, wpe (GPT-2) or wte
     for (int l = 0; l < L; ++l)
       if (int e = piece(first(l), first(l + 1), 2 + l)) return e;
     x->adam_pending = true;
@@ -1067,7 +1304,8 @@ int gpt_set_tensor(gpt_ctx* x, int kind, int id, const float* host, int64_t n) {
       HIPCHK(gk::fill_f32(x->G_(T_WTE), d.numel(), 0.f, x->stream));
       x->wte_fresh = false;
     } else if (id != T_WTE && x->others_fresh) {
-      HIPCHK(gk::fill_f32(x->grads + x->tensors[T_WPE].off, x->P - x->tensors[T_WPE].off, 0.f, x->stream));
+      const int64_t rest = align_up(x->tensors[T_WTE].numel(), 64);  // everything after wte
+      HIPCHK(gk::fill_f32(x->grads + rest, x->P - rest, 0.f, x->stream));
       x->others_fresh = false;
     }
   }

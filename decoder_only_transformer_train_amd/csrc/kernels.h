@@ -58,21 +58,31 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main = nullptr, h
 // workspace is gemm_pick_splits(...) * M * N floats when that is > 1)
 int gemm_pick_splits(int M, int N, int K, int a_trans, int b_trans);
 
-// ---- LayerNorm ----
+// ---- LayerNorm (rms = 1: RMSNorm, mu = 0 and no shift; b may be null) ----
 // y = (x - mu) * rstd * g + b per row of C; x fp32 [rows][C]; y T; mu, rstd fp32 [rows]
 hipError_t layernorm_fwd(int dtype, const float* x, const float* g, const float* b, void* y,
-                         float* mu, float* rstd, int rows, int C, hipStream_t s);
-// embedding (wte[tok] + wpe[t]) -> res0 (f32), fused with the first LayerNorm
+                         float* mu, float* rstd, int rows, int C, hipStream_t s, int rms = 0);
+// embedding (wte[tok] + wpe[t], wpe nullable) -> res0 (f32), fused with the first LayerNorm
 hipError_t embed_ln_fwd(int dtype, const int32_t* tok, const float* wte, const float* wpe, int T,
                         float* res0, const float* g, const float* b, void* y, float* mu,
-                        float* rstd, int rows, int C, hipStream_t s);
+                        float* rstd, int rows, int C, hipStream_t s, int rms = 0);
 // LayerNorm backward: dres_out = dres_in + dx (f32, may alias dres_in), dres_T = T(dres_out);
 // part [nblk][3C]: per-block column sums of dy*xhat, dy and dres_out
 // dy is T when dy_is_t (bf16 or fp32 as dtype), else fp32
 hipError_t layernorm_bwd(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu,
                          const float* rstd, const float* g, const float* dres_in, float* dres_out, void* dres_T,
-                         float* part, int rows, int C, int* nblk_out, hipStream_t s);
+                         float* part, int rows, int C, int* nblk_out, hipStream_t s, int rms = 0);
 int layernorm_bwd_blocks(int rows);
+
+// ---- the second block variant's elementwise steps ----
+// RoPE on the q and k thirds of qkv [rows][3C] (T, in place), head size D,
+// position t = row % Tn; tab [Tmax][D/2] holds (cos, sin) of the pair angles;
+// inverse rotates by minus the angles (the backward, on dqkv)
+hipError_t rope_qk(int dtype, void* qkv, int rows, int C, int Tn, int D, const float2* tab, int inverse, hipStream_t s);
+// SwiGLU: u [rows][2F] = [gate | up] (T) -> h [rows][F] = silu(gate) * up (T)
+hipError_t swiglu_fwd(int dtype, const void* u, void* h, int rows, int F, hipStream_t s);
+// backward: dh [rows][F] (T) -> du [rows][2F] = [dh up silu'(gate) | dh silu(gate)] (T)
+hipError_t swiglu_bwd(int dtype, const void* u, const void* dh, void* du, int rows, int F, hipStream_t s);
 // One column reduction of a batch: out[c] (+)= sum_r part[r * ld + c], c < cols;
 // blocks [first_block, first_block + cdiv(cols, 16)) of the batch launch serve it.
 struct RedJob {

@@ -4,7 +4,9 @@
 //
 // LayerNorm (lecture, pre-LN blocks and final LayerNorm; Zero page,
 // Transformer Block): y = (x - mu) / sqrt(var + 1e-5) * g + b over the C
-// channels of a row, biased variance, statistics in fp32.  One wavefront owns
+// channels of a row, biased variance, statistics in fp32.  With rms set the
+// same kernels compute RMSNorm (CS336 pretraining page, the second block
+// variant): mu = 0, no shift, y = x / sqrt(mean(x^2) + 1e-5) * g.  One wavefront owns
 // one row; each lane keeps its float4 slices of the row in registers, so the
 // row is read once.
 #include "common.h"
@@ -24,7 +26,8 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
                                                      const float* __restrict__ wte, const float* __restrict__ wpe,
                                                      int Tn, float* __restrict__ res0, const float* __restrict__ g,
                                                      const float* __restrict__ bb, T* __restrict__ y,
-                                                     float* __restrict__ mu, float* __restrict__ rs, int rows, int C) {
+                                                     float* __restrict__ mu, float* __restrict__ rs, int rows, int C,
+                                                     int rms) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -40,13 +43,13 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
     if (j < nc) {
       if constexpr (EMBED) {
         const float4 a = load4(wte + wrow + 4 * j);
-        const float4 p = load4(wpe + (int64_t)(row % Tn) * C + 4 * j);
+        const float4 p = wpe ? load4(wpe + (int64_t)(row % Tn) * C + 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
         v[i] = make_float4(a.x + p.x, a.y + p.y, a.z + p.z, a.w + p.w);
       } else {
         v[i] = load4(x + (int64_t)row * C + 4 * j);
       }
       gv[i] = load4(g + 4 * j);
-      bv[i] = load4(bb + 4 * j);
+      bv[i] = rms ? make_float4(0.f, 0.f, 0.f, 0.f) : load4(bb + 4 * j);
     }
   }
   float s = 0.f;
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
       s += v[i].x + v[i].y + v[i].z + v[i].w;
     }
   }
-  const float mean = wave_sum(s) / C;
+  const float mean = rms ? 0.f : wave_sum(s) / C;
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(256, NV <= 3 ? 4 : (NV <= 7 ? 2 : 1)) void ln_bwd_k
                                                          const float* __restrict__ mu, const float* __restrict__ rs,
                                                          const float* __restrict__ g, const float* __restrict__ dres_in,
                                                          float* __restrict__ dres_out, T* __restrict__ dres_T,
-                                                         float* __restrict__ part, int rows, int C) {
+                                                         float* __restrict__ part, int rows, int C, int rms) {
   __shared__ float red[4][NV * 256];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(256, NV <= 3 ? 4 : (NV <= 7 ? 2 : 1)) void ln_bwd_k
       pg[i].x += d.x * xh.x; pg[i].y += d.y * xh.y; pg[i].z += d.z * xh.z; pg[i].w += d.w * xh.w;
       pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
     }
-    const float m1 = wave_sum(s1) / C, m2 = wave_sum(s2) / C;
+    const float m1 = rms ? 0.f : wave_sum(s1) / C, m2 = wave_sum(s2) / C;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int64_t o = (int64_t)row * C + 4 * jj[i];
@@ -190,7 +193,7 @@ template <typename TY, typename T, int WPR, bool DRES>
 __global__ __launch_bounds__(64 * WPR, 8) void ln_bwd_rows_kernel(
     const TY* __restrict__ dy, const float* __restrict__ x, const float* __restrict__ mu,
     const float* __restrict__ rs, const float* __restrict__ g, const float* __restrict__ dres_in,
-    float* __restrict__ dres_out, T* __restrict__ dres_T, float* __restrict__ part, int rows) {
+    float* __restrict__ dres_out, T* __restrict__ dres_T, float* __restrict__ part, int rows, int rms) {
   constexpr int C = 256 * WPR;
   __shared__ float2 sums[2][WPR];
   const int lane = threadIdx.x & 63;
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(64 * WPR, 8) void ln_bwd_rows_kernel(
       t1 += v.x;
       t2 += v.y;
     }
-    const float m1 = t1 / C, m2 = t2 / C;
+    const float m1 = rms ? 0.f : t1 / C, m2 = t2 / C;
     const float4 out = make_float4(prev.x + r * (dxh.x - m1 - xh.x * m2), prev.y + r * (dxh.y - m1 - xh.y * m2),
                                    prev.z + r * (dxh.z - m1 - xh.z * m2), prev.w + r * (dxh.w - m1 - xh.w * m2));
     const int64_t o = (int64_t)row * C + col;
@@ -356,37 +359,39 @@ __global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x,
 
 template <typename T, bool EMBED, int NV>
 void ln_fwd_launch(const float* x, const int32_t* tok, const float* wte, const float* wpe, int Tn, float* res0,
-                   const float* g, const float* b, void* y, float* mu, float* rstd, int rows, int C, hipStream_t s) {
+                   const float* g, const float* b, void* y, float* mu, float* rstd, int rows, int C, hipStream_t s,
+                   int rms) {
   hipLaunchKernelGGL((ln_fwd_kernel<T, EMBED, NV>), dim3(cdiv(rows, 4)), dim3(256), 0, s, x, tok, wte, wpe, Tn, res0,
-                     g, b, (T*)y, mu, rstd, rows, C);
+                     g, b, (T*)y, mu, rstd, rows, C, rms);
 }
 template <typename T, bool EMBED>
 hipError_t ln_fwd_nv(const float* x, const int32_t* tok, const float* wte, const float* wpe, int Tn, float* res0,
-                     const float* g, const float* b, void* y, float* mu, float* rstd, int rows, int C, hipStream_t s) {
+                     const float* g, const float* b, void* y, float* mu, float* rstd, int rows, int C, hipStream_t s,
+                     int rms) {
   if (C % 4 || C > 4 * 64 * MAXV) return hipErrorInvalidValue;
   switch ((C / 4 + 63) / 64) {  // float4 slices per lane
-    case 1: ln_fwd_launch<T, EMBED, 1>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
-    case 2: ln_fwd_launch<T, EMBED, 2>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
-    case 3: ln_fwd_launch<T, EMBED, 3>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
-    case 4: ln_fwd_launch<T, EMBED, 4>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
+    case 1: ln_fwd_launch<T, EMBED, 1>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s, rms); break;
+    case 2: ln_fwd_launch<T, EMBED, 2>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s, rms); break;
+    case 3: ln_fwd_launch<T, EMBED, 3>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s, rms); break;
+    case 4: ln_fwd_launch<T, EMBED, 4>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s, rms); break;
     case 5:
-    case 6: ln_fwd_launch<T, EMBED, 6>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
-    default: ln_fwd_launch<T, EMBED, 8>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s); break;
+    case 6: ln_fwd_launch<T, EMBED, 6>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s, rms); break;
+    default: ln_fwd_launch<T, EMBED, 8>(x, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s, rms); break;
   }
   return hipGetLastError();
 }
 
 hipError_t layernorm_fwd(int dtype, const float* x, const float* g, const float* b, void* y, float* mu,
-                         float* rstd, int rows, int C, hipStream_t s) {
-  if (dtype == BF16) return ln_fwd_nv<bf16, false>(x, nullptr, nullptr, nullptr, 1, nullptr, g, b, y, mu, rstd, rows, C, s);
-  return ln_fwd_nv<float, false>(x, nullptr, nullptr, nullptr, 1, nullptr, g, b, y, mu, rstd, rows, C, s);
+                         float* rstd, int rows, int C, hipStream_t s, int rms) {
+  if (dtype == BF16) return ln_fwd_nv<bf16, false>(x, nullptr, nullptr, nullptr, 1, nullptr, g, b, y, mu, rstd, rows, C, s, rms);
+  return ln_fwd_nv<float, false>(x, nullptr, nullptr, nullptr, 1, nullptr, g, b, y, mu, rstd, rows, C, s, rms);
 }
 
 hipError_t embed_ln_fwd(int dtype, const int32_t* tok, const float* wte, const float* wpe, int Tn, float* res0,
                         const float* g, const float* b, void* y, float* mu, float* rstd, int rows, int C,
-                        hipStream_t s) {
-  if (dtype == BF16) return ln_fwd_nv<bf16, true>(nullptr, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s);
-  return ln_fwd_nv<float, true>(nullptr, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s);
+                        hipStream_t s, int rms) {
+  if (dtype == BF16) return ln_fwd_nv<bf16, true>(nullptr, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s, rms);
+  return ln_fwd_nv<float, true>(nullptr, tok, wte, wpe, Tn, res0, g, b, y, mu, rstd, rows, C, s, rms);
 }
 
 int layernorm_bwd_blocks(int rows) { return cdiv(rows, LNB_ROWS); }
@@ -394,46 +399,46 @@ int layernorm_bwd_blocks(int rows) { return cdiv(rows, LNB_ROWS); }
 template <int NV, bool DRES>
 hipError_t ln_bwd_nvd(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu, const float* rstd,
                       const float* g, const float* dres_in, float* dres_out, void* dres_T, float* part, int rows,
-                      int C, int nblk, hipStream_t s) {
+                      int C, int nblk, hipStream_t s, int rms) {
   if (dtype == BF16 && dy_is_t)
     hipLaunchKernelGGL((ln_bwd_kernel<bf16, bf16, NV, DRES>), dim3(nblk), dim3(256), 0, s, (const bf16*)dy, x, mu,
-                       rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, C);
+                       rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, C, rms);
   else if (dtype == BF16)
     hipLaunchKernelGGL((ln_bwd_kernel<float, bf16, NV, DRES>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu,
-                       rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, C);
+                       rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, C, rms);
   else
     hipLaunchKernelGGL((ln_bwd_kernel<float, float, NV, DRES>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu,
-                       rstd, g, dres_in, dres_out, (float*)dres_T, part, rows, C);
+                       rstd, g, dres_in, dres_out, (float*)dres_T, part, rows, C, rms);
   return hipGetLastError();
 }
 template <int NV>
 hipError_t ln_bwd_nv(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu, const float* rstd,
                      const float* g, const float* dres_in, float* dres_out, void* dres_T, float* part, int rows,
-                     int C, int nblk, hipStream_t s) {
+                     int C, int nblk, hipStream_t s, int rms) {
   return dres_in ? ln_bwd_nvd<NV, true>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C,
-                                        nblk, s)
+                                        nblk, s, rms)
                  : ln_bwd_nvd<NV, false>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C,
-                                         nblk, s);
+                                         nblk, s, rms);
 }
 
 template <int WPR, bool DRES>
 hipError_t ln_bwd_rows_d(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu, const float* rstd,
                          const float* g, const float* dres_in, float* dres_out, void* dres_T, float* part, int rows,
-                         int nblk, hipStream_t s) {
+                         int nblk, hipStream_t s, int rms) {
   if (dtype == BF16 && dy_is_t)
     hipLaunchKernelGGL((ln_bwd_rows_kernel<bf16, bf16, WPR, DRES>), dim3(nblk), dim3(64 * WPR), 0, s,
-                       (const bf16*)dy, x, mu, rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows);
+                       (const bf16*)dy, x, mu, rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, rms);
   else if (dtype == BF16)
     hipLaunchKernelGGL((ln_bwd_rows_kernel<float, bf16, WPR, DRES>), dim3(nblk), dim3(64 * WPR), 0, s,
-                       (const float*)dy, x, mu, rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows);
+                       (const float*)dy, x, mu, rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, rms);
   else
     hipLaunchKernelGGL((ln_bwd_rows_kernel<float, float, WPR, DRES>), dim3(nblk), dim3(64 * WPR), 0, s,
-                       (const float*)dy, x, mu, rstd, g, dres_in, dres_out, (float*)dres_T, part, rows);
+                       (const float*)dy, x, mu, rstd, g, dres_in, dres_out, (float*)dres_T, part, rows, rms);
   return hipGetLastError();
 }
 hipError_t layernorm_bwd(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu,
                          const float* rstd, const float* g, const float* dres_in, float* dres_out, void* dres_T,
-                         float* part, int rows, int C, int* nblk_out, hipStream_t s) {
+                         float* part, int rows, int C, int* nblk_out, hipStream_t s, int rms) {
   const int nblk = layernorm_bwd_blocks(rows);
   if (nblk_out) *nblk_out = nblk;
   if (C % 4 || C > 4 * 64 * MAXV) return hipErrorInvalidValue;
@@ -443,19 +448,19 @@ hipError_t layernorm_bwd(int dtype, const void* dy, int dy_is_t, const float* x,
   // layers the one-wave-per-row kernel was faster in the step (same box,
   // 3 x 20 steps: +0.1 ms with the split-row kernel there).
   if (!dy_is_t && !dres_in) {
-    if (C == 512) return ln_bwd_rows_d<2, false>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, nblk, s);
-    if (C == 768) return ln_bwd_rows_d<3, false>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, nblk, s);
-    if (C == 1024) return ln_bwd_rows_d<4, false>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, nblk, s);
+    if (C == 512) return ln_bwd_rows_d<2, false>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, nblk, s, rms);
+    if (C == 768) return ln_bwd_rows_d<3, false>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, nblk, s, rms);
+    if (C == 1024) return ln_bwd_rows_d<4, false>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, nblk, s, rms);
   }
   switch ((C / 4 + 63) / 64) {  // float4 slices per lane
-    case 1: return ln_bwd_nv<1>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
-    case 2: return ln_bwd_nv<2>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
-    case 3: return ln_bwd_nv<3>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
-    case 4: return ln_bwd_nv<4>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
+    case 1: return ln_bwd_nv<1>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s, rms);
+    case 2: return ln_bwd_nv<2>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s, rms);
+    case 3: return ln_bwd_nv<3>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s, rms);
+    case 4: return ln_bwd_nv<4>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s, rms);
     case 5:
-    case 6: return ln_bwd_nv<6>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
-    case 7: return ln_bwd_nv<7>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
-    default: return ln_bwd_nv<8>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s);
+    case 6: return ln_bwd_nv<6>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s, rms);
+    case 7: return ln_bwd_nv<7>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s, rms);
+    default: return ln_bwd_nv<8>(dtype, dy, dy_is_t, x, mu, rstd, g, dres_in, dres_out, dres_T, part, rows, C, nblk, s, rms);
   }
 }
 

@@ -85,7 +85,26 @@ typedef struct {
   int32_t vocab, padded_vocab;
   int32_t max_seq, batch, seq;
   int32_t dtype; /* GPT_F32 or GPT_BF16 */
+  int32_t block; /* GPT_BLOCK_GPT2 (0) or GPT_BLOCK_RMS_ROPE_SWIGLU */
+  int32_t d_ff;  /* GPT_BLOCK_RMS_ROPE_SWIGLU: SwiGLU hidden width, a multiple of 64 */
+  float rope_theta; /* GPT_BLOCK_RMS_ROPE_SWIGLU: RoPE base (CS336 page: 10000), > 0 */
 } gpt_config;
+
+/*
+ * Block types (CS336 pretraining page, sections 4 and 6, for the second).
+ *   GPT_BLOCK_GPT2: pre-LayerNorm blocks with biases, tanh-GELU MLP of width
+ *     4C, learned position table, LM head tied to the token embedding.
+ *   GPT_BLOCK_RMS_ROPE_SWIGLU: pre-RMSNorm blocks without biases, RoPE on Q
+ *     and K (channel pairs (2i, 2i+1) rotated by t * rope_theta^(-2i/D) at
+ *     position t), SwiGLU feed-forward (W2 (silu(W1 x) * W3 x)) of width
+ *     d_ff, no position table, final RMSNorm and an LM head of its own
+ *     ("lm_head", [padded_vocab, C]).  Tensors, in order: wte; per block
+ *     h{l}.rms1.g, h{l}.attn.w [3C, C], h{l}.proj.w [C, C], h{l}.rms2.g,
+ *     h{l}.w1 [d_ff, C], h{l}.w3 [d_ff, C], h{l}.w2 [C, d_ff]; rmsf.g, lm_head.
+ *     RMSNorm epsilon 1e-5.  max_seq bounds the positions RoPE is set up for.
+ */
+#define GPT_BLOCK_GPT2 0
+#define GPT_BLOCK_RMS_ROPE_SWIGLU 1
 
 /* Bytes of device memory gpt_init needs for this configuration (0 if invalid). */
 size_t gpt_arena_bytes(const gpt_config* cfg);

@@ -32,7 +32,10 @@ def context(cfg, params=None, seed=0):
     return g
 
 
-def init_for(cfg, seed=0):
+def init_for(cfg, seed=0, gain_jitter=0.0):
+    if cfg.block == binding.GPT_BLOCK_RMS_ROPE_SWIGLU:
+        return synthetic.init_params_cs336(cfg.n_layer, cfg.n_embd, cfg.d_ff, cfg.padded_vocab, seed=seed,
+                                           gain_jitter=gain_jitter)
     return synthetic.init_params(cfg.n_layer, cfg.n_embd, cfg.padded_vocab, cfg.max_seq, seed=seed)
 
 

@@ -100,3 +100,19 @@ def test_lmhead_ws_bytes():
     lib = binding.load()
     assert lib.gpt_lmhead_ce_ws_bytes(65536, 50257, 768, 1) > 0
     assert lib.gpt_lmhead_ce_ws_bytes(65536, 50257, 100, 1) == 0
+
+
+def test_block_variant_config_checks():
+    # the RMSNorm / RoPE / SwiGLU variant: valid presets size an arena; bad widths and bases do not
+    lib = binding.load()
+    for cfg in (configs.CS336_TINY_F32, configs.CS336_TINYSTORIES, configs.CS336_TINYSTORIES_BF16):
+        assert lib.gpt_arena_bytes(ctypes.byref(cfg.to_c())) > 0, cfg
+    base = configs.CS336_TINY_F32
+    for bad in (base.with_(d_ff=0), base.with_(d_ff=100), base.with_(rope_theta=0.0), base.with_(block=7)):
+        assert lib.gpt_arena_bytes(ctypes.byref(bad.to_c())) == 0, bad
+    # the GPT-2 block ignores d_ff and rope_theta
+    assert lib.gpt_arena_bytes(ctypes.byref(configs.TINY_F32.with_(d_ff=3, rope_theta=-1.0).to_c())) > 0
+    # the variant holds no biases and no position table: fewer bytes than GPT-2 at the same sizes
+    g2 = configs.TINY_F32
+    v = configs.CS336_TINY_F32.with_(d_ff=4 * g2.n_embd)
+    assert lib.gpt_arena_bytes(ctypes.byref(v.to_c())) != lib.gpt_arena_bytes(ctypes.byref(g2.to_c()))

@@ -72,8 +72,9 @@ def test_validation_loss_fixed_windows():
     assert g.step_count() == 2
 
 
-@pytest.mark.parametrize("cfg", [CFG, configs.GPT2_124M.with_(n_layer=1, batch=2, seq=128, max_seq=128)],
-                         ids=["tiny-fp32", "124m-shaped-bf16"])
+@pytest.mark.parametrize("cfg", [CFG, configs.GPT2_124M.with_(n_layer=1, batch=2, seq=128, max_seq=128),
+                                 configs.CS336_TINY_F32],
+                         ids=["tiny-fp32", "124m-shaped-bf16", "rms-rope-swiglu-fp32"])
 def test_checkpoint_exact_resume(cfg, tmp_path):
     announce(f"driver: exact resume ({cfg.n_layer}L C={cfg.n_embd})")
     p = init_for(cfg, seed=6)
