@@ -43,6 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
+PEAK_F32 = 157.3e12     # MI355X fp32 (MFMA and vector), FLOP/s
 PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
 # kernel classes the library can time (each GEMM class times its main kernel only)
 PROFILE_CLASSES = ["gemm_qkv_fwd", "gemm_proj_fwd", "gemm_fc_fwd", "gemm_mlpproj_fwd", "gemm_dgrad_mlp",
@@ -58,6 +59,10 @@ WORKLOADS = {
     "gpt2-350m": "GPT-2 350M training step: L=24, C=1024, H=16, V=50257 padded to 50304, T=1024, B=8",
     "gpt2-1.5b": ("GPT-2 1.5B training step: L=48, C=1600, H=25, V=50257 padded to 50304, T=1024, "
                   "B=4 x 4 gradient-accumulation micro-steps"),
+    "cs336-tinystories": ("RMSNorm/RoPE/SwiGLU block, untied head (CS336 TinyStories model) training step: "
+                          "L=4, C=512, H=16, d_ff=1344, V=10000, T=256, B=32, fp32"),
+    "cs336-tinystories-bf16": ("RMSNorm/RoPE/SwiGLU block, untied head, TinyStories sizes with 8 heads of 64: "
+                               "L=4, C=512, H=8, d_ff=1344, V=10000, T=256, B=32, bf16"),
 }
 WORKLOAD_TAIL = (", bf16 GEMM/attention operands with fp32 master weights and AdamW state; Zipf(1.1) tokens "
                  "with end-of-text every Geometric(1/600), random init")
@@ -180,9 +185,10 @@ def bench_model(args, name):
     B, T, A = cfg.batch, cfg.seq, cfg.accum
     W, K, R = args.warmup, args.steps, args.repeats
     n_tok = (W + K * R + 2 + len(MORE_CLASSES)) * A * B * T + 1
-    stream = synthetic.zipf_eot_stream(n_tok, cfg.vocab, seed=0)
+    stream = synthetic.zipf_eot_stream(n_tok, cfg.vocab, seed=0, eot=min(synthetic.EOT_ID, cfg.vocab - 1))
     g = binding.GPT(cfg, seed=0, device="cuda:0")
-    init_params = None if args.no_cpu_baseline else g.get_all(binding.PARAM)  # the step-1 weights
+    # the step-1 weights for the CPU oracle baseline (GPT-2 blocks only)
+    init_params = None if args.no_cpu_baseline or cfg.block != binding.GPT_BLOCK_GPT2 else g.get_all(binding.PARAM)
     adam = configs.ADAMW
 
     def step(pos):
@@ -242,8 +248,10 @@ def bench_model(args, name):
     dt = statistics.median(loops)
     tokens = K * A * B * T
     tps = tokens / dt
-    fpt = accounting.training_flops_per_token(cfg.n_layer, cfg.n_embd, T, cfg.padded_vocab)
-    mfu = tps * fpt / PEAK_BF16
+    fp32 = cfg.dtype == binding.GPT_F32
+    fpt = accounting.training_flops_per_token(cfg.n_layer, cfg.n_embd, T, cfg.padded_vocab,
+                                              cfg.d_ff if cfg.block == binding.GPT_BLOCK_RMS_ROPE_SWIGLU else 0)
+    mfu = tps * fpt / (PEAK_F32 if fp32 else PEAK_BF16)
     roof = rate(prof)
     roof["traffic"] = stored_traffic(args.roofline_kernel, name)
     roof["kernel"] = args.roofline_kernel
@@ -253,8 +261,10 @@ def bench_model(args, name):
         "metric": METRIC if name == "gpt2-124m" else f"train tokens/sec + MFU, {WORKLOADS[name].split(':')[0]}, 1×MI355X",
         "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(dt / K * 1e3, 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": WORKLOADS[name] + WORKLOAD_TAIL, "global_batch": B * A, "seq_len": T,
+        "vs_baseline": None, "dtype": "f32" if fp32 else "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOADS[name] + (WORKLOAD_TAIL if name.startswith("gpt2") else
+                                                  ", Zipf(1.1) tokens with end-of-text separators, random init"),
+                   "global_batch": B * A, "seq_len": T,
                    "tokens_per_step": A * B * T, "accumulation": A},
         "mfu": round(mfu, 4), "model_tflop_per_step": round(fpt * A * B * T / 1e12, 3),
         "repeats_ms_per_step": [round(x / K * 1e3, 3) for x in loops],
@@ -268,7 +278,7 @@ def bench_model(args, name):
     g.close()
     del g
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
+    if init_params is not None:
         out["cpu_baseline"] = cpu_baseline(cfg, init_params, stream, 3 if name == "gpt2-124m" else 1)
     return out
 

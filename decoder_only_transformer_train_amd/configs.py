@@ -51,7 +51,7 @@ CS336_TINY_F32 = GPTConfig(2, 64, 4, 256, 256, 32, 4, 32, binding.GPT_F32,
 CS336_TINYSTORIES_BF16 = CS336_TINYSTORIES.with_(n_head=8, dtype=binding.GPT_BF16)
 
 PRESETS = {"tiny": TINY_F32, "gpt2-124m": GPT2_124M, "gpt2-350m": GPT2_350M, "gpt2-1.5b": GPT2_1P5B,
-           "cs336-tinystories": CS336_TINYSTORIES}
+           "cs336-tinystories": CS336_TINYSTORIES, "cs336-tinystories-bf16": CS336_TINYSTORIES_BF16}
 
 # AdamW settings of the step (lecture: GPT-3 small peak lr 6e-4; betas (0.9, 0.95), eps 1e-8, wd 0.1)
 ADAMW = dict(lr=6e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)

@@ -330,3 +330,15 @@ def test_lr_schedule_boundaries_and_shape():
         oracle.lr_schedule(0, mx, mn, 10, 10)
     # no warm-up: the schedule starts at the peak
     assert oracle.lr_schedule(0, mx, mn, 0, tot) == mx
+
+
+def test_variant_flops_match_oracle_and_pages():
+    # the RMSNorm / RoPE / SwiGLU block: the bench's accounting equals the oracle's generic count with
+    # 4 D^2 + 3 D d_ff weights per block, and the oracle reproduces the page's 3.52 TFLOP per
+    # 1024-token sequence of the XL-shaped variant (CS336 page, section 4)
+    from decoder_only_transformer_train_amd import accounting
+    for L, C, F, T, V in [(4, 512, 1344, 256, 10000), (48, 1600, 4288, 1024, 50257), (2, 64, 192, 32, 256)]:
+        want = 3.0 * oracle.forward_matmul_flops(T, C, L, V, 4 * C * C + 3 * C * F, causal=True) / T
+        assert accounting.training_flops_per_token(L, C, T, V, F) == pytest.approx(want, rel=1e-14)
+    xl = oracle.forward_matmul_flops(1024, 1600, 48, 50257, 4 * 1600 * 1600 + 3 * 1600 * 4288)
+    assert xl / 1e12 == pytest.approx(3.52, abs=0.005)
