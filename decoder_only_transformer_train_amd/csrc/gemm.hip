@@ -1030,6 +1030,19 @@ void choose(int M, int N, int K, bool can_split, int dtype, int a_trans, int b_t
 
 }  // namespace
 
+hipError_t splits_reduce(const float* ws, int splits, int M, int N, float* out, int64_t ldc, int accumulate,
+                         hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  const int64_t total = (int64_t)M * N;
+  if ((N & 3) == 0 && (ldc & 3) == 0 && ((uintptr_t)out & 15) == 0 && ((uintptr_t)ws & 15) == 0)
+    hipLaunchKernelGGL(splitk_reduce4, dim3(cdiv(total / 4, 256)), dim3(256), 0, s, ws, splits, M, N, out, ldc,
+                       accumulate);
+  else
+    hipLaunchKernelGGL(splitk_reduce, dim3(cdiv(total, 256)), dim3(256), 0, s, ws, splits, M, N, out, ldc,
+                       accumulate);
+  return hipGetLastError();
+}
+
 int gemm_pick_splits(int M, int N, int K, int a_trans, int b_trans) {
   int tile = 2, splits = 1;
   choose(M, N, K, true, BF16, a_trans, b_trans, &tile, &splits);

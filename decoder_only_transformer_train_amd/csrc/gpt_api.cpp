@@ -105,6 +105,8 @@ struct gpt_ctx {
   int64_t head_cols = 0;
   float* head_skws = nullptr;  // split-K workspace of the head's dW blocks (head_skn floats)
   int64_t head_skn = 0;
+  float* head_tail = nullptr;  // partial sums of the head dW pass's split last round (head_tail_n floats)
+  int64_t head_tail_n = 0;
   float* ring;
   int ring_wr = 0, ring_rd = 0;
   // backward
@@ -313,6 +315,8 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->tok_loss = cv.take<float>(N * 4);
   x->tok_lse = cv.take<float>(N * 4);
   x->dF = cv.take<float>(N * C * 4);
+  x->head_tail_n = gk::lmhead_dw_tail_floats(x->dt, (int)N, (int)x->Vp, (int)C);
+  x->head_tail = x->head_tail_n ? cv.take<float>(x->head_tail_n * 4) : nullptr;
   if (head_gemm_mode()) {
     x->head_cols = head_block_cols(N, x->Vp, es);
     x->gchunk = cv.take<void>(N * x->head_cols * es);
@@ -555,7 +559,8 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
     // leave more CUs to the backward running beside it
     const char* cap = x->hside ? getenv("GPT_HEAD_DW_WGS") : nullptr;
     HIPCHK(gk::lmhead_dw(dtype, Fin, W, (int)N, (int)V, (int)C, y, tok_lse, scale, dW, dW_acc, ds,
-                         cap ? atoi(cap) : 0));
+                         cap ? atoi(cap) : 0, getenv("GPT_HEAD_DW_NOTAIL") ? nullptr : x->head_tail,
+                         x->head_tail_n));
     return 0;
   }
   const int64_t es = dtype == GPT_BF16 ? 2 : 4, cols = x->head_cols;
@@ -1151,6 +1156,8 @@ size_t gpt_lmhead_ce_ws_bytes(int64_t N, int64_t V, int64_t C, int32_t dtype) {
   // form of dW also the logit gradient of one block of vocabulary columns and a
   // split-K workspace
   size_t b = (size_t)(2 * align_up(N * 4, ALIGN) + ALIGN);
+  // the dW pass's split last round (bf16)
+  b += (size_t)align_up(gk::lmhead_dw_tail_floats(dtype, (int)N, (int)V, (int)C) * 4, ALIGN);
   if (head_gemm_mode()) {
     const int64_t es = dtype == GPT_BF16 ? 2 : 4, cols = head_block_cols(N, V, es);
     b += (size_t)align_up(N * cols * es, ALIGN);
@@ -1172,6 +1179,8 @@ int gpt_lmhead_ce(const void* X, const void* W, const int32_t* y, int64_t N, int
   float* tl = cv.take<float>(N * 4);
   float* tlse = cv.take<float>(N * 4);
   int* bad = cv.take<int>(ALIGN);
+  tmp.head_tail_n = gk::lmhead_dw_tail_floats(dtype, (int)N, (int)V, (int)C);
+  tmp.head_tail = tmp.head_tail_n ? cv.take<float>(tmp.head_tail_n * 4) : nullptr;
   if (head_gemm_mode()) {
     const int64_t es = dtype == GPT_BF16 ? 2 : 4;
     tmp.head_cols = head_block_cols(N, V, es);

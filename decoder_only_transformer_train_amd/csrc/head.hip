@@ -60,6 +60,11 @@ struct Args {
   float scale;       // gradients are those of scale * (sum of row losses)
   int* bad;          // pass 1: set to 1 when a target lies outside [0, V)
   int blk0;          // index of the launch's first block of fixed rows
+  // pass 2's split of the streamed rows (nz > 1): workgroup z * tb + b takes
+  // fixed block blk0 + b over streamed rows [z z_rows, (z + 1) z_rows) and
+  // writes its partial dW to out + z z_stride, row f at (f - out_row0) C
+  int nz, tb, z_rows, out_row0;
+  int64_t z_stride;
 };
 
 // Column groups of 64 dealt to the 4 waves in order: wave w gets ng of them from column c_lo.
@@ -364,7 +369,20 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
   wave_range(C, w, ng, c_lo);
   S.ng = __builtin_amdgcn_readfirstlane(ng);  // uniform in the wave: scalar branches
   c_lo = __builtin_amdgcn_readfirstlane(c_lo);
-  S.f0 = (a.blk0 + blockIdx.x) * (32 * NQT);  // first fixed row of the workgroup
+  int bidx = blockIdx.x;
+  if constexpr (MODE == 1) {
+    if (a.nz > 1) {
+      const int z = bidx / a.tb;
+      bidx -= z * a.tb;
+      const int r0 = z * a.z_rows;
+      a.str += (int64_t)r0 * a.C;
+      a.lse += r0;
+      a.y += r0;
+      a.n_str = min(a.z_rows, a.n_str - r0);
+      a.out += (int64_t)z * a.z_stride;
+    }
+  }
+  S.f0 = (a.blk0 + bidx) * (32 * NQT);  // first fixed row of the workgroup
   const int nblk = (a.n_str + BV - 1) / BV;
 
 #pragma unroll
@@ -511,7 +529,7 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
   for (int qt = 0; qt < NQT; ++qt) {
     const int fr = S.f0 + qt * 32 + c32;
     if (fr >= a.n_fix) continue;
-    float* orow = a.out + (int64_t)fr * C + c_lo;
+    float* orow = a.out + (int64_t)(fr - a.out_row0) * C + c_lo;
     if constexpr (MODE == 0) {
       const float lt = S.l[qt], zt = S.zy[qt];
       const float lse = (S.m[qt] + hw_log2(lt)) * LN2;
@@ -797,7 +815,38 @@ hipError_t launch_bf16_range(const Args& a, int ngmax, dim3 grid, hipStream_t s)
   return hipGetLastError();
 }
 
+// Pass 2's last round: with nfix blocks of W rows over the 256 CUs, a last
+// round of t <= 128 blocks would run nearly alone (V = 50304, 64-row blocks:
+// 786 = 3 x 256 + 18).  Those t blocks instead split the streamed rows into Z
+// parts (Z t about 256 workgroups) whose partial dW go to a workspace and are
+// summed in order afterwards.
+struct TailPlan {
+  int t = 0, Z = 1, z_rows = 0, row0 = 0, rows_valid = 0;
+  int64_t floats = 0;
+};
+TailPlan tail_plan(int N, int V, int C) {
+  TailPlan p;
+  const int ngmax = (C / 64 + 3) / 4;
+  const int rows = ngmax <= 3 ? 64 : 32;
+  const int nfix = (V + rows - 1) / rows;
+  const int t = nfix % 256;
+  if (nfix <= 256 || t == 0 || t > 128) return p;
+  const int Z = std::min(256 / t, std::max(1, N / (8 * BV)));  // at least 8 streamed blocks per part
+  if (Z < 2) return p;
+  p.t = t;
+  p.row0 = (nfix - t) * rows;
+  p.rows_valid = V - p.row0;
+  p.z_rows = ((N + Z - 1) / Z + BV - 1) / BV * BV;
+  p.Z = (N + p.z_rows - 1) / p.z_rows;
+  p.floats = (int64_t)p.Z * p.rows_valid * C;
+  return p;
+}
+
 }  // namespace hd
+
+int64_t lmhead_dw_tail_floats(int dtype, int N, int V, int C) {
+  return dtype == BF16 ? hd::tail_plan(N, V, C).floats : 0;
+}
 
 // bf16: up to 7 column groups of 64 per wave; fp32: the plain kernels keep 8 rows of C floats
 // plus a 256-row gradient chunk in LDS (40 KB at C = 1024)
@@ -831,7 +880,8 @@ hipError_t lmhead_fwd(int dtype, const void* F, const void* W, int N, int V, int
 }
 
 hipError_t lmhead_dw(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, const float* lse,
-                     float scale, float* dW, int accumulate, hipStream_t s, int max_wgs) {
+                     float scale, float* dW, int accumulate, hipStream_t s, int max_wgs, float* tail_ws,
+                     int64_t tail_floats) {
   if (V <= 0) return hipSuccess;
   if (N <= 0 || C <= 0 || C % 64 || C > lmhead_max_embd(dtype)) return hipErrorInvalidValue;
   if (dtype == BF16) {
@@ -847,7 +897,23 @@ hipError_t lmhead_dw(int dtype, const void* F, const void* W, int N, int V, int 
     a.out = dW;
     a.accumulate = accumulate;
     a.scale = scale;
-    return hd::launch_bf16<1>(a, s, max_wgs);
+    const hd::TailPlan tp = tail_ws ? hd::tail_plan(N, V, C) : hd::TailPlan{};
+    if (tp.t == 0 || tp.floats > tail_floats) return hd::launch_bf16<1>(a, s, max_wgs);
+    hd::Args m = a;  // the full rounds: W rows [0, row0)
+    m.n_fix = tp.row0;
+    if (hipError_t e = hd::launch_bf16<1>(m, s, max_wgs)) return e;
+    hd::Args t = a;  // the last blocks, split over the rows of F
+    const int ngmax = (C / 64 + 3) / 4, rows = ngmax <= 3 ? 64 : 32;
+    t.blk0 = tp.row0 / rows;
+    t.nz = tp.Z;
+    t.tb = tp.t;
+    t.z_rows = tp.z_rows;
+    t.out = tail_ws;
+    t.out_row0 = tp.row0;
+    t.z_stride = (int64_t)tp.rows_valid * C;
+    t.accumulate = 0;
+    if (hipError_t e = hd::launch_bf16_range<1>(t, ngmax, dim3(tp.Z * tp.t), s)) return e;
+    return splits_reduce(tail_ws, tp.Z, tp.rows_valid, C, dW + (int64_t)tp.row0 * C, C, accumulate, s);
   }
   const size_t sh = (size_t)(hd::FR * C + hd::FR * hd::FCH) * 4;
   hipLaunchKernelGGL(hd::head_f32_dw, dim3((V + hd::FR - 1) / hd::FR), dim3(256), sh, s, (const float*)F,

@@ -57,6 +57,9 @@ hipError_t gemm(const Gemm& g, hipStream_t s, hipEvent_t after_main = nullptr, h
 // split count a GEMM of this shape with an fp32 output would use (its split-K
 // workspace is gemm_pick_splits(...) * M * N floats when that is > 1)
 int gemm_pick_splits(int M, int N, int K, int a_trans, int b_trans);
+// out[m][n] (+)= sum over z < splits of ws[z][m][n] (fixed order); ws [splits][M][N], out row stride ldc
+hipError_t splits_reduce(const float* ws, int splits, int M, int N, float* out, int64_t ldc, int accumulate,
+                         hipStream_t s);
 
 // ---- LayerNorm (rms = 1: RMSNorm, mu = 0 and no shift; b may be null) ----
 // y = (x - mu) * rstd * g + b per row of C; x fp32 [rows][C]; y T; mu, rstd fp32 [rows]
@@ -123,9 +126,13 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, c
 int lmhead_max_embd(int dtype);
 hipError_t lmhead_fwd(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, float scale,
                       float* loss, float* lse, float* dF, int* bad, hipStream_t s);
-// max_wgs > 0 (bf16): at most that many workgroups, each looping over blocks of W rows
+// max_wgs > 0 (bf16): launches of at most that many workgroups.  tail_ws (bf16, nullable): at
+// least lmhead_dw_tail_floats(...) floats; with it the last partial round of W-row blocks is
+// split over the rows of F (partial sums there, then added in order)
 hipError_t lmhead_dw(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, const float* lse,
-                     float scale, float* dW, int accumulate, hipStream_t s, int max_wgs = 0);
+                     float scale, float* dW, int accumulate, hipStream_t s, int max_wgs = 0,
+                     float* tail_ws = nullptr, int64_t tail_floats = 0);
+int64_t lmhead_dw_tail_floats(int dtype, int N, int V, int C);
 // mean of n floats in fixed order -> out[0] (and ring[slot] if ring != null)
 hipError_t mean_f32(const float* x, int n, float* out, float* ring, int slot, hipStream_t s);
 

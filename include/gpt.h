@@ -196,7 +196,8 @@ int gpt_adamw_step(gpt_ctx* ctx, float lr, float beta1, float beta2, float eps,
  *   dW  device fp32 [V, C] (nullable): gradient w.r.t. W (overwritten).
  *   ws  device workspace of at least gpt_lmhead_ce_ws_bytes(N, V, C, dtype)
  *       bytes (0 for an invalid shape), 256-byte aligned.  It holds the
- *       per-row losses and log-sum-exps and the out-of-range flag.  The loss,
+ *       per-row losses and log-sum-exps, the out-of-range flag and (bf16)
+ *       the partial dW sums of the last, split round of the dW kernel.  The loss,
  *       the log-sum-exps and dX come from one pass that streams W through each
  *       workgroup and never stores a logit; dW comes from a second kernel that
  *       streams the rows of X past each block of W rows, recomputing the
