@@ -15,11 +15,10 @@ of K timed steps, each between torch.cuda.synchronize() calls; the line
 reports the median loop.  It carries tokens/s, MFU, the roofline of the
 dominant kernel (timed with HIP events on the library's stream in the last
 step of the last loop), the rates of a few more kernel classes (timed in
-extra steps after the loops).  The dominant kernel is the LM head's second
-pass (the tied dW, 3.99 ms of the step's 22.96 ms of kernel time when each
-kernel runs alone; then the first pass, 3.24 ms, and attention backward,
-1.45 ms); it runs on its own stream beside the backward, so its in-step time
-includes the CUs it shares and the fp64 CPU oracle timed on the GPU's own
+extra steps after the loops).  The dominant kernel is the LM head's first
+pass (loss, log-sum-exp and dF: 3.20 ms of the step's 21.95 ms of kernel time
+when each kernel runs alone; then the second pass, the tied dW, 3.10 ms in its
+two launches, and attention backward, 1.41 ms) and the fp64 CPU oracle timed on the GPU's own
 step-1 weights and window.
 
 The roofline's "traffic" (HBM bytes per launch of that kernel) comes from
@@ -51,7 +50,7 @@ PROFILE_CLASSES = ["gemm_qkv_fwd", "gemm_proj_fwd", "gemm_fc_fwd", "gemm_mlpproj
                    "layernorm_fwd", "layernorm_bwd", "head_fwd", "head_dz", "head_dw",
                    "bias_colsum", "param_reduce", "embed_bwd", "adamw"]
 # further classes reported beside the dominant one (one extra step each)
-MORE_CLASSES = ["head_fwd", "attn_bwd", "attn_fwd", "gemm_fc_fwd", "layernorm_bwd", "adamw"]
+MORE_CLASSES = ["head_dw", "attn_bwd", "attn_fwd", "gemm_fc_fwd", "layernorm_bwd", "adamw"]
 METRIC = "train tokens/sec + MFU, GPT-2 124M B=16 T=1024 bf16, 1×MI355X"
 
 WORKLOADS = {
@@ -346,7 +345,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true")
     # the dominant kernel class of the step (largest share of the step's kernel time)
-    ap.add_argument("--roofline-kernel", default="head_dw", choices=PROFILE_CLASSES)
+    ap.add_argument("--roofline-kernel", default="head_fwd", choices=PROFILE_CLASSES)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="after the timed steps, copy this many bytes device-to-device once")
     args = ap.parse_args()

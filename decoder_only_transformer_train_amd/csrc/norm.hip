@@ -21,13 +21,12 @@ constexpr int MAXV = 8;  // float4 slices per lane: C <= 2048
 // NV float4 slices per lane (C <= 256 NV): the registers, and so the
 // occupancy, follow the row width (with a fixed 8 slots: 132 VGPRs, 3 waves
 // per SIMD at C = 768)
-template <typename T, bool EMBED, int NV>
+template <typename T, bool EMBED, int NV, bool RMS>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x, const int32_t* __restrict__ tok,
                                                      const float* __restrict__ wte, const float* __restrict__ wpe,
                                                      int Tn, float* __restrict__ res0, const float* __restrict__ g,
                                                      const float* __restrict__ bb, T* __restrict__ y,
-                                                     float* __restrict__ mu, float* __restrict__ rs, int rows, int C,
-                                                     int rms) {
+                                                     float* __restrict__ mu, float* __restrict__ rs, int rows, int C) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -49,7 +48,8 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
         v[i] = load4(x + (int64_t)row * C + 4 * j);
       }
       gv[i] = load4(g + 4 * j);
-      bv[i] = rms ? make_float4(0.f, 0.f, 0.f, 0.f) : load4(bb + 4 * j);
+      if constexpr (RMS) bv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      else bv[i] = load4(bb + 4 * j);
     }
   }
   float s = 0.f;
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
       s += v[i].x + v[i].y + v[i].z + v[i].w;
     }
   }
-  const float mean = rms ? 0.f : wave_sum(s) / C;
+  const float mean = RMS ? 0.f : wave_sum(s) / C;
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -106,12 +106,12 @@ constexpr int LNB_ROWS = 32;
 // instead of spilling to scratch (C = 1024: 28-84 bytes per lane, C = 1600:
 // 520-592 at four per CU; C = 1600 takes NV = 7).  A lane
 // past the row (C not a multiple of 256) loads the last column slice and drops it.
-template <typename TY, typename T, int NV, bool DRES>
+template <typename TY, typename T, int NV, bool DRES, bool RMS>
 __global__ __launch_bounds__(256, NV <= 3 ? 4 : (NV <= 7 ? 2 : 1)) void ln_bwd_kernel(const TY* __restrict__ dy, const float* __restrict__ x,
                                                          const float* __restrict__ mu, const float* __restrict__ rs,
                                                          const float* __restrict__ g, const float* __restrict__ dres_in,
                                                          float* __restrict__ dres_out, T* __restrict__ dres_T,
-                                                         float* __restrict__ part, int rows, int C, int rms) {
+                                                         float* __restrict__ part, int rows, int C) {
   __shared__ float red[4][NV * 256];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256, NV <= 3 ? 4 : (NV <= 7 ? 2 : 1)) void ln_bwd_k
       pg[i].x += d.x * xh.x; pg[i].y += d.y * xh.y; pg[i].z += d.z * xh.z; pg[i].w += d.w * xh.w;
       pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
     }
-    const float m1 = rms ? 0.f : wave_sum(s1) / C, m2 = wave_sum(s2) / C;
+    const float m1 = RMS ? 0.f : wave_sum(s1) / C, m2 = wave_sum(s2) / C;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int64_t o = (int64_t)row * C + 4 * jj[i];
@@ -189,11 +189,11 @@ __global__ __launch_bounds__(256, NV <= 3 ? 4 : (NV <= 7 ? 2 : 1)) void ln_bwd_k
 // row, so a wave that runs ahead never overwrites sums still being read).  The
 // next row's loads are issued before this row's barrier.  Column partials need
 // no LDS reduction: no two threads of a workgroup own the same column.
-template <typename TY, typename T, int WPR, bool DRES>
+template <typename TY, typename T, int WPR, bool DRES, bool RMS>
 __global__ __launch_bounds__(64 * WPR, 8) void ln_bwd_rows_kernel(
     const TY* __restrict__ dy, const float* __restrict__ x, const float* __restrict__ mu,
     const float* __restrict__ rs, const float* __restrict__ g, const float* __restrict__ dres_in,
-    float* __restrict__ dres_out, T* __restrict__ dres_T, float* __restrict__ part, int rows, int rms) {
+    float* __restrict__ dres_out, T* __restrict__ dres_T, float* __restrict__ part, int rows) {
   constexpr int C = 256 * WPR;
   __shared__ float2 sums[2][WPR];
   const int lane = threadIdx.x & 63;
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(64 * WPR, 8) void ln_bwd_rows_kernel(
       t1 += v.x;
       t2 += v.y;
     }
-    const float m1 = rms ? 0.f : t1 / C, m2 = t2 / C;
+    const float m1 = RMS ? 0.f : t1 / C, m2 = t2 / C;
     const float4 out = make_float4(prev.x + r * (dxh.x - m1 - xh.x * m2), prev.y + r * (dxh.y - m1 - xh.y * m2),
                                    prev.z + r * (dxh.z - m1 - xh.z * m2), prev.w + r * (dxh.w - m1 - xh.w * m2));
     const int64_t o = (int64_t)row * C + col;
@@ -361,8 +361,12 @@ template <typename T, bool EMBED, int NV>
 void ln_fwd_launch(const float* x, const int32_t* tok, const float* wte, const float* wpe, int Tn, float* res0,
                    const float* g, const float* b, void* y, float* mu, float* rstd, int rows, int C, hipStream_t s,
                    int rms) {
-  hipLaunchKernelGGL((ln_fwd_kernel<T, EMBED, NV>), dim3(cdiv(rows, 4)), dim3(256), 0, s, x, tok, wte, wpe, Tn, res0,
-                     g, b, (T*)y, mu, rstd, rows, C, rms);
+  if (rms)
+    hipLaunchKernelGGL((ln_fwd_kernel<T, EMBED, NV, true>), dim3(cdiv(rows, 4)), dim3(256), 0, s, x, tok, wte, wpe,
+                       Tn, res0, g, b, (T*)y, mu, rstd, rows, C);
+  else
+    hipLaunchKernelGGL((ln_fwd_kernel<T, EMBED, NV, false>), dim3(cdiv(rows, 4)), dim3(256), 0, s, x, tok, wte, wpe,
+                       Tn, res0, g, b, (T*)y, mu, rstd, rows, C);
 }
 template <typename T, bool EMBED>
 hipError_t ln_fwd_nv(const float* x, const int32_t* tok, const float* wte, const float* wpe, int Tn, float* res0,
@@ -396,19 +400,31 @@ hipError_t embed_ln_fwd(int dtype, const int32_t* tok, const float* wte, const f
 
 int layernorm_bwd_blocks(int rows) { return cdiv(rows, LNB_ROWS); }
 
+// launch an instance of a LayerNorm-backward kernel with RMS chosen at run time
+template <typename TY, typename T, int NV, bool DRES, typename... A>
+void ln_bwd_launch(int rms, dim3 grid, hipStream_t s, A... args) {
+  if (rms) hipLaunchKernelGGL((ln_bwd_kernel<TY, T, NV, DRES, true>), grid, dim3(256), 0, s, args...);
+  else hipLaunchKernelGGL((ln_bwd_kernel<TY, T, NV, DRES, false>), grid, dim3(256), 0, s, args...);
+}
+template <typename TY, typename T, int WPR, bool DRES, typename... A>
+void ln_bwd_rows_launch(int rms, dim3 grid, hipStream_t s, A... args) {
+  if (rms) hipLaunchKernelGGL((ln_bwd_rows_kernel<TY, T, WPR, DRES, true>), grid, dim3(64 * WPR), 0, s, args...);
+  else hipLaunchKernelGGL((ln_bwd_rows_kernel<TY, T, WPR, DRES, false>), grid, dim3(64 * WPR), 0, s, args...);
+}
+
 template <int NV, bool DRES>
 hipError_t ln_bwd_nvd(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu, const float* rstd,
                       const float* g, const float* dres_in, float* dres_out, void* dres_T, float* part, int rows,
                       int C, int nblk, hipStream_t s, int rms) {
   if (dtype == BF16 && dy_is_t)
-    hipLaunchKernelGGL((ln_bwd_kernel<bf16, bf16, NV, DRES>), dim3(nblk), dim3(256), 0, s, (const bf16*)dy, x, mu,
-                       rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, C, rms);
+    ln_bwd_launch<bf16, bf16, NV, DRES>(rms, dim3(nblk), s, (const bf16*)dy, x, mu, rstd, g, dres_in, dres_out,
+                                        (bf16*)dres_T, part, rows, C);
   else if (dtype == BF16)
-    hipLaunchKernelGGL((ln_bwd_kernel<float, bf16, NV, DRES>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu,
-                       rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, C, rms);
+    ln_bwd_launch<float, bf16, NV, DRES>(rms, dim3(nblk), s, (const float*)dy, x, mu, rstd, g, dres_in, dres_out,
+                                         (bf16*)dres_T, part, rows, C);
   else
-    hipLaunchKernelGGL((ln_bwd_kernel<float, float, NV, DRES>), dim3(nblk), dim3(256), 0, s, (const float*)dy, x, mu,
-                       rstd, g, dres_in, dres_out, (float*)dres_T, part, rows, C, rms);
+    ln_bwd_launch<float, float, NV, DRES>(rms, dim3(nblk), s, (const float*)dy, x, mu, rstd, g, dres_in, dres_out,
+                                          (float*)dres_T, part, rows, C);
   return hipGetLastError();
 }
 template <int NV>
@@ -426,14 +442,14 @@ hipError_t ln_bwd_rows_d(int dtype, const void* dy, int dy_is_t, const float* x,
                          const float* g, const float* dres_in, float* dres_out, void* dres_T, float* part, int rows,
                          int nblk, hipStream_t s, int rms) {
   if (dtype == BF16 && dy_is_t)
-    hipLaunchKernelGGL((ln_bwd_rows_kernel<bf16, bf16, WPR, DRES>), dim3(nblk), dim3(64 * WPR), 0, s,
-                       (const bf16*)dy, x, mu, rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, rms);
+    ln_bwd_rows_launch<bf16, bf16, WPR, DRES>(rms, dim3(nblk), s, (const bf16*)dy, x, mu, rstd, g, dres_in,
+                                              dres_out, (bf16*)dres_T, part, rows);
   else if (dtype == BF16)
-    hipLaunchKernelGGL((ln_bwd_rows_kernel<float, bf16, WPR, DRES>), dim3(nblk), dim3(64 * WPR), 0, s,
-                       (const float*)dy, x, mu, rstd, g, dres_in, dres_out, (bf16*)dres_T, part, rows, rms);
+    ln_bwd_rows_launch<float, bf16, WPR, DRES>(rms, dim3(nblk), s, (const float*)dy, x, mu, rstd, g, dres_in,
+                                               dres_out, (bf16*)dres_T, part, rows);
   else
-    hipLaunchKernelGGL((ln_bwd_rows_kernel<float, float, WPR, DRES>), dim3(nblk), dim3(64 * WPR), 0, s,
-                       (const float*)dy, x, mu, rstd, g, dres_in, dres_out, (float*)dres_T, part, rows, rms);
+    ln_bwd_rows_launch<float, float, WPR, DRES>(rms, dim3(nblk), s, (const float*)dy, x, mu, rstd, g, dres_in,
+                                                dres_out, (float*)dres_T, part, rows);
   return hipGetLastError();
 }
 hipError_t layernorm_bwd(int dtype, const void* dy, int dy_is_t, const float* x, const float* mu,

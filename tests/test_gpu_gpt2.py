@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from decoder_only_transformer_train_amd import binding, configs, synthetic
-from gpu_util import announce, context, cosine, init_for
+from gpu_util import announce, context, cosine, init_for, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -74,7 +74,10 @@ def test_gpt2_124m_bench_batch_sampled_rows():
         announce(f"oracle row {b}")
         ref, per, _ = oracle.forward(p, x[b:b + 1], y[b:b + 1], cfg.n_head, keep=False)
         assert abs(rows[b].mean() - ref) <= 2e-2
-        assert np.abs(rows[b] - per[0]).max() <= 0.15
+        # per position: the bf16 losses as a vector against the oracle's (relative L2), and the
+        # positions' deviations from the row mean by cosine (the benchmark spec's cosine criterion)
+        assert rel_err(rows[b], per[0]) <= 5e-3, rel_err(rows[b], per[0])
+        assert cosine(rows[b] - rows[b].mean(), per[0] - per[0].mean()) >= 0.99
     # lecture: the loss at initialisation is about ln V
     assert abs(loss - np.log(cfg.padded_vocab)) < 0.25
 
