@@ -350,7 +350,7 @@ def main():
                     help="after the timed steps, copy this many bytes device-to-device once")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.repeats < 1 or args.warmup < 0:

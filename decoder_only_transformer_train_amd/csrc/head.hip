@@ -44,6 +44,7 @@ namespace gk {
 namespace hd {
 using namespace mx;
 
+#define SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
 constexpr int BV = 32;          // streamed rows per block
 constexpr float HEADROOM = 64.f; // pass 1: p = 2^(z log2e - m) may reach 2^64 before a sweep is redone
 
@@ -174,6 +175,35 @@ struct Loader {
     tail(blk, st);
   }
   static constexpr int PER_BLOCK = Slice<NG>::NLD + (MODE ? 2 : 0);  // load instructions per block
+
+  // The same loads through descriptors that start at block blk (built with
+  // scalar arithmetic once per block, so a load needs no address arithmetic):
+  // rows past the end of the streamed rows, a whole block past it included,
+  // read zeros.
+  const bf16* str;
+  const float* lse;
+  const int32_t* yv;
+  int n_str, C;
+  struct Block {
+    rsrc_t rs, rl, ry;
+  };
+  __device__ __forceinline__ Block block(int blk) const {
+    const int left = max(n_str - blk * BV, 0);
+    Block b;
+    b.rs = make_rsrc(str + (int64_t)blk * BV * C, (int64_t)left * C * 2);
+    if constexpr (MODE == 1) {
+      b.rl = make_rsrc(lse + (int64_t)blk * BV, (int64_t)left * 4);
+      b.ry = make_rsrc(yv + (int64_t)blk * BV, (int64_t)left * 4);
+    }
+    return b;
+  }
+  __device__ __forceinline__ void one(int i, const Block& b, char* st) const { dma16(b.rs, st + i * 1024, off[i]); }
+  __device__ __forceinline__ void tail(const Block& b, char* st) const {
+    if constexpr (MODE == 1) {
+      dma4(b.rl, st + Slice<NG>::BYTES, (uint32_t)lane * 4);
+      dma4(b.ry, st + Slice<NG>::BYTES + 256, (uint32_t)lane * 4);
+    }
+  }
 };
 
 // second product over this wave's columns: O^T[c][fixed] += (block^T)[c][streamed] P^T[streamed][fixed]
@@ -201,62 +231,75 @@ __device__ __forceinline__ void second_product(const char* __restrict__ rd, cons
   }
 }
 
-// One streamed block (its slice in rd, streamed rows r0 ..):
-//  1. partial z^T tiles over this wave's columns (z[qt][e]: streamed row
-//     r0 + crow(e, g), fixed row f0 + 32 qt + c32); meanwhile, when refill >= 0,
-//     block `refill` is loaded into wr (one instruction per k-step: a wave that
-//     issues its loads back to back stalls at issue);
-//  2. through LDS, wave w adds accumulator quarter w (e = 4 w .. 4 w + 3, the
-//     streamed rows 8 w + 4 g + i) over the 4 waves, in wave order, and turns
-//     it into bf16 probabilities (pass 1, against the row's reference m) or
-//     gradients (pass 2); the quarters go back through LDS and every wave
-//     assembles the B fragments of the second product from them.
-// At block 0 of pass 1 (first), the reference m of each fixed row is set to
-// the block's maximum, exchanged through LDS.  The pointers are distinct and
-// __restrict__, so the compiler need not wait for the loads into wr before
-// the LDS accesses here.
-template <int NG, int NQT, int MODE>
-__device__ __forceinline__ void block_p(const char* __restrict__ rd, char* __restrict__ wr, int refill,
-                                        const Loader<NG, MODE>& ld, float4* __restrict__ part,
-                                        uint2* __restrict__ pq, float* __restrict__ colv, const Args& a, int r0,
-                                        bool first, State<NG, NQT>& S, uint4 (&pb)[NQT][2]) {
-  const int lane = S.lane, w = S.w, g = S.g, c32 = S.c32;
-  {
-    f32x16 z[NQT];
+// Partial z^T tiles of one streamed block over this wave's columns (z[qt][e]:
+// streamed row r0 + crow(e, g), fixed row f0 + 32 qt + c32).  Block `refill`
+// is loaded into wr meanwhile, one instruction per k-step (a wave that issues
+// its loads back to back stalls at issue): when refill >= 0, or always with
+// ALWAYS (a block past the end of the streamed rows loads zeros).
+// Every k-step runs in every wave, also past a wave's own columns (fewer
+// groups than NG): those k-steps have zero fixed fragments, and the slot data
+// there is real memory from the loads, so it is finite; the waves meet at every
+// block and wait for the widest one anyway.
+template <int NG, int NQT, int MODE, bool ALWAYS>
+__device__ __forceinline__ void z_partials(const char* __restrict__ rd, char* __restrict__ wr, int refill,
+                                           const Loader<NG, MODE>& ld, const State<NG, NQT>& S,
+                                           f32x16 (&z)[NQT]) {
+  const int g = S.g, c32 = S.c32;
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) zero16(z[qt]);
-    // Every k-step runs in every wave, also past a wave's own columns (fewer
-    // groups than NG): those k-steps have zero fixed fragments, and the slot
-    // data there is real memory from the loads, so it is finite; the waves meet
-    // at every block and wait for the widest one anyway.
-    // the fragment of k-step ks + 2 is read while k-step ks's products run
-    uint4 af[3];
-    af[0] = frag_row<NG>(rd, c32, 0, g);
-    af[1] = frag_row<NG>(rd, c32, 1, g);
+  for (int qt = 0; qt < NQT; ++qt) zero16(z[qt]);
+  // the fragment of k-step ks + 2 is read while k-step ks's products run
+  uint4 af[3];
+  af[0] = frag_row<NG>(rd, c32, 0, g);
+  af[1] = frag_row<NG>(rd, c32, 1, g);
 #pragma unroll
-    for (int ks = 0; ks < NG * 4; ++ks) {
-      if (ks + 2 < NG * 4) af[(ks + 2) % 3] = frag_row<NG>(rd, c32, ks + 2, g);
-      if (refill >= 0) ld.one(ks, refill, wr);  // NLD == 4 NG == the number of k-steps
-      asm volatile("" ::: "memory");
+  for (int ks = 0; ks < NG * 4; ++ks) {
+    if (ks + 2 < NG * 4) af[(ks + 2) % 3] = frag_row<NG>(rd, c32, ks + 2, g);
+    if (ALWAYS || refill >= 0) ld.one(ks, refill, wr);  // NLD == 4 NG == the number of k-steps
+    asm volatile("" ::: "memory");
 #pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) mma32(z[qt], af[ks % 3], S.qf[qt][ks]);  // serves every fixed tile
-    }
-    if (refill >= 0) ld.tail(refill, wr);
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4)
-        part[((w * NQT + qt) * 4 + e4) * 64 + lane] =
-            make_float4(z[qt][4 * e4], z[qt][4 * e4 + 1], z[qt][4 * e4 + 2], z[qt][4 * e4 + 3]);
+    for (int qt = 0; qt < NQT; ++qt) mma32(z[qt], af[ks % 3], S.qf[qt][ks]);  // serves every fixed tile
   }
-  lds_barrier();
+  if (ALWAYS || refill >= 0) ld.tail(refill, wr);
+}
+
+template <int NQT>
+__device__ __forceinline__ void write_part(float4* __restrict__ part, const f32x16 (&z)[NQT], int w, int lane) {
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4)
+      part[((w * NQT + qt) * 4 + e4) * 64 + lane] =
+          make_float4(z[qt][4 * e4], z[qt][4 * e4 + 1], z[qt][4 * e4 + 2], z[qt][4 * e4 + 3]);
+}
+
+// After the partial tiles of a block are in `part` (and a barrier): wave w adds
+// accumulator quarter w (e = 4 w .. 4 w + 3, the streamed rows 8 w + 4 g + i)
+// over the 4 waves, in wave order, and turns it into bf16 probabilities (pass
+// 1, against the row's reference m) or gradients (pass 2, from the block rows'
+// log-sum-exps l4 and targets y4 of those rows) in pq.  At block 0 of pass 1
+// (first), the reference m of each fixed row is set to the block's maximum,
+// exchanged through LDS.
+// this wave's quarter of the 4 waves' partial tiles (pp[qt][v]: wave v's)
+template <int NQT>
+__device__ __forceinline__ void read_quarter(const float4* __restrict__ part, int w, int lane, float4 (&pp)[NQT][4]) {
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) pp[qt][v] = part[((v * NQT + qt) * 4 + w) * 64 + lane];
+}
+
+template <int NG, int NQT, int MODE>
+__device__ __forceinline__ void quarter_p(const float4 (&pp)[NQT][4], uint2* __restrict__ pq,
+                                          float* __restrict__ colv, const Args& a, int r0, bool first,
+                                          float4 l4, int4 y4, State<NG, NQT>& S) {
+  const int lane = S.lane, w = S.w, g = S.g, c32 = S.c32;
   float q[NQT][4];  // this wave's quarter of z: streamed rows r0 + 8 w + 4 g + i
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
-    float4 s4 = part[(qt * 4 + w) * 64 + lane];
+    float4 s4 = pp[qt][0];
 #pragma unroll
     for (int v = 1; v < 4; ++v) {
-      const float4 p4 = part[((v * NQT + qt) * 4 + w) * 64 + lane];
+      const float4 p4 = pp[qt][v];
       s4.x += p4.x;
       s4.y += p4.y;
       s4.z += p4.z;
@@ -309,10 +352,6 @@ __device__ __forceinline__ void block_p(const char* __restrict__ rd, char* __res
     }
   } else {
     // pass 2: g = scale (exp(z - lse) - [y == v]); F rows past N (loaded as zeros) give 0
-    const float* sl = reinterpret_cast<const float*>(rd + Slice<NG>::BYTES);
-    const int* sy = reinterpret_cast<const int*>(rd + Slice<NG>::BYTES + 256);
-    const float4 l4 = *reinterpret_cast<const float4*>(sl + 8 * w + 4 * g);
-    const int4 y4 = *reinterpret_cast<const int4*>(sy + 8 * w + 4 * g);
     const float lv[4] = {l4.x * LOG2E, l4.y * LOG2E, l4.z * LOG2E, l4.w * LOG2E};
     const int yv[4] = {y4.x, y4.y, y4.z, y4.w};
 #pragma unroll
@@ -328,7 +367,11 @@ __device__ __forceinline__ void block_p(const char* __restrict__ rd, char* __res
       pq[(qt * 4 + w) * 64 + lane] = bitcast<uint2>(v);
     }
   }
-  lds_barrier();
+}
+
+// the B fragments of the second product, assembled from the 4 quarters in pq
+template <int NQT>
+__device__ __forceinline__ void read_pb(const uint2* __restrict__ pq, int lane, uint4 (&pb)[NQT][2]) {
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
@@ -336,6 +379,180 @@ __device__ __forceinline__ void block_p(const char* __restrict__ rd, char* __res
       const uint2 lo = pq[(qt * 4 + 2 * hh) * 64 + lane], hi = pq[(qt * 4 + 2 * hh + 1) * 64 + lane];
       pb[qt][hh] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
+}
+
+// the streamed rows' log-sum-exps and targets of this lane's quarter (pass 2: the stage tail)
+template <int NG, int MODE>
+__device__ __forceinline__ void quarter_tail(const char* rd, int w, int g, float4& l4, int4& y4) {
+  if constexpr (MODE == 1) {
+    const float* sl = reinterpret_cast<const float*>(rd + Slice<NG>::BYTES);
+    const int* sy = reinterpret_cast<const int*>(rd + Slice<NG>::BYTES + 256);
+    l4 = *reinterpret_cast<const float4*>(sl + 8 * w + 4 * g);
+    y4 = *reinterpret_cast<const int4*>(sy + 8 * w + 4 * g);
+  } else {
+    l4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    y4 = make_int4(0, 0, 0, 0);
+  }
+}
+
+// One streamed block (its slice in rd, streamed rows r0 ..), in sequence: the
+// partial z tiles (loading block `refill` into wr meanwhile), their sum and
+// softmax through LDS, and the B fragments of the second product.  The
+// pointers are distinct and __restrict__, so the compiler need not wait for
+// the loads into wr before the LDS accesses here.
+template <int NG, int NQT, int MODE>
+__device__ __forceinline__ void block_p(const char* __restrict__ rd, char* __restrict__ wr, int refill,
+                                        const Loader<NG, MODE>& ld, float4* __restrict__ part,
+                                        uint2* __restrict__ pq, float* __restrict__ colv, const Args& a, int r0,
+                                        bool first, State<NG, NQT>& S, uint4 (&pb)[NQT][2]) {
+  {
+    f32x16 z[NQT];
+    z_partials<NG, NQT, MODE, false>(rd, wr, refill, ld, S, z);
+    write_part<NQT>(part, z, S.w, S.lane);
+  }
+  lds_barrier();
+  float4 l4;
+  int4 y4;
+  quarter_tail<NG, MODE>(rd, S.w, S.g, l4, y4);
+  float4 pp[NQT][4];
+  read_quarter<NQT>(part, S.w, S.lane, pp);
+  quarter_p<NG, NQT, MODE>(pp, pq, colv, a, r0, first, l4, y4, S);
+  lds_barrier();
+  read_pb<NQT>(pq, S.lane, pb);
+}
+
+// Element (qt, i) of this wave's quarter of a block past a pass's reference
+// block (streamed row rq + i): the bf16 probability (pass 1, with the running
+// sum, maximum and target logit) or gradient (pass 2, from the row's
+// log-sum-exp lv in log2 units and target yv) into v[i]; the same arithmetic,
+// in the same order, as quarter_p.
+template <int NG, int NQT, int MODE>
+__device__ __forceinline__ void quarter_elem(float qv, int qt, int i, int rq, const Args& a, float lv, int yv,
+                                             State<NG, NQT>& S, bf16x4& v) {
+  if constexpr (MODE == 0) {
+    if (rq + i >= a.n_str) qv = NEG_INF;
+    if (rq + i == S.yq[qt]) S.zy[qt] = qv;
+    S.seen[qt] = fmaxf(S.seen[qt], qv * LOG2E);
+    const bf16 p = (bf16)hw_exp2(fmaf(qv, LOG2E, -S.m[qt]));
+    v[i] = p;
+    S.l[qt] += (float)p;
+  } else {
+    const int vq = S.f0 + qt * 32 + S.c32;
+    float p = hw_exp2(fmaf(qv, LOG2E, -lv)) - (yv == vq ? 1.f : 0.f);
+    if (rq + i >= a.n_str) p = 0.f;
+    v[i] = (bf16)(p * a.scale);
+  }
+}
+
+// Software-pipelined step j of a sweep (block j in cur, block j + 1 in nxt;
+// block j's transposed fragments T and its quarter's row scalars l4, y4 are
+// already in registers, read during step j - 1):
+//  phase 1: the partial z tiles of block j + 1 (NEXT) on the matrix cores,
+//    loading block j + 2 into cur meanwhile, interleaved with the sum and
+//    softmax of block j (its partials in `part`) on the vector ALUs;
+//  phase 2: the second product of block j, interleaved with the reads of block
+//    j + 1's transposed fragments and row scalars into T, l4, y4 and the
+//    store of block j + 1's partials into `part`.
+// Barrier 1 separates pq's writes from its reads and part's reads from its
+// rewrite; barrier 2 ends the step (LDS reads of nxt complete, part written).
+// Block j + 1's loads were issued in step j - 1; the loads of block j + 2 go to
+// cur, whose reads ended with step j - 1.  A block past the end loads zeros.
+template <int NG, int NQT, int MODE, bool FIRST, bool NEXT>
+__device__ __forceinline__ void pipe_step(char* __restrict__ cur, const char* __restrict__ nxt, int j,
+                                          const Loader<NG, MODE>& ld, float4* __restrict__ part,
+                                          uint2* __restrict__ pq, float* __restrict__ colv, const Args& a,
+                                          State<NG, NQT>& S, uint4 (&T)[NG * 4], float4& l4, int4& y4) {
+  constexpr int NT = NG * 2, KS = NG * 4;
+  const int lane = S.lane, g = S.g, c32 = S.c32;
+  f32x16 zn[NQT];
+  float4 pp[NQT][4];
+  if constexpr (NEXT && !FIRST && KS >= 6 * NQT) {
+    // Explicitly interleaved: k-step ks issues its fragment read, one slice
+    // load and its MFMAs, and then a slice of block j's vector work (the sums
+    // of quarter qt at ks = qt, element e at ks = NQT + e, the stores of quarter
+    // qt at ks = 5 NQT + qt); scheduling barriers keep the slices in place.
+    wait_vm<0>();  // block j + 1 has landed in nxt
+    const typename Loader<NG, MODE>::Block nb = ld.block(j + 2);
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) zero16(zn[qt]);
+    const int rq = j * BV + 8 * S.w + 4 * g;
+    const float lv[4] = {l4.x * LOG2E, l4.y * LOG2E, l4.z * LOG2E, l4.w * LOG2E};
+    const int yv[4] = {y4.x, y4.y, y4.z, y4.w};
+    float4 q4[NQT];
+    bf16x4 v[NQT];
+    uint4 af[3];
+    af[0] = frag_row<NG>(nxt, c32, 0, g);
+    af[1] = frag_row<NG>(nxt, c32, 1, g);
+    read_quarter<NQT>(part, S.w, lane, pp);  // ahead of the loads into cur, which the compiler may take to alias
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 2 < KS) af[(ks + 2) % 3] = frag_row<NG>(nxt, c32, ks + 2, g);
+      ld.one(ks, nb, cur);
+      if (ks == KS - 1) ld.tail(nb, cur);
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) mma32(zn[qt], af[ks % 3], S.qf[qt][ks]);
+      if (ks < NQT) {
+        float4 s4 = pp[ks][0];
+#pragma unroll
+        for (int u = 1; u < 4; ++u) {
+          s4.x += pp[ks][u].x;
+          s4.y += pp[ks][u].y;
+          s4.z += pp[ks][u].z;
+          s4.w += pp[ks][u].w;
+        }
+        q4[ks] = s4;
+      } else if (ks < 5 * NQT) {
+        const int e = ks - NQT, qt = e >> 2, i = e & 3;
+        const float qv = i == 0 ? q4[qt].x : i == 1 ? q4[qt].y : i == 2 ? q4[qt].z : q4[qt].w;
+        quarter_elem<NG, NQT, MODE>(qv, qt, i, rq, a, lv[i], yv[i], S, v[qt]);
+      } else if (ks < 6 * NQT) {
+        const int qt = ks - 5 * NQT;
+        pq[(qt * 4 + S.w) * 64 + lane] = bitcast<uint2>(v[qt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    read_quarter<NQT>(part, S.w, lane, pp);
+    if constexpr (NEXT) {
+      wait_vm<0>();  // block j + 1 has landed in nxt
+      const typename Loader<NG, MODE>::Block nb = ld.block(j + 2);
+      uint4 af[3];
+      af[0] = frag_row<NG>(nxt, c32, 0, g);
+      af[1] = frag_row<NG>(nxt, c32, 1, g);
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) zero16(zn[qt]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 2 < KS) af[(ks + 2) % 3] = frag_row<NG>(nxt, c32, ks + 2, g);
+        ld.one(ks, nb, cur);
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) mma32(zn[qt], af[ks % 3], S.qf[qt][ks]);
+      }
+      ld.tail(nb, cur);
+    }
+    quarter_p<NG, NQT, MODE>(pp, pq, colv, a, j * BV, FIRST, l4, y4, S);
+  }
+  lds_barrier();
+  uint4 pb[NQT][2];
+  read_pb<NQT>(pq, lane, pb);
+  if constexpr (NEXT) write_part<NQT>(part, zn, S.w, lane);
+#pragma unroll
+  for (int i = 0; i < 2 * NT; ++i) {
+    const int hh = i / NT, ct = i % NT;
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) mma32(S.O[qt][ct], T[i], pb[qt][hh]);
+    if constexpr (NEXT) T[i] = frag_tr<NG>(nxt, ct * 32, hh * 16, lane);
+  }
+  if constexpr (NEXT) {
+    quarter_tail<NG, MODE>(nxt, S.w, g, l4, y4);
+#pragma unroll
+    for (int i = 0; i < 2 * NT; ++i) {
+      SGB(0x008, NQT);
+      SGB(0x100, 1);
+      if (i < 8) SGB(0x200, 1);  // the partial-tile stores
+    }
+  }
+  lds_barrier();
 }
 
 // Sum (or max) of a per-lane value over the 4 waves and the two lane halves,
@@ -351,7 +568,7 @@ __device__ __forceinline__ float wg_column(float v, float* __restrict__ colv, in
   return MAX ? halves_max(t) : halves_sum(t);
 }
 
-template <int NG, int NQT, int ST, int MODE>
+template <int NG, int NQT, int ST, int MODE, bool PIPE>
 __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
   using L = Lds<NG, NQT, ST, MODE>;
   using SL = Slice<NG>;
@@ -360,7 +577,7 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
   State<NG, NQT> S;
   const int t = threadIdx.x;
   S.lane = t & 63;
-  S.w = t >> 6;
+  S.w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform in the wave: scalar LDS bases
   S.g = S.lane >> 5;
   S.c32 = S.lane & 31;
   const int lane = S.lane, w = S.w, g = S.g, c32 = S.c32;
@@ -416,6 +633,11 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
   ld.ry = make_rsrc(MODE == 1 ? (const void*)a.y : nullptr, MODE == 1 ? (int64_t)a.n_str * 4 : 0);
   ld.lane = lane;
   ld.blk_bytes = (uint32_t)(BV * C * 2);
+  ld.str = a.str;
+  ld.lse = a.lse;
+  ld.yv = a.y;
+  ld.n_str = a.n_str;
+  ld.C = C;
 #pragma unroll
   for (int i = 0; i < SL::NLD; ++i) {
     const int q = i * 1024 + 16 * lane;
@@ -452,7 +674,7 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
         if (s2 < nblk) ld.all(s2, stage(s2));
     }
   };
-  prologue();
+  if constexpr (!PIPE) prologue();
   // the stage to refill while block j (in stage sc) is used, and the block it gets (-1: none)
   auto refill_of = [&](int j, int sc, char*& wr) {
     if constexpr (ST == 1) {
@@ -462,6 +684,49 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
       wr = stage(sc == 0 ? ST - 1 : sc - 1);
       return j + ST - 1 < nblk ? j + ST - 1 : -1;
     }
+  };
+
+  // The software-pipelined sweep over the streamed blocks; first: the pass's
+  // first (pass 1 sets the reference m of each fixed row at its block 0).
+  auto sweep_pipe = [&](bool first) {
+    static_assert(!PIPE || ST == 2, "the pipelined sweep holds blocks j and j + 1 in two stages");
+    ld.all(0, stage(0));
+    ld.all(1, stage(1));  // past the end of the streamed rows: zeros, never read
+    wait_vm<LPB>();       // block 0 has landed
+    uint4 T[NG * 4];
+    float4 l4;
+    int4 y4;
+    {
+      f32x16 z[NQT];
+      z_partials<NG, NQT, MODE, false>(stage(0), stage(1), -1, ld, S, z);
+      write_part<NQT>(part, z, w, lane);
+#pragma unroll
+      for (int i = 0; i < NG * 4; ++i)
+        T[i] = frag_tr<NG>(stage(0), (i % (NG * 2)) * 32, (i / (NG * 2)) * 16, lane);
+      quarter_tail<NG, MODE>(stage(0), w, S.g, l4, y4);
+    }
+    lds_barrier();
+    const bool f0 = MODE == 0 && first;
+    if (nblk == 1) {
+      if (f0) pipe_step<NG, NQT, MODE, true, false>(stage(0), stage(1), 0, ld, part, pq, colv, a, S, T, l4, y4);
+      else pipe_step<NG, NQT, MODE, false, false>(stage(0), stage(1), 0, ld, part, pq, colv, a, S, T, l4, y4);
+    } else {
+      if (f0) pipe_step<NG, NQT, MODE, true, true>(stage(0), stage(1), 0, ld, part, pq, colv, a, S, T, l4, y4);
+      else pipe_step<NG, NQT, MODE, false, true>(stage(0), stage(1), 0, ld, part, pq, colv, a, S, T, l4, y4);
+      // two steps per trip, so that each step's stages are fixed offsets from the wave's base
+      int j = 1;
+      for (; j + 2 < nblk; j += 2) {
+        pipe_step<NG, NQT, MODE, false, true>(stage(1), stage(0), j, ld, part, pq, colv, a, S, T, l4, y4);
+        pipe_step<NG, NQT, MODE, false, true>(stage(0), stage(1), j + 1, ld, part, pq, colv, a, S, T, l4, y4);
+      }
+      if (j + 1 < nblk) {
+        pipe_step<NG, NQT, MODE, false, true>(stage(1), stage(0), j, ld, part, pq, colv, a, S, T, l4, y4);
+        ++j;
+      }
+      if (j & 1) pipe_step<NG, NQT, MODE, false, false>(stage(1), stage(0), j, ld, part, pq, colv, a, S, T, l4, y4);
+      else pipe_step<NG, NQT, MODE, false, false>(stage(0), stage(1), j, ld, part, pq, colv, a, S, T, l4, y4);
+    }
+    wait_vm<0>();  // the loads past the end have landed before the stages are reloaded or released
   };
 
   uint4 pb[NQT][2];
@@ -480,18 +745,22 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
         S.l[qt] = 0.f;
         S.seen[qt] = NEG_INF;
       }
-      if (attempt > 0) prologue();  // the sweep starts over: reload the first blocks
-      int sc = 0;
-      for (int j = 0; j < nblk; ++j) {
-        char* wr;
-        const int rf = refill_of(j, sc, wr);
-        wait_block(j);
-        block_p<NG, NQT, MODE>(stage(sc), wr, rf, ld, part, pq, colv, a, j * BV, j == 0 && attempt == 0,
-                               S, pb);
-        second_product<NG, NQT>(stage(sc), pb, S);
-        if constexpr (ST == 1)
-          if (j + 1 < nblk) ld.all(j + 1, wbase);
-        sc = sc + 1 == ST ? 0 : sc + 1;
+      if constexpr (PIPE) {
+        sweep_pipe(attempt == 0);
+      } else {
+        if (attempt > 0) prologue();  // the sweep starts over: reload the first blocks
+        int sc = 0;
+        for (int j = 0; j < nblk; ++j) {
+          char* wr;
+          const int rf = refill_of(j, sc, wr);
+          wait_block(j);
+          block_p<NG, NQT, MODE>(stage(sc), wr, rf, ld, part, pq, colv, a, j * BV, j == 0 && attempt == 0,
+                                 S, pb);
+          second_product<NG, NQT>(stage(sc), pb, S);
+          if constexpr (ST == 1)
+            if (j + 1 < nblk) ld.all(j + 1, wbase);
+          sc = sc + 1 == ST ? 0 : sc + 1;
+        }
       }
       bool redo = false;
       float seen[NQT];
@@ -510,6 +779,8 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
       S.l[qt] = wg_column<false>(S.l[qt], colv, w, lane);
       S.zy[qt] = wg_column<false>(S.zy[qt], colv, w, lane);  // exactly one quarter saw the target
     }
+  } else if constexpr (PIPE) {
+    sweep_pipe(true);
   } else {
     int sc = 0;
     for (int j = 0; j < nblk; ++j) {
@@ -802,14 +1073,23 @@ hipError_t launch_bf16(const Args& a, hipStream_t s, int max_wgs) {
 
 template <int MODE>
 hipError_t launch_bf16_range(const Args& a, int ngmax, dim3 grid, hipStream_t s) {
+  // the software-pipelined sweep where its registers fit (GPT_HEAD_PIPE=0: the sequential one)
+  const char* e = getenv("GPT_HEAD_PIPE");
+  const bool pipe = !(e && e[0] == '0');
   switch (ngmax) {
-    case 1: hipLaunchKernelGGL((head_kernel<1, 2, 3, MODE>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((head_kernel<2, 2, 3, MODE>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((head_kernel<3, 2, 2, MODE>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((head_kernel<4, 1, 2, MODE>), grid, dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((head_kernel<5, 1, 1, MODE>), grid, dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((head_kernel<6, 1, 1, MODE>), grid, dim3(256), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((head_kernel<7, 1, 1, MODE>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((head_kernel<1, 2, 3, MODE, false>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((head_kernel<2, 2, 3, MODE, false>), grid, dim3(256), 0, s, a); break;
+    case 3:
+      if (pipe) hipLaunchKernelGGL((head_kernel<3, 2, 2, MODE, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((head_kernel<3, 2, 2, MODE, false>), grid, dim3(256), 0, s, a);
+      break;
+    case 4:
+      if (pipe) hipLaunchKernelGGL((head_kernel<4, 1, 2, MODE, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((head_kernel<4, 1, 2, MODE, false>), grid, dim3(256), 0, s, a);
+      break;
+    case 5: hipLaunchKernelGGL((head_kernel<5, 1, 1, MODE, false>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((head_kernel<6, 1, 1, MODE, false>), grid, dim3(256), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((head_kernel<7, 1, 1, MODE, false>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -107,3 +107,50 @@ def test_head_target_out_of_range_is_erange():
     rl, _, _, _ = oracle.lmhead_ce(X, W, y)
     assert abs(loss.item() - rl) <= 2e-2
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("N,V,C", [(2048, 50257, 768), (333, 1000, 768), (200, 32, 768), (130, 64, 768),
+                                   (97, 95, 768), (333, 129, 1024), (4352, 300, 1024)])
+def test_head_pipelined_sweep_matches_sequential(N, V, C, monkeypatch):
+    # C = 768 and 1024 run the software-pipelined sweep (GPT_HEAD_PIPE=0: the sequential one); it
+    # forms the same products and sums in the same order, so every output has the same bits.
+    # Streamed blocks per sweep: V / 32 = 1, 2, 3, 5, 32, 1571 (pass 1), N / 32 = 4 .. 136 (pass 2).
+    import torch
+    announce(f"head pipelined vs sequential N={N} V={V} C={C}")
+    X, W, y = synthetic.lmhead_inputs(N, V, C, seed=6)
+    dev = to_dev(X, W, y, binding.GPT_BF16)
+    loss1, dX1, dW1 = binding.lmhead_ce(*dev, binding.GPT_BF16)
+    monkeypatch.setenv("GPT_HEAD_PIPE", "0")
+    loss0, dX0, dW0 = binding.lmhead_ce(*dev, binding.GPT_BF16)
+    assert loss1.item() == loss0.item()
+    assert torch.equal(dX1, dX0)
+    assert torch.equal(dW1, dW0)
+    rl, _, rdX, rdW = oracle.lmhead_ce(X, W, y)
+    assert abs(loss1.item() - rl) <= 2e-2
+    assert cosine(dX1.cpu().numpy(), rdX) >= 0.999
+    assert cosine(dW1.cpu().numpy(), rdW) >= 0.999
+
+
+@pytest.mark.parametrize("C", [768, 1024, 64])
+def test_head_softmax_reference_redo(C, monkeypatch):
+    # rows whose largest logit (about 0.13 |x|^2, 100 at C = 768) lies in a W block after the
+    # first and exceeds that block's maximum by far more than 2^64 in exp2 units: their sweep
+    # is redone with the larger reference; the loss and gradients still match the oracle
+    import torch
+    announce(f"head softmax reference redo C={C}")
+    N, V = 256, 1000
+    X, W, y = synthetic.lmhead_inputs(N, V, C, seed=7)
+    s = 100.0 / C
+    for r, v in [(0, 500), (77, 999), (200, 40), (201, 33)]:
+        W[v] = synthetic.round_bf16((s * X[r]).astype(np.float32))
+    y[0] = 500  # one peaked row whose target is its peak, one whose target is elsewhere
+    dev = to_dev(X, W, y, binding.GPT_BF16)
+    loss, dX, dW = binding.lmhead_ce(*dev, binding.GPT_BF16)
+    rl, per, rdX, rdW = oracle.lmhead_ce(X, W, y)
+    assert np.isfinite(loss.item())
+    assert abs(loss.item() - rl) <= 2e-2
+    assert cosine(dX.cpu().numpy(), rdX) >= 0.999
+    assert cosine(dW.cpu().numpy(), rdW) >= 0.999
+    monkeypatch.setenv("GPT_HEAD_PIPE", "0")
+    loss0, dX0, dW0 = binding.lmhead_ce(*dev, binding.GPT_BF16)
+    assert loss.item() == loss0.item() and torch.equal(dX, dX0) and torch.equal(dW, dW0)
