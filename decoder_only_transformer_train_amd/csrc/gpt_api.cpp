@@ -95,6 +95,11 @@ struct gpt_ctx {
   float *params, *grads, *m, *v;
   void* shadow;  // bf16 copy of params (bf16 mode) or null
   int32_t* win;  // [N + 1] tokens
+  // two pinned host buffers the batch windows are copied through, so that the
+  // host-to-device copy is asynchronous; stage_ev[k]: the last copy out of buffer k
+  int32_t* stage_host[2] = {nullptr, nullptr};
+  hipEvent_t stage_ev[2] = {nullptr, nullptr};
+  int stage_i = 0;
   std::vector<float*> res;  // L + 1 residual streams
   std::vector<Layer> layers;
   void* lnf;
@@ -823,6 +828,10 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
   chk(hipEventCreateWithFlags(&x->norm_done, hipEventDisableTiming));
   x->adam_ev.assign((size_t)x->L + 2, nullptr);
   for (auto& e : x->adam_ev) chk(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  for (int k = 0; k < 2; ++k) {
+    chk(hipHostMalloc((void**)&x->stage_host[k], (size_t)(x->N + 1) * 4, hipHostMallocDefault));
+    chk(hipEventCreateWithFlags(&x->stage_ev[k], hipEventDisableTiming));
+  }
   if (rc) {
     gpt_destroy(x);
     return rc;
@@ -842,6 +851,13 @@ int gpt_destroy(gpt_ctx* x) {
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : {x->head_fork, x->side_tail, x->hside_tail, x->fwd_start, x->norm_done})
     if (e) (void)hipEventDestroy(e);
+  for (int k = 0; k < 2; ++k) {
+    if (x->stage_ev[k]) {
+      (void)hipEventSynchronize(x->stage_ev[k]);
+      (void)hipEventDestroy(x->stage_ev[k]);
+    }
+    if (x->stage_host[k]) (void)hipHostFree(x->stage_host[k]);
+  }
   if (x->side) (void)hipStreamDestroy(x->side);
   if (x->hside) (void)hipStreamDestroy(x->hside);
   delete x;
@@ -861,8 +877,15 @@ int gpt_make_batch(gpt_ctx* x, const int32_t* host_tokens, int64_t n_tokens, int
   // it holds only AdamW pieces: the update joined everything queued before them)
   if (!x->adam_pending)
     if (int e = join_side(x)) return e;
-  HIPCHK(hipMemcpyAsync(x->win, host_tokens + start, need * 4, hipMemcpyHostToDevice, x->stream));
-  HIPCHK(hipStreamSynchronize(x->stream));
+  // the window goes through a pinned buffer whose previous copy (two batches
+  // ago) has completed, so the copy needs no wait on the stream: the host can
+  // queue the forward while the GPU still runs the previous step
+  const int k = x->stage_i;
+  HIPCHK(hipEventSynchronize(x->stage_ev[k]));
+  std::memcpy(x->stage_host[k], host_tokens + start, (size_t)need * 4);
+  HIPCHK(hipMemcpyAsync(x->win, x->stage_host[k], need * 4, hipMemcpyHostToDevice, x->stream));
+  HIPCHK(hipEventRecord(x->stage_ev[k], x->stream));
+  x->stage_i = k ^ 1;
   return 0;
 }
 

@@ -36,7 +36,8 @@
  *     gpt_get_tensor).  Only calls that are given a non-NULL host result
  *     pointer synchronise the context stream.
  *   - the library never allocates device memory: the caller owns the
- *     arena and every buffer passed in.
+ *     arena and every buffer passed in (gpt_init allocates only host memory,
+ *     including two small pinned buffers for the batch windows).
  */
 #ifndef GPT_MI355X_H
 #define GPT_MI355X_H
@@ -133,7 +134,11 @@ int gpt_destroy(gpt_ctx* ctx);
  * n_tokens int32).  The window starts at `start`.
  * Errors: ERANGE if start < 0, start + B*T + 1 > n_tokens, or any token of the
  * window is outside [0, vocab) (checked on the host before any copy).
- * The copy is synchronous with respect to host_tokens.
+ * The call copies the window out of host_tokens before it returns (the
+ * caller may reuse that memory at once) and does not wait for the GPU: the
+ * window goes through one of two pinned host buffers the context owns
+ * (2 * (B*T+1) int32, allocated by gpt_init), and the host-to-device copy is
+ * queued on the context stream after the work already there.
  */
 int gpt_make_batch(gpt_ctx* ctx, const int32_t* host_tokens, int64_t n_tokens, int64_t start);
 
