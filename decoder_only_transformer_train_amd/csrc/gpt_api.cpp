@@ -112,6 +112,8 @@ struct gpt_ctx {
   int64_t head_skn = 0;
   float* head_tail = nullptr;  // partial sums of the head dW pass's split last round (head_tail_n floats)
   int64_t head_tail_n = 0;
+  float* head_seg = nullptr;  // the head pass 1's vocabulary-segment results (head_seg_n floats; in-model only)
+  int64_t head_seg_n = 0;
   float* ring;
   int ring_wr = 0, ring_rd = 0;
   // backward
@@ -322,6 +324,8 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->dF = cv.take<float>(N * C * 4);
   x->head_tail_n = gk::lmhead_dw_tail_floats(x->dt, (int)N, (int)x->Vp, (int)C);
   x->head_tail = x->head_tail_n ? cv.take<float>(x->head_tail_n * 4) : nullptr;
+  x->head_seg_n = gk::lmhead_fwd_seg_floats(x->dt, (int)N, (int)x->Vp, (int)C);
+  x->head_seg = x->head_seg_n ? cv.take<float>(x->head_seg_n * 4) : nullptr;
   if (head_gemm_mode()) {
     x->head_cols = head_block_cols(N, x->Vp, es);
     x->gchunk = cv.take<void>(N * x->head_cols * es);
@@ -549,7 +553,8 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
          int slot, int* bad, bool fused_dw = false) {
   {
     ProfScope ps(x, "head_fwd", (dF ? 4.0 : 2.0) * N * V * C, 0.0);
-    HIPCHK(gk::lmhead_fwd(dtype, Fin, W, (int)N, (int)V, (int)C, y, scale, tok_loss, tok_lse, dF, bad, x->stream));
+    HIPCHK(gk::lmhead_fwd(dtype, Fin, W, (int)N, (int)V, (int)C, y, scale, tok_loss, tok_lse, dF, bad, x->stream,
+                          x->head_seg, x->head_seg_n));
   }
   HIPCHK(gk::mean_f32(tok_loss, (int)N, loss, ring, slot, x->stream));
   if (!dW) return 0;

@@ -66,6 +66,12 @@ struct Args {
   // writes its partial dW to out + z z_stride, row f at (f - out_row0) C
   int nz, tb, z_rows, out_row0;
   int64_t z_stride;
+  // pass 1 split over vocabulary segments (nz > 1): workgroup z * tb + b takes
+  // fixed block blk0 + b against the streamed rows [z z_rows, (z + 1) z_rows)
+  // and writes the segment's per-row reference, sum and target logit to
+  // seg_s + z n_fix 4 and, when out is set, its unnormalised sum p W to
+  // out + z z_stride; seg_combine_kernel then forms the row results
+  float* seg_s;
 };
 
 // Column groups of 64 dealt to the 4 waves in order: wave w gets ng of them from column c_lo.
@@ -568,7 +574,7 @@ __device__ __forceinline__ float wg_column(float v, float* __restrict__ colv, in
   return MAX ? halves_max(t) : halves_sum(t);
 }
 
-template <int NG, int NQT, int ST, int MODE, bool PIPE>
+template <int NG, int NQT, int ST, int MODE, bool PIPE, bool SEG = false>
 __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
   using L = Lds<NG, NQT, ST, MODE>;
   using SL = Slice<NG>;
@@ -587,6 +593,19 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
   S.ng = __builtin_amdgcn_readfirstlane(ng);  // uniform in the wave: scalar branches
   c_lo = __builtin_amdgcn_readfirstlane(c_lo);
   int bidx = blockIdx.x;
+  const int n_vocab = a.n_str;  // pass 1: targets are checked against the whole vocabulary
+  int y_off = 0;                // pass 1: first vocabulary row of this workgroup's segment
+  if constexpr (MODE == 0 && SEG) {
+    {
+      const int z = bidx / a.tb;
+      bidx -= z * a.tb;
+      y_off = z * a.z_rows;
+      a.str += (int64_t)y_off * a.C;
+      a.n_str = min(a.z_rows, a.n_str - y_off);
+      if (a.out) a.out += (int64_t)z * a.z_stride;
+      a.seg_s += (int64_t)z * a.n_fix * 4;
+    }
+  }
   if constexpr (MODE == 1) {
     if (a.nz > 1) {
       const int z = bidx / a.tb;
@@ -619,11 +638,12 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
     S.yq[qt] = 0;
     if constexpr (MODE == 0) {
       int yy = fr < a.n_fix ? a.y[fr] : 0;
-      if (yy < 0 || yy >= a.n_str) {  // clamped into the row; reported through a.bad
+      if (yy < 0 || yy >= n_vocab) {  // clamped into the row; reported through a.bad
         if (fr < a.n_fix && a.bad) *a.bad = 1;
-        yy = yy < 0 ? 0 : a.n_str - 1;
+        yy = yy < 0 ? 0 : n_vocab - 1;
       }
-      S.yq[qt] = yy;
+      yy -= y_off;  // a target outside this segment is never matched
+      S.yq[qt] = (yy >= 0 && yy < a.n_str) ? yy : -1;
     }
   }
 
@@ -803,6 +823,25 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
     float* orow = a.out + (int64_t)(fr - a.out_row0) * C + c_lo;
     if constexpr (MODE == 0) {
       const float lt = S.l[qt], zt = S.zy[qt];
+      if constexpr (SEG) {  // a vocabulary segment: its reference, sum, target logit and unnormalised sum p W
+        if (w == 0 && g == 0) {
+          a.seg_s[(int64_t)fr * 4] = S.m[qt];
+          a.seg_s[(int64_t)fr * 4 + 1] = lt;
+          a.seg_s[(int64_t)fr * 4 + 2] = zt;
+        }
+        if (a.out == nullptr) continue;
+#pragma unroll
+        for (int ct = 0; ct < NG * 2; ++ct) {
+          if (ct >= S.ng * 2) continue;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int c = ct * 32 + r4 * 8 + g * 4;
+            const f32x16& o = S.O[qt][ct];
+            store4(orow + c, make_float4(o[4 * r4], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]));
+          }
+        }
+        continue;
+      }
       const float lse = (S.m[qt] + hw_log2(lt)) * LN2;
       if (w == 0 && g == 0) {
         a.loss[fr] = lse - zt;
@@ -843,6 +882,59 @@ __global__ __launch_bounds__(256, 1) void head_kernel(Args a) {
         }
       }
     }
+  }
+}
+
+// Pass 1 over vocabulary segments, combined per row in segment order.  With
+// segment z's reference m_z (log2 units), sum l_z of 2^(z log2 e - m_z), target
+// logit zy_z (zero outside the target's segment) and unnormalised sum O_z of
+// p W: M = max_z m_z, f_z = 2^(m_z - M), l = sum_z f_z l_z,
+// lse = (M + log2 l) ln 2, loss = lse - sum_z zy_z and
+// dF = scale ((sum_z f_z O_z) / l - W_y).  One workgroup per row.
+constexpr int MAX_SEG = 8;
+__global__ __launch_bounds__(256) void seg_combine_kernel(const float* __restrict__ seg_s,
+                                                          const float* __restrict__ seg_O, int nvs, int N, int V,
+                                                          int C, const bf16* __restrict__ W,
+                                                          const int32_t* __restrict__ y, float scale,
+                                                          float* __restrict__ loss, float* __restrict__ lse_out,
+                                                          float* __restrict__ dF) {
+  __shared__ float fz[MAX_SEG];
+  __shared__ float inv_l;
+  const int n = blockIdx.x;
+  if (threadIdx.x == 0) {
+    float M = NEG_INF;
+    for (int z = 0; z < nvs; ++z) M = fmaxf(M, seg_s[((int64_t)z * N + n) * 4]);
+    float l = 0.f, zy = 0.f;
+    for (int z = 0; z < nvs; ++z) {
+      const float* sz = seg_s + ((int64_t)z * N + n) * 4;
+      const float f = hw_exp2(sz[0] - M);
+      fz[z] = f;
+      l += f * sz[1];
+      zy += sz[2];
+    }
+    const float lse = (M + hw_log2(l)) * LN2;
+    loss[n] = lse - zy;
+    lse_out[n] = lse;
+    inv_l = 1.f / l;
+  }
+  __syncthreads();
+  if (!dF) return;
+  int yy = y[n];
+  yy = yy < 0 ? 0 : (yy >= V ? V - 1 : yy);  // out-of-range targets were flagged by pass 1
+  const float il = inv_l;
+  for (int c = 4 * (int)threadIdx.x; c < C; c += 1024) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z = 0; z < nvs; ++z) {
+      const float4 o = load4(seg_O + ((int64_t)z * N + n) * C + c);
+      const float f = fz[z];
+      acc.x = fmaf(f, o.x, acc.x);
+      acc.y = fmaf(f, o.y, acc.y);
+      acc.z = fmaf(f, o.z, acc.z);
+      acc.w = fmaf(f, o.w, acc.w);
+    }
+    const float4 wv = load4(W + (int64_t)yy * C + c);
+    store4(dF + (int64_t)n * C + c, make_float4((acc.x * il - wv.x) * scale, (acc.y * il - wv.y) * scale,
+                                                (acc.z * il - wv.z) * scale, (acc.w * il - wv.w) * scale));
   }
 }
 
@@ -1049,7 +1141,7 @@ __global__ __launch_bounds__(256) void head_f32_dw(const float* __restrict__ F, 
 }
 
 // launch a bf16 pass with the register/LDS shape for C
-template <int MODE>
+template <int MODE, bool SEG = false>
 hipError_t launch_bf16_range(const Args& a, int ngmax, dim3 grid, hipStream_t s);
 
 template <int MODE>
@@ -1071,25 +1163,25 @@ hipError_t launch_bf16(const Args& a, hipStream_t s, int max_wgs) {
   return hipSuccess;
 }
 
-template <int MODE>
+template <int MODE, bool SEG>
 hipError_t launch_bf16_range(const Args& a, int ngmax, dim3 grid, hipStream_t s) {
   // the software-pipelined sweep where its registers fit (GPT_HEAD_PIPE=0: the sequential one)
   const char* e = getenv("GPT_HEAD_PIPE");
   const bool pipe = !(e && e[0] == '0');
   switch (ngmax) {
-    case 1: hipLaunchKernelGGL((head_kernel<1, 2, 3, MODE, false>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((head_kernel<2, 2, 3, MODE, false>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((head_kernel<1, 2, 3, MODE, false, SEG>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((head_kernel<2, 2, 3, MODE, false, SEG>), grid, dim3(256), 0, s, a); break;
     case 3:
-      if (pipe) hipLaunchKernelGGL((head_kernel<3, 2, 2, MODE, true>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((head_kernel<3, 2, 2, MODE, false>), grid, dim3(256), 0, s, a);
+      if (pipe) hipLaunchKernelGGL((head_kernel<3, 2, 2, MODE, true, SEG>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((head_kernel<3, 2, 2, MODE, false, SEG>), grid, dim3(256), 0, s, a);
       break;
     case 4:
-      if (pipe) hipLaunchKernelGGL((head_kernel<4, 1, 2, MODE, true>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((head_kernel<4, 1, 2, MODE, false>), grid, dim3(256), 0, s, a);
+      if (pipe) hipLaunchKernelGGL((head_kernel<4, 1, 2, MODE, true, SEG>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((head_kernel<4, 1, 2, MODE, false, SEG>), grid, dim3(256), 0, s, a);
       break;
-    case 5: hipLaunchKernelGGL((head_kernel<5, 1, 1, MODE, false>), grid, dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((head_kernel<6, 1, 1, MODE, false>), grid, dim3(256), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((head_kernel<7, 1, 1, MODE, false>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((head_kernel<5, 1, 1, MODE, false, SEG>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((head_kernel<6, 1, 1, MODE, false, SEG>), grid, dim3(256), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((head_kernel<7, 1, 1, MODE, false, SEG>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1122,7 +1214,36 @@ TailPlan tail_plan(int N, int V, int C) {
   return p;
 }
 
+// Pass 1 over vocabulary segments when its row blocks would leave CUs idle:
+// with fewer than 256 blocks of fixed rows, the vocabulary is cut into nvs
+// segments of vs_rows rows (at most 8, each at least 8 streamed blocks), so
+// that about 256 workgroups run; the segments' partial results (nvs * N *
+// (4 + C) floats) are combined per row afterwards.
+struct SegPlan {
+  int nvs = 1, vs_rows = 0, nfix = 0;
+  int64_t floats = 0;
+};
+SegPlan seg_plan(int N, int V, int C) {
+  SegPlan p;
+  const int ngmax = (C / 64 + 3) / 4;
+  const int rows = ngmax <= 3 ? 64 : 32;
+  const int nfix = (N + rows - 1) / rows;
+  if (nfix >= 256) return p;
+  const int nvs = std::min(std::min(MAX_SEG, (256 + nfix - 1) / nfix), V / (8 * BV));
+  if (nvs < 2) return p;
+  p.vs_rows = ((V + nvs - 1) / nvs + BV - 1) / BV * BV;
+  p.nvs = (V + p.vs_rows - 1) / p.vs_rows;
+  if (p.nvs < 2) return SegPlan{};
+  p.nfix = nfix;
+  p.floats = (int64_t)p.nvs * N * (4 + C);
+  return p;
+}
+
 }  // namespace hd
+
+int64_t lmhead_fwd_seg_floats(int dtype, int N, int V, int C) {
+  return dtype == BF16 ? hd::seg_plan(N, V, C).floats : 0;
+}
 
 int64_t lmhead_dw_tail_floats(int dtype, int N, int V, int C) {
   return dtype == BF16 ? hd::tail_plan(N, V, C).floats : 0;
@@ -1133,7 +1254,8 @@ int64_t lmhead_dw_tail_floats(int dtype, int N, int V, int C) {
 int lmhead_max_embd(int dtype) { return dtype == BF16 ? 7 * 4 * 64 : 1024; }
 
 hipError_t lmhead_fwd(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, float scale,
-                      float* loss, float* lse, float* dF, int* bad, hipStream_t s) {
+                      float* loss, float* lse, float* dF, int* bad, hipStream_t s, float* seg_ws,
+                      int64_t seg_floats) {
   if (N <= 0) return hipSuccess;
   if (V <= 0 || C <= 0 || C % 64 || C > lmhead_max_embd(dtype)) return hipErrorInvalidValue;
   if (dtype == BF16) {
@@ -1151,7 +1273,19 @@ hipError_t lmhead_fwd(int dtype, const void* F, const void* W, int N, int V, int
     a.out = dF;
     a.scale = scale;
     a.bad = bad;
-    return hd::launch_bf16<0>(a, s, 0);
+    const hd::SegPlan sp = seg_ws ? hd::seg_plan(N, V, C) : hd::SegPlan{};
+    if (sp.nvs < 2 || sp.floats > seg_floats) return hd::launch_bf16<0>(a, s, 0);
+    hd::Args b = a;  // segment z of every block of rows, then the per-row combination
+    b.nz = sp.nvs;
+    b.tb = sp.nfix;
+    b.z_rows = sp.vs_rows;
+    b.seg_s = seg_ws;
+    b.out = dF ? seg_ws + (int64_t)sp.nvs * N * 4 : nullptr;
+    b.z_stride = (int64_t)N * C;
+    if (hipError_t e = hd::launch_bf16_range<0, true>(b, (C / 64 + 3) / 4, dim3(sp.nvs * sp.nfix), s)) return e;
+    hipLaunchKernelGGL(hd::seg_combine_kernel, dim3(N), dim3(256), 0, s, seg_ws, b.out, sp.nvs, N, V, C,
+                       (const bf16*)W, y, scale, loss, lse, dF);
+    return hipGetLastError();
   }
   const size_t sh = (size_t)(hd::FR * C + hd::FR * hd::FCH) * 4;
   hipLaunchKernelGGL(hd::head_f32_fwd, dim3((N + hd::FR - 1) / hd::FR), dim3(256), sh, s, (const float*)F,

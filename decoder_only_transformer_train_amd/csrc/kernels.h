@@ -124,8 +124,12 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, c
 // C a multiple of 64, at most lmhead_max_embd(dtype); bf16 needs V*C*2 and
 // N*C*2 below 4 GB (32-bit buffer offsets).
 int lmhead_max_embd(int dtype);
+// seg_ws (bf16, nullable): at least lmhead_fwd_seg_floats(...) floats; with it a pass whose
+// blocks of rows would leave CUs idle runs over vocabulary segments, combined per row after
 hipError_t lmhead_fwd(int dtype, const void* F, const void* W, int N, int V, int C, const int32_t* y, float scale,
-                      float* loss, float* lse, float* dF, int* bad, hipStream_t s);
+                      float* loss, float* lse, float* dF, int* bad, hipStream_t s, float* seg_ws = nullptr,
+                      int64_t seg_floats = 0);
+int64_t lmhead_fwd_seg_floats(int dtype, int N, int V, int C);
 // max_wgs > 0 (bf16): launches of at most that many workgroups.  tail_ws (bf16, nullable): at
 // least lmhead_dw_tail_floats(...) floats; with it the last partial round of W-row blocks is
 // split over the rows of F (partial sums there, then added in order)
