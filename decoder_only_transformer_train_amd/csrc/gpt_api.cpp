@@ -143,6 +143,7 @@ struct gpt_ctx {
   std::vector<gk::RedJob> jobs;
   int nred_blocks = 0;
   uint32_t* keys;
+  uint32_t* keys_tmp = nullptr;
   float *norm_part, *scal;
   int* step_dev;
   bool wte_fresh = true, others_fresh = true, have_fwd = false, fwd_grad = false;
@@ -187,7 +188,7 @@ int check_cfg(const gpt_config* c) {
   }
   if (c->seq > c->max_seq) return fail(GPT_EINVAL, "seq > max_seq");
   const int64_t N = (int64_t)c->batch * c->seq;
-  if (N > 16384) return fail(GPT_EINVAL, "batch * seq must be <= 16384");
+  if (N > gk::SORT_MAX_TOKENS) return fail(GPT_EINVAL, "batch * seq must be <= 262144");
   int shift = 0;
   while ((1 << shift) < N) ++shift;
   if (((uint64_t)c->padded_vocab << shift) > 0xFFFFFFFFull) return fail(GPT_EINVAL, "padded_vocab too large for this batch");
@@ -355,6 +356,7 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->splitk_n = std::max<int64_t>(1, splitk_floats(N, C, x->F));
   x->splitk_ws = cv.take<float>(x->splitk_n * 4);
   x->keys = cv.take<uint32_t>(N * 4);
+  x->keys_tmp = N > 16384 ? cv.take<uint32_t>(N * 4) : nullptr;  // the chunked sort's sorted chunks
   x->norm_part = cv.take<float>(gk::sumsq_blocks(x->P) * 4);
   x->scal = cv.take<float>(64);
   x->step_dev = cv.take<int>(64);
@@ -922,7 +924,7 @@ int gpt_forward_loss(gpt_ctx* x, float loss_scale, float* loss_host) {
     // side stream beside the forward (its keys are read after backward's join)
     HIPCHK(hipEventRecord(x->fwd_start, s));
     HIPCHK(hipStreamWaitEvent(x->side, x->fwd_start, 0));
-    HIPCHK(gk::sort_tokens(x->win, (int)N, x->keys, x->side));
+    HIPCHK(gk::sort_tokens(x->win, (int)N, x->keys, x->keys_tmp, x->side));
   }
   if (x->blk == GPT_BLOCK_RMS_ROPE_SWIGLU) {
     if (int e = forward_variant(x, adam)) return e;

@@ -141,8 +141,10 @@ int64_t lmhead_dw_tail_floats(int dtype, int N, int V, int C);
 hipError_t mean_f32(const float* x, int n, float* out, float* ring, int slot, hipStream_t s);
 
 // ---- embedding backward ----
-// sort (tok[n], n) keys in one workgroup; keys u32 [n]; n <= 16384
-hipError_t sort_tokens(const int32_t* tok, int n, uint32_t* keys, hipStream_t s);
+// sort the (tok[i], i) keys, u32 [n]: one workgroup up to 16384 keys; above that
+// 16384-key chunks side by side in tmp (u32 [n]), merged by rank into keys
+constexpr int SORT_MAX_TOKENS = 262144;
+hipError_t sort_tokens(const int32_t* tok, int n, uint32_t* keys, uint32_t* tmp, hipStream_t s);
 // dwte[tok] += sum of dres rows with that token, in sorted order (deterministic);
 // part: workspace f32 [n][C]
 hipError_t embed_bwd_ws(const uint32_t* keys, int n, const float* dres, int C, float* part,

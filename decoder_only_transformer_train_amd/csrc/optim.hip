@@ -156,13 +156,18 @@ __global__ void init_normal_kernel(float* __restrict__ x, int64_t n, float std, 
   }
 }
 
-// keys[i] = (tok << shift) | position, sorted ascending (bitonic, one workgroup)
+// keys (tok << shift) | position of positions [base, base + n), sorted ascending
+// into keys[base ..] (bitonic over P >= n slots in LDS, one workgroup per chunk:
+// chunk c = blockIdx.x starts at base = c * SORT_MAX)
 constexpr int SORT_MAX = 16384;
-__global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ tok, int n, int shift, int P,
+__global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ tok, int n_total, int shift, int P,
                                                     uint32_t* __restrict__ keys) {
   __shared__ uint32_t sk[SORT_MAX];
   const int t = threadIdx.x;
-  for (int i = t; i < P; i += 1024) sk[i] = (i < n) ? (((uint32_t)tok[i] << shift) | (uint32_t)i) : 0xFFFFFFFFu;
+  const int base = blockIdx.x * SORT_MAX;
+  const int n = min(SORT_MAX, n_total - base);
+  for (int i = t; i < P; i += 1024)
+    sk[i] = (i < n) ? (((uint32_t)tok[base + i] << shift) | (uint32_t)(base + i)) : 0xFFFFFFFFu;
   __syncthreads();
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
@@ -180,7 +185,32 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
       __syncthreads();
     }
   }
-  for (int i = t; i < n; i += 1024) keys[i] = sk[i];
+  for (int i = t; i < n; i += 1024) keys[base + i] = sk[i];
+}
+
+// Merge of nch sorted chunks (chunk c: chunk[c * SORT_MAX ..], its length
+// min(SORT_MAX, n - c * SORT_MAX)) by rank: keys are distinct (they hold the
+// position), so a key's place in the merged order is its index in its own
+// chunk plus the number of smaller keys in each other chunk (a lower bound).
+__global__ __launch_bounds__(256) void merge_rank_kernel(const uint32_t* __restrict__ chunk, int n, int nch,
+                                                         uint32_t* __restrict__ keys) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int c = i / SORT_MAX;
+  const uint32_t k = chunk[i];
+  int rank = i - c * SORT_MAX;
+  for (int d = 0; d < nch; ++d) {
+    if (d == c) continue;
+    const uint32_t* a = chunk + (int64_t)d * SORT_MAX;
+    int lo = 0, hi = min(SORT_MAX, n - d * SORT_MAX);  // first index with a[idx] >= k
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a[mid] < k) lo = mid + 1;
+      else hi = mid;
+    }
+    rank += lo;
+  }
+  keys[rank] = k;
 }
 
 // pass 1: per 64-row chunk of sorted positions, sum each run of equal ids into part[run start]
@@ -298,13 +328,22 @@ hipError_t init_normal(float* x, int64_t n, float std, uint64_t seed, uint64_t o
   return hipGetLastError();
 }
 
-hipError_t sort_tokens(const int32_t* tok, int n, uint32_t* keys, hipStream_t s) {
-  if (n > SORT_MAX) return hipErrorInvalidValue;
+hipError_t sort_tokens(const int32_t* tok, int n, uint32_t* keys, uint32_t* tmp, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n > SORT_MAX_TOKENS) return hipErrorInvalidValue;
   int shift = 0;
   while ((1 << shift) < n) ++shift;
-  int P = 1;
-  while (P < n) P <<= 1;
-  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(1024), 0, s, tok, n, shift, P, keys);
+  if (n <= SORT_MAX) {
+    int P = 1;
+    while (P < n) P <<= 1;
+    hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(1024), 0, s, tok, n, shift, P, keys);
+    return hipGetLastError();
+  }
+  if (!tmp) return hipErrorInvalidValue;
+  // chunks of SORT_MAX sorted side by side into tmp, then merged by rank into keys
+  const int nch = (n + SORT_MAX - 1) / SORT_MAX;
+  hipLaunchKernelGGL(sort_kernel, dim3(nch), dim3(1024), 0, s, tok, n, shift, SORT_MAX, tmp);
+  hipLaunchKernelGGL(merge_rank_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, tmp, n, nch, keys);
   return hipGetLastError();
 }
 

@@ -78,8 +78,9 @@ typedef struct gpt_ctx gpt_ctx; /* opaque, library-owned host object */
  *   vocabulary padding: padded rows stay in the output distribution) that
  *   never occur as input or target.
  *   max_seq T_max rows of the position table; seq T <= T_max; batch B.
- *   B*T at most 16384 (the token sort of the embedding gradient runs in one
- *   workgroup), and padded_vocab * 2^ceil(log2(B*T)) below 2^32.
+ *   B*T at most 262144 (the token sort of the embedding gradient takes
+ *   16384-token chunks, one workgroup each, and merges them), and
+ *   padded_vocab * 2^ceil(log2(B*T)) below 2^32.
  */
 typedef struct {
   int32_t n_layer, n_embd, n_head;

@@ -116,3 +116,10 @@ def test_block_variant_config_checks():
     g2 = configs.TINY_F32
     v = configs.CS336_TINY_F32.with_(d_ff=4 * g2.n_embd)
     assert lib.gpt_arena_bytes(ctypes.byref(v.to_c())) != lib.gpt_arena_bytes(ctypes.byref(g2.to_c()))
+
+
+def test_batch_token_limit():
+    """B*T up to 262144 (the chunked token sort); one more sequence is rejected."""
+    ok = configs.TINY_F32.with_(batch=262144 // configs.TINY_F32.seq)
+    assert binding.arena_bytes(ok) > 0
+    assert binding.arena_bytes(ok.with_(batch=ok.batch + 1)) == 0
