@@ -95,6 +95,36 @@ def test_make_batch_bit_exact_and_errors():
         g.make_batch(bad, 0)
 
 
+def test_make_batch_copies_before_returning():
+    """make_batch returns without waiting for the GPU (the window goes through a pinned
+    staging buffer), yet the caller may overwrite its tokens at once: batches queued
+    back to back, each followed by an overwrite of the caller's array, are the
+    windows that were passed, and a forward queued behind them sees the last one."""
+    announce("make_batch staging")
+    p, _ = tiny_inputs()
+    g = context(CFG, p)
+    stream = synthetic.uniform_tokens(3000, CFG.vocab, seed=11)
+    n = CFG.batch * CFG.seq + 1
+    for start in (0, 5, 333):
+        buf = stream.copy()
+        g.make_batch(buf, start)
+        buf[:] = (buf + 1) % CFG.vocab  # the caller reuses its array straight away
+        x, y = g.get_batch()
+        ex, ey = oracle.make_batch(stream, start, CFG.batch, CFG.seq)
+        np.testing.assert_array_equal(x, ex)
+        np.testing.assert_array_equal(y, ey)
+    # three windows queued without a synchronisation in between (two staging buffers
+    # alternate), the last one feeds the forward
+    for start in (7, 70, 700):
+        buf = stream[start:start + n].copy()
+        g.make_batch(buf, 0)
+        buf[:] = 0
+    loss = g.forward_loss(1.0)
+    x, y = oracle.make_batch(stream, 700, CFG.batch, CFG.seq)
+    ref_loss, _, _ = oracle.loss_and_grads(p, x, y, CFG.n_head)
+    assert abs(loss - ref_loss) <= 1e-4 * ref_loss, (loss, ref_loss)
+
+
 def test_causality_on_gpu():
     announce("causality")
     p, toks = tiny_inputs()
