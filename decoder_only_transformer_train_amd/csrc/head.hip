@@ -490,6 +490,23 @@ __device__ __forceinline__ void pipe_step(char* __restrict__ cur, const char* __
     af[0] = frag_row<NG>(nxt, c32, 0, g);
     af[1] = frag_row<NG>(nxt, c32, 1, g);
     read_quarter<NQT>(part, S.w, lane, pp);  // ahead of the loads into cur, which the compiler may take to alias
+    // The four waves' partials are summed here, before the k-steps, so that only
+    // the sums live through them: summed k-step by k-step the partials stayed
+    // live and the sweep spilled registers inside its loop (8 scratch accesses
+    // per two blocks in pass 1, whose waits also wait on the block loads issued
+    // before them); summed here, 3 in pass 1 and none in pass 2.
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      float4 s4 = pp[qt][0];
+#pragma unroll
+      for (int u = 1; u < 4; ++u) {
+        s4.x += pp[qt][u].x;
+        s4.y += pp[qt][u].y;
+        s4.z += pp[qt][u].z;
+        s4.w += pp[qt][u].w;
+      }
+      q4[qt] = s4;
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 2 < KS) af[(ks + 2) % 3] = frag_row<NG>(nxt, c32, ks + 2, g);
@@ -498,15 +515,6 @@ __device__ __forceinline__ void pipe_step(char* __restrict__ cur, const char* __
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) mma32(zn[qt], af[ks % 3], S.qf[qt][ks]);
       if (ks < NQT) {
-        float4 s4 = pp[ks][0];
-#pragma unroll
-        for (int u = 1; u < 4; ++u) {
-          s4.x += pp[ks][u].x;
-          s4.y += pp[ks][u].y;
-          s4.z += pp[ks][u].z;
-          s4.w += pp[ks][u].w;
-        }
-        q4[ks] = s4;
       } else if (ks < 5 * NQT) {
         const int e = ks - NQT, qt = e >> 2, i = e & 3;
         const float qv = i == 0 ? q4[qt].x : i == 1 ? q4[qt].y : i == 2 ? q4[qt].z : q4[qt].w;
