@@ -294,6 +294,19 @@ __device__ __forceinline__ void read_quarter(const float4* __restrict__ part, in
     for (int v = 0; v < 4; ++v) pp[qt][v] = part[((v * NQT + qt) * 4 + w) * 64 + lane];
 }
 
+
+// Sum of the four waves' partial logit tiles of one quarter.
+__device__ __forceinline__ float4 sum4(const float4 (&p)[4]) {
+  float4 s = p[0];
+#pragma unroll
+  for (int u = 1; u < 4; ++u) {
+    s.x += p[u].x;
+    s.y += p[u].y;
+    s.z += p[u].z;
+    s.w += p[u].w;
+  }
+  return s;
+}
 template <int NG, int NQT, int MODE>
 __device__ __forceinline__ void quarter_p(const float4 (&pp)[NQT][4], uint2* __restrict__ pq,
                                           float* __restrict__ colv, const Args& a, int r0, bool first,
@@ -490,22 +503,16 @@ __device__ __forceinline__ void pipe_step(char* __restrict__ cur, const char* __
     af[0] = frag_row<NG>(nxt, c32, 0, g);
     af[1] = frag_row<NG>(nxt, c32, 1, g);
     read_quarter<NQT>(part, S.w, lane, pp);  // ahead of the loads into cur, which the compiler may take to alias
-    // The four waves' partials are summed here, before the k-steps, so that only
-    // the sums live through them: summed k-step by k-step the partials stayed
-    // live and the sweep spilled registers inside its loop (8 scratch accesses
-    // per two blocks in pass 1, whose waits also wait on the block loads issued
-    // before them); summed here, 3 in pass 1 and none in pass 2.
+    // Pass 1 sums the four waves' partials here, before the k-steps, so that
+    // only the sums live through them: summed one quarter per k-step, the
+    // partials stayed live and pass 1 spilled registers inside its loop (8
+    // scratch accesses per two blocks, whose waits also wait on the block loads
+    // issued before them; 3 this way). Pass 2 keeps the per-k-step sums: it
+    // spills less either way and measured a little faster so.
+    constexpr bool EARLY = MODE == 0;
+    if constexpr (EARLY) {
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      float4 s4 = pp[qt][0];
-#pragma unroll
-      for (int u = 1; u < 4; ++u) {
-        s4.x += pp[qt][u].x;
-        s4.y += pp[qt][u].y;
-        s4.z += pp[qt][u].z;
-        s4.w += pp[qt][u].w;
-      }
-      q4[qt] = s4;
+      for (int qt = 0; qt < NQT; ++qt) q4[qt] = sum4(pp[qt]);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -515,6 +522,7 @@ __device__ __forceinline__ void pipe_step(char* __restrict__ cur, const char* __
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) mma32(zn[qt], af[ks % 3], S.qf[qt][ks]);
       if (ks < NQT) {
+        if constexpr (!EARLY) q4[ks] = sum4(pp[ks]);
       } else if (ks < 5 * NQT) {
         const int e = ks - NQT, qt = e >> 2, i = e & 3;
         const float qv = i == 0 ? q4[qt].x : i == 1 ? q4[qt].y : i == 2 ? q4[qt].z : q4[qt].w;
