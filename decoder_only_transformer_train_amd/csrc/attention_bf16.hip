@@ -396,6 +396,7 @@ struct KvLoads {
   }
 };
 
+template <bool MASK>
 __device__ __forceinline__ void kv_block(const char* __restrict__ rd, char* __restrict__ wr, int j, int nblk,
                                          int qb0, const KvLoads& L, KvState& S, int Tn, int w, int lane) {
   const int g = lane >> 5, c32 = lane & 31;
@@ -405,7 +406,7 @@ __device__ __forceinline__ void kv_block(const char* __restrict__ rd, char* __re
   __syncthreads();
   if (j + ST - 1 < nblk) L.issue(wr, qb0 + j + ST - 1, w, lane);
   const int qb = qb0 + j;
-  if (qb * 64 + 63 < S.klo) return;  // every query of the block is before every key of the tile
+  if (MASK && qb * 64 + 63 < S.klo) return;  // every query of the block is before every key of the tile
   const char* sQ = rd;
   const char* sdO = rd + TILE;
   const float* slse = reinterpret_cast<const float*>(rd + 2 * TILE);
@@ -424,7 +425,7 @@ __device__ __forceinline__ void kv_block(const char* __restrict__ rd, char* __re
     // Rows past the sequence need no mask: their Q and dO rows load as zeros, so
     // their dS = p (dO.V - D) = p (0 - 0) and their P^T dO terms vanish.  Only the
     // causal mask is left, and only on tiles that reach past the diagonal.
-    const bool diag = S.klo + 31 > qb * 64 + qt * 32;
+    const bool diag = MASK && S.klo + 31 > qb * 64 + qt * 32;
     float lv[16], dv[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -468,7 +469,7 @@ __device__ __forceinline__ void dkdv_item(char* smem, int kb, int bh, const bf16
   const int64_t ld = 3 * (int64_t)Cc;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
   const bf16* dob = dO + (int64_t)b * Tn * Cc;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, c32 = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), g = lane >> 5, c32 = lane & 31;
   KvLoads L;
   L.rq = make_rsrc(base, (int64_t)Tn * ld * 2);
   L.rdo = make_rsrc(dob, (int64_t)Tn * Cc * 2);
@@ -499,10 +500,19 @@ __device__ __forceinline__ void dkdv_item(char* smem, int kb, int bh, const bf16
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
     if (s < nblk) L.issue(smem + s * KV_STAGE, qb0 + s, w, lane);
-  int sc = 0;
-  for (int j = 0; j < nblk; ++j) {
+  // Only the first two query blocks reach the diagonal of this workgroup's
+  // keys; the rest run a copy of the block without the mask and its branches,
+  // so that one tile's softmax and the next tile's products share one
+  // straight-line stretch of code the compiler can interleave.
+  int sc = 0, j = 0;
+  for (; j < min(2, nblk); ++j) {
     const int sw = sc == 0 ? ST - 1 : sc - 1;
-    kv_block(smem + sc * KV_STAGE, smem + sw * KV_STAGE, j, nblk, qb0, L, S, Tn, w, lane);
+    kv_block<true>(smem + sc * KV_STAGE, smem + sw * KV_STAGE, j, nblk, qb0, L, S, Tn, w, lane);
+    sc = sc + 1 == ST ? 0 : sc + 1;
+  }
+  for (; j < nblk; ++j) {
+    const int sw = sc == 0 ? ST - 1 : sc - 1;
+    kv_block<false>(smem + sc * KV_STAGE, smem + sw * KV_STAGE, j, nblk, qb0, L, S, Tn, w, lane);
     sc = sc + 1 == ST ? 0 : sc + 1;
   }
   if (S.key < Tn) {
@@ -531,6 +541,7 @@ struct DqState {
   int q[2], qlo[2];
 };
 
+template <bool MASK>
 __device__ __forceinline__ void dq_block(const char* __restrict__ rd, char* __restrict__ wr, int kb, int nkb, rsrc_t r,
                                          const BlockLoad& lk, const BlockLoad& lv, uint32_t blk_bytes, DqState& S,
                                          int w, int lane) {
@@ -544,12 +555,13 @@ __device__ __forceinline__ void dq_block(const char* __restrict__ rd, char* __re
   const char* sK = rd;
   const char* sV = rd + TILE;
   const float cs = LOG2E / 8.0f;
+  // one 32-key half at a time (its K and V fragments serve both query tiles):
+  // scores, dP, dS, then its two 16-key dQ steps
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (kb * 64 > S.qlo[i] + 31) continue;
-    // one 32-key half at a time: scores, dP, dS, then its two 16-key dQ steps
+  for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int i = 0; i < 2; ++i) {
+      if (MASK && kb * 64 > S.qlo[i] + 31) continue;
       f32x16 s, dp;
       zero16(s);
       zero16(dp);
@@ -562,7 +574,7 @@ __device__ __forceinline__ void dq_block(const char* __restrict__ rd, char* __re
       // keys past the sequence come after every valid query
       // Only the causal mask, only where this half reaches past the tile's
       // first query (keys past the sequence load as zeros and contribute nothing).
-      if (kb * 64 + kt * 32 + 31 > S.qlo[i]) {
+      if (MASK && kb * 64 + kt * 32 + 31 > S.qlo[i]) {
         const int rel = S.q[i] - (kb * 64 + kt * 32);  // this lane's query minus the half's first key
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = (crow(e, g) <= rel) ? s[e] : NEG_INF;
@@ -588,7 +600,7 @@ __device__ __forceinline__ void dq_item(char* smem, int qb, int bh, const bf16* 
   const int64_t ld = 3 * (int64_t)Cc;
   const bf16* base = qkv + (int64_t)b * Tn * ld;
   const rsrc_t r = make_rsrc(base, (int64_t)Tn * ld * 2);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, c32 = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), g = lane >> 5, c32 = lane & 31;
   const int q0 = qb * 256;
   DqState S;
   const int qt[2] = {w, 7 - w};
@@ -621,10 +633,16 @@ __device__ __forceinline__ void dq_item(char* smem, int qb, int bh, const bf16* 
       lk.issue(r, smem + s * 2 * TILE, (uint32_t)s * blk_bytes, w);
       lv.issue(r, smem + s * 2 * TILE + TILE, (uint32_t)s * blk_bytes, w);
     }
-  int sc = 0;
-  for (int kb = 0; kb < nkb; ++kb) {
+  // key blocks before the query block's first row need no mask (see dkdv_item)
+  int sc = 0, kb = 0;
+  for (; kb < min(nkb, q0 / 64); ++kb) {
     const int sw = sc == 0 ? ST - 1 : sc - 1;
-    dq_block(smem + sc * 2 * TILE, smem + sw * 2 * TILE, kb, nkb, r, lk, lv, blk_bytes, S, w, lane);
+    dq_block<false>(smem + sc * 2 * TILE, smem + sw * 2 * TILE, kb, nkb, r, lk, lv, blk_bytes, S, w, lane);
+    sc = sc + 1 == ST ? 0 : sc + 1;
+  }
+  for (; kb < nkb; ++kb) {
+    const int sw = sc == 0 ? ST - 1 : sc - 1;
+    dq_block<true>(smem + sc * 2 * TILE, smem + sw * 2 * TILE, kb, nkb, r, lk, lv, blk_bytes, S, w, lane);
     sc = sc + 1 == ST ? 0 : sc + 1;
   }
 #pragma unroll
