@@ -192,6 +192,13 @@ int check_cfg(const gpt_config* c) {
   int shift = 0;
   while ((1 << shift) < N) ++shift;
   if (((uint64_t)c->padded_vocab << shift) > 0xFFFFFFFFull) return fail(GPT_EINVAL, "padded_vocab too large for this batch");
+  // GEMM operands are read through buffer descriptors with 32-bit byte
+  // offsets: the widest activation ([N, 4C], or [N, 2 d_ff] for the gate and
+  // up projections of the variant block) and the embedding must stay below 4 GiB
+  const int64_t es = c->dtype == GPT_BF16 ? 2 : 4, C = c->n_embd;
+  const int64_t wide = c->block == GPT_BLOCK_RMS_ROPE_SWIGLU ? std::max<int64_t>(3 * C, 2 * (int64_t)c->d_ff) : 4 * C;
+  if (N * wide * es >= (1ll << 32) || (int64_t)c->padded_vocab * C * es >= (1ll << 32))
+    return fail(GPT_EINVAL, "an activation or the embedding reaches 4 GiB (32-bit buffer offsets)");
   return 0;
 }
 

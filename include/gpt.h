@@ -80,7 +80,9 @@ typedef struct gpt_ctx gpt_ctx; /* opaque, library-owned host object */
  *   max_seq T_max rows of the position table; seq T <= T_max; batch B.
  *   B*T at most 262144 (the token sort of the embedding gradient takes
  *   16384-token chunks, one workgroup each, and merges them), and
- *   padded_vocab * 2^ceil(log2(B*T)) below 2^32.
+ *   padded_vocab * 2^ceil(log2(B*T)) below 2^32.  GEMM operands are read
+ *   with 32-bit byte offsets: B*T * 4C (variant block: B*T * max(3C, 2 d_ff))
+ *   and padded_vocab * C, times the element size (4 fp32, 2 bf16), below 2^32.
  */
 typedef struct {
   int32_t n_layer, n_embd, n_head;

@@ -123,3 +123,18 @@ def test_batch_token_limit():
     ok = configs.TINY_F32.with_(batch=262144 // configs.TINY_F32.seq)
     assert binding.arena_bytes(ok) > 0
     assert binding.arena_bytes(ok.with_(batch=ok.batch + 1)) == 0
+
+
+def test_operand_4gib_limit():
+    """GEMM operands use 32-bit buffer offsets: a config whose widest activation
+    ([N, 4C], or [N, 2 d_ff] for the variant block) or embedding reaches 4 GiB
+    is rejected; one just below is accepted."""
+    # fp32, N = 262144, C = 1024: [N, 4C] is exactly 4 GiB
+    big = configs.TINY_F32.with_(n_embd=1024, n_head=16, batch=262144 // configs.TINY_F32.seq)
+    assert binding.arena_bytes(big) == 0
+    assert binding.arena_bytes(big.with_(n_embd=960, n_head=15)) > 0
+    # variant block: [N, 2 d_ff] in bf16 at N = 65536
+    v = configs.CS336_TINY_F32.with_(dtype=binding.GPT_BF16, n_embd=64, n_head=1, batch=65536 // 32)
+    assert binding.arena_bytes(v.with_(d_ff=16384)) == 0
+    assert binding.arena_bytes(v.with_(d_ff=16384 - 64)) > 0
+
