@@ -108,6 +108,19 @@ def test_gpt2_124m_ragged_sequence():
     check_step(cfg, stream, seed=5)
 
 
+@pytest.mark.parametrize("B,T", [(2, 1), (3, 17), (1, 65)])
+def test_gpt2_124m_degenerate_sequence_lengths(B, T):
+    # T = 1: each query sees only itself (p = 1 and dP = D, so dQ = dK = 0 and
+    # dV = dO); T = 17: less than one 32-row tile; T = 65: one 64-key block and
+    # one more row.  B*T of 2 to 65 rows: every GEMM tile runs mostly past the
+    # rows, and the LM head's single block of rows takes the vocabulary in
+    # segments combined per row
+    cfg = configs.GPT2_124M.with_(n_layer=1, batch=B, seq=T, max_seq=128)
+    stream = synthetic.zipf_eot_stream(B * T + 1, cfg.vocab, seed=6)
+    announce(f"124M-shaped 1-layer step, B={B} T={T}")
+    check_step(cfg, stream, seed=6)
+
+
 def test_bf16_adamw_update_matches_oracle():
     cfg = configs.GPT2_124M.with_(n_layer=1, batch=1, seq=256, max_seq=256)
     stream = synthetic.zipf_eot_stream(257, cfg.vocab, seed=4)
