@@ -152,15 +152,16 @@ def cpu_baseline(cfg, params, stream, repeats):
             "cpu_model": model, "host_cpus": cores, "blas": blas, "blas_threads": threads}
 
 
-def rate(r):
-    """Algorithmic rate of a profiled class against its roofline."""
+def rate(r, peak_mfma=PEAK_BF16):
+    """Algorithmic rate of a profiled class against its roofline (contractions
+    against the MFMA peak of the context's dtype)."""
     if r["launches"] == 0 or r["ms"] <= 0:
         return None
     avg_ms = r["ms"] / r["launches"]
     if r["flops"] > 0:
         a = r["flops"] / r["launches"] / (avg_ms / 1e3)
-        return {"bound": "mfma", "achieved": round(a / 1e12, 2), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                "frac": round(a / PEAK_BF16, 4), "avg_launch_ms": round(avg_ms, 4), "launches": r["launches"]}
+        return {"bound": "mfma", "achieved": round(a / 1e12, 2), "peak": peak_mfma / 1e12, "unit": "TFLOP/s",
+                "frac": round(a / peak_mfma, 4), "avg_launch_ms": round(avg_ms, 4), "launches": r["launches"]}
     a = r["bytes"] / r["launches"] / (avg_ms / 1e3)
     return {"bound": "hbm", "achieved": round(a / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "frac": round(a / PEAK_HBM, 4), "avg_launch_ms": round(avg_ms, 4), "launches": r["launches"]}
@@ -189,6 +190,7 @@ def bench_model(args, name):
     # the step-1 weights for the CPU oracle baseline (GPT-2 blocks only)
     init_params = None if args.no_cpu_baseline or cfg.block != binding.GPT_BLOCK_GPT2 else g.get_all(binding.PARAM)
     adam = configs.ADAMW
+    peak_mfma = PEAK_F32 if cfg.dtype == binding.GPT_F32 else PEAK_BF16
 
     def step(pos):
         for _ in range(A):
@@ -215,7 +217,7 @@ def bench_model(args, name):
             step(0)
             r = g.profile_end()
             breakdown[cls] = round(r["ms"], 3)
-            rates[cls] = rate(r)
+            rates[cls] = rate(r, peak_mfma)
         g.read_losses()
 
     loops = []
@@ -241,7 +243,7 @@ def bench_model(args, name):
             continue
         g.profile_begin(cls)
         pos = step(pos)
-        more[cls] = rate(g.profile_end())
+        more[cls] = rate(g.profile_end(), peak_mfma)
     g.read_losses()
 
     dt = statistics.median(loops)
@@ -250,8 +252,8 @@ def bench_model(args, name):
     fp32 = cfg.dtype == binding.GPT_F32
     fpt = accounting.training_flops_per_token(cfg.n_layer, cfg.n_embd, T, cfg.padded_vocab,
                                               cfg.d_ff if cfg.block == binding.GPT_BLOCK_RMS_ROPE_SWIGLU else 0)
-    mfu = tps * fpt / (PEAK_F32 if fp32 else PEAK_BF16)
-    roof = rate(prof)
+    mfu = tps * fpt / peak_mfma
+    roof = rate(prof, peak_mfma)
     roof["traffic"] = stored_traffic(args.roofline_kernel, name)
     roof["kernel"] = args.roofline_kernel
     if args.copy_calibration > 0:

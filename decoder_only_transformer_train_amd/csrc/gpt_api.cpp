@@ -109,6 +109,9 @@ struct gpt_ctx {
   void* gchunk = nullptr;  // GEMM form of the head dW: T [N][head_cols], one column block's logit gradient
   int64_t head_cols = 0;
   float* head_skws = nullptr;  // split-K workspace of the head's dW blocks (head_skn floats)
+  // GEMM form of pass 1 (fp32): running row maximum and sum of exp [N][2], target logits [N]
+  float* head_ml = nullptr;
+  float* head_zy = nullptr;
   int64_t head_skn = 0;
   float* head_tail = nullptr;  // partial sums of the head dW pass's split last round (head_tail_n floats)
   int64_t head_tail_n = 0;
@@ -273,6 +276,18 @@ bool head_gemm_mode() {
   const char* e = getenv("GPT_HEAD_DW");
   return e && std::string(e) == "gemm";
 }
+// A model context's choice: fp32 contexts take the GEMM form of both passes
+// unless GPT_HEAD_DW=kernel (their products run on the fp32 MFMAs, the fused
+// kernels' fp32 variant on plain FMAs: the CS336 TinyStories step in fp32,
+// 23.7 ms with the fused kernels, 18.8 ms with the GEMM-form dW, 11.1 ms with
+// both passes, same box); bf16 contexts keep the fused kernels unless
+// GPT_HEAD_DW=gemm (dW only).  The public head entry points size their
+// workspace by head_gemm_mode() alone, so their default stays the kernel.
+bool head_gemm_ctx(int dtype) {
+  const char* e = getenv("GPT_HEAD_DW");
+  if (dtype == GPT_F32) return !(e && std::string(e) == "kernel");
+  return head_gemm_mode();
+}
 
 // Vocabulary columns per block of the GEMM form of the head's weight gradient:
 // the block's logit gradient [N][cols] (T) is about 128 MB, a multiple of 256
@@ -334,15 +349,18 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->head_tail = x->head_tail_n ? cv.take<float>(x->head_tail_n * 4) : nullptr;
   x->head_seg_n = gk::lmhead_fwd_seg_floats(x->dt, (int)N, (int)x->Vp, (int)C);
   x->head_seg = x->head_seg_n ? cv.take<float>(x->head_seg_n * 4) : nullptr;
-  if (head_gemm_mode()) {
+  if (head_gemm_ctx(x->dt)) {
     x->head_cols = head_block_cols(N, x->Vp, es);
     x->gchunk = cv.take<void>(N * x->head_cols * es);
     const int sp = gk::gemm_pick_splits((int)x->head_cols, (int)C, (int)N, 1, 1);
     x->head_skn = sp > 1 ? (int64_t)sp * x->head_cols * C : 0;
     x->head_skws = x->head_skn ? cv.take<float>(x->head_skn * 4) : nullptr;
+    x->head_ml = x->dt == GPT_F32 ? cv.take<float>(N * 8) : nullptr;
+    x->head_zy = x->dt == GPT_F32 ? cv.take<float>(N * 4) : nullptr;
   } else {
     x->gchunk = nullptr;
     x->head_skws = nullptr;
+    x->head_ml = x->head_zy = nullptr;
     x->head_cols = x->head_skn = 0;
   }
   x->loss = cv.take<float>(64);
@@ -557,10 +575,51 @@ int join_side(gpt_ctx* x) {
 // box, 124M step: 20.25 ms with the single kernel against 20.47 ms with the
 // GEMM form, which also moves the [N, V] logit gradient through memory once
 // each way (about 6 GB per step).
+// Pass 1 in GEMM form (fp32 model contexts): the logits of one block of
+// head_cols vocabulary columns at a time go to the block buffer through an
+// fp32 product, and lmhead_block_stats merges the block into each row's
+// maximum and sum of exp (after the last block: log-sum-exp and row loss).
+// For dF each block's logit gradient (exp(z - lse) - onehot) * scale is then
+// formed again by the product's cross-entropy-gradient epilogue and
+// dF += G_blk W_blk.  The same softmax as the fused kernel, on the fp32 MFMAs
+// instead of plain FMAs; the buffer holds one block, never [N, V].
+int head_fwd_gemm(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C,
+                  float scale, float* tok_loss, float* tok_lse, float* dF, int* bad) {
+  const int64_t cols = x->head_cols;
+  const char* Wb = (const char*)W;
+  for (int64_t v0 = 0; v0 < V; v0 += cols) {
+    const int64_t n = std::min(cols, V - v0);
+    gk::Gemm g = mk(x, 0, 0, gk::EPI_STORE, Fin, C, Wb + v0 * C * 4, C, N, n, C, x->gchunk, cols);
+    g.dtype = GPT_F32;
+    if (int e = run_gemm(x, "head_z", g)) return e;
+    HIPCHK(gk::lmhead_block_stats((const float*)x->gchunk, (int)cols, (int)N, (int)n, (int)v0, (int)V, y, x->head_ml,
+                                  x->head_zy, tok_loss, tok_lse, v0 == 0, v0 + n >= V, bad, x->stream));
+  }
+  if (!dF) return 0;
+  for (int64_t v0 = 0; v0 < V; v0 += cols) {
+    const int64_t n = std::min(cols, V - v0);
+    gk::Gemm g = mk(x, 0, 0, gk::EPI_CE_GRAD, Fin, C, Wb + v0 * C * 4, C, N, n, C, x->gchunk, cols);
+    g.dtype = GPT_F32;
+    g.lse = tok_lse;
+    g.rowi = y;
+    g.col0 = (int)v0;
+    g.scale = scale;
+    if (int e = run_gemm(x, "head_dz", g)) return e;
+    g = mk(x, 0, 1, gk::EPI_F32, x->gchunk, cols, Wb + v0 * C * 4, C, N, C, n, dF, C);
+    g.dtype = GPT_F32;
+    g.accumulate = v0 > 0;
+    if (int e = run_gemm(x, "head_df", g)) return e;
+  }
+  return 0;
+}
+
 int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C, float scale,
          float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, int dtype, float* loss, float* ring,
          int slot, int* bad, bool fused_dw = false) {
-  {
+  if (dtype == GPT_F32 && !fused_dw && x->gchunk && x->head_ml && head_gemm_ctx(dtype)) {
+    ProfScope ps(x, "head_fwd", (dF ? 4.0 : 2.0) * N * V * C, 0.0);
+    if (int e = head_fwd_gemm(x, Fin, W, V, y, N, C, scale, tok_loss, tok_lse, dF, bad)) return e;
+  } else {
     ProfScope ps(x, "head_fwd", (dF ? 4.0 : 2.0) * N * V * C, 0.0);
     HIPCHK(gk::lmhead_fwd(dtype, Fin, W, (int)N, (int)V, (int)C, y, scale, tok_loss, tok_lse, dF, bad, x->stream,
                           x->head_seg, x->head_seg_n));
@@ -572,7 +631,7 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
     HIPCHK(hipEventRecord(x->head_fork, x->stream));
     HIPCHK(hipStreamWaitEvent(x->hside, x->head_fork, 0));
   }
-  if (fused_dw || !x->gchunk || !head_gemm_mode()) {
+  if (fused_dw || !x->gchunk || !head_gemm_ctx(dtype)) {
     ProfScope ps(x, "head_dw", 2.0 * N * V * C, 0.0, ds);
     // GPT_HEAD_DW_WGS caps its grid (tuning runs): fewer resident workgroups
     // leave more CUs to the backward running beside it
@@ -805,6 +864,9 @@ int gpt_init(const gpt_config* cfg, void* arena, size_t arena_bytes, void* hip_s
   chk(gk::fill_f32(x->scal, 16, 0.f, s));
   chk(gk::fill_f32((float*)x->step_dev, 16, 0.f, s));
   chk(gk::fill_f32(x->ring, RING, 0.f, s));
+  // the head's block buffer is read past a short last block's columns (k-tile
+  // padding, multiplied by zeros): it must hold finite values from the start
+  if (x->gchunk && x->dt == GPT_F32) chk(gk::fill_f32((float*)x->gchunk, x->N * x->head_cols, 0.f, s));
   const float std_r = 0.02f / std::sqrt(2.0f * (float)x->L);
   uint64_t logical = 0;
   for (auto& d : x->tensors) {

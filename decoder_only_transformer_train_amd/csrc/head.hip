@@ -1255,7 +1255,81 @@ SegPlan seg_plan(int N, int V, int C) {
   return p;
 }
 
+// Row statistics of one block of logit columns for the GEMM form of pass 1
+// (the same softmax, reached a column block at a time): z holds the block's
+// logits [N][ldz] for vocabulary columns v0 .. v0 + n - 1.  One wave per row:
+// each lane keeps a running maximum and sum of exp over its columns, the
+// lanes' pairs are combined by the usual rescaling, and the block's pair is
+// merged into the row's (m, l) the same way (block 0 starts them).  The block
+// holding the row's target records its logit; the last block writes
+// lse = m + ln l and the row loss lse - z_y.  A target outside [0, V) is
+// clamped into the row and sets *bad.
+__device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2) {
+  const float M = fmaxf(m, m2);
+  const float a = m == NEG_INF ? 0.f : l * hw_exp(m - M);
+  const float b = m2 == NEG_INF ? 0.f : l2 * hw_exp(m2 - M);
+  m = M;
+  l = a + b;
+}
+__global__ __launch_bounds__(256) void block_stats_kernel(const float* __restrict__ z, int ldz, int N, int n, int v0,
+                                                          int V, const int32_t* __restrict__ y, float* __restrict__ ml,
+                                                          float* __restrict__ zy, float* __restrict__ loss,
+                                                          float* __restrict__ lse, int first, int last,
+                                                          int* __restrict__ bad) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const float* zr = z + (int64_t)row * ldz;
+  float m = NEG_INF, l = 0.f;
+  for (int c = lane * 4; c < n; c += 256) {
+    if (c + 3 < n) {
+      const float4 v = *reinterpret_cast<const float4*>(zr + c);
+      ml_merge(m, l, v.x, 1.f);
+      ml_merge(m, l, v.y, 1.f);
+      ml_merge(m, l, v.z, 1.f);
+      ml_merge(m, l, v.w, 1.f);
+    } else {
+      for (int k = c; k < n; ++k) ml_merge(m, l, zr[k], 1.f);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+    ml_merge(m, l, m2, l2);
+  }
+  if (lane != 0) return;
+  float* mlr = ml + 2 * (int64_t)row;
+  float rm = m, rl = l;
+  if (!first) {
+    rm = mlr[0];
+    rl = mlr[1];
+    ml_merge(rm, rl, m, l);
+  }
+  int t = y[row];
+  if (t < 0 || t >= V) {
+    if (bad) *bad = 1;
+    t = t < 0 ? 0 : V - 1;
+  }
+  if (t >= v0 && t < v0 + n) zy[row] = zr[t - v0];
+  if (last) {
+    const float s = rm + hw_log2(rl) * LN2;
+    lse[row] = s;
+    loss[row] = s - zy[row];
+  } else {
+    mlr[0] = rm;
+    mlr[1] = rl;
+  }
+}
+
 }  // namespace hd
+
+hipError_t lmhead_block_stats(const float* z, int ldz, int N, int n, int v0, int V, const int32_t* y, float* ml,
+                              float* zy, float* loss, float* lse, int first, int last, int* bad, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  if (n <= 0 || ldz < n || ((uintptr_t)z & 15) || (ldz & 3)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(hd::block_stats_kernel, dim3((N + 3) / 4), dim3(256), 0, s, z, ldz, N, n, v0, V, y, ml, zy,
+                     loss, lse, first, last, bad);
+  return hipGetLastError();
+}
 
 int64_t lmhead_fwd_seg_floats(int dtype, int N, int V, int C) {
   return dtype == BF16 ? hd::seg_plan(N, V, C).floats : 0;

@@ -130,6 +130,14 @@ hipError_t lmhead_fwd(int dtype, const void* F, const void* W, int N, int V, int
                       float* loss, float* lse, float* dF, int* bad, hipStream_t s, float* seg_ws = nullptr,
                       int64_t seg_floats = 0);
 int64_t lmhead_fwd_seg_floats(int dtype, int N, int V, int C);
+// Pass 1 a block of vocabulary columns at a time (fp32 GEMM form): given the
+// block's logits z [N][ldz] (columns v0 .. v0 + n - 1, ldz a multiple of 4, z
+// 16-byte aligned), merge each row's maximum and sum of exp into ml [N][2]
+// (first: start them), record the target's logit in zy [N] from the block
+// holding it, and on the last block write lse [N] (natural log) and
+// loss [N] = lse - z_y.  Targets outside [0, V) are clamped and set *bad.
+hipError_t lmhead_block_stats(const float* z, int ldz, int N, int n, int v0, int V, const int32_t* y, float* ml,
+                              float* zy, float* loss, float* lse, int first, int last, int* bad, hipStream_t s);
 // max_wgs > 0 (bf16): launches of at most that many workgroups.  tail_ws (bf16, nullable): at
 // least lmhead_dw_tail_floats(...) floats; with it the last partial round of W-row blocks is
 // split over the rows of F (partial sums there, then added in order)

@@ -49,6 +49,32 @@ def test_tiny_fp32_full_step_matches_oracle():
     assert not np.any(g.get("h0.fc.w", binding.GRAD))
 
 
+def test_fp32_head_forms_agree_with_oracle(monkeypatch):
+    """fp32 contexts run the LM head as column-block fp32 MFMA products (the
+    default); the fused plain-FMA kernels stay selectable with GPT_HEAD_DW=kernel
+    (read when the context is laid out and at each step).  Both match the oracle
+    and each other."""
+    announce("tiny fp32 step, both forms of the LM head")
+    p, toks = tiny_inputs(seed=3)
+    x, y = oracle.make_batch(toks, 0, CFG.batch, CFG.seq)
+    ref_loss, _, ref = oracle.loss_and_grads(p, x, y, CFG.n_head)
+    out = {}
+    for form in ("gemm", "kernel"):
+        if form == "kernel":
+            monkeypatch.setenv("GPT_HEAD_DW", "kernel")
+        g = context(CFG, p)
+        g.make_batch(toks, 0)
+        loss = g.forward_loss(1.0)
+        g.backward()
+        out[form] = (loss, g.token_losses(), g.get_all(binding.GRAD))
+        g.close()
+        assert abs(loss - ref_loss) <= 1e-4 * abs(ref_loss), form
+        for k in ref:
+            assert rel_err(out[form][2][k], ref[k]) <= 1e-4, (form, k)
+    np.testing.assert_allclose(out["gemm"][1], out["kernel"][1], rtol=1e-5, atol=1e-6)
+    assert rel_err(out["gemm"][2]["wte"], out["kernel"][2]["wte"]) <= 1e-5
+
+
 def test_two_steps_match_oracle():
     announce("tiny two steps")
     p, toks = tiny_inputs(seed=3, n_extra=CFG.batch * CFG.seq)
