@@ -280,13 +280,17 @@ bool head_gemm_mode() {
 // unless GPT_HEAD_DW=kernel (their products run on the fp32 MFMAs, the fused
 // kernels' fp32 variant on plain FMAs: the CS336 TinyStories step in fp32,
 // 23.7 ms with the fused kernels, 18.8 ms with the GEMM-form dW, 11.1 ms with
-// both passes, same box); bf16 contexts keep the fused kernels unless
-// GPT_HEAD_DW=gemm (dW only).  The public head entry points size their
-// workspace by head_gemm_mode() alone, so their default stays the kernel.
-bool head_gemm_ctx(int dtype) {
+// both passes, same box).  bf16 contexts take the GEMM form of dW where the
+// fused dW kernel has no software-pipelined sweep (C above 1024: GPT-2 1.5B,
+// 244.8-245.0 -> 241.2-241.5 ms per step, same box) and keep the fused kernels
+// at C <= 1024, where they are faster; GPT_HEAD_DW=gemm or =kernel forces
+// either.  The public head entry points size their workspace by
+// head_gemm_mode() alone, so their default stays the kernel.
+bool head_gemm_ctx(int dtype, int64_t C) {
   const char* e = getenv("GPT_HEAD_DW");
-  if (dtype == GPT_F32) return !(e && std::string(e) == "kernel");
-  return head_gemm_mode();
+  if (e && std::string(e) == "kernel") return false;
+  if (e && std::string(e) == "gemm") return true;
+  return dtype == GPT_F32 || C > 1024;
 }
 
 // Vocabulary columns per block of the GEMM form of the head's weight gradient:
@@ -349,7 +353,7 @@ int64_t carve(gpt_ctx* x, void* base) {
   x->head_tail = x->head_tail_n ? cv.take<float>(x->head_tail_n * 4) : nullptr;
   x->head_seg_n = gk::lmhead_fwd_seg_floats(x->dt, (int)N, (int)x->Vp, (int)C);
   x->head_seg = x->head_seg_n ? cv.take<float>(x->head_seg_n * 4) : nullptr;
-  if (head_gemm_ctx(x->dt)) {
+  if (head_gemm_ctx(x->dt, C)) {
     x->head_cols = head_block_cols(N, x->Vp, es);
     x->gchunk = cv.take<void>(N * x->head_cols * es);
     const int sp = gk::gemm_pick_splits((int)x->head_cols, (int)C, (int)N, 1, 1);
@@ -616,7 +620,7 @@ int head_fwd_gemm(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const i
 int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y, int64_t N, int64_t C, float scale,
          float* tok_loss, float* tok_lse, float* dF, float* dW, int dW_acc, int dtype, float* loss, float* ring,
          int slot, int* bad, bool fused_dw = false) {
-  if (dtype == GPT_F32 && !fused_dw && x->gchunk && x->head_ml && head_gemm_ctx(dtype)) {
+  if (dtype == GPT_F32 && !fused_dw && x->gchunk && x->head_ml && head_gemm_ctx(dtype, C)) {
     ProfScope ps(x, "head_fwd", (dF ? 4.0 : 2.0) * N * V * C, 0.0);
     if (int e = head_fwd_gemm(x, Fin, W, V, y, N, C, scale, tok_loss, tok_lse, dF, bad)) return e;
   } else {
@@ -631,7 +635,7 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
     HIPCHK(hipEventRecord(x->head_fork, x->stream));
     HIPCHK(hipStreamWaitEvent(x->hside, x->head_fork, 0));
   }
-  if (fused_dw || !x->gchunk || !head_gemm_ctx(dtype)) {
+  if (fused_dw || !x->gchunk || !head_gemm_ctx(dtype, C)) {
     ProfScope ps(x, "head_dw", 2.0 * N * V * C, 0.0, ds);
     // GPT_HEAD_DW_WGS caps its grid (tuning runs): fewer resident workgroups
     // leave more CUs to the backward running beside it
