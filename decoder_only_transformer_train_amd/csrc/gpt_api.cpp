@@ -280,17 +280,18 @@ bool head_gemm_mode() {
 // unless GPT_HEAD_DW=kernel (their products run on the fp32 MFMAs, the fused
 // kernels' fp32 variant on plain FMAs: the CS336 TinyStories step in fp32,
 // 23.7 ms with the fused kernels, 18.8 ms with the GEMM-form dW, 11.1 ms with
-// both passes, same box).  bf16 contexts take the GEMM form of dW where the
-// fused dW kernel has no software-pipelined sweep (C above 1024: GPT-2 1.5B,
-// 244.8-245.0 -> 241.2-241.5 ms per step, same box) and keep the fused kernels
-// at C <= 1024, where they are faster; GPT_HEAD_DW=gemm or =kernel forces
-// either.  The public head entry points size their workspace by
+// both passes, same box).  bf16 contexts take the GEMM form of dW from
+// C = 1024 up (same box each: GPT-2 350M, C = 1024, 28.28-28.31 -> 27.87-27.94
+// ms per step; GPT-2 1.5B, C = 1600, where the fused dW kernel has no
+// software-pipelined sweep, 244.8-245.0 -> 241.2-241.5 ms) and keep the fused
+// kernels at C = 768 (GPT-2 124M: 18.43-18.50 ms against 19.19-19.22 ms with
+// the GEMM form); GPT_HEAD_DW=gemm or =kernel forces either.  The public head entry points size their workspace by
 // head_gemm_mode() alone, so their default stays the kernel.
 bool head_gemm_ctx(int dtype, int64_t C) {
   const char* e = getenv("GPT_HEAD_DW");
   if (e && std::string(e) == "kernel") return false;
   if (e && std::string(e) == "gemm") return true;
-  return dtype == GPT_F32 || C > 1024;
+  return dtype == GPT_F32 || C >= 1024;
 }
 
 // Vocabulary columns per block of the GEMM form of the head's weight gradient:
