@@ -13,13 +13,17 @@ Zipf(1.1) stream with end-of-text separators) -> forward + head/CE ->
 backward, then AdamW, all through libgpt.so.  W warm-up steps, then R loops
 of K timed steps, each between torch.cuda.synchronize() calls; the line
 reports the median loop.  It carries tokens/s, MFU, the roofline of the
-dominant kernel (timed with HIP events on the library's stream in the last
-step of the last loop), the rates of a few more kernel classes (timed in
-extra steps after the loops).  The dominant kernel is the LM head's first
-pass (loss, log-sum-exp and dF: 3.20 ms of the step's 21.95 ms of kernel time
-when each kernel runs alone; then the second pass, the tied dW, 3.10 ms in its
-two launches, and attention backward, 1.41 ms) and the fp64 CPU oracle timed on the GPU's own
-step-1 weights and window.
+dominant kernel, the rates of a few more kernel classes (timed in extra steps
+after the loops) and the fp64 CPU oracle timed on the GPU's own step-1 weights
+and window.  The dominant kernel is the fused LM head + cross-entropy, taken as
+one unit: its two passes are the two largest kernels of the step when each runs
+alone (GPT-2 124M: pass 2, the tied dW, 2.51 ms in its two launches; pass 1,
+loss, log-sum-exp and dF, 2.27 ms; then attention backward, 1.40 ms, of 20.6 ms
+of serialised kernel time).  Pass 1 is timed with HIP events in the last step
+of the last loop, pass 2 (which runs beside the backward on a stream of its
+own, sharing the CUs) in a step of its own; achieved = the head's algorithmic
+FLOPs, 6*N*V_pad*C per step (its logit recompute not counted), over the sum of
+both passes' times.  Each pass's own rate is listed under kernel_rates.
 
 The roofline's "traffic" (HBM bytes per launch of that kernel) comes from
 profiles/traffic.json, written from two rocprofv3 --pmc runs (FETCH_SIZE,
@@ -47,10 +51,10 @@ PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
 # kernel classes the library can time (each GEMM class times its main kernel only)
 PROFILE_CLASSES = ["gemm_qkv_fwd", "gemm_proj_fwd", "gemm_fc_fwd", "gemm_mlpproj_fwd", "gemm_dgrad_mlp",
                    "gemm_dgrad_attn", "gemm_wgrad_mlp", "gemm_wgrad_attn", "attn_fwd", "attn_bwd",
-                   "layernorm_fwd", "layernorm_bwd", "head_fwd", "head_dz", "head_dw",
+                   "layernorm_fwd", "layernorm_bwd", "head_fwd", "head_dz", "head_dw", "head_dw_dz",
                    "bias_colsum", "param_reduce", "embed_bwd", "adamw"]
 # further classes reported beside the dominant one (one extra step each)
-MORE_CLASSES = ["head_dw", "attn_bwd", "attn_fwd", "gemm_fc_fwd", "layernorm_bwd", "adamw"]
+MORE_CLASSES = ["head_fwd", "head_dw", "attn_bwd", "attn_fwd", "gemm_fc_fwd", "layernorm_bwd", "adamw"]
 METRIC = "train tokens/sec + MFU, GPT-2 124M B=16 T=1024 bf16, 1×MI355X"
 
 WORKLOADS = {
@@ -167,6 +171,17 @@ def rate(r, peak_mfma=PEAK_BF16):
             "frac": round(a / PEAK_HBM, 4), "avg_launch_ms": round(avg_ms, 4), "launches": r["launches"]}
 
 
+def head_operator(fwd, dw, dw_dz):
+    """The LM head + cross-entropy of one step as one unit: pass 1 (loss, lse
+    and dF: 4*N*V*C) and pass 2 (the tied dW: 2*N*V*C) summed over all their
+    launches.  The GEMM form of pass 2 adds the product that recomputes each
+    vocabulary block's logits (head_dw_dz): its time counts, its FLOPs do not,
+    like the recompute inside the fused pass-2 kernel."""
+    return {"ms": fwd["ms"] + dw["ms"] + dw_dz["ms"], "launches": 1,
+            "flops": fwd["flops"] + dw["flops"], "bytes": 0.0,
+            "parts": fwd["launches"] + dw["launches"] + dw_dz["launches"]}
+
+
 def copy_calibration(nbytes):
     import torch
     n = nbytes // 4
@@ -230,21 +245,26 @@ def bench_model(args, name):
             # barrier packets around each launch (a few us of idle GPU each), which the other
             # steps are spared
             if rep == R - 1 and i == K - 1:
-                g.profile_begin(args.roofline_kernel)
+                g.profile_begin("head_fwd" if args.roofline_kernel == "lm_head" else args.roofline_kernel)
             pos = step(pos)
         torch.cuda.synchronize()
         loops.append(time.perf_counter() - t0)
         if rep == R - 1:
             prof = g.profile_end()
     losses = g.read_losses()
-    more = {}
-    for cls in MORE_CLASSES:
-        if cls == args.roofline_kernel:
+    more, raw = {}, {}
+    for cls in MORE_CLASSES + (["head_dw_dz"] if args.roofline_kernel == "lm_head" else []):
+        if cls == args.roofline_kernel or (cls == "head_fwd" and args.roofline_kernel == "lm_head"):
             continue
         g.profile_begin(cls)
         pos = step(pos)
-        more[cls] = rate(g.profile_end(), peak_mfma)
+        raw[cls] = g.profile_end()
+        if cls in MORE_CLASSES:
+            more[cls] = rate(raw[cls], peak_mfma)
     g.read_losses()
+    if args.roofline_kernel == "lm_head":
+        more = {"head_fwd": rate(prof, peak_mfma), **more}
+        prof = head_operator(prof, raw["head_dw"], raw["head_dw_dz"])
 
     dt = statistics.median(loops)
     tokens = K * A * B * T
@@ -254,8 +274,16 @@ def bench_model(args, name):
                                               cfg.d_ff if cfg.block == binding.GPT_BLOCK_RMS_ROPE_SWIGLU else 0)
     mfu = tps * fpt / peak_mfma
     roof = rate(prof, peak_mfma)
-    roof["traffic"] = stored_traffic(args.roofline_kernel, name)
-    roof["kernel"] = args.roofline_kernel
+    if args.roofline_kernel == "lm_head":
+        parts = [stored_traffic(k, name) for k in ("head_fwd", "head_dw")]
+        roof["traffic"] = (sum(parts) if None not in parts and not raw["head_dw_dz"]["launches"]
+                           else None)
+        roof["kernel"] = ("lm_head: LM head + cross-entropy, pass 1 (loss, lse, dF) and pass 2 "
+                          "(head weight gradient dW) of one step as one unit; recomputed logits not counted")
+        roof["timed_spans"] = prof["parts"]
+    else:
+        roof["traffic"] = stored_traffic(args.roofline_kernel, name)
+        roof["kernel"] = args.roofline_kernel
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
     out = {
@@ -347,7 +375,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true")
     # the dominant kernel class of the step (largest share of the step's kernel time)
-    ap.add_argument("--roofline-kernel", default="head_fwd", choices=PROFILE_CLASSES)
+    # (lm_head: the fused LM head + cross-entropy as one operator, all its launches)
+    ap.add_argument("--roofline-kernel", default="lm_head", choices=["lm_head"] + PROFILE_CLASSES)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="after the timed steps, copy this many bytes device-to-device once")
     args = ap.parse_args()

@@ -655,7 +655,7 @@ int head(gpt_ctx* x, const void* Fin, const void* W, int64_t V, const int32_t* y
     g.rowi = y;
     g.col0 = (int)v0;
     g.scale = scale;
-    if (int e = run_gemm(x, "head_dz", g, ds)) return e;
+    if (int e = run_gemm(x, "head_dw_dz", g, ds)) return e;
     g = mk(x, 1, 1, gk::EPI_F32, x->gchunk, cols, Fin, C, n, C, N, dW + v0 * C, C);
     g.dtype = dtype;
     g.accumulate = dW_acc;
